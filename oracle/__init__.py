@@ -1,0 +1,19 @@
+"""CPU oracle for the KDA forward pass (double precision).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library (``gated_delta_rule_17_amd``) and never imports it.
+
+Two independent forms:
+
+* :func:`recurrent` -- oracle R, the token-by-token recurrence written in
+  plain C (``kda_recurrence.c``), parallel over the independent
+  (batch, head) sequences with OpenMP.
+* :func:`chunkwise` -- oracle C, the chunkwise-parallel form in NumPy
+  (``chunkwise.py``), used to pin R on small inputs and to document the
+  reading of the truncated chunkwise derivation.
+
+Both take the state transposed, ``H = S^T`` with shape ``[B, H, Dk, Dv]``.
+"""
+from .recurrence import recurrent, build_oracle_library, oracle_threads  # noqa: F401
+from .chunkwise import chunkwise  # noqa: F401
