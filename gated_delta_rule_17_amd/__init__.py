@@ -1,0 +1,192 @@
+"""MI355X-native Kimi Delta Attention (KDA) forward: Python binding.
+
+A thin ctypes layer over the C ABI of ``libkda.so`` (declared in
+``include/kda.h``).  It only marshals arguments: tensors are passed as device
+pointers, the stream is torch's current HIP stream, and every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, importing works but every call raises.
+
+Entry points (same names as the C ABI):
+  kda_recurrent_step(q, k, v, g, beta, state, o=None, scale=None, mode=None)
+  kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None,
+                o=None, chunk=64, scale=None, mode=None, workspace=None)
+  kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
+
+GATE_CHANNEL, GATE_SCALAR, GATE_NONE = 0, 1, 2
+F32, BF16 = 0, 1
+_MODE_NAMES = {"channel": GATE_CHANNEL, "scalar": GATE_SCALAR, "none": GATE_NONE}
+STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
+          3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_WORKSPACE", 5: "KDA_ERROR_HIP"}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded C-ABI library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gated_delta_rule_17_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.kda_recurrent_step.restype = i
+    L.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    L.kda_chunk_fwd_workspace_size.restype = sz
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i,
+                                vp, sz, vp]
+    L.kda_chunk_fwd.restype = i
+    L.kda_status_string.argtypes = [i]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_version.restype = i
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions ``include/kda.h`` declares."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _mode_of(g, mode):
+    if mode is None:
+        if g is None:
+            return GATE_NONE
+        return GATE_CHANNEL if g.dim() == 4 else GATE_SCALAR
+    if isinstance(mode, str):
+        return _MODE_NAMES[mode]
+    return int(mode)
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] = None,
+                       mode=None, out_dtype=None):
+    """Recurrent form over T >= 1 tokens; updates ``state`` in place.
+
+    q, k [B,T,H,Dk] and v [B,T,H,Dv] (float32 or bfloat16), g float32 log-gates
+    ([B,T,H,Dk] channel / [B,T,H] scalar / None), beta float32 [B,T,H],
+    state float32 [B,H,Dk,Dv].  Returns o [B,T,H,Dv] (``out_dtype``, default the
+    dtype of q; ignored when ``o`` is given).
+    """
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    m = _mode_of(g, mode)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    _check_dev("state", state, torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    _check_dev("o", o, None, (B, T, H, Dv))
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                  _ptr(o), B, T, H, Dk, Dv, float(scale), m, _dtype_code(q),
+                                  _dtype_code(o), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_recurrent_step")
+    return o
+
+
+def kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype) -> int:
+    if isinstance(mode, str):
+        mode = _MODE_NAMES[mode]
+    return int(lib().kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, int(mode), int(dtype)))
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
+                  chunk: int = 64, scale: Optional[float] = None, mode=None, workspace=None,
+                  output_final_state: bool = True, out_dtype=None):
+    """Chunkwise form.  Returns (o, final_state).
+
+    ``final_state`` may be passed (it may be ``initial_state`` itself); if it
+    is None and ``output_final_state`` is true a new float32 tensor is made.
+    ``workspace`` (a uint8 device tensor) is allocated when not given.
+    """
+    torch = _torch()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    m = _mode_of(g, mode)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    _check_dev("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev("final_state", final_state, torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    _check_dev("o", o, None, (B, T, H, Dv))
+    dt = _dtype_code(q)
+    need = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, m, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                             _ptr(final_state), _ptr(o), B, T, H, Dk, Dv, int(chunk), float(scale),
+                             m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state

@@ -1,0 +1,106 @@
+// C ABI entry points of the KDA library: argument validation and dispatch.
+// Every check runs on the host before any HIP call, so a bad argument returns
+// a status and enqueues nothing.
+#include <stdint.h>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+kda_status check_common(const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, const void* o, int B, int T, int H, int Dk,
+                        int Dv, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype)
+{
+    if (B < 1 || H < 1 || T < 0) return KDA_ERROR_INVALID_VALUE;
+    if (mode != KDA_GATE_CHANNEL && mode != KDA_GATE_SCALAR && mode != KDA_GATE_NONE)
+        return KDA_ERROR_INVALID_VALUE;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
+    if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_dim(Dk) || !supported_dim(Dv)) return KDA_ERROR_NOT_SUPPORTED;
+    // sizes must fit the 64-bit index arithmetic of the kernels comfortably
+    const double tok = (double)B * (double)T * (double)H;
+    if (tok * (double)(Dk > Dv ? Dk : Dv) > 9.0e15) return KDA_ERROR_INVALID_VALUE;
+    if ((double)B * H > 2.0e9) return KDA_ERROR_INVALID_VALUE;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+        if (mode != KDA_GATE_NONE && !g) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(o))
+            return KDA_ERROR_MISALIGNED;
+        if (g && !aligned16(g)) return KDA_ERROR_MISALIGNED;
+    }
+    return KDA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s)
+{
+    switch (s) {
+        case KDA_SUCCESS: return "KDA_SUCCESS";
+        case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+        case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+        case KDA_ERROR_MISALIGNED: return "KDA_ERROR_MISALIGNED";
+        case KDA_ERROR_WORKSPACE: return "KDA_ERROR_WORKSPACE";
+        case KDA_ERROR_HIP: return "KDA_ERROR_HIP";
+    }
+    return "KDA_ERROR_UNKNOWN";
+}
+
+int kda_version(void) { return 10000; }
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, int B, int T, int H,
+                              int Dk, int Dv, float scale, kda_gate_mode mode, kda_dtype dtype,
+                              kda_dtype o_dtype, void* stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Dk, Dv, mode, dtype, o_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if (T == 0) return KDA_SUCCESS;
+    if (!state) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned16(state)) return KDA_ERROR_MISALIGNED;
+    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, scale, mode, dtype, o_dtype};
+    hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_gate_mode mode, kda_dtype dtype)
+{
+    (void)mode;
+    if (B < 1 || H < 1 || T <= 0) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return kda::chunk_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         void* o, int B, int T, int H, int Dk, int Dv, int chunk, float scale,
+                         kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Dk, Dv, mode, dtype, o_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    if (Dk != Dv) return KDA_ERROR_NOT_SUPPORTED;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERROR_MISALIGNED;
+    const size_t need = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype);
+    if (T > 0) {
+        if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
+    }
+    if (T == 0 && !final_state) return KDA_SUCCESS;
+    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk,
+                     scale, mode, dtype, o_dtype, workspace, workspace_bytes};
+    hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,683 @@
+// Chunkwise-parallel KDA forward (prefill / training forward).
+//
+// GeekNews #31925, section "Chunkwise KDA: recasting the recurrence as matrix
+// products" with "Cumulative decay and provisional errors" and "Restoring
+// causal dependence"; F29 course outline, Objectives ("pseudo-values from a
+// triangular solve; log-space decay ratios", "WY/UT form").
+//
+// Per (batch, head) and chunk of C tokens i = 0..C-1 entering with state H
+// (transposed, Dk x Dv):
+//   G_i   = g_0 + ... + g_i                       cumulative log-decay per key channel
+//   A_ij  = beta_i sum_c k_i[c] k_j[c] exp(G_i[c] - G_j[c])    j < i
+//   T     = (I + A)^-1                            (unit lower triangular)
+//   W     = T Diag(beta) (K * exp(G)),  U = T Diag(beta) V    (pseudo-values: E = U - W H)
+//   o     = (Q~ * exp(G)) H + Aqk E,  Aqk_ij = sum_c q~_i[c] k_j[c] exp(G_i[c] - G_j[c]), j <= i
+//   H'    = Diag(exp G_last) H + (K * exp(G_last - G))^T E
+//
+// Two kernels:
+//  chunk_prepare  one workgroup per (b, h, chunk), fully parallel.  Everything
+//                 that does not depend on the incoming state: G, A and Aqk on
+//                 the matrix cores, T by blocked forward substitution in LDS,
+//                 W and U on the matrix cores.  Writes one record per chunk.
+//  chunk_state    one workgroup per (b, h, 16 value columns), sequential over
+//                 the chunks.  The 16 state columns live in matrix-core
+//                 accumulators (float32) for the whole sequence; per chunk:
+//                 E = U - W H, o = Qg H + Aqk E, H = gl * H + Kr^T E.
+//
+// Overflow-free decay ratios.  exp(G_i - G_j) is split into factors that
+// each stay <= 1 using reference tokens at 16-token block boundaries: for
+// blocks J < I, exp(G_i - G_s(I)) * exp(G_s(I) - G_e(J)) * exp(G_e(J) - G_j)
+// with s = first and e = last token of a block.  Inside a diagonal block the
+// key side exp(G_s(I) - G_j) >= 1 grows with the decay inside the block; any
+// key channel whose decay across one block exceeds kRangeMax is removed from
+// that diagonal block's matrix-core product and added exactly, term by term,
+// on the vector units instead.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+constexpr float kRangeMax = 80.f;
+
+template <int C, int DK, int DV, typename OT>
+struct CS {
+    static constexpr int NB = C / 16;                 // 16-token blocks per chunk
+    static constexpr int CP = C < 32 ? 32 : C;        // token dim padded to the 32-wide k step
+    static constexpr int DKP = DK < 32 ? 32 : DK;     // key dim padded likewise
+    static constexpr int PAD = 16 / (int)sizeof(OT);  // LDS row padding (16 bytes)
+    static constexpr int SK = DKP + PAD;              // stride of [token][channel] operands
+    static constexpr int SKF = DKP + 4;               // stride of the float32 key array
+    static constexpr int SC = CP + PAD;               // stride of [channel][token] operands
+    static constexpr int SA = C + 4;                  // stride of float32 A / T
+    static constexpr int NT = 256;
+    static constexpr int NSEG = NT / DKP;             // threads per key channel (prefix sums)
+    static constexpr int TPS = C / NSEG;              // tokens per thread
+    static constexpr int NPAIR = NB * (NB - 1) / 2;
+    static constexpr bool SPLIT = sizeof(OT) == 2;    // bf16: precise operands are hi/lo pairs
+    static constexpr int NP = SPLIT ? 2 : 1;
+    static constexpr int SZ = (int)sizeof(OT);
+    // per-chunk record, elements per part
+    static constexpr size_t W_N = (size_t)C * DKP;    // -W      [C][DKP]   precise
+    static constexpr size_t Q_N = (size_t)C * DKP;    // Qg      [C][DKP]   precise
+    static constexpr size_t KR_N = (size_t)DK * CP;   // Kr^T    [DK][CP]   precise
+    static constexpr size_t AQ_N = (size_t)C * CP;    // Aqk     [C][CP]    precise
+    static constexpr size_t U_N = (size_t)DV * C;     // U^T     [DV][C]    float32
+    // LDS, stage A: Qk (plain), Qq and Kd (precise), Kk (float32)
+    static constexpr int STAGE_A = (1 + 2 * NP) * C * SK * SZ + C * SKF * 4;
+    // stage B: BkT, BvT (precise), A and T (float32); T as a precise operand aliases A
+    static constexpr int TB_BYTES = NP * C * SC * SZ;
+    static constexpr int AS_BYTES = (C * SA * 4 > TB_BYTES) ? C * SA * 4 : TB_BYTES;
+    static constexpr int STAGE_B = NP * (DK + DV) * SC * SZ + AS_BYTES + C * SA * 4;
+    static constexpr int BIG = STAGE_A > STAGE_B ? STAGE_A : STAGE_B;
+    static_assert(NSEG >= 1 && TPS >= 1 && NSEG * TPS == C, "shape");
+    static_assert((C * SK * SZ) % 16 == 0 && (C * SC * SZ) % 16 == 0, "alignment");
+};
+
+// The per-chunk records inside the workspace: one array per record field
+// (hi and lo parts of precise operands are separate arrays of equal layout).
+template <int C, int DK, int DV, typename OT>
+struct WsLayout {
+    using S = CS<C, DK, DV, OT>;
+    OT *wneg_h, *wneg_l, *qg_h, *qg_l, *krt_h, *krt_l, *aqk_h, *aqk_l;
+    float *ut, *gl;
+    __host__ __device__ WsLayout(void* base, size_t nrec) {
+        char* p = (char*)base;
+        auto take = [&](size_t elems, size_t sz) { char* r = p; p += nrec * elems * sz; return r; };
+        wneg_h = (OT*)take(S::W_N, S::SZ);
+        wneg_l = S::SPLIT ? (OT*)take(S::W_N, S::SZ) : wneg_h;
+        qg_h = (OT*)take(S::Q_N, S::SZ);
+        qg_l = S::SPLIT ? (OT*)take(S::Q_N, S::SZ) : qg_h;
+        krt_h = (OT*)take(S::KR_N, S::SZ);
+        krt_l = S::SPLIT ? (OT*)take(S::KR_N, S::SZ) : krt_h;
+        aqk_h = (OT*)take(S::AQ_N, S::SZ);
+        aqk_l = S::SPLIT ? (OT*)take(S::AQ_N, S::SZ) : aqk_h;
+        ut = (float*)take(S::U_N, 4);
+        gl = (float*)p;
+    }
+    static size_t bytes(size_t nrec) {
+        return nrec * (S::NP * (S::W_N + S::Q_N + S::KR_N + S::AQ_N) * S::SZ + S::U_N * 4 + DK * 4);
+    }
+    __device__ PArr<OT> wneg(size_t rec) const { return {wneg_h + rec * S::W_N, wneg_l + rec * S::W_N}; }
+    __device__ PArr<OT> qg(size_t rec) const { return {qg_h + rec * S::Q_N, qg_l + rec * S::Q_N}; }
+    __device__ PArr<OT> krt(size_t rec) const { return {krt_h + rec * S::KR_N, krt_l + rec * S::KR_N}; }
+    __device__ PArr<OT> aqk(size_t rec) const { return {aqk_h + rec * S::AQ_N, aqk_l + rec * S::AQ_N}; }
+};
+
+template <typename OT>
+__device__ __forceinline__ void store_op(OT* p, float x) { io<OT>::store(p, x); }
+
+// ---------------------------------------------------------------------------
+// chunk_prepare
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV, typename OT>
+__global__ void __launch_bounds__(256)
+chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
+              const float* __restrict__ g, const float* __restrict__ beta,
+              int T, int H, int NC, float scale, int mode, void* __restrict__ ws, size_t nrec)
+{
+    using S = CS<C, DK, DV, OT>;
+    constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SKF = S::SKF, SC = S::SC,
+                  SA = S::SA, NP = S::NP;
+    constexpr int NSEG = S::NSEG, TPS = S::TPS;
+
+    __shared__ __align__(16) char big[S::BIG];
+    __shared__ float sb[C];
+    __shared__ float segtot[NSEG][DKP];
+    __shared__ float Gs[NB][DKP], Ge[NB][DKP], GLs[DKP];
+    __shared__ float eS[NB][DKP], eL[NB][DKP];
+    __shared__ float fpair[S::NPAIR > 0 ? S::NPAIR : 1][DKP];
+    __shared__ unsigned char flag[NB][DKP];
+    __shared__ int anyflag;
+
+    const int c_idx = blockIdx.x;        // chunk
+    const int bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
+    const int t0 = c_idx * C;
+    const int L = min(C, T - t0);       // valid tokens
+    const size_t rec = (size_t)bh * NC + c_idx;
+    const WsLayout<C, DK, DV, OT> W(ws, nrec);
+    const PArr<OT> Wq = W.qg(rec), Wkr = W.krt(rec), Waq = W.aqk(rec), Wwn = W.wneg(rec);
+    float* Wut = W.ut + rec * S::U_N;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+
+    // stage-A arrays
+    OT* Qk = (OT*)big;                                             // [C][SK] plain
+    const PArr<OT> Qq{Qk + C * SK, Qk + 2 * C * SK};               // [C][SK] precise
+    const PArr<OT> Kd{Qk + (1 + NP) * C * SK, Qk + (2 + NP) * C * SK};  // [C][SK] precise
+    float* Kk = (float*)(Qk + (1 + 2 * NP) * C * SK);              // [C][SKF] float32
+
+    if (tid == 0) anyflag = 0;
+    for (int i = tid; i < C; i += S::NT) sb[i] = (i < L) ? beta[((size_t)b * T + t0 + i) * H + h] : 0.f;
+
+    // ---- cumulative log-decay: thread (seg, c) owns tokens seg*TPS .. +TPS-1 of channel c
+    const int c = tid % DKP, seg = tid / DKP;
+    const int i0 = seg * TPS;
+    float G[TPS];
+    {
+        float run = 0.f;
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = i0 + u;
+            float gv = 0.f;
+            if (i < L && c < DK) {
+                const size_t tok = ((size_t)b * T + t0 + i) * H + h;
+                if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + c];
+                else if (mode == KDA_GATE_SCALAR) gv = g[tok];
+            }
+            run += gv;
+            G[u] = run;
+        }
+        segtot[seg][c] = run;
+    }
+    __syncthreads();
+    {
+        float off = 0.f;
+        for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2][c];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) G[u] += off;
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = i0 + u;
+            if ((i & 15) == 0) Gs[i >> 4][c] = G[u];
+            if ((i & 15) == 15) Ge[i >> 4][c] = G[u];
+            if (i == C - 1) GLs[c] = G[u];
+        }
+    }
+    __syncthreads();
+    // ---- per-block factors, gl, range flags
+    for (int p = tid; p < NB * DKP; p += S::NT) {
+        const int I = p / DKP, cc = p % DKP;
+        eS[I][cc] = __expf(Gs[I][cc]);
+        eL[I][cc] = __expf(GLs[cc] - Ge[I][cc]);
+        const bool bad = (Gs[I][cc] - Ge[I][cc]) > kRangeMax;
+        flag[I][cc] = bad ? 1 : 0;
+        if (bad) atomicOr(&anyflag, 1);
+    }
+    for (int p = tid; p < S::NPAIR * DKP; p += S::NT) {
+        const int pi = p / DKP, cc = p % DKP;
+        // pair index pi enumerates (I, J), J < I, row by row: I=1:J=0; I=2:J=0,1; ...
+        int I = 1, base = 0;
+        while (base + I <= pi) { base += I; ++I; }
+        const int J = pi - base;
+        fpair[pi][cc] = __expf(Gs[I][cc] - Ge[J][cc]);
+    }
+    for (int cc = tid; cc < DK; cc += S::NT) W.gl[rec * DK + cc] = __expf(GLs[cc]);
+    __syncthreads();
+
+    // ---- element-wise operands
+    float kreg[TPS], egreg[TPS];
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const int i = i0 + u;
+        const int I = i >> 4;
+        float kv = 0.f, qv = 0.f;
+        if (i < L && c < DK) {
+            const size_t tok = ((size_t)b * T + t0 + i) * H + h;
+            kv = io<OT>::load(k + tok * DK + c);
+            qv = io<OT>::load(q + tok * DK + c) * scale;
+        }
+        const float x = __expf(G[u] - Gs[I][c]);          // <= 1
+        const float kk = kv * __expf(Ge[I][c] - G[u]);    // <= |k|
+        const float kd = flag[I][c] ? 0.f : kv * __expf(Gs[I][c] - G[u]);  // >= |k|, bounded
+        store_op(Qk + i * SK + c, kv * x);
+        store_p(Qq, i * SK + c, qv * x);
+        store_p(Kd, i * SK + c, kd);
+        Kk[i * SKF + c] = kk;
+        const float eg = x * eS[I][c];                     // exp(G_i) <= 1
+        kreg[u] = kv;
+        egreg[u] = eg;
+        store_p(Wq, i * DKP + c, qv * eg);
+        if (c < DK) store_p(Wkr, c * CP + i, kk * eL[I][c]);
+    }
+    if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
+        for (int p = tid; p < DK * (CP - C); p += S::NT) {
+            const int cc = p / (CP - C), i = C + p % (CP - C);
+            store_p(Wkr, cc * CP + i, 0.f);
+        }
+        for (int p = tid; p < C * (CP - C); p += S::NT) {
+            const int i = p / (CP - C), j = C + p % (CP - C);
+            store_p(Waq, i * CP + j, 0.f);
+        }
+    }
+    __syncthreads();
+
+    // ---- A^T and Aqk^T tiles on the matrix cores: tile (J, I), J <= I
+    // lane result: A[i = 16I + r][j = 16J + 4gq + u]
+    constexpr int NTILE = NB * (NB + 1) / 2;
+    constexpr int TPW = (NTILE + 3) / 4;
+    f32x4 accA[TPW], accQ[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+        accA[s] = zero4();
+        accQ[s] = zero4();
+        const int tix = wave + 4 * s;
+        if (tix < NTILE) {
+            int I = 0, base = 0;
+            while (base + I + 1 <= tix) { base += I + 1; ++I; }
+            const int J = tix - base;
+            const bool diag = (I == J);
+            const int pi = diag ? 0 : I * (I - 1) / 2 + J;
+#pragma unroll
+            for (int ks = 0; ks < DKP / 32; ++ks) {
+                const int ch = 32 * ks + 8 * gq;
+                PFrag<OT> key;
+                if (diag) {
+                    key = Kd.frag((16 * J + r) * SK + ch);
+                } else {
+                    float t8[8];
+                    const f32x4 k0 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch);
+                    const f32x4 k1 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        t8[e] = k0[e] * fpair[pi][ch + e];
+                        t8[4 + e] = k1[e] * fpair[pi][ch + 4 + e];
+                    }
+                    key.from_f32(t8);
+                }
+                Frag<OT> bk;
+                bk.load(Qk + (16 * I + r) * SK + ch);
+                const PFrag<OT> bq = Qq.frag((16 * I + r) * SK + ch);
+                accA[s] = mma(key.h, bk, accA[s]);
+                accQ[s] = mma3(key, bq, accQ[s]);
+            }
+        }
+    }
+    __syncthreads();   // stage-A operands are dead from here on
+
+    // stage-B layout (aliases stage A)
+    OT* bkt_h = (OT*)big;
+    const PArr<OT> BkT{bkt_h, bkt_h + DK * SC};                    // [DK][SC] beta_j k_j exp(G_j)
+    OT* bvt_h = bkt_h + NP * DK * SC;
+    const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j
+    float* As = (float*)(bvt_h + NP * DV * SC);                    // [C][SA]  A (strictly lower, with beta)
+    float* Ts = (float*)((char*)As + S::AS_BYTES);                 // [C][SA]  T = (I + A)^-1
+    const PArr<OT> Tb{(OT*)As, (OT*)As + C * SC};                  // [C][SC]  T as an operand (after the solve)
+    const bool fallback = anyflag != 0;
+    float* Aq32 = Ts;                          // Aqk staging when the exact fallback runs
+
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) {
+        const int tix = wave + 4 * s;
+        if (tix < NTILE) {
+            int I = 0, base = 0;
+            while (base + I + 1 <= tix) { base += I + 1; ++I; }
+            const int J = tix - base;
+            const int i = 16 * I + r;
+            const int j0 = 16 * J + 4 * gq;
+            f32x4 av = accA[s] * sb[i];
+            f32x4 qv = accQ[s];
+            if (I == J) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (j0 + u >= i) av[u] = 0.f;
+                    if (j0 + u > i) qv[u] = 0.f;
+                }
+            }
+            *reinterpret_cast<f32x4*>(As + i * SA + j0) = av;
+            if (fallback) *reinterpret_cast<f32x4*>(Aq32 + i * SA + j0) = qv;
+            else store4_p(Waq, i * CP + j0, qv);
+        }
+    }
+    // zero the strictly upper blocks of A (and of the Aqk staging / record)
+    for (int p = tid; p < C * C; p += S::NT) {
+        const int i = p / C, j = p % C;
+        if ((j >> 4) > (i >> 4)) {
+            As[i * SA + j] = 0.f;
+            if (fallback) Aq32[i * SA + j] = 0.f;
+            else store_p(Waq, i * CP + j, 0.f);
+        }
+    }
+    // beta_j k_j exp(G_j) and beta_j v_j, transposed ([channel][token])
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const int i = i0 + u;
+        if (c < DK) store_p(BkT, c * SC + i, sb[i] * kreg[u] * egreg[u]);
+    }
+    for (int p = tid; p < C * DV; p += S::NT) {
+        const int i = p / DV, n = p % DV;
+        float vv = 0.f;
+        if (i < L) vv = io<OT>::load(v + (((size_t)b * T + t0 + i) * H + h) * DV + n);
+        store_p(BvT, n * SC + i, sb[i] * vv);
+    }
+    if (CP > C) {
+        for (int p = tid; p < DK * (CP - C); p += S::NT) {
+            const int row = p / (CP - C), i = C + p % (CP - C);
+            store_p(BkT, row * SC + i, 0.f);
+        }
+        for (int p = tid; p < DV * (CP - C); p += S::NT) {
+            const int row = p / (CP - C), i = C + p % (CP - C);
+            store_p(BvT, row * SC + i, 0.f);
+        }
+    }
+    __syncthreads();
+
+    if (fallback) {
+        // exact diagonal-block terms for key channels whose decay across the block
+        // exceeds kRangeMax (their factorised key side was zeroed above)
+        for (int p = tid; p < NB * DK; p += S::NT) {
+            const int I = p / DK, cc = p % DK;
+            if (!flag[I][cc]) continue;
+            float gi[16], ki[16], qi[16];
+            float run = 0.f;
+            for (int u = 0; u < 16; ++u) {
+                const int i = 16 * I + u;
+                float gv = 0.f, kv = 0.f, qv = 0.f;
+                if (i < L) {
+                    const size_t tok = ((size_t)b * T + t0 + i) * H + h;
+                    if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
+                    else if (mode == KDA_GATE_SCALAR) gv = g[tok];
+                    kv = io<OT>::load(k + tok * DK + cc);
+                    qv = io<OT>::load(q + tok * DK + cc) * scale;
+                }
+                run += gv;
+                gi[u] = run; ki[u] = kv; qi[u] = qv;
+            }
+            for (int ii = 0; ii < 16; ++ii) {
+                const int i = 16 * I + ii;
+                for (int jj = 0; jj <= ii; ++jj) {
+                    const int j = 16 * I + jj;
+                    const float w = __expf(gi[ii] - gi[jj]) * ki[jj];
+                    atomicAdd(&Aq32[i * SA + j], qi[ii] * w);
+                    if (jj < ii) atomicAdd(&As[i * SA + j], sb[i] * ki[ii] * w);
+                }
+            }
+        }
+        __syncthreads();
+        for (int p = tid; p < C * C; p += S::NT) {
+            const int i = p / C, j = p % C;
+            store_p(Waq, i * CP + j, Aq32[i * SA + j]);
+        }
+        __syncthreads();
+    }
+
+    // ---- T = (I + A)^-1: diagonal 16x16 blocks by a column sweep (one wave each)
+    if (wave < NB) {
+        const int I = wave;
+        float arow[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) arow[jj] = As[(16 * I + r) * SA + 16 * I + jj];
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = (4 * gq + u == r) ? 1.f : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 15; ++jj) {
+            float xj[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xj[u] = __shfl(x[u], jj, 16);
+            if (r > jj) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] -= arow[jj] * xj[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u] = x[u];
+    }
+    // strictly upper blocks of T are zero
+    for (int p = tid; p < C * C; p += S::NT) {
+        const int i = p / C, j = p % C;
+        if ((j >> 4) > (i >> 4)) Ts[i * SA + j] = 0.f;
+    }
+    __syncthreads();
+    // off-diagonal blocks, one block-diagonal at a time:
+    // T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
+    for (int d = 1; d < NB; ++d) {
+        const int I = d + wave, J = wave;
+        if (I < NB) {
+            f32x4 P = zero4();
+            for (int Kb = J; Kb < I; ++Kb) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const float a = As[(16 * I + r) * SA + 16 * Kb + 4 * s + gq];
+                    const float bb = Ts[(16 * Kb + 4 * s + gq) * SA + 16 * J + r];
+                    P = mma4(a, bb, P);
+                }
+            }
+            // lane holds P[4gq + u][r]; contract k = 4gq' + u in step u
+            f32x4 R = zero4();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float a = Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u];
+                R = mma4(a, P[u], R);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Ts[(16 * I + 4 * gq + u) * SA + 16 * J + r] = -R[u];
+        }
+        __syncthreads();
+    }
+    // T as a precise operand, row-major [i][j], padded columns zero (overwrites A)
+    for (int p = tid; p < C * CP; p += S::NT) {
+        const int i = p / CP, j = p % CP;
+        store_p(Tb, i * SC + j, j < C ? Ts[i * SA + j] : 0.f);
+    }
+    __syncthreads();
+
+    // ---- W^T = (Diag(beta) K exp(G))^T T^T  and  U = T Diag(beta) V
+    {
+        constexpr int MW = DK / 16;          // channel tiles of W^T
+        constexpr int NWT = MW * NB;         // W tiles
+        constexpr int NUT = NB * (DV / 16);  // U tiles
+        for (int tix = wave; tix < NWT + NUT; tix += 4) {
+            if (tix < NWT) {
+                const int m = tix / NB, I = tix % NB;     // channels 16m.., tokens 16I..
+                f32x4 acc = zero4();
+                const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
+                for (int ks = 0; ks < nks; ++ks)
+                    acc = mma3(BkT.frag((16 * m + r) * SC + 32 * ks + 8 * gq),
+                               Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq), acc);
+                // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
+                store4_p(Wwn, (16 * I + r) * DKP + 16 * m + 4 * gq, -acc);
+            } else {
+                const int t2 = tix - NWT;
+                const int I = t2 % NB, nn = t2 / NB;      // tokens 16I.., value cols 16nn..
+                f32x4 acc = zero4();
+                const int nks = (16 * I + 15) / 32 + 1;
+                for (int ks = 0; ks < nks; ++ks)
+                    acc = mma3(Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq),
+                               BvT.frag((16 * nn + r) * SC + 32 * ks + 8 * gq), acc);
+                // lane holds U[16I + 4gq + u][16nn + r] -> U^T[n][i..i+3]
+                Vec4<float>::store(Wut + (16 * nn + r) * C + 16 * I + 4 * gq, acc);
+            }
+        }
+        if (DKP > DK) {   // padded key channels of -W are zero
+            for (int p = tid; p < C * (DKP - DK); p += S::NT) {
+                const int i = p / (DKP - DK), cc = DK + p % (DKP - DK);
+                store_p(Wwn, i * DKP + cc, 0.f);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_state: sequential pass over the chunks of one (b, h), 16 value columns
+// (h0 and hT may be the same buffer: each workgroup reads exactly the state
+// entries it later writes, and reads them first)
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV, typename OT, typename OUT>
+__global__ void __launch_bounds__(256)
+chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
+            int T, int H, int BH, int NC, const void* __restrict__ ws, size_t nrec)
+{
+    using S = CS<C, DK, DV, OT>;
+    constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SC = S::SC, NP = S::NP;
+    constexpr int NCT = DV / 16;          // column tiles per head
+    constexpr int MH = DK / 16;           // 16-row tiles of the state
+    constexpr int MHW = (MH + 3) / 4;     // state tiles per wave
+
+    __shared__ __align__(16) OT HTs[NP * 16 * SK];   // H^T tile [n][c] (precise operand)
+    __shared__ __align__(16) OT ETs[NP * 16 * SC];   // E^T tile [n][j] (precise operand)
+    const PArr<OT> HT{HTs, HTs + 16 * SK};
+    const PArr<OT> ET{ETs, ETs + 16 * SC};
+
+    // XCD-aware mapping: all column tiles of one head on the same XCD (id % 8),
+    // so the chunk records they all read are shared through that XCD's L2.
+    const int id = blockIdx.x;
+    const int xcd = id & 7, slot = id >> 3;
+    const int bh = (slot / NCT) * 8 + xcd;
+    const int ct = slot % NCT;
+    if (bh >= BH) return;
+    const int b = bh / H, h = bh - b * H;
+    const int n0 = 16 * ct;
+    const WsLayout<C, DK, DV, OT> W(const_cast<void*>(ws), nrec);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+
+    // zero the operand tiles (padding stays zero)
+    for (int p = tid; p < NP * 16 * SK; p += 256) store_op(HTs + p, 0.f);
+    for (int p = tid; p < NP * 16 * SC; p += 256) store_op(ETs + p, 0.f);
+    __syncthreads();
+
+    f32x4 hacc[MHW];
+#pragma unroll
+    for (int s = 0; s < MHW; ++s) {
+        hacc[s] = zero4();
+        const int mt = wave + 4 * s;
+        if (mt < MH && h0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                hacc[s][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r];
+        }
+        if (mt < MH) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+    }
+    __syncthreads();
+
+    for (int cidx = 0; cidx < NC; ++cidx) {
+        const size_t rec = (size_t)bh * NC + cidx;
+        const int t0 = cidx * C;
+        const int L = min(C, T - t0);
+        const PArr<OT> wneg = W.wneg(rec), qg = W.qg(rec), krt = W.krt(rec), aqk = W.aqk(rec);
+        const float* ut = W.ut + rec * S::U_N;
+        const float* gl = W.gl + rec * DK;
+
+        f32x4 oacc = zero4();
+        if (wave < NB) {
+            // E = U - W H for tokens 16*wave ..
+            f32x4 e = Vec4<float>::load(ut + (n0 + r) * C + 16 * wave + 4 * gq);
+#pragma unroll
+            for (int ks = 0; ks < DKP / 32; ++ks)
+                e = mma3(wneg.frag((16 * wave + r) * DKP + 32 * ks + 8 * gq),
+                         HT.frag(r * SK + 32 * ks + 8 * gq), e);
+            // o^T (state part): rows n, tokens 16*wave ..
+#pragma unroll
+            for (int ks = 0; ks < DKP / 32; ++ks)
+                oacc = mma3(HT.frag(r * SK + 32 * ks + 8 * gq),
+                            qg.frag((16 * wave + r) * DKP + 32 * ks + 8 * gq), oacc);
+            store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
+        }
+        __syncthreads();
+        if (wave < NB) {
+            // o^T += E^T Aqk^T (intra-chunk part); Aqk[i][j] = 0 for j > i
+            const int nks = (16 * wave + 15) / 32 + 1;
+            for (int ks = 0; ks < nks; ++ks)
+                oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq),
+                            aqk.frag((16 * wave + r) * CP + 32 * ks + 8 * gq), oacc);
+            // lane holds o^T[n = 4gq + u][i = 16*wave + r]
+            const int i = 16 * wave + r;
+            if (i < L) {
+                OUT* op = o + (((size_t)b * T + t0 + i) * H + h) * DV + n0 + 4 * gq;
+                Vec4<OUT>::store(op, oacc);
+            }
+        }
+        // H = Diag(gl) H + Kr^T E
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = wave + 4 * s;
+            if (mt < MH) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * mt + 4 * gq);
+                hacc[s] *= gv;
+#pragma unroll
+                for (int ks = 0; ks < CP / 32; ++ks)
+                    hacc[s] = mma3(krt.frag((16 * mt + r) * CP + 32 * ks + 8 * gq),
+                                   ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
+                store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+            }
+        }
+        __syncthreads();
+    }
+    if (hT) {
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = wave + 4 * s;
+            if (mt < MH) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r] = hacc[s][u];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+template <int C, int DK, int DV, typename OT>
+static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
+{
+    const int BH = a.B * a.H;
+    const int NC = (a.T + C - 1) / C;
+    const size_t nrec = (size_t)BH * NC;
+    if (NC > 0) {
+        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(NC, BH), dim3(256), 0, s,
+                           (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
+                           a.T, a.H, NC, a.scale, (int)a.mode, a.ws, nrec);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int groups = (BH + 7) / 8;
+    const dim3 grid(groups * 8 * (DV / 16));
+    if (a.o_dtype == KDA_F32)
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float>), grid, dim3(256), 0, s,
+                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
+    else
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(256), 0, s,
+                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
+    return hipGetLastError();
+}
+
+template <int C, int D, typename OT>
+static size_t ws3(int B, int T, int H)
+{
+    const int NC = (T + C - 1) / C;
+    return WsLayout<C, D, D, OT>::bytes((size_t)B * H * NC);
+}
+
+template <typename OT>
+static hipError_t dispatch_chunk(const ChunkArgs& a, hipStream_t s)
+{
+#define KDA_CASE(CC, DD) \
+    if (a.chunk == CC && a.Dk == DD) return launch3<CC, DD, DD, OT>(a, s);
+    KDA_CASE(16, 16) KDA_CASE(16, 32) KDA_CASE(16, 64) KDA_CASE(16, 128)
+    KDA_CASE(32, 16) KDA_CASE(32, 32) KDA_CASE(32, 64) KDA_CASE(32, 128)
+    KDA_CASE(64, 16) KDA_CASE(64, 32) KDA_CASE(64, 64) KDA_CASE(64, 128)
+#undef KDA_CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename OT>
+static size_t ws_dispatch(int B, int T, int H, int D, int chunk)
+{
+#define KDA_CASE(CC, DD) \
+    if (chunk == CC && D == DD) return ws3<CC, DD, OT>(B, T, H);
+    KDA_CASE(16, 16) KDA_CASE(16, 32) KDA_CASE(16, 64) KDA_CASE(16, 128)
+    KDA_CASE(32, 16) KDA_CASE(32, 32) KDA_CASE(32, 64) KDA_CASE(32, 128)
+    KDA_CASE(64, 16) KDA_CASE(64, 32) KDA_CASE(64, 64) KDA_CASE(64, 128)
+#undef KDA_CASE
+    return 0;
+}
+
+size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype)
+{
+    if (Dk != Dv) return 0;
+    if (dtype == KDA_BF16) return ws_dispatch<bf16_t>(B, T, H, Dk, chunk);
+    return ws_dispatch<float>(B, T, H, Dk, chunk);
+}
+
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s)
+{
+    if (a.dtype == KDA_BF16) return dispatch_chunk<bf16_t>(a, s);
+    return dispatch_chunk<float>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,40 @@
+// Host-side interfaces between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "kda.h"
+
+namespace kda {
+
+struct RecArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    float* state; void* o;
+    int B, T, H, Dk, Dv;
+    float scale;
+    kda_gate_mode mode;
+    kda_dtype dtype;      // q, k, v
+    kda_dtype o_dtype;    // o
+};
+
+struct ChunkArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta;
+    const float* h0; float* hT; void* o;
+    int B, T, H, Dk, Dv, chunk;
+    float scale;
+    kda_gate_mode mode;
+    kda_dtype dtype;      // q, k, v
+    kda_dtype o_dtype;    // o
+    void* ws; size_t ws_bytes;
+};
+
+hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);
+
+// Workspace layout of the chunk path (bytes); 0 if unsupported.
+size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
+hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,176 @@
+// Recurrent (token-by-token) KDA forward: the decode kernel.
+//
+// GeekNews #31925, section "Fused recurrent kernel for decode": the state of
+// one sequence and head stays on chip while the tokens are processed in
+// order, each token doing decay -> prediction (a reduction over the key
+// dimension) -> residual -> rank-1 write -> read (a second reduction).
+//
+// MI355X mapping: one workgroup per (batch, head).  The transposed state
+// H = S^T (Dk x Dv, float32) is loaded ONCE from HBM into registers with
+// 16-byte loads -- thread (rg, cx) holds columns 4cx..4cx+3 of rows
+// rg, rg+RG, rg+2RG, ... so each wave instruction reads whole contiguous
+// rows -- and written back ONCE at the end.  Per token:
+//   Ht   = Diag(exp g_t) H                          (rows scaled)
+//   vhat = Ht^T k,  r = Ht^T q~,  kq = k . q~       (one pass over the rows)
+//   e    = beta (v - vhat)
+//   H    = Ht + k e^T
+//   o    = H^T q~ = r + e * kq                      (no second pass needed)
+// The partial sums are reduced across the rows a wavefront holds with lane
+// shuffles, then across wavefronts through LDS.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+
+template <int DK, int DV>
+struct RecShape {
+    static constexpr int NT = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;  // threads
+    static constexpr int CX = DV / 4;        // threads across the columns (float4 each)
+    static constexpr int RG = NT / CX;       // row groups
+    static constexpr int RPT = DK / RG;      // rows per thread
+    static constexpr int NW = NT / 64;       // wavefronts
+    static_assert(NT % 64 == 0 && RPT >= 1 && RG * RPT == DK && CX <= 64, "shape");
+};
+
+template <int DK, int DV, typename IO, typename OUT>
+__global__ void __launch_bounds__((RecShape<DK, DV>::NT))
+recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+                 const float* __restrict__ g, const float* __restrict__ beta,
+                 float* __restrict__ state, OUT* __restrict__ o,
+                 int T, int H, float scale, int mode)
+{
+    using S = RecShape<DK, DV>;
+    const int bh = blockIdx.x;
+    const int b = bh / H, h = bh - (bh / H) * H;
+    const int tid = threadIdx.x;
+    const int cx = tid % S::CX, rg = tid / S::CX;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    __shared__ float sk[DK], sq[DK], sa[DK], sv[DV];
+    __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][9];
+
+    float* st = state + (size_t)bh * DK * DV;
+    f32x4 hr[S::RPT];
+#pragma unroll
+    for (int i = 0; i < S::RPT; ++i)
+        hr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = ((size_t)b * T + t) * H + h;
+        for (int c = tid; c < DK; c += S::NT) {
+            sk[c] = io<IO>::load(k + tok * DK + c);
+            sq[c] = io<IO>::load(q + tok * DK + c) * scale;
+            float a = 1.f;
+            if (mode == KDA_GATE_CHANNEL) a = expf(g[tok * DK + c]);
+            else if (mode == KDA_GATE_SCALAR) a = expf(g[tok]);
+            sa[c] = a;
+        }
+        for (int j = tid; j < DV; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + j);
+        __syncthreads();
+
+        f32x4 ak = zero4(), aq = zero4();
+        float kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < S::RPT; ++i) {
+            const int r = rg + S::RG * i;
+            const float a = sa[r], kr = sk[r], qr = sq[r];
+            hr[i] *= a;
+            ak += hr[i] * kr;
+            aq += hr[i] * qr;
+            kq += kr * qr;
+        }
+        // reduce over the row groups held by this wavefront
+#pragma unroll
+        for (int off = S::CX; off < 64; off <<= 1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ak[u] += __shfl_xor(ak[u], off);
+                aq[u] += __shfl_xor(aq[u], off);
+            }
+            kq += __shfl_xor(kq, off);
+        }
+        if constexpr (S::NW > 1) {
+            if (lane < S::CX) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    red[wave][cx][u] = ak[u];
+                    red[wave][cx][4 + u] = aq[u];
+                }
+                red[wave][cx][8] = kq;
+            }
+            __syncthreads();
+            ak = zero4(); aq = zero4(); kq = 0.f;
+#pragma unroll
+            for (int w = 0; w < S::NW; ++w) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ak[u] += red[w][cx][u];
+                    aq[u] += red[w][cx][4 + u];
+                }
+                kq += red[w][cx][8];
+            }
+        }
+        const float bt = beta[tok];
+        f32x4 e;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
+#pragma unroll
+        for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * e;
+        if (rg == 0) {
+            Vec4<OUT>::store(o + tok * DV + 4 * cx, aq + e * kq);
+        }
+        __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
+    }
+#pragma unroll
+    for (int i = 0; i < S::RPT; ++i)
+        __builtin_nontemporal_store(
+            hr[i], reinterpret_cast<f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
+{
+    using S = RecShape<DK, DV>;
+    if (a.o_dtype == KDA_F32)
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H), dim3(S::NT), 0, s,
+                           (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
+                           (float*)a.o, a.T, a.H, a.scale, (int)a.mode);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H), dim3(S::NT), 0, s,
+                           (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
+                           (bf16_t*)a.o, a.T, a.H, a.scale, (int)a.mode);
+    return hipGetLastError();
+}
+
+template <int DK, typename IO>
+static hipError_t dispatch_dv(const RecArgs& a, hipStream_t s)
+{
+    switch (a.Dv) {
+        case 16: return launch_rec<DK, 16, IO>(a, s);
+        case 32: return launch_rec<DK, 32, IO>(a, s);
+        case 64: return launch_rec<DK, 64, IO>(a, s);
+        case 128: return launch_rec<DK, 128, IO>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename IO>
+static hipError_t dispatch_dk(const RecArgs& a, hipStream_t s)
+{
+    switch (a.Dk) {
+        case 16: return dispatch_dv<16, IO>(a, s);
+        case 32: return dispatch_dv<32, IO>(a, s);
+        case 64: return dispatch_dv<64, IO>(a, s);
+        case 128: return dispatch_dv<128, IO>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_recurrent(const RecArgs& a, hipStream_t s)
+{
+    if (a.dtype == KDA_BF16) return dispatch_dk<bf16_t>(a, s);
+    return dispatch_dk<float>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,155 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * The library computes the forward pass of the channel-wise gated delta rule
+ * ("Kimi Delta Attention", KDA) and its two special cases:
+ *
+ *   KDA_GATE_CHANNEL  Kimi Delta Attention: one decay per key channel,
+ *                     S~_t = S_{t-1} Diag(alpha_t)
+ *                     ("You could have come up with Kimi Delta Attention",
+ *                     the five state-update equations at the top; GeekNews
+ *                     #31925, section "Kimi Delta Attention: per-channel decay")
+ *   KDA_GATE_SCALAR   Gated DeltaNet: one decay per token and head,
+ *                     S~_t = alpha_t S_{t-1}
+ *                     (GeekNews #31925, section "Gated DeltaNet: forget the
+ *                     whole state first")
+ *   KDA_GATE_NONE     DeltaNet: no decay
+ *                     (GeekNews #31925, section "DeltaNet: write the error,
+ *                     not the value")
+ *
+ * and then, in every mode, per token t of every (batch, head) sequence:
+ *   vhat = S~_t k_t ;  e_t = beta_t (v_t - vhat) ;  S_t = S~_t + e_t k_t^T ;
+ *   o_t  = S_t (scale * q_t)      (scale is d_k^-1/2 in the article)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Token tensors are contiguous [B, T, H, D]: q and k have D = Dk,
+ *   v and o have D = Dv.  beta is [B, T, H] float.  Gates are log-gates
+ *   g = log(alpha) <= 0 (GeekNews #31925, section "Diagonal-plus-low-rank
+ *   transition": implementations store g and use exp(g)) as float:
+ *   [B, T, H, Dk] for KDA_GATE_CHANNEL, [B, T, H] for KDA_GATE_SCALAR, and
+ *   NULL for KDA_GATE_NONE.  The recurrent state is stored transposed,
+ *   H = S^T, as contiguous float [B, H, Dk, Dv] (row = key channel, column =
+ *   value channel), the d_k x d_v layout named in the same summary.
+ * dtype.  q, k and v share one storage type `dtype`: KDA_F32 (float) or
+ *   KDA_BF16 (bfloat16 bit patterns).  o has its own storage type `o_dtype`
+ *   (either one, independently).  The state is float32.  Arithmetic keeps
+ *   about float32 accuracy throughout: every product that carries the state
+ *   or the output uses float32 operands, or bf16 hi/lo pairs of them on the
+ *   matrix cores (see the kernel sources); a bf16 o is the float32 result
+ *   rounded to nearest-even at the final store.
+ * Pointers.  All tensor pointers are DEVICE pointers owned by the caller.
+ *   The library never allocates, frees or synchronises; all work is enqueued
+ *   on `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *   is asynchronous with respect to the host.  Pointers must be 16-byte
+ *   aligned.  Inputs are not modified except where stated.
+ * Shapes.  B, H >= 1, T >= 0 (T = 0 leaves every output untouched except
+ *   that kda_chunk_fwd copies the initial state to the final state).
+ *   Dk, Dv in {16, 32, 64, 128} (kda_chunk_fwd: Dk == Dv); chunk in
+ *   {16, 32, 64}; T need not be a multiple of chunk.
+ * Values.  g must be finite (a hard forget is g = -30, say, not -inf).
+ *   Keys are used as given: the article assumes unit keys, but nothing here
+ *   normalises or checks them.  beta is not clamped.
+ * Errors.  Arguments are validated on the host before any HIP call; a bad
+ *   argument returns a status and enqueues nothing.  A failed launch returns
+ *   KDA_ERROR_HIP.  Nothing is printed and nothing aborts.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_GATE_CHANNEL = 0,
+    KDA_GATE_SCALAR = 1,
+    KDA_GATE_NONE = 2
+} kda_gate_mode;
+
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,  /* NULL required pointer, negative size, bad enum */
+    KDA_ERROR_NOT_SUPPORTED = 2,  /* Dk, Dv or chunk outside the supported set     */
+    KDA_ERROR_MISALIGNED = 3,     /* a pointer is not 16-byte aligned               */
+    KDA_ERROR_WORKSPACE = 4,      /* workspace NULL or smaller than required        */
+    KDA_ERROR_HIP = 5             /* the HIP runtime reported an error at launch    */
+} kda_status;
+
+/*
+ * kda_recurrent_step -- the recurrent (token-by-token) form.
+ *
+ * Runs T >= 1 tokens of every (b, h) sequence in order, starting from and
+ * updating `state` IN PLACE; T = 1 is one decode step.  This is the fused
+ * recurrent execution of GeekNews #31925, section "Fused recurrent kernel for
+ * decode": one workgroup owns one (batch, head) state, streams it once from
+ * HBM, applies decay, prediction, correction, the rank-1 write and the read,
+ * and writes it back once.
+ *
+ *   q, k   [B,T,H,Dk]  dtype        in
+ *   v      [B,T,H,Dv]  dtype        in
+ *   g      see "Layout" (float)     in   (NULL iff mode == KDA_GATE_NONE)
+ *   beta   [B,T,H]     float        in
+ *   state  [B,H,Dk,Dv] float        in/out (S_{t0-1} on entry, S_{t0+T-1} on exit)
+ *   o      [B,T,H,Dv]  o_dtype      out  (must not alias any input)
+ *   scale  query scale (pass 1/sqrt(Dk) for the article's d_k^-1/2)
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v,
+                              const float* g, const float* beta,
+                              float* state, void* o,
+                              int B, int T, int H, int Dk, int Dv, float scale,
+                              kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                              void* stream);
+
+/*
+ * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
+ * needs for these arguments (0 when T == 0).  Returns 0 as well for
+ * unsupported arguments; kda_chunk_fwd then reports the precise error.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_gate_mode mode, kda_dtype dtype);
+
+/*
+ * kda_chunk_fwd -- the chunkwise-parallel form (prefill / training forward).
+ *
+ * Same mathematics and results (up to rounding) as running
+ * kda_recurrent_step over all T tokens (GeekNews #31925, section "Chunkwise
+ * KDA: recasting the recurrence as matrix products": per chunk of `chunk`
+ * tokens, cumulative log-decay, the strictly lower coupling matrix and a
+ * triangular (UT/WY) solve for pseudo-values; then a sequential carry of
+ * the state from chunk to chunk, and intra- plus inter-chunk outputs).
+ *
+ *   q, k, v, g, beta, o   as for kda_recurrent_step
+ *   initial_state  [B,H,Dk,Dv] float in, or NULL for a zero state
+ *   final_state    [B,H,Dk,Dv] float out, or NULL (not stored); it may be the
+ *                  same pointer as initial_state (in-place hand-off)
+ *   chunk          16, 32 or 64 tokens
+ *   workspace      device buffer of at least
+ *                  kda_chunk_fwd_workspace_size(...) bytes, owned by the
+ *                  caller, 256-byte aligned; its contents are scratch
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta,
+                         const float* initial_state, float* final_state, void* o,
+                         int B, int T, int H, int Dk, int Dv, int chunk, float scale,
+                         kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

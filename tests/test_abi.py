@@ -1,0 +1,89 @@
+"""The C-ABI library loads, exports what include/kda.h declares, and rejects
+bad arguments on the host before any HIP call (CPU only: every call here
+fails validation, so nothing is ever enqueued)."""
+import ctypes
+
+import pytest
+
+import gated_delta_rule_17_amd as K
+
+A = 0x10000          # a 16-byte aligned fake device address (never dereferenced)
+MIS = 0x10004        # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return K.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = K.header_functions()
+    assert set(names) >= {"kda_recurrent_step", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+                          "kda_status_string", "kda_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in K.STATUS.items():
+        assert L.kda_status_string(code).decode() == name
+    assert L.kda_status_string(99).decode() == "KDA_ERROR_UNKNOWN"
+    assert L.kda_version() >= 10000
+
+
+def _rec(L, q=A, k=A, v=A, g=A, beta=A, state=A, o=A, B=1, T=1, H=1, Dk=128, Dv=128,
+         scale=1.0, mode=0, dtype=1, o_dtype=0):
+    return L.kda_recurrent_step(q, k, v, g, beta, state, o, B, T, H, Dk, Dv, scale, mode,
+                                dtype, o_dtype, None)
+
+
+def _chunk(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, B=1, T=64, H=1, Dk=128,
+           Dv=128, chunk=64, scale=1.0, mode=0, dtype=1, o_dtype=0, ws=A, wsb=None):
+    if wsb is None:
+        wsb = L.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype)
+    return L.kda_chunk_fwd(q, k, v, g, beta, h0, hT, o, B, T, H, Dk, Dv, chunk, scale, mode,
+                           dtype, o_dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(beta=None), 1),
+    (dict(o=None), 1), (dict(state=None), 1), (dict(g=None, mode=0), 1),
+    (dict(g=None, mode=1), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
+    (dict(mode=3), 1), (dict(dtype=2), 1), (dict(o_dtype=-1), 1), (dict(Dk=48), 2), (dict(Dv=256), 2),
+    (dict(Dk=8), 2), (dict(q=MIS), 3), (dict(state=MIS), 3), (dict(g=MIS), 3),
+    (dict(o=MIS), 3),
+])
+def test_recurrent_validation(L, kw, code):
+    assert _rec(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(g=None, mode=0), 1), (dict(B=0), 1), (dict(mode=7), 1),
+    (dict(o_dtype=5), 1),
+    (dict(chunk=48), 2), (dict(chunk=128), 2), (dict(Dk=64, Dv=128), 2), (dict(Dk=256, Dv=256), 2),
+    (dict(q=MIS), 3), (dict(h0=MIS), 3), (dict(hT=MIS), 3), (dict(ws=None), 4),
+    (dict(wsb=16), 4), (dict(ws=A + 16), 3),
+])
+def test_chunk_validation(L, kw, code):
+    assert _chunk(L, **kw) == code
+
+
+def test_none_mode_accepts_null_gate(L):
+    # only the workspace check remains to fail, proving g=NULL passed validation
+    assert _chunk(L, g=None, mode=2, ws=None) == 4
+
+
+def test_zero_length_recurrent_is_a_no_op(L):
+    # T = 0: nothing to do, nothing enqueued, even with NULL tensors
+    assert _rec(L, q=None, k=None, v=None, g=None, beta=None, o=None, T=0) == 0
+
+
+def test_workspace_size(L):
+    f = L.kda_chunk_fwd_workspace_size
+    assert f(1, 0, 1, 128, 128, 64, 0, 1) == 0
+    assert f(1, 64, 1, 128, 128, 48, 0, 1) == 0
+    a = f(1, 64, 1, 128, 128, 64, 0, 1)
+    b = f(1, 65, 1, 128, 128, 64, 0, 1)         # a ragged tail costs a whole chunk record
+    assert 0 < a < b == 2 * a
+    assert f(2, 64, 3, 128, 128, 64, 0, 1) == 6 * a
+    assert f(1, 64, 1, 128, 128, 64, 0, 0) >= a  # float32 records are no smaller
