@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * chunked prefill  B=1, H=16, T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v,
+    fp32 gates/beta/state, bf16 output            (kda_chunk_fwd)
+  * decode step      B=256, H=32, d_k=d_v=128, one token, fp32 state
+    (512 MiB) updated in place, bf16 q/k/v/o       (kda_recurrent_step)
+
+Prints ONE JSON line.  ``value`` is prefill tokens/s; the decode step's state
+GB/s is reported next to it (the metric names both).  Timing uses HIP events
+on the stream the kernels are launched on (torch's current stream), W untimed
+warm-up steps, then exactly K timed steps between device synchronisations.
+Prefill inputs rotate over three resident copies so that they do not sit in
+the 256 MB last-level cache between steps.
+
+``roofline`` is the decode kernel (the step's dominant kernel by time, HBM
+bound); ``roofline_prefill`` is the prefill call (two kernels).  Achieved
+figures use algorithmic bytes: decode 132 612 B per (b, h); prefill 1540 B per
+token-head plus 2 * d_k * d_v * 4 B of initial/final state per (b, h).
+``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs stored in
+profiles/traffic.json and is null when the kernel source changed since.
+``cpu_baseline`` times the fp64 CPU oracle (test infrastructure) on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+PREFILL = dict(B=1, H=16, T=4096, D=128, chunk=64)
+DECODE = dict(B=256, H=32, D=128)
+
+
+def decode_bytes(B, H, D):
+    # state read + write (fp32), q, k, v (bf16), g (fp32 per channel), beta, o (bf16)
+    return B * H * (2 * D * D * 4 + 3 * D * 2 + D * 4 + 4 + D * 2)
+
+
+def prefill_bytes(B, H, T, D):
+    per_token_head = 4 * D * 2 + D * 4 + 4          # q, k, v, o bf16; g fp32; beta
+    return B * H * T * per_token_head + B * H * 2 * D * D * 4
+
+
+def prefill_flops(B, H, T, D, C):
+    # triangle-exploiting count per token-head: 6 d^2 + (C-1) d + (C+1)(2d + 2d) + C^2/3
+    per = 6 * D * D + (C - 1) * D + (C + 1) * (4 * D) + C * C / 3.0
+    return B * H * T * per
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_17_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return {}
+    with open(p) as f:
+        return json.load(f)
+
+
+def cpu_baseline():
+    """The oracle as it stands, on the host cores: the full prefill workload
+    (all 16 heads x 4096 tokens) and one full decode step."""
+    import oracle
+    from kda_workloads import make_config
+    w = make_config("prefill_h16_t4096")
+    t0 = time.perf_counter()
+    oracle.recurrent(w.q, w.k, w.v, w.g, w.beta, w.h0, scale=w.scale, mode=w.mode)
+    tp = time.perf_counter() - t0
+    d = make_config("decode_b256_h32")
+    t0 = time.perf_counter()
+    oracle.recurrent(d.q, d.k, d.v, d.g, d.beta, d.h0, scale=d.scale, mode=d.mode)
+    td = time.perf_counter() - t0
+    state_bytes = d.B * d.H * d.Dk * d.Dv * 4 * 2
+    return {"value": w.B * w.T / tp, "unit": "tokens/s", "cores": oracle.oracle_threads(),
+            "kind": "oracle",
+            "sample": "fp64 oracle R over the whole prefill workload (B1 H16 T4096 d128, "
+                      f"{tp:.2f} s) and one whole decode step (B256 H32 d128, {td:.2f} s)",
+            "decode_state_GBps": state_bytes / td / 1e9,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_17_amd as K
+    from kda_workloads import make_config
+    dev = torch.device("cuda:0")
+
+    def dev_inputs(w):
+        dt = torch.bfloat16
+        t = lambda x, d=torch.float32: None if x is None else torch.from_numpy(x).to(dev).to(d)
+        return dict(q=t(w.q, dt), k=t(w.k, dt), v=t(w.v, dt), g=t(w.g), beta=t(w.beta), h0=t(w.h0))
+
+    # prefill: three resident input sets (different seeds), shared workspace
+    P = PREFILL
+    sets = [dev_inputs(make_config("prefill_h16_t4096", seed=s)) for s in range(3)]
+    ws_bytes = K.kda_chunk_fwd_workspace_size(P["B"], P["T"], P["H"], P["D"], P["D"], P["chunk"], 0, K.BF16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    o_pre = torch.empty((P["B"], P["T"], P["H"], P["D"]), dtype=torch.bfloat16, device=dev)
+    h_fin = torch.empty((P["B"], P["H"], P["D"], P["D"]), dtype=torch.float32, device=dev)
+    # decode
+    Dc = DECODE
+    dw = make_config("decode_b256_h32")
+    dd = dev_inputs(dw)
+    state = dd["h0"]
+    o_dec = torch.empty((Dc["B"], 1, Dc["H"], Dc["D"]), dtype=torch.bfloat16, device=dev)
+
+    def prefill(i):
+        s = sets[i % 3]
+        K.kda_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], initial_state=s["h0"],
+                        final_state=h_fin, o=o_pre, chunk=P["chunk"], workspace=ws)
+
+    def decode():
+        K.kda_recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, o=o_dec)
+
+    for i in range(args.warmup):
+        prefill(i)
+        decode()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        prefill(i)
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = wall * 1e3 / args.steps
+
+    pre_s = pre_ms.mean() / 1e3
+    dec_s = dec_ms.mean() / 1e3
+    tokens = P["B"] * P["T"]
+    pbytes = prefill_bytes(P["B"], P["H"], P["T"], P["D"])
+    pflops = prefill_flops(P["B"], P["H"], P["T"], P["D"], P["chunk"])
+    dbytes = decode_bytes(Dc["B"], Dc["H"], Dc["D"])
+    state_bytes = Dc["B"] * Dc["H"] * Dc["D"] * Dc["D"] * 4 * 2
+
+    traffic = load_traffic()
+    rec_hash = source_hash("kda_recurrent.hip", "kda_device.hpp")
+    chk_hash = source_hash("kda_chunk.hip", "kda_device.hpp")
+    t_dec = traffic.get("decode")
+    t_dec_bytes = t_dec["bytes_per_launch"] if t_dec and t_dec.get("source_hash") == rec_hash else None
+    t_pre = traffic.get("prefill")
+    t_pre_bytes = t_pre["bytes_per_launch"] if t_pre and t_pre.get("source_hash") == chk_hash else None
+    mfma = traffic.get("prefill_mfma")
+    mfma_util = mfma.get("mfma_util") if mfma and mfma.get("source_hash") == chk_hash else None
+
+    out = {
+        "metric": "KDA chunked prefill tokens/s (H=16,d=128,T=4096) + decode-step state GB/s",
+        "value": tokens / pre_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA prefill B1 H16 T4096 d128 chunk64 bf16 (value) + "
+                               "decode step B256 H32 d128 fp32 state (decode_state_GBps)",
+                   "global_batch": P["B"], "seq_len": P["T"], "heads": P["H"],
+                   "d_k": P["D"], "d_v": P["D"], "chunk": P["chunk"],
+                   "decode_batch": Dc["B"], "decode_heads": Dc["H"],
+                   "parallelism": "single GPU"},
+        "prefill_ms": float(pre_s * 1e3),
+        "prefill_token_heads_per_s": tokens * P["H"] / pre_s,
+        "decode_ms": float(dec_s * 1e3),
+        "decode_state_GBps": state_bytes / dec_s / 1e9,
+        "decode_total_GBps": dbytes / dec_s / 1e9,
+        "roofline": {
+            "kernel": "recurrent_kernel<128,128,bf16,bf16> (decode step)",
+            "bound": "hbm", "achieved": dbytes / dec_s / 1e9, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": dbytes / dec_s / 1e9 / HBM_PEAK_GBPS,
+            "traffic": t_dec_bytes,
+            "algorithmic_bytes_per_launch": dbytes,
+        },
+        "roofline_prefill": {
+            "kernel": "kda_chunk_fwd (chunk_prepare + chunk_state)",
+            "bound": "hbm", "achieved": pbytes / pre_s / 1e9, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBPS,
+            "traffic": t_pre_bytes,
+            "algorithmic_bytes_per_launch": pbytes,
+            "mfma_tflops_algorithmic": pflops / pre_s / 1e12,
+            "mfma_frac_algorithmic": pflops / pre_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "mfma_util_counters": mfma_util,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

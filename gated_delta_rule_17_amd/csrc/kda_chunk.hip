@@ -106,6 +106,21 @@ struct WsLayout {
 template <typename OT>
 __device__ __forceinline__ void store_op(OT* p, float x) { io<OT>::store(p, x); }
 
+// Store N consecutive values of a precise operand with the widest aligned stores
+// (N is a power of two; idx is a multiple of N).
+template <typename OT, int N>
+__device__ __forceinline__ void store_run(const PArr<OT>& a, int idx, const float* x)
+{
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int u = 0; u < N; u += 4)
+            store4_p(a, idx + u, (f32x4){x[u], x[u + 1], x[u + 2], x[u + 3]});
+    } else {
+#pragma unroll
+        for (int u = 0; u < N; ++u) store_p(a, idx + u, x[u]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // chunk_prepare
 // ---------------------------------------------------------------------------
@@ -155,19 +170,45 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     // ---- cumulative log-decay: thread (seg, c) owns tokens seg*TPS .. +TPS-1 of channel c
     const int c = tid % DKP, seg = tid / DKP;
     const int i0 = seg * TPS;
-    float G[TPS];
+    // all global loads of this thread first (g, k, q, v), issued as straight-line
+    // code with clamped addresses so that they are all in flight together;
+    // out-of-range elements are zeroed afterwards
+    const int cc = c < DK ? c : DK - 1;
+    float G[TPS], kreg[TPS], qreg[TPS];
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const int i = i0 + u;
+        const int ic = i < L ? i : L - 1;
+        const size_t tok = ((size_t)b * T + t0 + ic) * H + h;
+        const float* gp = mode == KDA_GATE_CHANNEL ? g + tok * DK + cc
+                        : (mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
+        G[u] = *gp;
+        kreg[u] = io<OT>::load(k + tok * DK + cc);
+        qreg[u] = io<OT>::load(q + tok * DK + cc);
+    }
+    // v rows as 8-element vectors (used for U = T Diag(beta) V later)
+    constexpr int NVEC = C * DV / 8, VPT = (NVEC + S::NT - 1) / S::NT;
+    Frag<OT> vreg[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int idx = min(tid + S::NT * u, NVEC - 1);
+        const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
+        const int ic = i < L ? i : L - 1;
+        vreg[u].load(v + (((size_t)b * T + t0 + ic) * H + h) * DV + n8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) {
+        const bool ok = (i0 + u < L) && (c < DK);
+        G[u] = (ok && mode != KDA_GATE_NONE) ? G[u] : 0.f;
+        kreg[u] = ok ? kreg[u] : 0.f;
+        qreg[u] = ok ? qreg[u] * scale : 0.f;
+    }
     {
         float run = 0.f;
 #pragma unroll
         for (int u = 0; u < TPS; ++u) {
-            const int i = i0 + u;
-            float gv = 0.f;
-            if (i < L && c < DK) {
-                const size_t tok = ((size_t)b * T + t0 + i) * H + h;
-                if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + c];
-                else if (mode == KDA_GATE_SCALAR) gv = g[tok];
-            }
-            run += gv;
+            run += G[u];
             G[u] = run;
         }
         segtot[seg][c] = run;
@@ -208,17 +249,12 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     __syncthreads();
 
     // ---- element-wise operands
-    float kreg[TPS], egreg[TPS];
+    float egreg[TPS], krv[TPS];
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
         const int i = i0 + u;
         const int I = i >> 4;
-        float kv = 0.f, qv = 0.f;
-        if (i < L && c < DK) {
-            const size_t tok = ((size_t)b * T + t0 + i) * H + h;
-            kv = io<OT>::load(k + tok * DK + c);
-            qv = io<OT>::load(q + tok * DK + c) * scale;
-        }
+        const float kv = kreg[u], qv = qreg[u];
         const float x = __expf(G[u] - Gs[I][c]);          // <= 1
         const float kk = kv * __expf(Ge[I][c] - G[u]);    // <= |k|
         const float kd = flag[I][c] ? 0.f : kv * __expf(Gs[I][c] - G[u]);  // >= |k|, bounded
@@ -227,11 +263,12 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         store_p(Kd, i * SK + c, kd);
         Kk[i * SKF + c] = kk;
         const float eg = x * eS[I][c];                     // exp(G_i) <= 1
-        kreg[u] = kv;
         egreg[u] = eg;
+        krv[u] = kk * eL[I][c];                            // k exp(G_last - G_i) <= |k|
         store_p(Wq, i * DKP + c, qv * eg);
-        if (c < DK) store_p(Wkr, c * CP + i, kk * eL[I][c]);
     }
+    // Kr^T row c, tokens i0 .. i0+TPS-1: contiguous, written with wide stores
+    if (c < DK) store_run<OT, TPS>(Wkr, c * CP + i0, krv);
     if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
         for (int p = tid; p < DK * (CP - C); p += S::NT) {
             const int cc = p / (CP - C), i = C + p % (CP - C);
@@ -336,11 +373,14 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         const int i = i0 + u;
         if (c < DK) store_p(BkT, c * SC + i, sb[i] * kreg[u] * egreg[u]);
     }
-    for (int p = tid; p < C * DV; p += S::NT) {
-        const int i = p / DV, n = p % DV;
-        float vv = 0.f;
-        if (i < L) vv = io<OT>::load(v + (((size_t)b * T + t0 + i) * H + h) * DV + n);
-        store_p(BvT, n * SC + i, sb[i] * vv);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int idx = tid + S::NT * u;
+        if (idx < NVEC) {
+            const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + i, sb[i] * vreg[u].get(e));
+        }
     }
     if (CP > C) {
         for (int p = tid; p < DK * (CP - C); p += S::NT) {
@@ -545,36 +585,64 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     }
     __syncthreads();
 
-    for (int cidx = 0; cidx < NC; ++cidx) {
+    // Operands of one chunk step held by this wave.  Two sets alternate: the
+    // next chunk's set is loaded while the current one is used, so the
+    // sequential chain does not wait on memory latency at every step.  The
+    // loads are unconditional straight-line code (indices clamped; zero
+    // padding in the records makes the extra fragments harmless) so that the
+    // wait for one set never includes the loads of the other.
+    constexpr int KS = DKP / 32, KC = CP / 32;
+    constexpr bool ALLE = NB >= 4;        // every wave owns an E / o tile
+    constexpr bool ALLH = (MH % 4) == 0;  // every wave owns MHW state tiles
+    const int we = ALLE ? wave : (wave < NB ? wave : NB - 1);
+    struct Ops {
+        PFrag<OT> wn[KS];        // -W rows 16*we.. (A operand of E)
+        PFrag<OT> qg[KS];        // Qg rows 16*we.. (B operand of o^T)
+        PFrag<OT> aq[KC];        // Aqk rows 16*we.. (B operand of o^T)
+        PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
+        f32x4 u;                 // U^T init of E
+        f32x4 gl[MHW];           // exp(G_last) for the state rows
+    };
+    auto load_ops = [&](Ops& P, int cidx) {
         const size_t rec = (size_t)bh * NC + cidx;
+        const PArr<OT> wneg = W.wneg(rec), qg = W.qg(rec), krt = W.krt(rec), aqk = W.aqk(rec);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            P.wn[ks] = wneg.frag((16 * we + r) * DKP + 32 * ks + 8 * gq);
+            P.qg[ks] = qg.frag((16 * we + r) * DKP + 32 * ks + 8 * gq);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks) P.aq[ks] = aqk.frag((16 * we + r) * CP + 32 * ks + 8 * gq);
+        P.u = Vec4<float>::load(W.ut + rec * S::U_N + (n0 + r) * C + 16 * we + 4 * gq);
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = ALLH ? wave + 4 * s : min(wave + 4 * s, MH - 1);
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks)
+                P.kr[s][ks] = krt.frag((16 * mt + r) * CP + 32 * ks + 8 * gq);
+            P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt + 4 * gq);
+        }
+    };
+    auto step = [&](const Ops& P, int cidx) {
         const int t0 = cidx * C;
         const int L = min(C, T - t0);
-        const PArr<OT> wneg = W.wneg(rec), qg = W.qg(rec), krt = W.krt(rec), aqk = W.aqk(rec);
-        const float* ut = W.ut + rec * S::U_N;
-        const float* gl = W.gl + rec * DK;
-
+        const bool has_e = ALLE || wave < NB;
         f32x4 oacc = zero4();
-        if (wave < NB) {
+        if (has_e) {
             // E = U - W H for tokens 16*wave ..
-            f32x4 e = Vec4<float>::load(ut + (n0 + r) * C + 16 * wave + 4 * gq);
+            f32x4 e = P.u;
 #pragma unroll
-            for (int ks = 0; ks < DKP / 32; ++ks)
-                e = mma3(wneg.frag((16 * wave + r) * DKP + 32 * ks + 8 * gq),
-                         HT.frag(r * SK + 32 * ks + 8 * gq), e);
+            for (int ks = 0; ks < KS; ++ks) e = mma3(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
             // o^T (state part): rows n, tokens 16*wave ..
 #pragma unroll
-            for (int ks = 0; ks < DKP / 32; ++ks)
-                oacc = mma3(HT.frag(r * SK + 32 * ks + 8 * gq),
-                            qg.frag((16 * wave + r) * DKP + 32 * ks + 8 * gq), oacc);
+            for (int ks = 0; ks < KS; ++ks) oacc = mma3(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
             store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
         }
         __syncthreads();
-        if (wave < NB) {
-            // o^T += E^T Aqk^T (intra-chunk part); Aqk[i][j] = 0 for j > i
-            const int nks = (16 * wave + 15) / 32 + 1;
-            for (int ks = 0; ks < nks; ++ks)
-                oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq),
-                            aqk.frag((16 * wave + r) * CP + 32 * ks + 8 * gq), oacc);
+        if (has_e) {
+            // o^T += E^T Aqk^T (intra-chunk part; Aqk[i][j] = 0 for j > i)
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
             // lane holds o^T[n = 4gq + u][i = 16*wave + r]
             const int i = 16 * wave + r;
             if (i < L) {
@@ -586,17 +654,30 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = wave + 4 * s;
-            if (mt < MH) {
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(gl + 16 * mt + 4 * gq);
-                hacc[s] *= gv;
+            if (ALLH || mt < MH) {
+                hacc[s] *= P.gl[s];
 #pragma unroll
-                for (int ks = 0; ks < CP / 32; ++ks)
-                    hacc[s] = mma3(krt.frag((16 * mt + r) * CP + 32 * ks + 8 * gq),
-                                   ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
+                for (int ks = 0; ks < KC; ++ks)
+                    hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
                 store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
             }
         }
         __syncthreads();
+    };
+
+    if (NC > 0) {
+        // sched_barrier keeps the compiler from sinking a load batch towards
+        // its first use, which would turn the prefetch back into a stall
+        Ops A, B;
+        load_ops(A, 0);
+        for (int cidx = 0; cidx < NC; cidx += 2) {
+            load_ops(B, min(cidx + 1, NC - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            step(A, cidx);
+            load_ops(A, min(cidx + 2, NC - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (cidx + 1 < NC) step(B, cidx + 1);
+        }
     }
     if (hT) {
 #pragma unroll
