@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a float32 copy of exactly 256 MiB (reads 256 MiB, writes "
+                         "256 MiB) three times, as the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -140,6 +143,14 @@ def main():
 
     def decode():
         K.kda_recurrent_step(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], state, o=o_dec)
+
+    if args.calibrate_copy:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         prefill(i)

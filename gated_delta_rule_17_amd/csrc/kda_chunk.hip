@@ -49,7 +49,8 @@ struct CS {
     static constexpr int SKF = DKP + 4;               // stride of the float32 key array
     static constexpr int SC = CP + PAD;               // stride of [channel][token] operands
     static constexpr int SA = C + 4;                  // stride of float32 A / T
-    static constexpr int NT = 256;
+    static constexpr int NT = 512;                    // chunk_prepare threads
+    static constexpr int NW = NT / 64;                // and wavefronts
     static constexpr int NSEG = NT / DKP;             // threads per key channel (prefix sums)
     static constexpr int TPS = C / NSEG;              // tokens per thread
     static constexpr int NPAIR = NB * (NB - 1) / 2;
@@ -57,8 +58,8 @@ struct CS {
     static constexpr int NP = SPLIT ? 2 : 1;
     static constexpr int SZ = (int)sizeof(OT);
     // per-chunk record, elements per part
-    static constexpr size_t W_N = (size_t)C * DKP;    // -W      [C][DKP]   precise
-    static constexpr size_t Q_N = (size_t)C * DKP;    // Qg      [C][DKP]   precise
+    static constexpr size_t W_N = (size_t)C * DKP;    // -W      [C][DKP]   plain
+    static constexpr size_t Q_N = (size_t)C * DKP;    // Qg      [C][DKP]   plain
     static constexpr size_t KR_N = (size_t)DK * CP;   // Kr^T    [DK][CP]   precise
     static constexpr size_t AQ_N = (size_t)C * CP;    // Aqk     [C][CP]    precise
     static constexpr size_t U_N = (size_t)DV * C;     // U^T     [DV][C]    float32
@@ -78,15 +79,13 @@ struct CS {
 template <int C, int DK, int DV, typename OT>
 struct WsLayout {
     using S = CS<C, DK, DV, OT>;
-    OT *wneg_h, *wneg_l, *qg_h, *qg_l, *krt_h, *krt_l, *aqk_h, *aqk_l;
+    OT *wneg, *qg, *krt_h, *krt_l, *aqk_h, *aqk_l;
     float *ut, *gl;
     __host__ __device__ WsLayout(void* base, size_t nrec) {
         char* p = (char*)base;
         auto take = [&](size_t elems, size_t sz) { char* r = p; p += nrec * elems * sz; return r; };
-        wneg_h = (OT*)take(S::W_N, S::SZ);
-        wneg_l = S::SPLIT ? (OT*)take(S::W_N, S::SZ) : wneg_h;
-        qg_h = (OT*)take(S::Q_N, S::SZ);
-        qg_l = S::SPLIT ? (OT*)take(S::Q_N, S::SZ) : qg_h;
+        wneg = (OT*)take(S::W_N, S::SZ);
+        qg = (OT*)take(S::Q_N, S::SZ);
         krt_h = (OT*)take(S::KR_N, S::SZ);
         krt_l = S::SPLIT ? (OT*)take(S::KR_N, S::SZ) : krt_h;
         aqk_h = (OT*)take(S::AQ_N, S::SZ);
@@ -95,10 +94,10 @@ struct WsLayout {
         gl = (float*)p;
     }
     static size_t bytes(size_t nrec) {
-        return nrec * (S::NP * (S::W_N + S::Q_N + S::KR_N + S::AQ_N) * S::SZ + S::U_N * 4 + DK * 4);
+        return nrec * ((S::W_N + S::Q_N + S::NP * (S::KR_N + S::AQ_N)) * S::SZ + S::U_N * 4 + DK * 4);
     }
-    __device__ PArr<OT> wneg(size_t rec) const { return {wneg_h + rec * S::W_N, wneg_l + rec * S::W_N}; }
-    __device__ PArr<OT> qg(size_t rec) const { return {qg_h + rec * S::Q_N, qg_l + rec * S::Q_N}; }
+    __device__ OT* wneg_rec(size_t rec) const { return wneg + rec * S::W_N; }
+    __device__ OT* qg_rec(size_t rec) const { return qg + rec * S::Q_N; }
     __device__ PArr<OT> krt(size_t rec) const { return {krt_h + rec * S::KR_N, krt_l + rec * S::KR_N}; }
     __device__ PArr<OT> aqk(size_t rec) const { return {aqk_h + rec * S::AQ_N, aqk_l + rec * S::AQ_N}; }
 };
@@ -125,7 +124,7 @@ __device__ __forceinline__ void store_run(const PArr<OT>& a, int idx, const floa
 // chunk_prepare
 // ---------------------------------------------------------------------------
 template <int C, int DK, int DV, typename OT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
               int T, int H, int NC, float scale, int mode, void* __restrict__ ws, size_t nrec)
@@ -151,7 +150,9 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     const int L = min(C, T - t0);       // valid tokens
     const size_t rec = (size_t)bh * NC + c_idx;
     const WsLayout<C, DK, DV, OT> W(ws, nrec);
-    const PArr<OT> Wq = W.qg(rec), Wkr = W.krt(rec), Waq = W.aqk(rec), Wwn = W.wneg(rec);
+    OT* const Wq = W.qg_rec(rec);
+    OT* const Wwn = W.wneg_rec(rec);
+    const PArr<OT> Wkr = W.krt(rec), Waq = W.aqk(rec);
     float* Wut = W.ut + rec * S::U_N;
 
     const int tid = threadIdx.x;
@@ -265,7 +266,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         const float eg = x * eS[I][c];                     // exp(G_i) <= 1
         egreg[u] = eg;
         krv[u] = kk * eL[I][c];                            // k exp(G_last - G_i) <= |k|
-        store_p(Wq, i * DKP + c, qv * eg);
+        store_op(Wq + i * DKP + c, qv * eg);
     }
     // Kr^T row c, tokens i0 .. i0+TPS-1: contiguous, written with wide stores
     if (c < DK) store_run<OT, TPS>(Wkr, c * CP + i0, krv);
@@ -284,13 +285,14 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     // ---- A^T and Aqk^T tiles on the matrix cores: tile (J, I), J <= I
     // lane result: A[i = 16I + r][j = 16J + 4gq + u]
     constexpr int NTILE = NB * (NB + 1) / 2;
-    constexpr int TPW = (NTILE + 3) / 4;
+    constexpr int NW = S::NW;
+    constexpr int TPW = (NTILE + NW - 1) / NW;
     f32x4 accA[TPW], accQ[TPW];
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
         accA[s] = zero4();
         accQ[s] = zero4();
-        const int tix = wave + 4 * s;
+        const int tix = wave + NW * s;
         if (tix < NTILE) {
             int I = 0, base = 0;
             while (base + I + 1 <= tix) { base += I + 1; ++I; }
@@ -337,7 +339,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 
 #pragma unroll
     for (int s = 0; s < TPW; ++s) {
-        const int tix = wave + 4 * s;
+        const int tix = wave + NW * s;
         if (tix < NTILE) {
             int I = 0, base = 0;
             while (base + I + 1 <= tix) { base += I + 1; ++I; }
@@ -499,16 +501,16 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         constexpr int MW = DK / 16;          // channel tiles of W^T
         constexpr int NWT = MW * NB;         // W tiles
         constexpr int NUT = NB * (DV / 16);  // U tiles
-        for (int tix = wave; tix < NWT + NUT; tix += 4) {
+        for (int tix = wave; tix < NWT + NUT; tix += S::NW) {
             if (tix < NWT) {
                 const int m = tix / NB, I = tix % NB;     // channels 16m.., tokens 16I..
                 f32x4 acc = zero4();
                 const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
-                for (int ks = 0; ks < nks; ++ks)
-                    acc = mma3(BkT.frag((16 * m + r) * SC + 32 * ks + 8 * gq),
-                               Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq), acc);
+                for (int ks = 0; ks < nks; ++ks)   // W is stored as a plain operand
+                    acc = mma(BkT.frag((16 * m + r) * SC + 32 * ks + 8 * gq).h,
+                              Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq).h, acc);
                 // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
-                store4_p(Wwn, (16 * I + r) * DKP + 16 * m + 4 * gq, -acc);
+                Vec4<OT>::store(Wwn + (16 * I + r) * DKP + 16 * m + 4 * gq, -acc);
             } else {
                 const int t2 = tix - NWT;
                 const int I = t2 % NB, nn = t2 / NB;      // tokens 16I.., value cols 16nn..
@@ -524,7 +526,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         if (DKP > DK) {   // padded key channels of -W are zero
             for (int p = tid; p < C * (DKP - DK); p += S::NT) {
                 const int i = p / (DKP - DK), cc = DK + p % (DKP - DK);
-                store_p(Wwn, i * DKP + cc, 0.f);
+                store_op(Wwn + i * DKP + cc, 0.f);
             }
         }
     }
@@ -596,8 +598,8 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     constexpr bool ALLH = (MH % 4) == 0;  // every wave owns MHW state tiles
     const int we = ALLE ? wave : (wave < NB ? wave : NB - 1);
     struct Ops {
-        PFrag<OT> wn[KS];        // -W rows 16*we.. (A operand of E)
-        PFrag<OT> qg[KS];        // Qg rows 16*we.. (B operand of o^T)
+        Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
+        Frag<OT> qg[KS];         // Qg rows 16*we.. (B operand of o^T)
         PFrag<OT> aq[KC];        // Aqk rows 16*we.. (B operand of o^T)
         PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
         f32x4 u;                 // U^T init of E
@@ -605,11 +607,13 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     };
     auto load_ops = [&](Ops& P, int cidx) {
         const size_t rec = (size_t)bh * NC + cidx;
-        const PArr<OT> wneg = W.wneg(rec), qg = W.qg(rec), krt = W.krt(rec), aqk = W.aqk(rec);
+        const OT* wneg = W.wneg_rec(rec);
+        const OT* qg = W.qg_rec(rec);
+        const PArr<OT> krt = W.krt(rec), aqk = W.aqk(rec);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            P.wn[ks] = wneg.frag((16 * we + r) * DKP + 32 * ks + 8 * gq);
-            P.qg[ks] = qg.frag((16 * we + r) * DKP + 32 * ks + 8 * gq);
+            P.wn[ks].load(wneg + (16 * we + r) * DKP + 32 * ks + 8 * gq);
+            P.qg[ks].load(qg + (16 * we + r) * DKP + 32 * ks + 8 * gq);
         }
 #pragma unroll
         for (int ks = 0; ks < KC; ++ks) P.aq[ks] = aqk.frag((16 * we + r) * CP + 32 * ks + 8 * gq);
@@ -632,10 +636,10 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             // E = U - W H for tokens 16*wave ..
             f32x4 e = P.u;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) e = mma3(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
+            for (int ks = 0; ks < KS; ++ks) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
             // o^T (state part): rows n, tokens 16*wave ..
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) oacc = mma3(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
+            for (int ks = 0; ks < KS; ++ks) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
             store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
         }
         __syncthreads();
@@ -700,7 +704,7 @@ static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
     const int NC = (a.T + C - 1) / C;
     const size_t nrec = (size_t)BH * NC;
     if (NC > 0) {
-        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(NC, BH), dim3(256), 0, s,
+        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(NC, BH), dim3(CS<C, DK, DV, OT>::NT), 0, s,
                            (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
                            a.T, a.H, NC, a.scale, (int)a.mode, a.ws, nrec);
         hipError_t e = hipGetLastError();

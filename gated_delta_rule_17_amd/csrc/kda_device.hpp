@@ -153,6 +153,22 @@ __device__ __forceinline__ f32x4 mma3(const PFrag<float>& a, const PFrag<float>&
     return mma(a.h, b.h, c);
 }
 
+// Plain operand times precise operand: a * (b.hi + b.lo), and the mirror.
+__device__ __forceinline__ f32x4 mma2(const Frag<bf16_t>& a, const PFrag<bf16_t>& b, f32x4 c) {
+    c = mma(a, b.l, c);
+    return mma(a, b.h, c);
+}
+__device__ __forceinline__ f32x4 mma2(const Frag<float>& a, const PFrag<float>& b, f32x4 c) {
+    return mma(a, b.h, c);
+}
+__device__ __forceinline__ f32x4 mma2(const PFrag<bf16_t>& a, const Frag<bf16_t>& b, f32x4 c) {
+    c = mma(a.l, b, c);
+    return mma(a.h, b, c);
+}
+__device__ __forceinline__ f32x4 mma2(const PFrag<float>& a, const Frag<float>& b, f32x4 c) {
+    return mma(a.h, b, c);
+}
+
 // Pair of arrays holding the hi and lo parts of a precise operand (lo is
 // unused, and may be null, for float32).
 template <typename T> struct PArr {

@@ -5,11 +5,14 @@
 // order, each token doing decay -> prediction (a reduction over the key
 // dimension) -> residual -> rank-1 write -> read (a second reduction).
 //
-// MI355X mapping: one workgroup per (batch, head).  The transposed state
+// MI355X mapping: value columns evolve independently, so one workgroup owns
+// a slab of DVT columns of one (batch, head) state (DVT = min(Dv, 64): two
+// workgroups per head at Dv = 128, which halves the registers per thread and
+// doubles the workgroups in flight).  The slab of the transposed state
 // H = S^T (Dk x Dv, float32) is loaded ONCE from HBM into registers with
-// 16-byte loads -- thread (rg, cx) holds columns 4cx..4cx+3 of rows
-// rg, rg+RG, rg+2RG, ... so each wave instruction reads whole contiguous
-// rows -- and written back ONCE at the end.  Per token:
+// 16-byte loads -- thread (rg, cx) holds columns 4cx..4cx+3 of the slab in
+// rows rg, rg+RG, rg+2RG, ... so each wave instruction reads contiguous row
+// segments -- and written back ONCE at the end.  Per token:
 //   Ht   = Diag(exp g_t) H                          (rows scaled)
 //   vhat = Ht^T k,  r = Ht^T q~,  kq = k . q~       (one pass over the rows)
 //   e    = beta (v - vhat)
@@ -24,8 +27,10 @@ namespace kda {
 
 template <int DK, int DV>
 struct RecShape {
-    static constexpr int NT = (DK * DV / 4 < 256) ? DK * DV / 4 : 256;  // threads
-    static constexpr int CX = DV / 4;        // threads across the columns (float4 each)
+    static constexpr int DVT = DV < 64 ? DV : 64;   // columns per workgroup
+    static constexpr int NCT = DV / DVT;            // workgroups per (b, h)
+    static constexpr int NT = (DK * DVT / 4 < 256) ? DK * DVT / 4 : 256;  // threads
+    static constexpr int CX = DVT / 4;       // threads across the slab (float4 each)
     static constexpr int RG = NT / CX;       // row groups
     static constexpr int RPT = DK / RG;      // rows per thread
     static constexpr int NW = NT / 64;       // wavefronts
@@ -40,16 +45,17 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                  int T, int H, float scale, int mode)
 {
     using S = RecShape<DK, DV>;
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / S::NCT;
+    const int c0 = (blockIdx.x - bh * S::NCT) * S::DVT;   // first column of the slab
     const int b = bh / H, h = bh - (bh / H) * H;
     const int tid = threadIdx.x;
     const int cx = tid % S::CX, rg = tid / S::CX;
     const int lane = tid & 63, wave = tid >> 6;
 
-    __shared__ float sk[DK], sq[DK], sa[DK], sv[DV];
+    __shared__ float sk[DK], sq[DK], sa[DK], sv[S::DVT];
     __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][9];
 
-    float* st = state + (size_t)bh * DK * DV;
+    float* st = state + (size_t)bh * DK * DV + c0;
     f32x4 hr[S::RPT];
 #pragma unroll
     for (int i = 0; i < S::RPT; ++i)
@@ -66,7 +72,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             else if (mode == KDA_GATE_SCALAR) a = expf(g[tok]);
             sa[c] = a;
         }
-        for (int j = tid; j < DV; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + j);
+        for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
         __syncthreads();
 
         f32x4 ak = zero4(), aq = zero4();
@@ -118,7 +124,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
 #pragma unroll
         for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * e;
         if (rg == 0) {
-            Vec4<OUT>::store(o + tok * DV + 4 * cx, aq + e * kq);
+            Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
         }
         __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
     }
@@ -128,16 +134,17 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             hr[i], reinterpret_cast<f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
 }
 
+
 template <int DK, int DV, typename IO>
 static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
 {
     using S = RecShape<DK, DV>;
     if (a.o_dtype == KDA_F32)
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H), dim3(S::NT), 0, s,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
                            (float*)a.o, a.T, a.H, a.scale, (int)a.mode);
     else
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H), dim3(S::NT), 0, s,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
                            (bf16_t*)a.o, a.T, a.H, a.scale, (int)a.mode);
     return hipGetLastError();
