@@ -631,28 +631,36 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
         f32x4 u;                 // U^T init of E
         f32x4 gl[MHW];           // exp(G_last) for the state rows
     };
-    auto load_ops = [&](Ops& P, int cidx) {
+    // record pointers of one chunk for this wave
+    struct Rec {
+        const OT* wn; const OT* qg; PArr<OT> kr, aq; const float* u; const float* gl;
+    };
+    auto rec_of = [&](int cidx) {
         const size_t rec = (size_t)bh * NC + cidx;
-        const OT* wneg = W.wneg_rec(rec);
-        const OT* qg = W.qg_rec(rec);
-        const PArr<OT> krt = W.krt(rec), aqk = W.aqk(rec);
+        Rec R;
+        R.wn = W.wneg_rec(rec); R.qg = W.qg_rec(rec); R.kr = W.krt(rec); R.aq = W.aqk(rec);
+        R.u = W.ut + rec * S::U_N; R.gl = W.gl + rec * DK;
+        return R;
+    };
+    auto mt_of = [&](int s) { return ALLH ? wave + 4 * s : min(wave + 4 * s, MH - 1); };
+    auto load_ops = [&](Ops& P, int cidx) {
+        const Rec R = rec_of(cidx);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            P.wn[ks].load(wneg + fragbase(we, ks, KS, lane));
-            P.qg[ks].load(qg + fragbase(we, ks, KS, lane));
+            P.wn[ks].load(R.wn + fragbase(we, ks, KS, lane));
+            P.qg[ks].load(R.qg + fragbase(we, ks, KS, lane));
         }
 #pragma unroll
-        for (int ks = 0; ks < KC; ++ks) P.aq[ks] = aqk.frag(fragbase(we, ks, KC, lane));
-        P.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+        for (int ks = 0; ks < KC; ++ks) P.aq[ks] = R.aq.frag(fragbase(we, ks, KC, lane));
+        P.u = Vec4<float>::load(R.u + accbase(ct, we, NB, lane));
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
-            const int mt = ALLH ? wave + 4 * s : min(wave + 4 * s, MH - 1);
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks)
-                P.kr[s][ks] = krt.frag(fragbase(mt, ks, KC, lane));
-            P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt + 4 * gq);
+            for (int ks = 0; ks < KC; ++ks) P.kr[s][ks] = R.kr.frag(fragbase(mt_of(s), ks, KC, lane));
+            P.gl[s] = *reinterpret_cast<const f32x4*>(R.gl + 16 * mt_of(s) + 4 * gq);
         }
     };
+
     // L2 prefetch: the NCT column-tile workgroups of a head run in lockstep and
     // would all miss on the same record lines at the same time.  Each one
     // therefore touches a disjoint 1/NCT of the shared part of record c + 3
@@ -694,26 +702,42 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
         return *reinterpret_cast<const float*>(p);
     };
 
-    auto step = [&](const Ops& P, int cidx) {
+    // One chunk step with operands P; the operands of chunk `nxt` are loaded
+    // into Q one fragment per matrix-core k-step, so the load traffic of the
+    // four wavefronts is spread over the step instead of queueing up at once.
+    auto step = [&](const Ops& P, int cidx, Ops& Q, int nxt) {
         const int t0 = cidx * C;
         const int L = min(C, T - t0);
         const bool has_e = ALLE || wave < NB;
+        const Rec R = rec_of(nxt);
         f32x4 oacc = zero4();
-        if (has_e) {
-            // E = U - W H for tokens 16*wave ..
-            f32x4 e = P.u;
+        f32x4 e = P.u;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
-            // o^T (state part): rows n, tokens 16*wave ..
+        for (int ks = 0; ks < KS; ++ks) {
+            Q.wn[ks].load(R.wn + fragbase(we, ks, KS, lane));
+            if (has_e) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
+        }
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
-            store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
+        for (int ks = 0; ks < KS; ++ks) {
+            Q.qg[ks].load(R.qg + fragbase(we, ks, KS, lane));
+            if (has_e) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
+        }
+        if (has_e) store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
+        // keep the compiler from clustering this region's loads ahead of its
+        // matrix-core work: alternate one global load with two MFMA steps
+#pragma unroll
+        for (int g2 = 0; g2 < 2 * KS; ++g2) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
         __syncthreads();
-        if (has_e) {
-            // o^T += E^T Aqk^T (intra-chunk part; Aqk[i][j] = 0 for j > i)
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
+        for (int ks = 0; ks < KC; ++ks) {
+            Q.aq[ks] = R.aq.frag(fragbase(we, ks, KC, lane));
+            if (has_e) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
+        }
+        Q.u = Vec4<float>::load(R.u + accbase(ct, we, NB, lane));
+        if (has_e) {
             // lane holds o^T[n = 4gq + u][i = 16*wave + r]
             const int i = 16 * wave + r;
             if (i < L) {
@@ -725,13 +749,21 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = wave + 4 * s;
-            if (ALLH || mt < MH) {
-                hacc[s] *= P.gl[s];
+            const bool own = ALLH || mt < MH;
+            if (own) hacc[s] *= P.gl[s];
 #pragma unroll
-                for (int ks = 0; ks < KC; ++ks)
-                    hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
-                store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+            for (int ks = 0; ks < KC; ++ks) {
+                Q.kr[s][ks] = R.kr.frag(fragbase(mt_of(s), ks, KC, lane));
+                if (own) hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
             }
+            Q.gl[s] = *reinterpret_cast<const f32x4*>(R.gl + 16 * mt_of(s) + 4 * gq);
+            if (own) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+        }
+        // alternate one global load with one MFMA step in this region too
+#pragma unroll
+        for (int g2 = 0; g2 < NP * KC * (1 + MHW) + 1 + MHW; ++g2) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
         }
         __syncthreads();
     };
@@ -747,14 +779,12 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
         for (int cidx = 0; cidx < NC; cidx += 2) {
             sink += tA;
             tA = touch(min(cidx + 3, NC - 1));
-            load_ops(B, min(cidx + 1, NC - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            step(A, cidx);
-            sink += tB;
-            tB = touch(min(cidx + 4, NC - 1));
-            load_ops(A, min(cidx + 2, NC - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            if (cidx + 1 < NC) step(B, cidx + 1);
+            step(A, cidx, B, min(cidx + 1, NC - 1));
+            if (cidx + 1 < NC) {
+                sink += tB;
+                tB = touch(min(cidx + 4, NC - 1));
+                step(B, cidx + 1, A, min(cidx + 2, NC - 1));
+            }
         }
         sink += tA + tB;
         if (never) hT[0] = sink;   // the host always passes never = 0
