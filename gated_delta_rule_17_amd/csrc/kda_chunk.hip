@@ -38,6 +38,10 @@
 namespace kda {
 
 constexpr float kRangeMax = 80.f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x on the transcendental unit (x in log2 units; underflows to 0)
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int C, int DK, int DV, typename OT>
 struct CS {
@@ -65,10 +69,10 @@ struct CS {
     static constexpr size_t U_N = (size_t)DV * C;     // U^T     [DV][C]    float32
     // LDS, stage A: Qk (plain), Qq and Kd (precise), Kk (float32)
     static constexpr int STAGE_A = (1 + 2 * NP) * C * SK * SZ + C * SKF * 4;
-    // stage B: BkT, BvT (precise), A and T (float32); T as a precise operand aliases A
+    // stage B: BkT (plain), BvT (precise), A and T (float32); T as a precise operand aliases A
     static constexpr int TB_BYTES = NP * C * SC * SZ;
     static constexpr int AS_BYTES = (C * SA * 4 > TB_BYTES) ? C * SA * 4 : TB_BYTES;
-    static constexpr int STAGE_B = NP * (DK + DV) * SC * SZ + AS_BYTES + C * SA * 4;
+    static constexpr int STAGE_B = (DK + NP * DV) * SC * SZ + AS_BYTES + C * SA * 4;
     static constexpr int BIG = STAGE_A > STAGE_B ? STAGE_A : STAGE_B;
     static_assert(NSEG >= 1 && TPS >= 1 && NSEG * TPS == C, "shape");
     static_assert((C * SK * SZ) % 16 == 0 && (C * SC * SZ) % 16 == 0, "alignment");
@@ -122,6 +126,36 @@ __device__ __forceinline__ int accbase(int nt, int it, int NB, int lane) {
     return ((nt * NB + it) * 64 + lane) * 4;
 }
 
+// Store N consecutive values (N a power of two, p aligned to N elements) of
+// a plain operand with one vector store.
+template <typename OT, int N>
+__device__ __forceinline__ void store_run(OT* p, const float* x)
+{
+    if constexpr (sizeof(OT) == 2 && N >= 2) {
+        typedef uint16_t vec __attribute__((ext_vector_type(N)));
+        vec u;
+#pragma unroll
+        for (int e = 0; e < N; ++e) u[e] = f32_to_bf16(x[e]);
+        *reinterpret_cast<vec*>(p) = u;
+    } else if constexpr (sizeof(OT) == 4 && N >= 4) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+            *reinterpret_cast<f32x4*>(p + e) = (f32x4){x[e], x[e + 1], x[e + 2], x[e + 3]};
+    } else {
+#pragma unroll
+        for (int e = 0; e < N; ++e) io<OT>::store(p + e, x[e]);
+    }
+}
+
+// Column swizzle of a [row][CP] operand that is written column-wise: the
+// 8-column group of (row, j) is XOR-ed with row / 8, so that the rows 8 apart
+// written by one store instruction fall into different LDS banks.  Runs of 8
+// columns stay contiguous, so fragment reads are unchanged in cost.
+template <int CP>
+__device__ __forceinline__ int swz(int row, int j) {
+    return ((((j >> 3) ^ (row >> 3)) & (CP / 8 - 1)) << 3) | (j & 7);
+}
+
 // Store N consecutive values of a precise operand with the widest aligned stores
 // (N is a power of two; idx is a multiple of N).
 template <typename OT, int N>
@@ -134,6 +168,30 @@ __device__ __forceinline__ void store_run(const PArr<OT>& a, int idx, const floa
     } else {
 #pragma unroll
         for (int u = 0; u < N; ++u) store_p(a, idx + u, x[u]);
+    }
+}
+
+// Value held by lane J of this lane's 16-lane row (DPP row broadcast).
+template <int J>
+__device__ __forceinline__ float row_lane(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xf, 0xf, false));
+}
+
+// Column sweep of forward substitution for X = (I + A)^-1 of one 16x16 unit
+// lower triangular block: lane (r, g) holds row r of A in arow and
+// X[r][4g .. 4g+3] in x (initially the identity).  Step J eliminates column J
+// from every later row using row J of X, broadcast within each 16-lane row.
+template <int J>
+__device__ __forceinline__ void sweep16(float (&x)[4], const float (&arow)[16], int r) {
+    if constexpr (J < 15) {
+        float xj[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xj[u] = row_lane<J>(x[u]);
+        if (r > J) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] -= arow[J] * xj[u];
+        }
+        sweep16<J + 1>(x, arow, r);
     }
 }
 
@@ -153,9 +211,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 
     __shared__ __align__(16) char big[S::BIG];
     __shared__ float sb[C];
-    __shared__ float segtot[NSEG][DKP];
-    __shared__ float Gs[NB][DKP], Ge[NB][DKP], GLs[DKP];
-    __shared__ float eS[NB][DKP], eL[NB][DKP];
+    __shared__ float segtot[NSEG][DKP], segfirst[NSEG][DKP];
     __shared__ float fpair[S::NPAIR > 0 ? S::NPAIR : 1][DKP];
     __shared__ unsigned char flag[NB][DKP];
     __shared__ int anyflag;
@@ -164,7 +220,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     const int bh = blockIdx.y;
     const int b = bh / H, h = bh - b * H;
     const int t0 = c_idx * C;
-    const int L = min(C, T - t0);       // valid tokens
+    const int L = min(C, T - t0);       // valid tokens (>= 1)
     const size_t rec = (size_t)bh * NC + c_idx;
     const WsLayout<C, DK, DV, OT> W(ws, nrec);
     OT* const Wq = W.qg_rec(rec);
@@ -183,45 +239,69 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     float* Kk = (float*)(Qk + (1 + 2 * NP) * C * SK);              // [C][SKF] float32
 
     if (tid == 0) anyflag = 0;
-    for (int i = tid; i < C; i += S::NT) sb[i] = (i < L) ? beta[((size_t)b * T + t0 + i) * H + h] : 0.f;
 
-    // ---- cumulative log-decay: thread (seg, c) owns tokens seg*TPS .. +TPS-1 of channel c
-    const int c = tid % DKP, seg = tid / DKP;
+    // Thread (seg, c) owns tokens seg*TPS .. +TPS-1 of key channel c.  All
+    // global loads of the thread come first (g, k, q, beta, v) as straight-line
+    // code with clamped addresses, so that they are in flight together;
+    // out-of-range elements are zeroed afterwards.
+    // (seg is uniform across a wavefront when DKP is a multiple of 64: tell the
+    // compiler, so that token-row addresses and segment bookkeeping are scalar)
+    const int c = tid % DKP;
+    const int seg = DKP % 64 == 0 ? __builtin_amdgcn_readfirstlane(tid / DKP) : tid / DKP;
     const int i0 = seg * TPS;
-    // all global loads of this thread first (g, k, q, v), issued as straight-line
-    // code with clamped addresses so that they are all in flight together;
-    // out-of-range elements are zeroed afterwards
     const int cc = c < DK ? c : DK - 1;
+    auto token = [&](int i) { return ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h; };
     float G[TPS], kreg[TPS], qreg[TPS];
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
-        const int i = i0 + u;
-        const int ic = i < L ? i : L - 1;
-        const size_t tok = ((size_t)b * T + t0 + ic) * H + h;
+        const size_t tok = token(i0 + u);
         const float* gp = mode == KDA_GATE_CHANNEL ? g + tok * DK + cc
                         : (mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
         G[u] = *gp;
         kreg[u] = io<OT>::load(k + tok * DK + cc);
         qreg[u] = io<OT>::load(q + tok * DK + cc);
     }
-    // v rows as 8-element vectors (used for U = T Diag(beta) V later)
+    const float bload = beta[token(tid < C ? tid : C - 1)];
+    // v rows as 8-element vectors and the beta of each row (U = T Diag(beta) V)
     constexpr int NVEC = C * DV / 8, VPT = (NVEC + S::NT - 1) / S::NT;
     Frag<OT> vreg[VPT];
+    float vbeta[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
         const int idx = min(tid + S::NT * u, NVEC - 1);
         const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
-        const int ic = i < L ? i : L - 1;
-        vreg[u].load(v + (((size_t)b * T + t0 + ic) * H + h) * DV + n8);
+        vreg[u].load(v + token(i) * DV + n8);
+        vbeta[u] = beta[token(i)];
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (tid < C) sb[tid] = tid < L ? bload : 0.f;
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
         const bool ok = (i0 + u < L) && (c < DK);
-        G[u] = (ok && mode != KDA_GATE_NONE) ? G[u] : 0.f;
+        G[u] = (ok && mode != KDA_GATE_NONE) ? G[u] * kLog2e : 0.f;   // log2 units
         kreg[u] = ok ? kreg[u] : 0.f;
         qreg[u] = ok ? qreg[u] * scale : 0.f;
     }
+    // beta_i v_i in float32, formed now: the wait for the v loads then happens
+    // before this workgroup has issued any global store (the vector-memory
+    // counter also counts stores, so a later wait would include them)
+    float bv[VPT][8];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int idx = tid + S::NT * u;
+        const int i = idx / (DV / 8);
+        const float bi = (idx < NVEC && i < L) ? vbeta[u] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bv[u][e] = bi * vreg[u].get(e);
+            asm volatile("" : "+v"(bv[u][e]));
+        }
+    }
+
+    // ---- cumulative log-decay (in log2 units from here on, so that every
+    // decay factor is one 2^x).  Local running sums, then segment totals in
+    // LDS; every thread derives the references it needs from the totals with
+    // one left-to-right pass, so all threads obtain bit-identical values.
     {
         float run = 0.f;
 #pragma unroll
@@ -230,59 +310,59 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             G[u] = run;
         }
         segtot[seg][c] = run;
+        segfirst[seg][c] = G[0];
     }
     __syncthreads();
+    const int Iblk = i0 >> 4;                     // this thread's 16-token block
+    const int s_first = (16 * Iblk) / TPS, s_last = (16 * Iblk + 15) / TPS;
+    // the block pair (pI, pJ), pJ < pI, whose cross factor this thread computes
+    const bool has_pair = seg < S::NPAIR;
+    int pI = 1, pJ = 0;
     {
-        float off = 0.f;
-        for (int s2 = 0; s2 < seg; ++s2) off += segtot[s2][c];
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) G[u] += off;
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-            const int i = i0 + u;
-            if ((i & 15) == 0) Gs[i >> 4][c] = G[u];
-            if ((i & 15) == 15) Ge[i >> 4][c] = G[u];
-            if (i == C - 1) GLs[c] = G[u];
-        }
+        int base = 0;
+        while (base + pI <= seg) { base += pI; ++pI; }
+        pJ = seg - base;
     }
-    __syncthreads();
-    // ---- per-block factors, gl, range flags
-    for (int p = tid; p < NB * DKP; p += S::NT) {
-        const int I = p / DKP, cc = p % DKP;
-        eS[I][cc] = __expf(Gs[I][cc]);
-        eL[I][cc] = __expf(GLs[cc] - Ge[I][cc]);
-        const bool bad = (Gs[I][cc] - Ge[I][cc]) > kRangeMax;
-        flag[I][cc] = bad ? 1 : 0;
+    const int p_first = (16 * pI) / TPS, p_last = (16 * pJ + 15) / TPS;
+    float off = 0.f, gs = 0.f, ge = 0.f, fgs = 0.f, fge = 0.f, acc = 0.f;
+    for (int s2 = 0; s2 < NSEG; ++s2) {
+        const float first = segfirst[s2][c];
+        if (s2 == seg) off = acc;
+        if (s2 == s_first) gs = acc + first;      // G at the block's first token
+        if (s2 == p_first) fgs = acc + first;
+        acc += segtot[s2][c];
+        if (s2 == s_last) ge = acc;               // G at the block's last token
+        if (s2 == p_last) fge = acc;
+    }
+    const float gL = acc;                         // G at the chunk's last token
+#pragma unroll
+    for (int u = 0; u < TPS; ++u) G[u] += off;
+    const float eS = exp2_fast(gs);               // exp(G_s(I)) <= 1
+    const float eL = exp2_fast(gL - ge);          // exp(G_last - G_e(I)) <= 1
+    const bool bad = (gs - ge) > kRangeMax * kLog2e;
+    if (seg == s_first) {
+        flag[Iblk][c] = bad ? 1 : 0;
         if (bad) atomicOr(&anyflag, 1);
     }
-    for (int p = tid; p < S::NPAIR * DKP; p += S::NT) {
-        const int pi = p / DKP, cc = p % DKP;
-        // pair index pi enumerates (I, J), J < I, row by row: I=1:J=0; I=2:J=0,1; ...
-        int I = 1, base = 0;
-        while (base + I <= pi) { base += I; ++I; }
-        const int J = pi - base;
-        fpair[pi][cc] = __expf(Gs[I][cc] - Ge[J][cc]);
-    }
-    for (int cc = tid; cc < DK; cc += S::NT) W.gl[rec * DK + cc] = __expf(GLs[cc]);
-    __syncthreads();
+    if (has_pair) fpair[seg][c] = exp2_fast(fgs - fge);   // exp(G_s(pI) - G_e(pJ)) <= 1
+    if (seg == 0 && c < DK) W.gl[rec * DK + c] = exp2_fast(gL);
 
     // ---- element-wise operands
     float egreg[TPS], krv[TPS];
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
         const int i = i0 + u;
-        const int I = i >> 4;
         const float kv = kreg[u], qv = qreg[u];
-        const float x = __expf(G[u] - Gs[I][c]);          // <= 1
-        const float kk = kv * __expf(Ge[I][c] - G[u]);    // <= |k|
-        const float kd = flag[I][c] ? 0.f : kv * __expf(Gs[I][c] - G[u]);  // >= |k|, bounded
+        const float x = exp2_fast(G[u] - gs);              // <= 1
+        const float kk = kv * exp2_fast(ge - G[u]);        // <= |k|
+        const float kd = bad ? 0.f : kv * exp2_fast(gs - G[u]);  // >= |k|, bounded
         store_op(Qk + i * SK + c, kv * x);
         store_p(Qq, i * SK + c, qv * x);
         store_p(Kd, i * SK + c, kd);
         Kk[i * SKF + c] = kk;
-        const float eg = x * eS[I][c];                     // exp(G_i) <= 1
+        const float eg = x * eS;                           // exp(G_i) <= 1
         egreg[u] = eg;
-        krv[u] = kk * eL[I][c];                            // k exp(G_last - G_i) <= |k|
+        krv[u] = kk * eL;                                  // k exp(G_last - G_i) <= |k|
         store_op(Wq + fragidx(i, c, DKP / 32), qv * eg);
     }
     // Kr^T row c, tokens i0 .. i0+TPS-1, four at a time (contiguous in the fragment layout)
@@ -353,10 +433,9 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     __syncthreads();   // stage-A operands are dead from here on
 
     // stage-B layout (aliases stage A)
-    OT* bkt_h = (OT*)big;
-    const PArr<OT> BkT{bkt_h, bkt_h + DK * SC};                    // [DK][SC] beta_j k_j exp(G_j)
-    OT* bvt_h = bkt_h + NP * DK * SC;
-    const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j
+    OT* const BkT = (OT*)big;                                      // [DK][SC] beta_j k_j exp(G_j), plain
+    OT* bvt_h = BkT + DK * SC;
+    const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j, swizzled
     float* As = (float*)(bvt_h + NP * DV * SC);                    // [C][SA]  A (strictly lower, with beta)
     float* Ts = (float*)((char*)As + S::AS_BYTES);                 // [C][SA]  T = (I + A)^-1
     const PArr<OT> Tb{(OT*)As, (OT*)As + C * SC};                  // [C][SC]  T as an operand (after the solve)
@@ -386,20 +465,28 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             else store4_p(Waq, fragidx(i, j0, CP / 32), qv);
         }
     }
-    // zero the strictly upper blocks of A (and of the Aqk staging / record)
-    for (int p = tid; p < C * C; p += S::NT) {
-        const int i = p / C, j = p % C;
-        if ((j >> 4) > (i >> 4)) {
-            As[i * SA + j] = 0.f;
-            if (fallback) Aq32[i * SA + j] = 0.f;
-            else store_p(Waq, fragidx(i, j, CP / 32), 0.f);
+    // zero the strictly upper blocks of A (and of the Aqk staging / record),
+    // eight columns at a time (a run of 8 is contiguous in the fragment layout)
+    for (int p = tid; p < C * (C / 8); p += S::NT) {
+        const int i = p / (C / 8), j8 = 8 * (p % (C / 8));
+        if ((j8 >> 4) > (i >> 4)) {
+            *reinterpret_cast<f32x4*>(As + i * SA + j8) = zero4();
+            *reinterpret_cast<f32x4*>(As + i * SA + j8 + 4) = zero4();
+            if (fallback) {
+                *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8) = zero4();
+                *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8 + 4) = zero4();
+            } else {
+                store4_p(Waq, fragidx(i, j8, CP / 32), zero4());
+                store4_p(Waq, fragidx(i, j8, CP / 32) + 4, zero4());
+            }
         }
     }
     // beta_j k_j exp(G_j) and beta_j v_j, transposed ([channel][token])
+    if (c < DK) {
+        float bk[TPS];
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const int i = i0 + u;
-        if (c < DK) store_p(BkT, c * SC + i, sb[i] * kreg[u] * egreg[u]);
+        for (int u = 0; u < TPS; ++u) bk[u] = sb[i0 + u] * kreg[u] * egreg[u];
+        store_run<OT, TPS>(BkT + c * SC + i0, bk);
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -407,17 +494,17 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         if (idx < NVEC) {
             const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + i, sb[i] * vreg[u].get(e));
+            for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
         }
     }
     if (CP > C) {
         for (int p = tid; p < DK * (CP - C); p += S::NT) {
             const int row = p / (CP - C), i = C + p % (CP - C);
-            store_p(BkT, row * SC + i, 0.f);
+            store_op(BkT + row * SC + i, 0.f);
         }
         for (int p = tid; p < DV * (CP - C); p += S::NT) {
             const int row = p / (CP - C), i = C + p % (CP - C);
-            store_p(BvT, row * SC + i, 0.f);
+            store_p(BvT, row * SC + swz<CP>(row, i), 0.f);
         }
     }
     __syncthreads();
@@ -470,16 +557,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         float x[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) x[u] = (4 * gq + u == r) ? 1.f : 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 15; ++jj) {
-            float xj[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) xj[u] = __shfl(x[u], jj, 16);
-            if (r > jj) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) x[u] -= arow[jj] * xj[u];
-            }
-        }
+        sweep16<0>(x, arow, r);
 #pragma unroll
         for (int u = 0; u < 4; ++u) Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u] = x[u];
     }
@@ -533,8 +611,12 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                 f32x4 acc = zero4();
                 const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
                 for (int ks = 0; ks < nks; ++ks)   // W is stored as a plain operand
-                    acc = mma(BkT.frag((16 * m + r) * SC + 32 * ks + 8 * gq).h,
-                              Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq).h, acc);
+                {
+                    Frag<OT> a, t;
+                    a.load(BkT + (16 * m + r) * SC + 32 * ks + 8 * gq);
+                    t.load(Tb.h + (16 * I + r) * SC + 32 * ks + 8 * gq);
+                    acc = mma(a, t, acc);
+                }
                 // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
                 Vec4<OT>::store(Wwn + fragidx(16 * I + r, 16 * m + 4 * gq, DKP / 32), -acc);
             } else {
@@ -544,7 +626,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                 const int nks = (16 * I + 15) / 32 + 1;
                 for (int ks = 0; ks < nks; ++ks)
                     acc = mma3(Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq),
-                               BvT.frag((16 * nn + r) * SC + 32 * ks + 8 * gq), acc);
+                               BvT.frag((16 * nn + r) * SC + swz<CP>(16 * nn + r, 32 * ks + 8 * gq)), acc);
                 // lane holds U[16I + 4gq + u][16nn + r]: accumulator-major block (nn, I)
                 Vec4<float>::store(Wut + accbase(nn, I, NB, lane), acc);
             }
