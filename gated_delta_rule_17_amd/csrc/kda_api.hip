@@ -89,6 +89,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
     if (Dk != Dv) return KDA_ERROR_NOT_SUPPORTED;
+    // chunk records and state workgroups are counted in 32-bit integers
+    const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
+    if (nrec > 1073741824.0 || (double)B * H * (Dv / 16) + 64.0 > 2147483647.0)
+        return KDA_ERROR_INVALID_VALUE;
     if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
         return KDA_ERROR_MISALIGNED;
     const size_t need = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype);

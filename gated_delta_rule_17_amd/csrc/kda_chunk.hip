@@ -644,17 +644,31 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 // chunk_state: sequential pass over the chunks of one (b, h), 16 value columns
 // (h0 and hT may be the same buffer: each workgroup reads exactly the state
 // entries it later writes, and reads them first)
+//
+// Eight wavefronts in two roles, two per SIMD:
+//   waves 0-3, the chain:  E = U - W H and H = Diag(gl) H + Kr^T E, the
+//                          sequential dependence from chunk to chunk;
+//   waves 4-7, the output: o = Qg H + Aqk E, which nothing later depends on.
+// Both roles meet at the two barriers of every chunk step (E published;
+// H published), so the output work and its operand loads run beside the
+// chain on the same SIMDs instead of in series with it.
 // ---------------------------------------------------------------------------
 template <int C, int DK, int DV, typename OT, typename OUT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
-            int T, int H, int BH, int NC, const void* __restrict__ ws, size_t nrec, int never)
+            int T, int H, int BH, int NC, const void* ws, size_t nrec)
 {
+    // (ws is deliberately not __restrict__: with it, the record loads count as
+    // invariant and the compiler sinks the next chunk's operand loads past the
+    // barriers to the point of use, which undoes the prefetch)
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SC = S::SC, NP = S::NP;
     constexpr int NCT = DV / 16;          // column tiles per head
     constexpr int MH = DK / 16;           // 16-row tiles of the state
-    constexpr int MHW = (MH + 3) / 4;     // state tiles per wave
+    constexpr int MHW = (MH + 3) / 4;     // state tiles per chain wave
+    constexpr int KS = DKP / 32, KC = CP / 32;
+    constexpr bool ALLE = NB >= 4;        // every wave of a role owns a token tile
+    constexpr bool ALLH = (MH % 4) == 0;  // every chain wave owns MHW state tiles
 
     __shared__ __align__(16) OT HTs[NP * 16 * SK];   // H^T tile [n][c] (precise operand)
     __shared__ __align__(16) OT ETs[NP * 16 * SC];   // E^T tile [n][j] (precise operand)
@@ -675,210 +689,173 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, gq = lane >> 4;
+    const bool chain = wave < 4;
+    const int wr = wave & 3;                               // index within the role
+    const int we = ALLE ? wr : (wr < NB ? wr : NB - 1);    // token tile of E / o
+    const bool has_t = ALLE || wr < NB;
 
     // zero the operand tiles (padding stays zero)
-    for (int p = tid; p < NP * 16 * SK; p += 256) store_op(HTs + p, 0.f);
-    for (int p = tid; p < NP * 16 * SC; p += 256) store_op(ETs + p, 0.f);
+    for (int p = tid; p < NP * 16 * SK; p += 512) store_op(HTs + p, 0.f);
+    for (int p = tid; p < NP * 16 * SC; p += 512) store_op(ETs + p, 0.f);
     __syncthreads();
 
-    f32x4 hacc[MHW];
-#pragma unroll
-    for (int s = 0; s < MHW; ++s) {
-        hacc[s] = zero4();
-        const int mt = wave + 4 * s;
-        if (mt < MH && h0) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                hacc[s][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r];
-        }
-        if (mt < MH) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
-    }
-    __syncthreads();
+    auto rec_of = [&](int cidx) { return (size_t)bh * NC + cidx; };
 
-    // Operands of one chunk step held by this wave.  Two sets alternate: the
-    // next chunk's set is loaded while the current one is used, so the
-    // sequential chain does not wait on memory latency at every step.  The
-    // loads are unconditional straight-line code (indices clamped; zero
-    // padding in the records makes the extra fragments harmless) so that the
-    // wait for one set never includes the loads of the other.
-    constexpr int KS = DKP / 32, KC = CP / 32;
-    constexpr bool ALLE = NB >= 4;        // every wave owns an E / o tile
-    constexpr bool ALLH = (MH % 4) == 0;  // every wave owns MHW state tiles
-    const int we = ALLE ? wave : (wave < NB ? wave : NB - 1);
-    struct Ops {
-        Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
-        Frag<OT> qg[KS];         // Qg rows 16*we.. (B operand of o^T)
-        PFrag<OT> aq[KC];        // Aqk rows 16*we.. (B operand of o^T)
-        PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
-        f32x4 u;                 // U^T init of E
-        f32x4 gl[MHW];           // exp(G_last) for the state rows
-    };
-    // record pointers of one chunk for this wave
-    struct Rec {
-        const OT* wn; const OT* qg; PArr<OT> kr, aq; const float* u; const float* gl;
-    };
-    auto rec_of = [&](int cidx) {
-        const size_t rec = (size_t)bh * NC + cidx;
-        Rec R;
-        R.wn = W.wneg_rec(rec); R.qg = W.qg_rec(rec); R.kr = W.krt(rec); R.aq = W.aqk(rec);
-        R.u = W.ut + rec * S::U_N; R.gl = W.gl + rec * DK;
-        return R;
-    };
-    auto mt_of = [&](int s) { return ALLH ? wave + 4 * s : min(wave + 4 * s, MH - 1); };
-    auto load_ops = [&](Ops& P, int cidx) {
-        const Rec R = rec_of(cidx);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            P.wn[ks].load(R.wn + fragbase(we, ks, KS, lane));
-            P.qg[ks].load(R.qg + fragbase(we, ks, KS, lane));
-        }
-#pragma unroll
-        for (int ks = 0; ks < KC; ++ks) P.aq[ks] = R.aq.frag(fragbase(we, ks, KC, lane));
-        P.u = Vec4<float>::load(R.u + accbase(ct, we, NB, lane));
+    if (chain) {
+        f32x4 hacc[MHW];
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
-#pragma unroll
-            for (int ks = 0; ks < KC; ++ks) P.kr[s][ks] = R.kr.frag(fragbase(mt_of(s), ks, KC, lane));
-            P.gl[s] = *reinterpret_cast<const f32x4*>(R.gl + 16 * mt_of(s) + 4 * gq);
-        }
-    };
-
-    // L2 prefetch: the NCT column-tile workgroups of a head run in lockstep and
-    // would all miss on the same record lines at the same time.  Each one
-    // therefore touches a disjoint 1/NCT of the shared part of record c + 3
-    // (one dword per 128-byte line) plus its own U^T slice, three steps before
-    // the register loads need them.  The touched values are folded into a sink
-    // one loop iteration later, so the loads stay in flight meanwhile.
-    constexpr int LINE = 128;
-    constexpr int SEG_W = (int)(S::W_N * S::SZ / LINE), SEG_Q = (int)(S::Q_N * S::SZ / LINE);
-    constexpr int SEG_K = (int)(S::KR_N * S::SZ / LINE), SEG_A = (int)(S::AQ_N * S::SZ / LINE);
-    constexpr int SHARED_LINES = SEG_W + SEG_Q + NP * (SEG_K + SEG_A);
-    constexpr int PER_TILE = (SHARED_LINES + NCT - 1) / NCT;
-    constexpr int UT_LINES = 16 * C * 4 / LINE;
-    constexpr int MAXT = 256 - UT_LINES;                // one touch per thread at most
-    constexpr int STRIDE = (PER_TILE + MAXT - 1) / MAXT;  // sparser touches for few tiles
-    constexpr int NSH = (PER_TILE + STRIDE - 1) / STRIDE;
-    constexpr int TOUCH = NSH + UT_LINES;               // lines this workgroup touches
-    constexpr int TW = (TOUCH + 63) / 64;               // waves that touch
-    static_assert(TW <= 4, "touch lines exceed one load per thread");
-    auto touch = [&](int cidx) -> float {
-        const size_t rec = (size_t)bh * NC + cidx;
-        const int m = (wave * 64 + lane);
-        if (wave >= TW || m >= TOUCH) return 0.f;
-        const char* p;
-        if (m < NSH) {
-            int L = ct + NCT * (m * STRIDE);
-            if (L >= SHARED_LINES) L = SHARED_LINES - 1;
-            if (L < SEG_W) p = (const char*)(W.wneg + rec * S::W_N) + L * LINE;
-            else if ((L -= SEG_W) < SEG_Q) p = (const char*)(W.qg + rec * S::Q_N) + L * LINE;
-            else if ((L -= SEG_Q) < SEG_K) p = (const char*)(W.krt_h + rec * S::KR_N) + L * LINE;
-            else if (NP == 2 && (L -= SEG_K) < SEG_K) p = (const char*)(W.krt_l + rec * S::KR_N) + L * LINE;
-            else {
-                L -= SEG_K;   // past Kr^T lo (hi/lo records) or past Kr^T (float32 records)
-                if (L < SEG_A) p = (const char*)(W.aqk_h + rec * S::AQ_N) + L * LINE;
-                else p = (const char*)(W.aqk_l + rec * S::AQ_N) + (L - SEG_A) * LINE;
-            }
-        } else {
-            p = (const char*)(W.ut + rec * S::U_N + (size_t)n0 * C) + (m - NSH) * LINE;
-        }
-        return *reinterpret_cast<const float*>(p);
-    };
-
-    // One chunk step with operands P; the operands of chunk `nxt` are loaded
-    // into Q one fragment per matrix-core k-step, so the load traffic of the
-    // four wavefronts is spread over the step instead of queueing up at once.
-    auto step = [&](const Ops& P, int cidx, Ops& Q, int nxt) {
-        const int t0 = cidx * C;
-        const int L = min(C, T - t0);
-        const bool has_e = ALLE || wave < NB;
-        const Rec R = rec_of(nxt);
-        f32x4 oacc = zero4();
-        f32x4 e = P.u;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            Q.wn[ks].load(R.wn + fragbase(we, ks, KS, lane));
-            if (has_e) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            Q.qg[ks].load(R.qg + fragbase(we, ks, KS, lane));
-            if (has_e) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
-        }
-        if (has_e) store4_p(ET, r * SC + 16 * wave + 4 * gq, e);
-        // keep the compiler from clustering this region's loads ahead of its
-        // matrix-core work: alternate one global load with two MFMA steps
-#pragma unroll
-        for (int g2 = 0; g2 < 2 * KS; ++g2) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < KC; ++ks) {
-            Q.aq[ks] = R.aq.frag(fragbase(we, ks, KC, lane));
-            if (has_e) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
-        }
-        Q.u = Vec4<float>::load(R.u + accbase(ct, we, NB, lane));
-        if (has_e) {
-            // lane holds o^T[n = 4gq + u][i = 16*wave + r]
-            const int i = 16 * wave + r;
-            if (i < L) {
-                OUT* op = o + (((size_t)b * T + t0 + i) * H + h) * DV + n0 + 4 * gq;
-                Vec4<OUT>::store(op, oacc);
-            }
-        }
-        // H = Diag(gl) H + Kr^T E
-#pragma unroll
-        for (int s = 0; s < MHW; ++s) {
-            const int mt = wave + 4 * s;
-            const bool own = ALLH || mt < MH;
-            if (own) hacc[s] *= P.gl[s];
-#pragma unroll
-            for (int ks = 0; ks < KC; ++ks) {
-                Q.kr[s][ks] = R.kr.frag(fragbase(mt_of(s), ks, KC, lane));
-                if (own) hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
-            }
-            Q.gl[s] = *reinterpret_cast<const f32x4*>(R.gl + 16 * mt_of(s) + 4 * gq);
-            if (own) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
-        }
-        // alternate one global load with one MFMA step in this region too
-#pragma unroll
-        for (int g2 = 0; g2 < NP * KC * (1 + MHW) + 1 + MHW; ++g2) {
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        }
-        __syncthreads();
-    };
-
-    if (NC > 0) {
-        // sched_barrier keeps the compiler from sinking a load batch towards
-        // its first use, which would turn the prefetch back into a stall
-        Ops A, B;
-        float sink = 0.f, tA = 0.f, tB = 0.f;
-        tA = touch(min(1, NC - 1));
-        tB = touch(min(2, NC - 1));
-        load_ops(A, 0);
-        for (int cidx = 0; cidx < NC; cidx += 2) {
-            sink += tA;
-            tA = touch(min(cidx + 3, NC - 1));
-            step(A, cidx, B, min(cidx + 1, NC - 1));
-            if (cidx + 1 < NC) {
-                sink += tB;
-                tB = touch(min(cidx + 4, NC - 1));
-                step(B, cidx + 1, A, min(cidx + 2, NC - 1));
-            }
-        }
-        sink += tA + tB;
-        if (never) hT[0] = sink;   // the host always passes never = 0
-    }
-    if (hT) {
-#pragma unroll
-        for (int s = 0; s < MHW; ++s) {
-            const int mt = wave + 4 * s;
-            if (mt < MH) {
+            hacc[s] = zero4();
+            const int mt = wr + 4 * s;
+            if (mt < MH && h0) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r] = hacc[s][u];
+                    hacc[s][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r];
+            }
+            if (mt < MH) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+        }
+        __syncthreads();
+
+        // Operands of one chunk step.  Two sets alternate: the next chunk's set
+        // is loaded while the current one is used.  The loads are
+        // unconditional straight-line code (indices clamped; zero padding in
+        // the records makes the extra fragments harmless) so that the wait for
+        // one set never includes the loads of the other.
+        struct Ops {
+            Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
+            PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
+            f32x4 u;                 // U^T init of E
+            f32x4 gl[MHW];           // exp(G_last) for the state rows
+        };
+        auto mt_of = [&](int s) { return ALLH ? wr + 4 * s : min(wr + 4 * s, MH - 1); };
+        auto load_ops = [&](Ops& P, int cidx) {
+            const size_t rec = rec_of(cidx);
+            const OT* wn = W.wneg_rec(rec);
+            const PArr<OT> kr = W.krt(rec);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) P.wn[ks].load(wn + fragbase(we, ks, KS, lane));
+            P.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+#pragma unroll
+                for (int ks = 0; ks < KC; ++ks) P.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
+                P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
+            }
+        };
+        // One chunk step with operands P; the operands of chunk `nxt` are
+        // loaded into Q one fragment per matrix-core step, spreading the load
+        // traffic over the step.
+        auto step = [&](const Ops& P, Ops& Q, int nxt) {
+            const size_t rec = rec_of(nxt);
+            const OT* wn = W.wneg_rec(rec);
+            const PArr<OT> kr = W.krt(rec);
+            f32x4 e = P.u;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Q.wn[ks].load(wn + fragbase(we, ks, KS, lane));
+                if (has_t) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
+            }
+            if (has_t) store4_p(ET, r * SC + 16 * wr + 4 * gq, e);
+#pragma unroll
+            for (int g2 = 0; g2 < KS; ++g2) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __syncthreads();
+            // H = Diag(gl) H + Kr^T E
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+                const int mt = wr + 4 * s;
+                const bool own = ALLH || mt < MH;
+                if (own) hacc[s] *= P.gl[s];
+#pragma unroll
+                for (int ks = 0; ks < KC; ++ks) {
+                    Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
+                    if (own) hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
+                }
+                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
+                if (own) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+            }
+            Q.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+#pragma unroll
+            for (int g2 = 0; g2 < NP * KC * MHW + MHW + 1; ++g2) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            }
+            __syncthreads();
+        };
+        if (NC > 0) {
+            Ops A, B;
+            load_ops(A, 0);
+            for (int cidx = 0; cidx < NC; cidx += 2) {
+                step(A, B, min(cidx + 1, NC - 1));
+                if (cidx + 1 < NC) step(B, A, min(cidx + 2, NC - 1));
+            }
+        }
+        if (hT) {
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+                const int mt = wr + 4 * s;
+                if (mt < MH) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r] = hacc[s][u];
+                }
+            }
+        }
+    } else {
+        __syncthreads();   // initial state published
+        struct Ops {
+            Frag<OT> qg[KS];         // Qg rows 16*we.. (B operand of o^T)
+            PFrag<OT> aq[KC];        // Aqk rows 16*we.. (B operand of o^T)
+        };
+        auto load_ops = [&](Ops& P, int cidx) {
+            const size_t rec = rec_of(cidx);
+            const OT* qg = W.qg_rec(rec);
+            const PArr<OT> aq = W.aqk(rec);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) P.qg[ks].load(qg + fragbase(we, ks, KS, lane));
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks) P.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
+        };
+        auto step = [&](const Ops& P, int cidx, Ops& Q, int nxt) {
+            const size_t rec = rec_of(nxt);
+            const OT* qg = W.qg_rec(rec);
+            const PArr<OT> aq = W.aqk(rec);
+            f32x4 oacc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                Q.qg[ks].load(qg + fragbase(we, ks, KS, lane));
+                if (has_t) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
+            }
+#pragma unroll
+            for (int g2 = 0; g2 < KS; ++g2) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks) {
+                Q.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
+                if (has_t) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
+            }
+            if (has_t) {
+                // lane holds o^T[n = 4gq + u][i = 16*wr + r]
+                const int t0 = cidx * C;
+                const int i = 16 * wr + r;
+                if (i < min(C, T - t0)) {
+                    OUT* op = o + (((size_t)b * T + t0 + i) * H + h) * DV + n0 + 4 * gq;
+                    Vec4<OUT>::store(op, oacc);
+                }
+            }
+            __syncthreads();
+        };
+        if (NC > 0) {
+            Ops A, B;
+            load_ops(A, 0);
+            for (int cidx = 0; cidx < NC; cidx += 2) {
+                step(A, cidx, B, min(cidx + 1, NC - 1));
+                if (cidx + 1 < NC) step(B, cidx + 1, A, min(cidx + 2, NC - 1));
             }
         }
     }
@@ -901,11 +878,11 @@ static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
     const int groups = (BH + 7) / 8;
     const dim3 grid(groups * 8 * (DV / 16));
     if (a.o_dtype == KDA_F32)
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float>), grid, dim3(256), 0, s,
-                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, 0);
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float>), grid, dim3(512), 0, s,
+                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
     else
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(256), 0, s,
-                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, 0);
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(512), 0, s,
+                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
     return hipGetLastError();
 }
 
