@@ -32,6 +32,8 @@
 // key channel whose decay across one block exceeds kRangeMax is removed from
 // that diagonal block's matrix-core product and added exactly, term by term,
 // on the vector units instead.
+#include <atomic>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -202,12 +204,13 @@ template <int C, int DK, int DV, typename OT>
 __global__ void __launch_bounds__(1024)
 chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
-              int T, int H, int NC, float scale, int mode, void* __restrict__ ws, size_t nrec)
+              int T, int H, int NC, int NITEM, float scale, int mode, void* __restrict__ ws, size_t nrec)
 {
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SKF = S::SKF, SC = S::SC,
                   SA = S::SA, NP = S::NP;
     constexpr int NSEG = S::NSEG, TPS = S::TPS;
+    constexpr int NVEC = C * DV / 8, VPT = (NVEC + S::NT - 1) / S::NT;
 
     __shared__ __align__(16) char big[S::BIG];
     __shared__ float sb[C];
@@ -216,427 +219,482 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     __shared__ unsigned char flag[NB][DKP];
     __shared__ int anyflag;
 
-    const int c_idx = blockIdx.x;        // chunk
-    const int bh = blockIdx.y;
-    const int b = bh / H, h = bh - b * H;
-    const int t0 = c_idx * C;
-    const int L = min(C, T - t0);       // valid tokens (>= 1)
-    const size_t rec = (size_t)bh * NC + c_idx;
     const WsLayout<C, DK, DV, OT> W(ws, nrec);
-    OT* const Wq = W.qg_rec(rec);
-    OT* const Wwn = W.wneg_rec(rec);
-    const PArr<OT> Wkr = W.krt(rec), Waq = W.aqk(rec);
-    float* Wut = W.ut + rec * S::U_N;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, gq = lane >> 4;
-
-    // stage-A arrays
-    OT* Qk = (OT*)big;                                             // [C][SK] plain
-    const PArr<OT> Qq{Qk + C * SK, Qk + 2 * C * SK};               // [C][SK] precise
-    const PArr<OT> Kd{Qk + (1 + NP) * C * SK, Qk + (2 + NP) * C * SK};  // [C][SK] precise
-    float* Kk = (float*)(Qk + (1 + 2 * NP) * C * SK);              // [C][SKF] float32
-
-    if (tid == 0) anyflag = 0;
-
-    // Thread (seg, c) owns tokens seg*TPS .. +TPS-1 of key channel c.  All
-    // global loads of the thread come first (g, k, q, beta, v) as straight-line
-    // code with clamped addresses, so that they are in flight together;
-    // out-of-range elements are zeroed afterwards.
+    // Thread (seg, c) owns tokens seg*TPS .. +TPS-1 of key channel c.
     // (seg is uniform across a wavefront when DKP is a multiple of 64: tell the
     // compiler, so that token-row addresses and segment bookkeeping are scalar)
-    const int c = tid % DKP;
-    const int seg = DKP % 64 == 0 ? __builtin_amdgcn_readfirstlane(tid / DKP) : tid / DKP;
-    const int i0 = seg * TPS;
-    const int cc = c < DK ? c : DK - 1;
-    auto token = [&](int i) { return ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h; };
-    float G[TPS], kreg[TPS], qreg[TPS];
-#pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const size_t tok = token(i0 + u);
-        const float* gp = mode == KDA_GATE_CHANNEL ? g + tok * DK + cc
-                        : (mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
-        G[u] = *gp;
-        kreg[u] = io<OT>::load(k + tok * DK + cc);
-        qreg[u] = io<OT>::load(q + tok * DK + cc);
-    }
-    const float bload = beta[token(tid < C ? tid : C - 1)];
-    // v rows as 8-element vectors and the beta of each row (U = T Diag(beta) V)
-    constexpr int NVEC = C * DV / 8, VPT = (NVEC + S::NT - 1) / S::NT;
-    Frag<OT> vreg[VPT];
-    float vbeta[VPT];
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int idx = min(tid + S::NT * u, NVEC - 1);
-        const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
-        vreg[u].load(v + token(i) * DV + n8);
-        vbeta[u] = beta[token(i)];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (tid < C) sb[tid] = tid < L ? bload : 0.f;
-#pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const bool ok = (i0 + u < L) && (c < DK);
-        G[u] = (ok && mode != KDA_GATE_NONE) ? G[u] * kLog2e : 0.f;   // log2 units
-        kreg[u] = ok ? kreg[u] : 0.f;
-        qreg[u] = ok ? qreg[u] * scale : 0.f;
-    }
-    // beta_i v_i in float32, formed now: the wait for the v loads then happens
-    // before this workgroup has issued any global store (the vector-memory
-    // counter also counts stores, so a later wait would include them)
-    float bv[VPT][8];
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int idx = tid + S::NT * u;
-        const int i = idx / (DV / 8);
-        const float bi = (idx < NVEC && i < L) ? vbeta[u] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bv[u][e] = bi * vreg[u].get(e);
-            asm volatile("" : "+v"(bv[u][e]));
-        }
-    }
+    auto seg_of = [](int tid) {
+        return DKP % 64 == 0 ? __builtin_amdgcn_readfirstlane(tid / DKP) : tid / DKP;
+    };
 
-    // ---- cumulative log-decay (in log2 units from here on, so that every
-    // decay factor is one 2^x).  Local running sums, then segment totals in
-    // LDS; every thread derives the references it needs from the totals with
-    // one left-to-right pass, so all threads obtain bit-identical values.
-    {
-        float run = 0.f;
+    // The global inputs of one chunk as this thread reads them: g, k, q of its
+    // tokens, the beta of token tid, and v rows as 8-element vectors with their
+    // beta.  Straight-line loads with clamped addresses (out-of-range elements
+    // are zeroed where they are used), in five groups: group 0 the v rows and
+    // betas, groups 1-4 a quarter of the tokens each.
+    struct In {
+        float G[TPS], k[TPS], q[TPS];
+        float bl;
+        Frag<OT> v[VPT];
+        float vb[VPT];
+    };
+    auto load_in = [&](In& x, int item, int tid, int grp) {
+        const int c = tid % DKP, i0 = seg_of(tid) * TPS;
+        const int cc = c < DK ? c : DK - 1;
+        const int bh = item / NC, c_idx = item - bh * NC;
+        const int b = bh / H, h = bh - b * H;
+        const int t0 = c_idx * C;
+        const int L = min(C, T - t0);
+        auto token = [&](int i) { return ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h; };
+        if (grp == 0) {
+            x.bl = beta[token(tid < C ? tid : C - 1)];
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) {
+                const int idx = min(tid + S::NT * u, NVEC - 1);
+                const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
+                x.v[u].load(v + token(i) * DV + n8);
+                x.vb[u] = beta[token(i)];
+            }
+        }
 #pragma unroll
         for (int u = 0; u < TPS; ++u) {
-            run += G[u];
-            G[u] = run;
+            if ((TPS >= 4 ? (u * 4) / TPS : u) + 1 != grp) continue;
+            const size_t tok = token(i0 + u);
+            const float* gp = mode == KDA_GATE_CHANNEL ? g + tok * DK + cc
+                            : (mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
+            x.G[u] = *gp;
+            x.k[u] = io<OT>::load(k + tok * DK + cc);
+            x.q[u] = io<OT>::load(q + tok * DK + cc);
         }
-        segtot[seg][c] = run;
-        segfirst[seg][c] = G[0];
-    }
-    __syncthreads();
-    const int Iblk = i0 >> 4;                     // this thread's 16-token block
-    const int s_first = (16 * Iblk) / TPS, s_last = (16 * Iblk + 15) / TPS;
-    // the block pair (pI, pJ), pJ < pI, whose cross factor this thread computes
-    const bool has_pair = seg < S::NPAIR;
-    int pI = 1, pJ = 0;
-    {
-        int base = 0;
-        while (base + pI <= seg) { base += pI; ++pI; }
-        pJ = seg - base;
-    }
-    const int p_first = (16 * pI) / TPS, p_last = (16 * pJ + 15) / TPS;
-    float off = 0.f, gs = 0.f, ge = 0.f, fgs = 0.f, fge = 0.f, acc = 0.f;
-    for (int s2 = 0; s2 < NSEG; ++s2) {
-        const float first = segfirst[s2][c];
-        if (s2 == seg) off = acc;
-        if (s2 == s_first) gs = acc + first;      // G at the block's first token
-        if (s2 == p_first) fgs = acc + first;
-        acc += segtot[s2][c];
-        if (s2 == s_last) ge = acc;               // G at the block's last token
-        if (s2 == p_last) fge = acc;
-    }
-    const float gL = acc;                         // G at the chunk's last token
+    };
+    // Make loaded values available at this point (the wait for their loads
+    // is placed here).
+    auto settle = [&](In& x) {
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) G[u] += off;
-    const float eS = exp2_fast(gs);               // exp(G_s(I)) <= 1
-    const float eL = exp2_fast(gL - ge);          // exp(G_last - G_e(I)) <= 1
-    const bool bad = (gs - ge) > kRangeMax * kLog2e;
-    if (seg == s_first) {
-        flag[Iblk][c] = bad ? 1 : 0;
-        if (bad) atomicOr(&anyflag, 1);
-    }
-    if (has_pair) fpair[seg][c] = exp2_fast(fgs - fge);   // exp(G_s(pI) - G_e(pJ)) <= 1
-    if (seg == 0 && c < DK) W.gl[rec * DK + c] = exp2_fast(gL);
+        for (int u = 0; u < TPS; ++u) asm volatile("" : "+v"(x.G[u]), "+v"(x.k[u]), "+v"(x.q[u]));
+        asm volatile("" : "+v"(x.bl));
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            x.v[u].settle();
+            asm volatile("" : "+v"(x.vb[u]));
+        }
+    };
 
-    // ---- element-wise operands
-    float egreg[TPS], krv[TPS];
+    // Persistent workgroups: item = (b*H + h) * NC + chunk, strided by the
+    // grid.  The inputs of the next item are requested in five small groups
+    // spread over the phases of the current one, so that their memory traffic
+    // overlaps its computation instead of arriving in one burst (all
+    // workgroups start their items together) that stalls instruction issue.
+    int item = blockIdx.x;
+    if (item >= NITEM) return;
+    In cur;
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-        const int i = i0 + u;
-        const float kv = kreg[u], qv = qreg[u];
-        const float x = exp2_fast(G[u] - gs);              // <= 1
-        const float kk = kv * exp2_fast(ge - G[u]);        // <= |k|
-        const float kd = bad ? 0.f : kv * exp2_fast(gs - G[u]);  // >= |k|, bounded
-        store_op(Qk + i * SK + c, kv * x);
-        store_p(Qq, i * SK + c, qv * x);
-        store_p(Kd, i * SK + c, kd);
-        Kk[i * SKF + c] = kk;
-        const float eg = x * eS;                           // exp(G_i) <= 1
-        egreg[u] = eg;
-        krv[u] = kk * eL;                                  // k exp(G_last - G_i) <= |k|
-        store_op(Wq + fragidx(i, c, DKP / 32), qv * eg);
-    }
-    // Kr^T row c, tokens i0 .. i0+TPS-1, four at a time (contiguous in the fragment layout)
-    if (c < DK) {
-        if constexpr (TPS >= 4) {
-#pragma unroll
-            for (int u = 0; u < TPS; u += 4)
-                store4_p(Wkr, fragidx(c, i0 + u, CP / 32), (f32x4){krv[u], krv[u + 1], krv[u + 2], krv[u + 3]});
-        } else {
-#pragma unroll
-            for (int u = 0; u < TPS; ++u) store_p(Wkr, fragidx(c, i0 + u, CP / 32), krv[u]);
-        }
-    }
-    if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
-        for (int p = tid; p < DK * (CP - C); p += S::NT) {
-            const int cc = p / (CP - C), i = C + p % (CP - C);
-            store_p(Wkr, fragidx(cc, i, CP / 32), 0.f);
-        }
-        for (int p = tid; p < C * (CP - C); p += S::NT) {
-            const int i = p / (CP - C), j = C + p % (CP - C);
-            store_p(Waq, fragidx(i, j, CP / 32), 0.f);
-        }
-    }
-    __syncthreads();
+    for (int grp = 0; grp < 5; ++grp) load_in(cur, item, threadIdx.x, grp);
+    settle(cur);
+    for (; item < NITEM; item += gridDim.x) {
+        // Thread indices are re-derived in every iteration from a value the
+        // compiler cannot see through, so that it does not hoist every
+        // per-lane address of the item out of the loop (which would keep them
+        // all live at once and spill).
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wave = tid >> 6;
+        const int r = lane & 15, gq = lane >> 4;
+        const int c = tid % DKP, seg = seg_of(tid);
+        const int i0 = seg * TPS;
+        // stage-A arrays
+        OT* Qk = (OT*)big;                                             // [C][SK] plain
+        const PArr<OT> Qq{Qk + C * SK, Qk + 2 * C * SK};               // [C][SK] precise
+        const PArr<OT> Kd{Qk + (1 + NP) * C * SK, Qk + (2 + NP) * C * SK};  // [C][SK] precise
+        float* Kk = (float*)(Qk + (1 + 2 * NP) * C * SK);              // [C][SKF] float32
 
-    // ---- A^T and Aqk^T tiles on the matrix cores: tile (J, I), J <= I
-    // lane result: A[i = 16I + r][j = 16J + 4gq + u]
-    constexpr int NTILE = NB * (NB + 1) / 2;
-    constexpr int NW = S::NW;
-    constexpr int TPW = (NTILE + NW - 1) / NW;
-    f32x4 accA[TPW], accQ[TPW];
-#pragma unroll
-    for (int s = 0; s < TPW; ++s) {
-        accA[s] = zero4();
-        accQ[s] = zero4();
-        const int tix = wave + NW * s;
-        if (tix < NTILE) {
-            int I = 0, base = 0;
-            while (base + I + 1 <= tix) { base += I + 1; ++I; }
-            const int J = tix - base;
-            const bool diag = (I == J);
-            const int pi = diag ? 0 : I * (I - 1) / 2 + J;
-#pragma unroll
-            for (int ks = 0; ks < DKP / 32; ++ks) {
-                const int ch = 32 * ks + 8 * gq;
-                PFrag<OT> key;
-                if (diag) {
-                    key = Kd.frag((16 * J + r) * SK + ch);
-                } else {
-                    float t8[8];
-                    const f32x4 k0 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch);
-                    const f32x4 k1 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch + 4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        t8[e] = k0[e] * fpair[pi][ch + e];
-                        t8[4 + e] = k1[e] * fpair[pi][ch + 4 + e];
-                    }
-                    key.from_f32(t8);
-                }
-                Frag<OT> bk;
-                bk.load(Qk + (16 * I + r) * SK + ch);
-                const PFrag<OT> bq = Qq.frag((16 * I + r) * SK + ch);
-                accA[s] = mma(key.h, bk, accA[s]);
-                accQ[s] = mma3(key, bq, accQ[s]);
-            }
-        }
-    }
-    __syncthreads();   // stage-A operands are dead from here on
+        const int nitem = min(item + (int)gridDim.x, NITEM - 1);
+        In nxt;
+        auto load_grp = [&](In& x, int grp) { load_in(x, nitem, tid, grp); };
+        load_grp(nxt, 0);
 
-    // stage-B layout (aliases stage A)
-    OT* const BkT = (OT*)big;                                      // [DK][SC] beta_j k_j exp(G_j), plain
-    OT* bvt_h = BkT + DK * SC;
-    const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j, swizzled
-    float* As = (float*)(bvt_h + NP * DV * SC);                    // [C][SA]  A (strictly lower, with beta)
-    float* Ts = (float*)((char*)As + S::AS_BYTES);                 // [C][SA]  T = (I + A)^-1
-    const PArr<OT> Tb{(OT*)As, (OT*)As + C * SC};                  // [C][SC]  T as an operand (after the solve)
-    const bool fallback = anyflag != 0;
-    float* Aq32 = Ts;                          // Aqk staging when the exact fallback runs
+        const int bh = item / NC, c_idx = item - bh * NC;
+        const int b = bh / H, h = bh - b * H;
+        const int t0 = c_idx * C;
+        const int L = min(C, T - t0);       // valid tokens (>= 1)
+        const size_t rec = (size_t)item;
+        OT* const Wq = W.qg_rec(rec);
+        OT* const Wwn = W.wneg_rec(rec);
+        const PArr<OT> Wkr = W.krt(rec), Waq = W.aqk(rec);
+        float* Wut = W.ut + rec * S::U_N;
+        if (tid == 0) anyflag = 0;
+        if (tid < C) sb[tid] = tid < L ? cur.bl : 0.f;
+        float G[TPS], kreg[TPS], qreg[TPS];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const bool ok = (i0 + u < L) && (c < DK);
+            G[u] = (ok && mode != KDA_GATE_NONE) ? cur.G[u] * kLog2e : 0.f;   // log2 units
+            kreg[u] = ok ? cur.k[u] : 0.f;
+            qreg[u] = ok ? cur.q[u] * scale : 0.f;
+        }
+        // beta_i v_i in float32
+        float bv[VPT][8];
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int idx = tid + S::NT * u;
+            const int i = idx / (DV / 8);
+            const float bi = (idx < NVEC && i < L) ? cur.vb[u] : 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bv[u][e] = bi * cur.v[u].get(e);
+        }
 
-#pragma unroll
-    for (int s = 0; s < TPW; ++s) {
-        const int tix = wave + NW * s;
-        if (tix < NTILE) {
-            int I = 0, base = 0;
-            while (base + I + 1 <= tix) { base += I + 1; ++I; }
-            const int J = tix - base;
-            const int i = 16 * I + r;
-            const int j0 = 16 * J + 4 * gq;
-            f32x4 av = accA[s] * sb[i];
-            f32x4 qv = accQ[s];
-            if (I == J) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    if (j0 + u >= i) av[u] = 0.f;
-                    if (j0 + u > i) qv[u] = 0.f;
-                }
-            }
-            *reinterpret_cast<f32x4*>(As + i * SA + j0) = av;
-            if (fallback) *reinterpret_cast<f32x4*>(Aq32 + i * SA + j0) = qv;
-            else store4_p(Waq, fragidx(i, j0, CP / 32), qv);
-        }
-    }
-    // zero the strictly upper blocks of A (and of the Aqk staging / record),
-    // eight columns at a time (a run of 8 is contiguous in the fragment layout)
-    for (int p = tid; p < C * (C / 8); p += S::NT) {
-        const int i = p / (C / 8), j8 = 8 * (p % (C / 8));
-        if ((j8 >> 4) > (i >> 4)) {
-            *reinterpret_cast<f32x4*>(As + i * SA + j8) = zero4();
-            *reinterpret_cast<f32x4*>(As + i * SA + j8 + 4) = zero4();
-            if (fallback) {
-                *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8) = zero4();
-                *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8 + 4) = zero4();
-            } else {
-                store4_p(Waq, fragidx(i, j8, CP / 32), zero4());
-                store4_p(Waq, fragidx(i, j8, CP / 32) + 4, zero4());
-            }
-        }
-    }
-    // beta_j k_j exp(G_j) and beta_j v_j, transposed ([channel][token])
-    if (c < DK) {
-        float bk[TPS];
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) bk[u] = sb[i0 + u] * kreg[u] * egreg[u];
-        store_run<OT, TPS>(BkT + c * SC + i0, bk);
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int idx = tid + S::NT * u;
-        if (idx < NVEC) {
-            const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
-        }
-    }
-    if (CP > C) {
-        for (int p = tid; p < DK * (CP - C); p += S::NT) {
-            const int row = p / (CP - C), i = C + p % (CP - C);
-            store_op(BkT + row * SC + i, 0.f);
-        }
-        for (int p = tid; p < DV * (CP - C); p += S::NT) {
-            const int row = p / (CP - C), i = C + p % (CP - C);
-            store_p(BvT, row * SC + swz<CP>(row, i), 0.f);
-        }
-    }
-    __syncthreads();
-
-    if (fallback) {
-        // exact diagonal-block terms for key channels whose decay across the block
-        // exceeds kRangeMax (their factorised key side was zeroed above)
-        for (int p = tid; p < NB * DK; p += S::NT) {
-            const int I = p / DK, cc = p % DK;
-            if (!flag[I][cc]) continue;
-            float gi[16], ki[16], qi[16];
+        // ---- cumulative log-decay (in log2 units from here on, so that every
+        // decay factor is one 2^x).  Local running sums, then segment totals in
+        // LDS; every thread derives the references it needs from the totals with
+        // one left-to-right pass, so all threads obtain bit-identical values.
+        {
             float run = 0.f;
-            for (int u = 0; u < 16; ++u) {
-                const int i = 16 * I + u;
-                float gv = 0.f, kv = 0.f, qv = 0.f;
-                if (i < L) {
-                    const size_t tok = ((size_t)b * T + t0 + i) * H + h;
-                    if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
-                    else if (mode == KDA_GATE_SCALAR) gv = g[tok];
-                    kv = io<OT>::load(k + tok * DK + cc);
-                    qv = io<OT>::load(q + tok * DK + cc) * scale;
-                }
-                run += gv;
-                gi[u] = run; ki[u] = kv; qi[u] = qv;
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) {
+                run += G[u];
+                G[u] = run;
             }
-            for (int ii = 0; ii < 16; ++ii) {
-                const int i = 16 * I + ii;
-                for (int jj = 0; jj <= ii; ++jj) {
-                    const int j = 16 * I + jj;
-                    const float w = __expf(gi[ii] - gi[jj]) * ki[jj];
-                    atomicAdd(&Aq32[i * SA + j], qi[ii] * w);
-                    if (jj < ii) atomicAdd(&As[i * SA + j], sb[i] * ki[ii] * w);
-                }
+            segtot[seg][c] = run;
+            segfirst[seg][c] = G[0];
+        }
+        __syncthreads();
+        load_grp(nxt, 1);
+        const int Iblk = i0 >> 4;                     // this thread's 16-token block
+        const int s_first = (16 * Iblk) / TPS, s_last = (16 * Iblk + 15) / TPS;
+        // the block pair (pI, pJ), pJ < pI, whose cross factor this thread computes
+        const bool has_pair = seg < S::NPAIR;
+        int pI = 1, pJ = 0;
+        {
+            int base = 0;
+            while (base + pI <= seg) { base += pI; ++pI; }
+            pJ = seg - base;
+        }
+        const int p_first = (16 * pI) / TPS, p_last = (16 * pJ + 15) / TPS;
+        float off = 0.f, gs = 0.f, ge = 0.f, fgs = 0.f, fge = 0.f, acc = 0.f;
+        for (int s2 = 0; s2 < NSEG; ++s2) {
+            const float first = segfirst[s2][c];
+            if (s2 == seg) off = acc;
+            if (s2 == s_first) gs = acc + first;      // G at the block's first token
+            if (s2 == p_first) fgs = acc + first;
+            acc += segtot[s2][c];
+            if (s2 == s_last) ge = acc;               // G at the block's last token
+            if (s2 == p_last) fge = acc;
+        }
+        const float gL = acc;                         // G at the chunk's last token
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) G[u] += off;
+        const float eS = exp2_fast(gs);               // exp(G_s(I)) <= 1
+        const float eL = exp2_fast(gL - ge);          // exp(G_last - G_e(I)) <= 1
+        const bool bad = (gs - ge) > kRangeMax * kLog2e;
+        if (seg == s_first) {
+            flag[Iblk][c] = bad ? 1 : 0;
+            if (bad) atomicOr(&anyflag, 1);
+        }
+        if (has_pair) fpair[seg][c] = exp2_fast(fgs - fge);   // exp(G_s(pI) - G_e(pJ)) <= 1
+        if (seg == 0 && c < DK) W.gl[rec * DK + c] = exp2_fast(gL);
+
+        // ---- element-wise operands
+        float egreg[TPS], krv[TPS];
+#pragma unroll
+        for (int u = 0; u < TPS; ++u) {
+            const int i = i0 + u;
+            const float kv = kreg[u], qv = qreg[u];
+            const float x = exp2_fast(G[u] - gs);              // <= 1
+            const float kk = kv * exp2_fast(ge - G[u]);        // <= |k|
+            const float kd = bad ? 0.f : kv * exp2_fast(gs - G[u]);  // >= |k|, bounded
+            store_op(Qk + i * SK + c, kv * x);
+            store_p(Qq, i * SK + c, qv * x);
+            store_p(Kd, i * SK + c, kd);
+            Kk[i * SKF + c] = kk;
+            const float eg = x * eS;                           // exp(G_i) <= 1
+            egreg[u] = eg;
+            krv[u] = kk * eL;                                  // k exp(G_last - G_i) <= |k|
+            store_op(Wq + fragidx(i, c, DKP / 32), qv * eg);
+        }
+        // Kr^T row c, tokens i0 .. i0+TPS-1, four at a time (contiguous in the fragment layout)
+        if (c < DK) {
+            if constexpr (TPS >= 4) {
+#pragma unroll
+                for (int u = 0; u < TPS; u += 4)
+                    store4_p(Wkr, fragidx(c, i0 + u, CP / 32), (f32x4){krv[u], krv[u + 1], krv[u + 2], krv[u + 3]});
+            } else {
+#pragma unroll
+                for (int u = 0; u < TPS; ++u) store_p(Wkr, fragidx(c, i0 + u, CP / 32), krv[u]);
+            }
+        }
+        if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
+            for (int p = tid; p < DK * (CP - C); p += S::NT) {
+                const int cc = p / (CP - C), i = C + p % (CP - C);
+                store_p(Wkr, fragidx(cc, i, CP / 32), 0.f);
+            }
+            for (int p = tid; p < C * (CP - C); p += S::NT) {
+                const int i = p / (CP - C), j = C + p % (CP - C);
+                store_p(Waq, fragidx(i, j, CP / 32), 0.f);
             }
         }
         __syncthreads();
+        load_grp(nxt, 2);
+
+        // ---- A^T and Aqk^T tiles on the matrix cores: tile (J, I), J <= I
+        // lane result: A[i = 16I + r][j = 16J + 4gq + u]
+        constexpr int NTILE = NB * (NB + 1) / 2;
+        constexpr int NW = S::NW;
+        constexpr int TPW = (NTILE + NW - 1) / NW;
+        f32x4 accA[TPW], accQ[TPW];
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            accA[s] = zero4();
+            accQ[s] = zero4();
+            const int tix = wave + NW * s;
+            if (tix < NTILE) {
+                int I = 0, base = 0;
+                while (base + I + 1 <= tix) { base += I + 1; ++I; }
+                const int J = tix - base;
+                const bool diag = (I == J);
+                const int pi = diag ? 0 : I * (I - 1) / 2 + J;
+#pragma unroll
+                for (int ks = 0; ks < DKP / 32; ++ks) {
+                    const int ch = 32 * ks + 8 * gq;
+                    PFrag<OT> key;
+                    if (diag) {
+                        key = Kd.frag((16 * J + r) * SK + ch);
+                    } else {
+                        float t8[8];
+                        const f32x4 k0 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch);
+                        const f32x4 k1 = *reinterpret_cast<const f32x4*>(Kk + (16 * J + r) * SKF + ch + 4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            t8[e] = k0[e] * fpair[pi][ch + e];
+                            t8[4 + e] = k1[e] * fpair[pi][ch + 4 + e];
+                        }
+                        key.from_f32(t8);
+                    }
+                    Frag<OT> bk;
+                    bk.load(Qk + (16 * I + r) * SK + ch);
+                    const PFrag<OT> bq = Qq.frag((16 * I + r) * SK + ch);
+                    accA[s] = mma(key.h, bk, accA[s]);
+                    accQ[s] = mma3(key, bq, accQ[s]);
+                }
+            }
+        }
+        __syncthreads();   // stage-A operands are dead from here on
+        load_grp(nxt, 3);
+
+        // stage-B layout (aliases stage A)
+        OT* const BkT = (OT*)big;                                      // [DK][SC] beta_j k_j exp(G_j), plain
+        OT* bvt_h = BkT + DK * SC;
+        const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j, swizzled
+        float* As = (float*)(bvt_h + NP * DV * SC);                    // [C][SA]  A (strictly lower, with beta)
+        float* Ts = (float*)((char*)As + S::AS_BYTES);                 // [C][SA]  T = (I + A)^-1
+        const PArr<OT> Tb{(OT*)As, (OT*)As + C * SC};                  // [C][SC]  T as an operand (after the solve)
+        const bool fallback = anyflag != 0;
+        float* Aq32 = Ts;                          // Aqk staging when the exact fallback runs
+
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int tix = wave + NW * s;
+            if (tix < NTILE) {
+                int I = 0, base = 0;
+                while (base + I + 1 <= tix) { base += I + 1; ++I; }
+                const int J = tix - base;
+                const int i = 16 * I + r;
+                const int j0 = 16 * J + 4 * gq;
+                f32x4 av = accA[s] * sb[i];
+                f32x4 qv = accQ[s];
+                if (I == J) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (j0 + u >= i) av[u] = 0.f;
+                        if (j0 + u > i) qv[u] = 0.f;
+                    }
+                }
+                *reinterpret_cast<f32x4*>(As + i * SA + j0) = av;
+                if (fallback) *reinterpret_cast<f32x4*>(Aq32 + i * SA + j0) = qv;
+                else store4_p(Waq, fragidx(i, j0, CP / 32), qv);
+            }
+        }
+        // zero the strictly upper blocks of A (and of the Aqk staging / record),
+        // eight columns at a time (a run of 8 is contiguous in the fragment layout)
+        for (int p = tid; p < C * (C / 8); p += S::NT) {
+            const int i = p / (C / 8), j8 = 8 * (p % (C / 8));
+            if ((j8 >> 4) > (i >> 4)) {
+                *reinterpret_cast<f32x4*>(As + i * SA + j8) = zero4();
+                *reinterpret_cast<f32x4*>(As + i * SA + j8 + 4) = zero4();
+                if (fallback) {
+                    *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8) = zero4();
+                    *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8 + 4) = zero4();
+                } else {
+                    store4_p(Waq, fragidx(i, j8, CP / 32), zero4());
+                    store4_p(Waq, fragidx(i, j8, CP / 32) + 4, zero4());
+                }
+            }
+        }
+        // beta_j k_j exp(G_j) and beta_j v_j, transposed ([channel][token])
+        if (c < DK) {
+            float bk[TPS];
+#pragma unroll
+            for (int u = 0; u < TPS; ++u) bk[u] = sb[i0 + u] * kreg[u] * egreg[u];
+            store_run<OT, TPS>(BkT + c * SC + i0, bk);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int idx = tid + S::NT * u;
+            if (idx < NVEC) {
+                const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
+            }
+        }
+        if (CP > C) {
+            for (int p = tid; p < DK * (CP - C); p += S::NT) {
+                const int row = p / (CP - C), i = C + p % (CP - C);
+                store_op(BkT + row * SC + i, 0.f);
+            }
+            for (int p = tid; p < DV * (CP - C); p += S::NT) {
+                const int row = p / (CP - C), i = C + p % (CP - C);
+                store_p(BvT, row * SC + swz<CP>(row, i), 0.f);
+            }
+        }
+        __syncthreads();
+        load_grp(nxt, 4);
+
+        if (fallback) {
+            // exact diagonal-block terms for key channels whose decay across the block
+            // exceeds kRangeMax (their factorised key side was zeroed above)
+            for (int p = tid; p < NB * DK; p += S::NT) {
+                const int I = p / DK, cc = p % DK;
+                if (!flag[I][cc]) continue;
+                float gi[16], ki[16], qi[16];
+                float run = 0.f;
+                for (int u = 0; u < 16; ++u) {
+                    const int i = 16 * I + u;
+                    float gv = 0.f, kv = 0.f, qv = 0.f;
+                    if (i < L) {
+                        const size_t tok = ((size_t)b * T + t0 + i) * H + h;
+                        if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
+                        else if (mode == KDA_GATE_SCALAR) gv = g[tok];
+                        kv = io<OT>::load(k + tok * DK + cc);
+                        qv = io<OT>::load(q + tok * DK + cc) * scale;
+                    }
+                    run += gv;
+                    gi[u] = run; ki[u] = kv; qi[u] = qv;
+                }
+                for (int ii = 0; ii < 16; ++ii) {
+                    const int i = 16 * I + ii;
+                    for (int jj = 0; jj <= ii; ++jj) {
+                        const int j = 16 * I + jj;
+                        const float w = __expf(gi[ii] - gi[jj]) * ki[jj];
+                        atomicAdd(&Aq32[i * SA + j], qi[ii] * w);
+                        if (jj < ii) atomicAdd(&As[i * SA + j], sb[i] * ki[ii] * w);
+                    }
+                }
+            }
+            __syncthreads();
+            for (int p = tid; p < C * C; p += S::NT) {
+                const int i = p / C, j = p % C;
+                store_p(Waq, fragidx(i, j, CP / 32), Aq32[i * SA + j]);
+            }
+            __syncthreads();
+        }
+
+        // ---- T = (I + A)^-1: diagonal 16x16 blocks by a column sweep (one wave each)
+        if (wave < NB) {
+            const int I = wave;
+            float arow[16];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) arow[jj] = As[(16 * I + r) * SA + 16 * I + jj];
+            float x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = (4 * gq + u == r) ? 1.f : 0.f;
+            sweep16<0>(x, arow, r);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u] = x[u];
+        }
+        // strictly upper blocks of T are zero
         for (int p = tid; p < C * C; p += S::NT) {
             const int i = p / C, j = p % C;
-            store_p(Waq, fragidx(i, j, CP / 32), Aq32[i * SA + j]);
+            if ((j >> 4) > (i >> 4)) Ts[i * SA + j] = 0.f;
         }
         __syncthreads();
-    }
-
-    // ---- T = (I + A)^-1: diagonal 16x16 blocks by a column sweep (one wave each)
-    if (wave < NB) {
-        const int I = wave;
-        float arow[16];
+        // off-diagonal blocks, one block-diagonal at a time:
+        // T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
+        for (int d = 1; d < NB; ++d) {
+            const int I = d + wave, J = wave;
+            if (I < NB) {
+                f32x4 P = zero4();
+                for (int Kb = J; Kb < I; ++Kb) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) arow[jj] = As[(16 * I + r) * SA + 16 * I + jj];
-        float x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) x[u] = (4 * gq + u == r) ? 1.f : 0.f;
-        sweep16<0>(x, arow, r);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u] = x[u];
-    }
-    // strictly upper blocks of T are zero
-    for (int p = tid; p < C * C; p += S::NT) {
-        const int i = p / C, j = p % C;
-        if ((j >> 4) > (i >> 4)) Ts[i * SA + j] = 0.f;
-    }
-    __syncthreads();
-    // off-diagonal blocks, one block-diagonal at a time:
-    // T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-    for (int d = 1; d < NB; ++d) {
-        const int I = d + wave, J = wave;
-        if (I < NB) {
-            f32x4 P = zero4();
-            for (int Kb = J; Kb < I; ++Kb) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float a = As[(16 * I + r) * SA + 16 * Kb + 4 * s + gq];
-                    const float bb = Ts[(16 * Kb + 4 * s + gq) * SA + 16 * J + r];
-                    P = mma4(a, bb, P);
+                    for (int s = 0; s < 4; ++s) {
+                        const float a = As[(16 * I + r) * SA + 16 * Kb + 4 * s + gq];
+                        const float bb = Ts[(16 * Kb + 4 * s + gq) * SA + 16 * J + r];
+                        P = mma4(a, bb, P);
+                    }
                 }
-            }
-            // lane holds P[4gq + u][r]; contract k = 4gq' + u in step u
-            f32x4 R = zero4();
+                // lane holds P[4gq + u][r]; contract k = 4gq' + u in step u
+                f32x4 R = zero4();
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float a = Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u];
-                R = mma4(a, P[u], R);
-            }
+                for (int u = 0; u < 4; ++u) {
+                    const float a = Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u];
+                    R = mma4(a, P[u], R);
+                }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) Ts[(16 * I + 4 * gq + u) * SA + 16 * J + r] = -R[u];
+                for (int u = 0; u < 4; ++u) Ts[(16 * I + 4 * gq + u) * SA + 16 * J + r] = -R[u];
+            }
+            __syncthreads();
+        }
+        // T as a precise operand, row-major [i][j], padded columns zero (overwrites A)
+        for (int p = tid; p < C * CP; p += S::NT) {
+            const int i = p / CP, j = p % CP;
+            store_p(Tb, i * SC + j, j < C ? Ts[i * SA + j] : 0.f);
         }
         __syncthreads();
-    }
-    // T as a precise operand, row-major [i][j], padded columns zero (overwrites A)
-    for (int p = tid; p < C * CP; p += S::NT) {
-        const int i = p / CP, j = p % CP;
-        store_p(Tb, i * SC + j, j < C ? Ts[i * SA + j] : 0.f);
-    }
-    __syncthreads();
+        // the next item's inputs were requested several phases ago: take them now,
+        // before the record stores of the last phase (whose completion a later
+        // wait would also include)
+        settle(nxt);
 
-    // ---- W^T = (Diag(beta) K exp(G))^T T^T  and  U = T Diag(beta) V
-    {
-        constexpr int MW = DK / 16;          // channel tiles of W^T
-        constexpr int NWT = MW * NB;         // W tiles
-        constexpr int NUT = NB * (DV / 16);  // U tiles
-        for (int tix = wave; tix < NWT + NUT; tix += S::NW) {
-            if (tix < NWT) {
-                const int m = tix / NB, I = tix % NB;     // channels 16m.., tokens 16I..
-                f32x4 acc = zero4();
-                const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
-                for (int ks = 0; ks < nks; ++ks)   // W is stored as a plain operand
-                {
-                    Frag<OT> a, t;
-                    a.load(BkT + (16 * m + r) * SC + 32 * ks + 8 * gq);
-                    t.load(Tb.h + (16 * I + r) * SC + 32 * ks + 8 * gq);
-                    acc = mma(a, t, acc);
+        // ---- W^T = (Diag(beta) K exp(G))^T T^T  and  U = T Diag(beta) V
+        {
+            constexpr int MW = DK / 16;          // channel tiles of W^T
+            constexpr int NWT = MW * NB;         // W tiles
+            constexpr int NUT = NB * (DV / 16);  // U tiles
+            for (int tix = wave; tix < NWT + NUT; tix += S::NW) {
+                if (tix < NWT) {
+                    const int m = tix / NB, I = tix % NB;     // channels 16m.., tokens 16I..
+                    f32x4 acc = zero4();
+                    const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
+                    for (int ks = 0; ks < nks; ++ks)   // W is stored as a plain operand
+                    {
+                        Frag<OT> a, t;
+                        a.load(BkT + (16 * m + r) * SC + 32 * ks + 8 * gq);
+                        t.load(Tb.h + (16 * I + r) * SC + 32 * ks + 8 * gq);
+                        acc = mma(a, t, acc);
+                    }
+                    // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
+                    Vec4<OT>::store(Wwn + fragidx(16 * I + r, 16 * m + 4 * gq, DKP / 32), -acc);
+                } else {
+                    const int t2 = tix - NWT;
+                    const int I = t2 % NB, nn = t2 / NB;      // tokens 16I.., value cols 16nn..
+                    f32x4 acc = zero4();
+                    const int nks = (16 * I + 15) / 32 + 1;
+                    for (int ks = 0; ks < nks; ++ks)
+                        acc = mma3(Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq),
+                                   BvT.frag((16 * nn + r) * SC + swz<CP>(16 * nn + r, 32 * ks + 8 * gq)), acc);
+                    // lane holds U[16I + 4gq + u][16nn + r]: accumulator-major block (nn, I)
+                    Vec4<float>::store(Wut + accbase(nn, I, NB, lane), acc);
                 }
-                // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
-                Vec4<OT>::store(Wwn + fragidx(16 * I + r, 16 * m + 4 * gq, DKP / 32), -acc);
-            } else {
-                const int t2 = tix - NWT;
-                const int I = t2 % NB, nn = t2 / NB;      // tokens 16I.., value cols 16nn..
-                f32x4 acc = zero4();
-                const int nks = (16 * I + 15) / 32 + 1;
-                for (int ks = 0; ks < nks; ++ks)
-                    acc = mma3(Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq),
-                               BvT.frag((16 * nn + r) * SC + swz<CP>(16 * nn + r, 32 * ks + 8 * gq)), acc);
-                // lane holds U[16I + 4gq + u][16nn + r]: accumulator-major block (nn, I)
-                Vec4<float>::store(Wut + accbase(nn, I, NB, lane), acc);
+            }
+            if (DKP > DK) {   // padded key channels of -W are zero
+                for (int p = tid; p < C * (DKP - DK); p += S::NT) {
+                    const int i = p / (DKP - DK), cc = DK + p % (DKP - DK);
+                    store_op(Wwn + fragidx(i, cc, DKP / 32), 0.f);
+                }
             }
         }
-        if (DKP > DK) {   // padded key channels of -W are zero
-            for (int p = tid; p < C * (DKP - DK); p += S::NT) {
-                const int i = p / (DKP - DK), cc = DK + p % (DKP - DK);
-                store_op(Wwn + fragidx(i, cc, DKP / 32), 0.f);
-            }
-        }
+
+        __syncthreads();   // LDS is reused by the next item
+        cur = nxt;
     }
 }
 
@@ -732,55 +790,80 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const size_t rec = rec_of(cidx);
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
+            P.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) P.wn[ks].load(wn + fragbase(we, ks, KS, lane));
-            P.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+#pragma unroll
+            for (int s = 0; s < MHW; ++s)
+                P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
 #pragma unroll
                 for (int ks = 0; ks < KC; ++ks) P.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
-                P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
             }
         };
         // One chunk step with operands P; the operands of chunk `nxt` are
         // loaded into Q one fragment per matrix-core step, spreading the load
         // traffic over the step.
+        // One chunk step with operands P.  The operands of chunk `nxt` are
+        // all loaded into Q in the first half of the step, in the order the
+        // next step consumes them (U, -W, gl, Kr^T): the memory counter
+        // retires in order, so every wait of the next step covers only loads
+        // issued a whole step before.  Accumulations are split into independent chains so
+        // that the matrix-core latency is not paid once per k step.
         auto step = [&](const Ops& P, Ops& Q, int nxt) {
             const size_t rec = rec_of(nxt);
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
-            f32x4 e = P.u;
+            Q.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+            f32x4 ea = P.u, eb = zero4();
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 Q.wn[ks].load(wn + fragbase(we, ks, KS, lane));
-                if (has_t) e = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), e);
+                if (has_t) {
+                    if (ks & 1) eb = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), eb);
+                    else ea = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), ea);
+                }
             }
-            if (has_t) store4_p(ET, r * SC + 16 * wr + 4 * gq, e);
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
+#pragma unroll
+                for (int ks = 0; ks < KC; ++ks) Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
+            }
+            if (has_t) store4_p(ET, r * SC + 16 * wr + 4 * gq, ea + eb);
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x020, 1 + MHW * (1 + NP * KC), 0);
             __syncthreads();
             // H = Diag(gl) H + Kr^T E
+            f32x4 part[MHW];
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+                if (ALLH || wr + 4 * s < MH) hacc[s] *= P.gl[s];
+                part[s] = zero4();
+            }
+#pragma unroll
+            for (int ks = 0; ks < KC; ++ks) {
+                const PFrag<OT> et = ET.frag(r * SC + 32 * ks + 8 * gq);
+#pragma unroll
+                for (int s = 0; s < MHW; ++s) {
+                    if (ALLH || wr + 4 * s < MH) {
+                        if (ks & 1) part[s] = mma3(P.kr[s][ks], et, part[s]);
+                        else hacc[s] = mma3(P.kr[s][ks], et, hacc[s]);
+                    }
+                }
+            }
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
                 const int mt = wr + 4 * s;
-                const bool own = ALLH || mt < MH;
-                if (own) hacc[s] *= P.gl[s];
-#pragma unroll
-                for (int ks = 0; ks < KC; ++ks) {
-                    Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
-                    if (own) hacc[s] = mma3(P.kr[s][ks], ET.frag(r * SC + 32 * ks + 8 * gq), hacc[s]);
+                if (ALLH || mt < MH) {
+                    hacc[s] += part[s];
+                    store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
                 }
-                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
-                if (own) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
-            }
-            Q.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
-#pragma unroll
-            for (int g2 = 0; g2 < NP * KC * MHW + MHW + 1; ++g2) {
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             }
             __syncthreads();
         };
@@ -822,11 +905,14 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const size_t rec = rec_of(nxt);
             const OT* qg = W.qg_rec(rec);
             const PArr<OT> aq = W.aqk(rec);
-            f32x4 oacc = zero4();
+            f32x4 oa = zero4(), ob = zero4();   // two independent accumulation chains
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 Q.qg[ks].load(qg + fragbase(we, ks, KS, lane));
-                if (has_t) oacc = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oacc);
+                if (has_t) {
+                    if (ks & 1) ob = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], ob);
+                    else oa = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oa);
+                }
             }
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
@@ -837,9 +923,13 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
                 Q.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
-                if (has_t) oacc = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oacc);
+                if (has_t) {
+                    if (ks & 1) ob = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], ob);
+                    else oa = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oa);
+                }
             }
             if (has_t) {
+                const f32x4 oacc = oa + ob;
                 // lane holds o^T[n = 4gq + u][i = 16*wr + r]
                 const int t0 = cidx * C;
                 const int i = 16 * wr + r;
@@ -862,6 +952,29 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 }
 
 // ---------------------------------------------------------------------------
+// Number of workgroups of `kernel` (with `threads` threads) that the current
+// device holds at once: compute units times the occupancy limit, queried once
+// per kernel and device.
+template <typename K>
+static int resident_blocks(K kernel, int threads)
+{
+    constexpr int MAXDEV = 64;
+    static std::atomic<int> cache[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < MAXDEV ? dev : MAXDEV - 1;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n > 0 && dev < MAXDEV) return n;
+    int ncu = 0, per = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+        ncu = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess || per < 1)
+        per = 1;
+    n = ncu * per;
+    if (dev < MAXDEV) cache[slot].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <int C, int DK, int DV, typename OT>
 static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
 {
@@ -869,9 +982,12 @@ static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
     const int NC = (a.T + C - 1) / C;
     const size_t nrec = (size_t)BH * NC;
     if (NC > 0) {
-        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(NC, BH), dim3(CS<C, DK, DV, OT>::NT), 0, s,
+        // persistent workgroups: as many as can be resident at once
+        const int nitem = (int)nrec;
+        const int grid = min(nitem, resident_blocks(chunk_prepare<C, DK, DV, OT>, CS<C, DK, DV, OT>::NT));
+        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(grid), dim3(CS<C, DK, DV, OT>::NT), 0, s,
                            (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
-                           a.T, a.H, NC, a.scale, (int)a.mode, a.ws, nrec);
+                           a.T, a.H, NC, nitem, a.scale, (int)a.mode, a.ws, nrec);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

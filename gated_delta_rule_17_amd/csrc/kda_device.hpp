@@ -60,6 +60,8 @@ template <> struct Frag<bf16_t> {
     __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
     __device__ __forceinline__ float get(int i) const { return bf16_to_f32(v[i]); }
     __device__ __forceinline__ void set(int i, float x) { v[i] = f32_to_bf16(x); }
+    // make the loaded value available here (the wait for its load goes here)
+    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(v)); }
 };
 
 template <> struct Frag<float> {
@@ -71,6 +73,7 @@ template <> struct Frag<float> {
     }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
     __device__ __forceinline__ void set(int i, float x) { if (i < 4) lo[i] = x; else hi[i - 4] = x; }
+    __device__ __forceinline__ void settle() { asm volatile("" : "+v"(lo), "+v"(hi)); }
 };
 
 // D += A * B over one 32-wide k step.
