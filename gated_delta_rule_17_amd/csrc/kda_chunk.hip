@@ -71,10 +71,14 @@ struct CS {
     static constexpr size_t U_N = (size_t)DV * C;     // U^T     [DV][C]    float32
     // LDS, stage A: Qk (plain), Qq and Kd (precise), Kk (float32)
     static constexpr int STAGE_A = (1 + 2 * NP) * C * SK * SZ + C * SKF * 4;
-    // stage B: BkT (plain), BvT (precise), A and T (float32); T as a precise operand aliases A
-    static constexpr int TB_BYTES = NP * C * SC * SZ;
-    static constexpr int AS_BYTES = (C * SA * 4 > TB_BYTES) ? C * SA * 4 : TB_BYTES;
-    static constexpr int STAGE_B = (DK + NP * DV) * SC * SZ + AS_BYTES + C * SA * 4;
+    // stage B: the right-hand sides Bk^T (plain) and Bv^T (precise), A off its
+    // diagonal blocks (precise), the diagonal blocks of A (float32), the
+    // inverted diagonal blocks of I + A (precise; the Aqk staging of the exact
+    // fallback aliases them) and -W staged row-major
+    static constexpr int AD_BYTES = NB * 16 * 20 * 4;
+    static constexpr int TB_BYTES = (C * SA * 4 > NP * C * SC * SZ) ? C * SA * 4 : NP * C * SC * SZ;
+    static constexpr int WS_BYTES = C * SK * SZ;
+    static constexpr int STAGE_B = (DK + NP * DV + NP * C) * SC * SZ + AD_BYTES + TB_BYTES + WS_BYTES;
     static constexpr int BIG = STAGE_A > STAGE_B ? STAGE_A : STAGE_B;
     static_assert(NSEG >= 1 && TPS >= 1 && NSEG * TPS == C, "shape");
     static_assert((C * SK * SZ) % 16 == 0 && (C * SC * SZ) % 16 == 0, "alignment");
@@ -299,7 +303,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         // all live at once and spill).
         int tid = threadIdx.x;
         asm volatile("" : "+v"(tid));
-        const int lane = tid & 63, wave = tid >> 6;
+        const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int r = lane & 15, gq = lane >> 4;
         const int c = tid % DKP, seg = seg_of(tid);
         const int i0 = seg * TPS;
@@ -482,14 +486,18 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         load_grp(nxt, 3);
 
         // stage-B layout (aliases stage A)
-        OT* const BkT = (OT*)big;                                      // [DK][SC] beta_j k_j exp(G_j), plain
-        OT* bvt_h = BkT + DK * SC;
-        const PArr<OT> BvT{bvt_h, bvt_h + DV * SC};                    // [DV][SC] beta_j v_j, swizzled
-        float* As = (float*)(bvt_h + NP * DV * SC);                    // [C][SA]  A (strictly lower, with beta)
-        float* Ts = (float*)((char*)As + S::AS_BYTES);                 // [C][SA]  T = (I + A)^-1
-        const PArr<OT> Tb{(OT*)As, (OT*)As + C * SC};                  // [C][SC]  T as an operand (after the solve)
+        OT* const XW = (OT*)big;                            // [DK][SC] beta_j k_j exp(G_j), plain
+        OT* const xu_h = XW + DK * SC;
+        const PArr<OT> XU{xu_h, xu_h + DV * SC};          // [DV][SC] beta_j v_j, precise, swizzled
+        OT* const m_h = xu_h + NP * DV * SC;
+        const PArr<OT> Mp{m_h, m_h + C * SC};             // [C][SC] A below the diagonal blocks, precise
+        float* const Ad = (float*)(m_h + NP * C * SC);    // [NB][16][20] diagonal blocks of A (float32)
+        OT* const tb_h = (OT*)((char*)Ad + S::AD_BYTES);
+        const PArr<OT> Tb{tb_h, tb_h + C * SC};           // [C][SC] (I + A_II)^-1 on the diagonal blocks
+        float* const Aq32 = (float*)tb_h;                  // [C][SA] Aqk staging of the exact fallback (dead before Tb)
+        OT* const Wst = (OT*)((char*)tb_h + S::TB_BYTES);  // [C][SK] -W, plain, row-major (staging of the record)
+        auto ad = [&](int I, int ii, int jj) -> float& { return Ad[(I * 16 + ii) * 20 + jj]; };
         const bool fallback = anyflag != 0;
-        float* Aq32 = Ts;                          // Aqk staging when the exact fallback runs
 
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
@@ -508,19 +516,19 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                         if (j0 + u >= i) av[u] = 0.f;
                         if (j0 + u > i) qv[u] = 0.f;
                     }
+                    *reinterpret_cast<f32x4*>(&ad(I, r, 4 * gq)) = av;
+                } else {
+                    store4_p(Mp, i * SC + j0, av);
                 }
-                *reinterpret_cast<f32x4*>(As + i * SA + j0) = av;
                 if (fallback) *reinterpret_cast<f32x4*>(Aq32 + i * SA + j0) = qv;
                 else store4_p(Waq, fragidx(i, j0, CP / 32), qv);
             }
         }
-        // zero the strictly upper blocks of A (and of the Aqk staging / record),
-        // eight columns at a time (a run of 8 is contiguous in the fragment layout)
+        // zero the strictly upper blocks of the Aqk staging / record, eight
+        // columns at a time (a run of 8 is contiguous in the fragment layout)
         for (int p = tid; p < C * (C / 8); p += S::NT) {
             const int i = p / (C / 8), j8 = 8 * (p % (C / 8));
             if ((j8 >> 4) > (i >> 4)) {
-                *reinterpret_cast<f32x4*>(As + i * SA + j8) = zero4();
-                *reinterpret_cast<f32x4*>(As + i * SA + j8 + 4) = zero4();
                 if (fallback) {
                     *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8) = zero4();
                     *reinterpret_cast<f32x4*>(Aq32 + i * SA + j8 + 4) = zero4();
@@ -535,7 +543,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             float bk[TPS];
 #pragma unroll
             for (int u = 0; u < TPS; ++u) bk[u] = sb[i0 + u] * kreg[u] * egreg[u];
-            store_run<OT, TPS>(BkT + c * SC + i0, bk);
+            store_run<OT, TPS>(XW + c * SC + i0, bk);
         }
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
@@ -543,17 +551,17 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             if (idx < NVEC) {
                 const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
 #pragma unroll
-                for (int e = 0; e < 8; ++e) store_p(BvT, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
+                for (int e = 0; e < 8; ++e) store_p(XU, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
             }
         }
         if (CP > C) {
             for (int p = tid; p < DK * (CP - C); p += S::NT) {
                 const int row = p / (CP - C), i = C + p % (CP - C);
-                store_op(BkT + row * SC + i, 0.f);
+                store_op(XW + row * SC + i, 0.f);
             }
             for (int p = tid; p < DV * (CP - C); p += S::NT) {
                 const int row = p / (CP - C), i = C + p % (CP - C);
-                store_p(BvT, row * SC + swz<CP>(row, i), 0.f);
+                store_p(XU, row * SC + swz<CP>(row, i), 0.f);
             }
         }
         __syncthreads();
@@ -586,7 +594,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                         const int j = 16 * I + jj;
                         const float w = __expf(gi[ii] - gi[jj]) * ki[jj];
                         atomicAdd(&Aq32[i * SA + j], qi[ii] * w);
-                        if (jj < ii) atomicAdd(&As[i * SA + j], sb[i] * ki[ii] * w);
+                        if (jj < ii) atomicAdd(&ad(I, ii, jj), sb[i] * ki[ii] * w);
                     }
                 }
             }
@@ -598,98 +606,68 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             __syncthreads();
         }
 
-        // ---- T = (I + A)^-1: diagonal 16x16 blocks by a column sweep (one wave each)
+        // ---- diagonal blocks of T = (I + A)^-1 by a column sweep (one wave each)
         if (wave < NB) {
             const int I = wave;
             float arow[16];
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) arow[jj] = As[(16 * I + r) * SA + 16 * I + jj];
+            for (int jj = 0; jj < 16; ++jj) arow[jj] = ad(I, r, jj);
             float x[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) x[u] = (4 * gq + u == r) ? 1.f : 0.f;
             sweep16<0>(x, arow, r);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u] = x[u];
-        }
-        // strictly upper blocks of T are zero
-        for (int p = tid; p < C * C; p += S::NT) {
-            const int i = p / C, j = p % C;
-            if ((j >> 4) > (i >> 4)) Ts[i * SA + j] = 0.f;
-        }
-        __syncthreads();
-        // off-diagonal blocks, one block-diagonal at a time:
-        // T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-        for (int d = 1; d < NB; ++d) {
-            const int I = d + wave, J = wave;
-            if (I < NB) {
-                f32x4 P = zero4();
-                for (int Kb = J; Kb < I; ++Kb) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const float a = As[(16 * I + r) * SA + 16 * Kb + 4 * s + gq];
-                        const float bb = Ts[(16 * Kb + 4 * s + gq) * SA + 16 * J + r];
-                        P = mma4(a, bb, P);
-                    }
-                }
-                // lane holds P[4gq + u][r]; contract k = 4gq' + u in step u
-                f32x4 R = zero4();
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float a = Ts[(16 * I + r) * SA + 16 * I + 4 * gq + u];
-                    R = mma4(a, P[u], R);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) Ts[(16 * I + 4 * gq + u) * SA + 16 * J + r] = -R[u];
-            }
-            __syncthreads();
-        }
-        // T as a precise operand, row-major [i][j], padded columns zero (overwrites A)
-        for (int p = tid; p < C * CP; p += S::NT) {
-            const int i = p / CP, j = p % CP;
-            store_p(Tb, i * SC + j, j < C ? Ts[i * SA + j] : 0.f);
+            store4_p(Tb, (16 * I + r) * SC + 16 * I + 4 * gq, (f32x4){x[0], x[1], x[2], x[3]});
         }
         __syncthreads();
         // the next item's inputs were requested several phases ago: take them now,
-        // before the record stores of the last phase (whose completion a later
+        // before the record stores of the last phases (whose completion a later
         // wait would also include)
         settle(nxt);
 
-        // ---- W^T = (Diag(beta) K exp(G))^T T^T  and  U = T Diag(beta) V
+        // ---- W = T Diag(beta) (K exp(G)) and U = T Diag(beta) V by block forward
+        // substitution over the 16-token block rows:
+        //   X_I = T_II (B_I - sum_{J<I} A_IJ X_J)      (X = W with B = Bk, X = U with B = Bv)
+        // One wavefront per 16-column tile of W or U carries the whole recursion
+        // in registers: an accumulator (lane: rows 4gq..4gq+3, column r) is
+        // exactly the right operand of a 16-wide matrix-core product, so X_J
+        // feeds the products with A_IJ and T_II without leaving the registers.
         {
-            constexpr int MW = DK / 16;          // channel tiles of W^T
-            constexpr int NWT = MW * NB;         // W tiles
-            constexpr int NUT = NB * (DV / 16);  // U tiles
-            for (int tix = wave; tix < NWT + NUT; tix += S::NW) {
-                if (tix < NWT) {
-                    const int m = tix / NB, I = tix % NB;     // channels 16m.., tokens 16I..
-                    f32x4 acc = zero4();
-                    const int nks = (16 * I + 15) / 32 + 1;   // T[i][j] = 0 for j > i
-                    for (int ks = 0; ks < nks; ++ks)   // W is stored as a plain operand
-                    {
-                        Frag<OT> a, t;
-                        a.load(BkT + (16 * m + r) * SC + 32 * ks + 8 * gq);
-                        t.load(Tb.h + (16 * I + r) * SC + 32 * ks + 8 * gq);
-                        acc = mma(a, t, acc);
+            constexpr int MW = DK / 16, NTL = DK / 16 + DV / 16;
+            for (int tix = wave; tix < NTL; tix += S::NW) {
+                const bool isw = tix < MW;
+                const int n = isw ? tix : tix - MW;
+                const int row = 16 * n + r;      // channel of the right-hand side
+                f32x4 negx[NB];                  // -X_J, lane: X[16J + 4gq + u][16n + r]
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const int jb = 16 * I + 4 * gq;
+                    f32x4 R = isw ? Vec4<OT>::load(XW + row * SC + jb) : XU.load4(row * SC + swz<CP>(row, jb));
+#pragma unroll
+                    for (int J = 0; J < I; ++J) {
+                        const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
+                        R = mma16_p(Mp.h + mi, Mp.l + mi, negx[J], R);
                     }
-                    // lane holds W^T[16m + 4gq + u][16I + r] = W[i][c..c+3]
-                    Vec4<OT>::store(Wwn + fragidx(16 * I + r, 16 * m + 4 * gq, DKP / 32), -acc);
-                } else {
-                    const int t2 = tix - NWT;
-                    const int I = t2 % NB, nn = t2 / NB;      // tokens 16I.., value cols 16nn..
-                    f32x4 acc = zero4();
-                    const int nks = (16 * I + 15) / 32 + 1;
-                    for (int ks = 0; ks < nks; ++ks)
-                        acc = mma3(Tb.frag((16 * I + r) * SC + 32 * ks + 8 * gq),
-                                   BvT.frag((16 * nn + r) * SC + swz<CP>(16 * nn + r, 32 * ks + 8 * gq)), acc);
-                    // lane holds U[16I + 4gq + u][16nn + r]: accumulator-major block (nn, I)
-                    Vec4<float>::store(Wut + accbase(nn, I, NB, lane), acc);
+                    const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
+                    const f32x4 y = mma16_p(Tb.h + ti, Tb.l + ti, R, zero4());
+                    negx[I] = -y;
+                    if (isw) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
+                    } else {
+                        // accumulator-major block (n, I) of the U^T record
+                        Vec4<float>::store(Wut + accbase(n, I, NB, lane), y);
+                    }
                 }
             }
-            if (DKP > DK) {   // padded key channels of -W are zero
-                for (int p = tid; p < C * (DKP - DK); p += S::NT) {
-                    const int i = p / (DKP - DK), cc = DK + p % (DKP - DK);
-                    store_op(Wwn + fragidx(i, cc, DKP / 32), 0.f);
-                }
+            __syncthreads();
+            // the -W record from its row-major staging, eight channels per store
+            // (padded key channels are zero)
+            for (int p = tid; p < C * (DKP / 8); p += S::NT) {
+                const int i = p / (DKP / 8), c8 = 8 * (p % (DKP / 8));
+                Frag<OT> f;
+                if (c8 < DK) f.load(Wst + i * SK + c8);
+                else f.zero();
+                f.store(Wwn + fragidx(i, c8, DKP / 32));
             }
         }
 

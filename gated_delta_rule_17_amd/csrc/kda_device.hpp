@@ -58,6 +58,7 @@ template <> struct Frag<bf16_t> {
     u16x8 v;
     __device__ __forceinline__ void zero() { v = (u16x8){0, 0, 0, 0, 0, 0, 0, 0}; }
     __device__ __forceinline__ void load(const bf16_t* p) { v = *reinterpret_cast<const u16x8*>(p); }
+    __device__ __forceinline__ void store(bf16_t* p) const { *reinterpret_cast<u16x8*>(p) = v; }
     __device__ __forceinline__ float get(int i) const { return bf16_to_f32(v[i]); }
     __device__ __forceinline__ void set(int i, float x) { v[i] = f32_to_bf16(x); }
     // make the loaded value available here (the wait for its load goes here)
@@ -70,6 +71,10 @@ template <> struct Frag<float> {
     __device__ __forceinline__ void load(const float* p) {
         lo = *reinterpret_cast<const f32x4*>(p);
         hi = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void store(float* p) const {
+        *reinterpret_cast<f32x4*>(p) = lo;
+        *reinterpret_cast<f32x4*>(p + 4) = hi;
     }
     __device__ __forceinline__ float get(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
     __device__ __forceinline__ void set(int i, float x) { if (i < 4) lo[i] = x; else hi[i - 4] = x; }
@@ -156,6 +161,34 @@ __device__ __forceinline__ f32x4 mma3(const PFrag<float>& a, const PFrag<float>&
     return mma(a.h, b.h, c);
 }
 
+// D += A B over a 16-wide k given as four values per lane: lane (r, g)
+// supplies A[r][4g .. 4g+3] (read from memory) and B[4g .. 4g+3][r], which is
+// the layout of a 16x16 accumulator, so an accumulator serves directly as the
+// right operand.  bf16: the precise product hi*hi + hi*lo + lo*hi of the
+// pairs on v_mfma_f32_16x16x16_bf16; float32: four 16x16x4 steps, step u
+// contracting the indices k = 4g + u.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mma16_p(const bf16_t* ah, const bf16_t* al, f32x4 b, f32x4 c) {
+    const s16x4 a_h = *reinterpret_cast<const s16x4*>(ah);
+    const s16x4 a_l = *reinterpret_cast<const s16x4*>(al);
+    s16x4 b_h, b_l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint16_t hb = f32_to_bf16(b[u]);
+        b_h[u] = (short)hb;
+        b_l[u] = (short)f32_to_bf16(b[u] - bf16_to_f32(hb));
+    }
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_l, b_h, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b_l, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b_h, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16_p(const float* a, const float*, f32x4 b, f32x4 c) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(a);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], b[u], c, 0, 0, 0);
+    return c;
+}
+
 // Plain operand times precise operand: a * (b.hi + b.lo), and the mirror.
 __device__ __forceinline__ f32x4 mma2(const Frag<bf16_t>& a, const PFrag<bf16_t>& b, f32x4 c) {
     c = mma(a, b.l, c);
@@ -177,6 +210,11 @@ __device__ __forceinline__ f32x4 mma2(const PFrag<float>& a, const Frag<float>& 
 template <typename T> struct PArr {
     T* h; T* l;
     __device__ __forceinline__ PFrag<T> frag(int idx) const { PFrag<T> f; f.load(h + idx, l + idx); return f; }
+    // four consecutive values as float32 (hi + lo)
+    __device__ __forceinline__ f32x4 load4(int idx) const {
+        if constexpr (sizeof(T) == 2) return Vec4<T>::load(h + idx) + Vec4<T>::load(l + idx);
+        else return Vec4<T>::load(h + idx);
+    }
 };
 
 __device__ __forceinline__ void store_p(const PArr<bf16_t>& a, int idx, float x) {
