@@ -637,25 +637,58 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                 const bool isw = tix < MW;
                 const int n = isw ? tix : tix - MW;
                 const int row = 16 * n + r;      // channel of the right-hand side
-                f32x4 negx[NB];                  // -X_J, lane: X[16J + 4gq + u][16n + r]
+                if constexpr (S::SPLIT) {
+                    // bf16 operands: U from precise products throughout; W (stored
+                    // plain) from plain products with A_IJ and a precise one with
+                    // T_II; -X_J is split into bf16 parts once
+                    B16 negx[NB];                // -X_J, lane: X[16J + 4gq + u][16n + r]
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    const int jb = 16 * I + 4 * gq;
-                    f32x4 R = isw ? Vec4<OT>::load(XW + row * SC + jb) : XU.load4(row * SC + swz<CP>(row, jb));
+                    for (int I = 0; I < NB; ++I) {
+                        const int jb = 16 * I + 4 * gq;
+                        const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
+                        f32x4 y;
+                        if (isw) {
+                            f32x4 R = Vec4<OT>::load(XW + row * SC + jb);
 #pragma unroll
-                    for (int J = 0; J < I; ++J) {
-                        const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
-                        R = mma16_p(Mp.h + mi, Mp.l + mi, negx[J], R);
+                            for (int J = 0; J < I; ++J)
+                                R = mma16(Mp.h + (16 * I + r) * SC + 16 * J + 4 * gq, negx[J], R);
+                            y = mma16_p(Tb.h + ti, Tb.l + ti, B16::from(R), zero4());
+                            negx[I] = B16::plain(-y);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
+                        } else {
+                            f32x4 R = XU.load4(row * SC + swz<CP>(row, jb));
+#pragma unroll
+                            for (int J = 0; J < I; ++J) {
+                                const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
+                                R = mma16_p(Mp.h + mi, Mp.l + mi, negx[J], R);
+                            }
+                            y = mma16_p(Tb.h + ti, Tb.l + ti, B16::from(R), zero4());
+                            negx[I] = B16::from(-y);
+                            // accumulator-major block (n, I) of the U^T record
+                            Vec4<float>::store(Wut + accbase(n, I, NB, lane), y);
+                        }
                     }
-                    const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
-                    const f32x4 y = mma16_p(Tb.h + ti, Tb.l + ti, R, zero4());
-                    negx[I] = -y;
-                    if (isw) {
+                } else {
+                    f32x4 negx[NB];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
-                    } else {
-                        // accumulator-major block (n, I) of the U^T record
-                        Vec4<float>::store(Wut + accbase(n, I, NB, lane), y);
+                    for (int I = 0; I < NB; ++I) {
+                        const int jb = 16 * I + 4 * gq;
+                        f32x4 R = isw ? Vec4<OT>::load(XW + row * SC + jb) : XU.load4(row * SC + swz<CP>(row, jb));
+#pragma unroll
+                        for (int J = 0; J < I; ++J) {
+                            const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
+                            R = mma16_p(Mp.h + mi, Mp.l + mi, negx[J], R);
+                        }
+                        const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
+                        const f32x4 y = mma16_p(Tb.h + ti, Tb.l + ti, R, zero4());
+                        negx[I] = -y;
+                        if (isw) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
+                        } else {
+                            Vec4<float>::store(Wut + accbase(n, I, NB, lane), y);
+                        }
                     }
                 }
             }

@@ -182,6 +182,40 @@ __device__ __forceinline__ f32x4 mma16_p(const bf16_t* ah, const bf16_t* al, f32
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b_l, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b_h, c, 0, 0, 0);
 }
+// A 16x16 accumulator (or any four values per lane in that layout) as a
+// right operand of the 16-wide products: plain and hi/lo bf16 parts.
+struct B16 {
+    s16x4 h, l;
+    __device__ __forceinline__ static B16 from(f32x4 x) {
+        B16 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint16_t hb = f32_to_bf16(x[u]);
+            r.h[u] = (short)hb;
+            r.l[u] = (short)f32_to_bf16(x[u] - bf16_to_f32(hb));
+        }
+        return r;
+    }
+    __device__ __forceinline__ static B16 plain(f32x4 x) {
+        B16 r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r.h[u] = (short)f32_to_bf16(x[u]);
+        r.l = r.h;
+        return r;
+    }
+};
+// precise: A pair from memory times a pre-split right operand
+__device__ __forceinline__ f32x4 mma16_p(const bf16_t* ah, const bf16_t* al, const B16& b, f32x4 c) {
+    const s16x4 a_h = *reinterpret_cast<const s16x4*>(ah);
+    const s16x4 a_l = *reinterpret_cast<const s16x4*>(al);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_l, b.h, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b.l, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b.h, c, 0, 0, 0);
+}
+// plain: one bf16 product (hi parts only)
+__device__ __forceinline__ f32x4 mma16(const bf16_t* a, const B16& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*reinterpret_cast<const s16x4*>(a), b.h, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x4 mma16_p(const float* a, const float*, f32x4 b, f32x4 c) {
     const f32x4 av = *reinterpret_cast<const f32x4*>(a);
 #pragma unroll
