@@ -5,14 +5,14 @@
 // order, each token doing decay -> prediction (a reduction over the key
 // dimension) -> residual -> rank-1 write -> read (a second reduction).
 //
-// MI355X mapping: value columns evolve independently, so one workgroup owns
-// a slab of DVT columns of one (batch, head) state (DVT = min(Dv, 64): two
-// workgroups per head at Dv = 128, which halves the registers per thread and
-// doubles the workgroups in flight).  The slab of the transposed state
+// MI355X mapping: one workgroup of up to 512 threads owns the whole state of
+// one (batch, head), so every wave instruction reads and writes whole
+// contiguous rows (a slab split of the columns over two workgroups, with
+// half-rows per instruction, measured 5% slower).  The transposed state
 // H = S^T (Dk x Dv, float32) is loaded ONCE from HBM into registers with
-// 16-byte loads -- thread (rg, cx) holds columns 4cx..4cx+3 of the slab in
-// rows rg, rg+RG, rg+2RG, ... so each wave instruction reads contiguous row
-// segments -- and written back ONCE at the end.  Per token:
+// 16-byte loads -- thread (rg, cx) holds columns 4cx..4cx+3 in rows rg,
+// rg+RG, rg+2RG, ... -- and written back ONCE at the end.  The first token's
+// inputs are requested before the state, so they arrive first.  Per token:
 //   Ht   = Diag(exp g_t) H                          (rows scaled)
 //   vhat = Ht^T k,  r = Ht^T q~,  kq = k . q~       (one pass over the rows)
 //   e    = beta (v - vhat)
@@ -27,9 +27,9 @@ namespace kda {
 
 template <int DK, int DV>
 struct RecShape {
-    static constexpr int DVT = DV < 64 ? DV : 64;   // columns per workgroup
+    static constexpr int DVT = DV;                  // columns per workgroup
     static constexpr int NCT = DV / DVT;            // workgroups per (b, h)
-    static constexpr int NT = (DK * DVT / 4 < 256) ? DK * DVT / 4 : 256;  // threads
+    static constexpr int NT = (DK * DVT / 4 < 512) ? DK * DVT / 4 : 512;  // threads
     static constexpr int CX = DVT / 4;       // threads across the slab (float4 each)
     static constexpr int RG = NT / CX;       // row groups
     static constexpr int RPT = DK / RG;      // rows per thread
@@ -56,14 +56,8 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][9];
 
     float* st = state + (size_t)bh * DK * DV + c0;
-    f32x4 hr[S::RPT];
-#pragma unroll
-    for (int i = 0; i < S::RPT; ++i)
-        hr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
-
-    for (int t = 0; t < T; ++t) {
-        const size_t tok = ((size_t)b * T + t) * H + h;
+    // the first token's inputs, requested before the state so that they arrive first
+    auto token_inputs = [&](size_t tok) {
         for (int c = tid; c < DK; c += S::NT) {
             sk[c] = io<IO>::load(k + tok * DK + c);
             sq[c] = io<IO>::load(q + tok * DK + c) * scale;
@@ -73,6 +67,17 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             sa[c] = a;
         }
         for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
+    };
+    if (T > 0) token_inputs(((size_t)b * T) * H + h);
+    f32x4 hr[S::RPT];
+#pragma unroll
+    for (int i = 0; i < S::RPT; ++i)
+        hr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
+
+    for (int t = 0; t < T; ++t) {
+        const size_t tok = ((size_t)b * T + t) * H + h;
+        if (t > 0) token_inputs(tok);
         __syncthreads();
 
         f32x4 ak = zero4(), aq = zero4();
