@@ -55,10 +55,9 @@ struct CS {
     static constexpr int SKF = DKP + 4;               // stride of the float32 key array
     static constexpr int SC = CP + PAD;               // stride of [channel][token] operands
     static constexpr int SA = C + 4;                  // stride of float32 A / T
-    static constexpr int NT = C * (DK < 32 ? 32 : DK) >= 1024 ? 1024 : C * (DK < 32 ? 32 : DK);  // chunk_prepare threads
-    static constexpr int NW = NT / 64;                // and wavefronts
-    static constexpr int NSEG = NT / DKP;             // threads per key channel (prefix sums)
-    static constexpr int TPS = C / NSEG;              // tokens per thread
+    static constexpr int KSN = DKP / 32;              // 32-channel slices
+    static constexpr int NW = NB * KSN;               // chunk_prepare wavefronts: one per 16 x 32 tile
+    static constexpr int NT = 64 * NW;                // and threads
     static constexpr int NPAIR = NB * (NB - 1) / 2;
     static constexpr bool SPLIT = sizeof(OT) == 2;    // bf16: precise operands are hi/lo pairs
     static constexpr int NP = SPLIT ? 2 : 1;
@@ -71,16 +70,16 @@ struct CS {
     static constexpr size_t U_N = (size_t)DV * C;     // U^T     [DV][C]    float32
     // LDS, stage A: Qk (plain), Qq and Kd (precise), Kk (float32)
     static constexpr int STAGE_A = (1 + 2 * NP) * C * SK * SZ + C * SKF * 4;
-    // stage B: the right-hand sides Bk^T (plain) and Bv^T (precise), A off its
-    // diagonal blocks (precise), the diagonal blocks of A (float32), the
-    // inverted diagonal blocks of I + A (precise; the Aqk staging of the exact
-    // fallback aliases them) and -W staged row-major
-    static constexpr int AD_BYTES = NB * 16 * 20 * 4;
+    // stage B: the right-hand sides Bk (plain) and Bv (precise) as [token][channel],
+    // A off its diagonal blocks (precise), the inverted diagonal blocks of
+    // I + A (precise; the Aqk staging of the exact fallback aliases them) and
+    // -W staged row-major
     static constexpr int TB_BYTES = (C * SA * 4 > NP * C * SC * SZ) ? C * SA * 4 : NP * C * SC * SZ;
     static constexpr int WS_BYTES = C * SK * SZ;
-    static constexpr int STAGE_B = (DK + NP * DV + NP * C) * SC * SZ + AD_BYTES + TB_BYTES + WS_BYTES;
+    static constexpr int STAGE_B = (1 + NP) * C * SK * SZ + NP * C * SC * SZ + TB_BYTES + WS_BYTES;
     static constexpr int BIG = STAGE_A > STAGE_B ? STAGE_A : STAGE_B;
-    static_assert(NSEG >= 1 && TPS >= 1 && NSEG * TPS == C, "shape");
+    static_assert(DV == DK, "v shares the key channels' layout");
+    static_assert(NT <= 1024, "one workgroup");
     static_assert((C * SK * SZ) % 16 == 0 && (C * SC * SZ) % 16 == 0, "alignment");
 };
 
@@ -204,97 +203,120 @@ __device__ __forceinline__ void sweep16(float (&x)[4], const float (&arow)[16], 
 // ---------------------------------------------------------------------------
 // chunk_prepare
 // ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 16 lanes of a row (DPP row shifts; a lane
+// shifted in from outside the row contributes 0).
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    return x;
+}
+
+// Right operand (32 x 16) that picks columns 16hh .. 16hh+15 out of a 16 x 32
+// left operand: lane (r, g) holds B[8g + e][r] = (8g + e == 16hh + r).  The
+// product D = A B is then an exact transpose into the accumulator layout,
+// lane (r, g) receiving A[4g + u][16hh + r] (one nonzero term per sum).
+template <typename OT>
+__device__ __forceinline__ Frag<OT> select_frag(int hh, int lane) {
+    Frag<OT> f;
+    const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.set(e, (8 * g + e == 16 * hh + r) ? 1.f : 0.f);
+    return f;
+}
+
 template <int C, int DK, int DV, typename OT>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__((CS<C, DK, DV, OT>::NT))
 chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
               int T, int H, int NC, int NITEM, float scale, int mode, void* __restrict__ ws, size_t nrec)
 {
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SKF = S::SKF, SC = S::SC,
-                  SA = S::SA, NP = S::NP;
-    constexpr int NSEG = S::NSEG, TPS = S::TPS;
-    constexpr int NVEC = C * DV / 8, VPT = (NVEC + S::NT - 1) / S::NT;
+                  SA = S::SA, NP = S::NP, KSN = S::KSN;
 
     __shared__ __align__(16) char big[S::BIG];
     __shared__ float sb[C];
-    __shared__ float segtot[NSEG][DKP], segfirst[NSEG][DKP];
-    __shared__ float fpair[S::NPAIR > 0 ? S::NPAIR : 1][DKP];
-    __shared__ unsigned char flag[NB][DKP];
+    __shared__ __align__(16) float btot[NB][DKP];       // per-block totals of the log2 decay
+    __shared__ __align__(16) float bfirst[NB][DKP];     // and its first term
+    __shared__ __align__(16) float eSb[NB][DKP];        // exp(G at the block's first token)
+    __shared__ __align__(16) float eLb[NB][DKP];        // exp(G_last - G at the block's last token)
+    __shared__ __align__(16) float fpair[S::NPAIR > 0 ? S::NPAIR : 1][DKP];
+    __shared__ __align__(8) unsigned char flag[NB][DKP];
     __shared__ int anyflag;
+    __shared__ __align__(16) float Ads[NB * 16 * 20];   // diagonal blocks of A (float32)
 
     const WsLayout<C, DK, DV, OT> W(ws, nrec);
 
-    // Thread (seg, c) owns tokens seg*TPS .. +TPS-1 of key channel c.
-    // (seg is uniform across a wavefront when DKP is a multiple of 64: tell the
-    // compiler, so that token-row addresses and segment bookkeeping are scalar)
-    auto seg_of = [](int tid) {
-        return DKP % 64 == 0 ? __builtin_amdgcn_readfirstlane(tid / DKP) : tid / DKP;
-    };
-
-    // The global inputs of one chunk as this thread reads them: g, k, q of its
-    // tokens, the beta of token tid, and v rows as 8-element vectors with their
-    // beta.  Straight-line loads with clamped addresses (out-of-range elements
-    // are zeroed where they are used), in five groups: group 0 the v rows and
-    // betas, groups 1-4 a quarter of the tokens each.
+    // Work layout: wavefront (I, ks) owns the 16 x 32 tile of tokens
+    // 16I .. 16I+15 and key channels 32ks .. 32ks+31 of its chunk, lane (r, gq)
+    // the token 16I + r and the channels 32ks + 8gq .. +7: the matrix-core
+    // fragment layout of the [token][channel] operands.  Every global load
+    // and every operand store is then 16 bytes wide, and the cumulative decay
+    // inside a block is a scan over the 16 lanes of a row.  (v has the key
+    // channels' shape: DV == DK.)
     struct In {
-        float G[TPS], k[TPS], q[TPS];
-        float bl;
-        Frag<OT> v[VPT];
-        float vb[VPT];
+        f32x4 g0, g1;          // per-channel log-gates of the 8 channels
+        float gt;              // per-token log-gate
+        Frag<OT> k, q, v;
+        float b;               // beta of the token
     };
     auto load_in = [&](In& x, int item, int tid, int grp) {
-        const int c = tid % DKP, i0 = seg_of(tid) * TPS;
-        const int cc = c < DK ? c : DK - 1;
+        const int wv = tid >> 6, ln = tid & 63;
+        const int I = wv / KSN, ksl = wv - I * KSN;
+        const int ch = 32 * ksl + 8 * (ln >> 4);
+        const int chc = ch < DK ? ch : 0;                  // padded channels read channel 0
         const int bh = item / NC, c_idx = item - bh * NC;
         const int b = bh / H, h = bh - b * H;
         const int t0 = c_idx * C;
         const int L = min(C, T - t0);
-        auto token = [&](int i) { return ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h; };
+        const int i = 16 * I + (ln & 15);
+        const size_t tok = ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h;
+        // Both gate forms are loaded unconditionally, from valid addresses, so
+        // that no branch joins loaded registers (a join would force a wait for
+        // the loads right where they are issued); the unused form is never
+        // read.  Without per-channel gates the 32 bytes at the start of the
+        // token's key row (DK >= 16) stand in, without a per-token gate beta.
         if (grp == 0) {
-            x.bl = beta[token(tid < C ? tid : C - 1)];
-#pragma unroll
-            for (int u = 0; u < VPT; ++u) {
-                const int idx = min(tid + S::NT * u, NVEC - 1);
-                const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
-                x.v[u].load(v + token(i) * DV + n8);
-                x.vb[u] = beta[token(i)];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-            if ((TPS >= 4 ? (u * 4) / TPS : u) + 1 != grp) continue;
-            const size_t tok = token(i0 + u);
-            const float* gp = mode == KDA_GATE_CHANNEL ? g + tok * DK + cc
-                            : (mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
-            x.G[u] = *gp;
-            x.k[u] = io<OT>::load(k + tok * DK + cc);
-            x.q[u] = io<OT>::load(q + tok * DK + cc);
+            const float* gch = mode == KDA_GATE_CHANNEL ? g + tok * DK + chc
+                                                        : reinterpret_cast<const float*>(k + tok * DK);
+            x.g0 = *reinterpret_cast<const f32x4*>(gch);
+            x.g1 = *reinterpret_cast<const f32x4*>(gch + 4);
+            x.gt = *(mode == KDA_GATE_SCALAR ? g + tok : beta + tok);
+        } else if (grp == 1) {
+            x.k.load(k + tok * DK + chc);
+            x.b = beta[tok];
+        } else if (grp == 2) {
+            x.q.load(q + tok * DK + chc);
+        } else {
+            x.v.load(v + tok * DV + chc);
         }
     };
     // Make loaded values available at this point (the wait for their loads
     // is placed here).
     auto settle = [&](In& x) {
-#pragma unroll
-        for (int u = 0; u < TPS; ++u) asm volatile("" : "+v"(x.G[u]), "+v"(x.k[u]), "+v"(x.q[u]));
-        asm volatile("" : "+v"(x.bl));
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            x.v[u].settle();
-            asm volatile("" : "+v"(x.vb[u]));
-        }
+        asm volatile("" : "+v"(x.g0), "+v"(x.g1), "+v"(x.gt), "+v"(x.b));
+        x.k.settle();
+        x.q.settle();
+        x.v.settle();
+    };
+    // eight consecutive values of a precise operand, hi and lo parts
+    auto store8_p = [&](const PArr<OT>& a, int idx, const float* x) {
+        PFrag<OT> f;
+        f.from_f32(x);
+        f.h.store(a.h + idx);
+        if constexpr (S::SPLIT) f.l.store(a.l + idx);
     };
 
     // Persistent workgroups: item = (b*H + h) * NC + chunk, strided by the
-    // grid.  The inputs of the next item are requested in five small groups
-    // spread over the phases of the current one, so that their memory traffic
-    // overlaps its computation instead of arriving in one burst (all
-    // workgroups start their items together) that stalls instruction issue.
+    // grid.  The inputs of the next item are requested at the start of the
+    // current one and taken after its matrix-core phases.
     int item = blockIdx.x;
     if (item >= NITEM) return;
     In cur;
 #pragma unroll
-    for (int grp = 0; grp < 5; ++grp) load_in(cur, item, threadIdx.x, grp);
+    for (int grp = 0; grp < 4; ++grp) load_in(cur, item, threadIdx.x, grp);
     settle(cur);
     for (; item < NITEM; item += gridDim.x) {
         // Thread indices are re-derived in every iteration from a value the
@@ -305,8 +327,9 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int r = lane & 15, gq = lane >> 4;
-        const int c = tid % DKP, seg = seg_of(tid);
-        const int i0 = seg * TPS;
+        const int Ib = wave / KSN, ksl = wave - Ib * KSN;   // this wave's block and channel slice
+        const int ch = 32 * ksl + 8 * gq;                   // this lane's first channel
+        const int it = 16 * Ib + r;                         // this lane's token
         // stage-A arrays
         OT* Qk = (OT*)big;                                             // [C][SK] plain
         const PArr<OT> Qq{Qk + C * SK, Qk + 2 * C * SK};               // [C][SK] precise
@@ -314,13 +337,14 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         float* Kk = (float*)(Qk + (1 + 2 * NP) * C * SK);              // [C][SKF] float32
 
         const int nitem = min(item + (int)gridDim.x, NITEM - 1);
+        // the next item's inputs, requested in four groups over the phases
+        // (gates here, then k and beta, q, v), so that their transfer overlaps
+        // the computation instead of stalling instruction issue in one burst
         In nxt;
-        auto load_grp = [&](In& x, int grp) { load_in(x, nitem, tid, grp); };
-        load_grp(nxt, 0);
 
         const int bh = item / NC, c_idx = item - bh * NC;
-        const int b = bh / H, h = bh - b * H;
         const int t0 = c_idx * C;
+        const int b = bh / H, h = bh - b * H;
         const int L = min(C, T - t0);       // valid tokens (>= 1)
         const size_t rec = (size_t)item;
         OT* const Wq = W.qg_rec(rec);
@@ -328,105 +352,134 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         const PArr<OT> Wkr = W.krt(rec), Waq = W.aqk(rec);
         float* Wut = W.ut + rec * S::U_N;
         if (tid == 0) anyflag = 0;
-        if (tid < C) sb[tid] = tid < L ? cur.bl : 0.f;
-        float G[TPS], kreg[TPS], qreg[TPS];
+        const bool tv = it < L;
+        if (ksl == 0 && gq == 0) sb[it] = tv ? cur.b : 0.f;
+        float gl[8], kv[8], qv[8];
 #pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-            const bool ok = (i0 + u < L) && (c < DK);
-            G[u] = (ok && mode != KDA_GATE_NONE) ? cur.G[u] * kLog2e : 0.f;   // log2 units
-            kreg[u] = ok ? cur.k[u] : 0.f;
-            qreg[u] = ok ? cur.q[u] * scale : 0.f;
-        }
-        // beta_i v_i in float32
-        float bv[VPT][8];
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int idx = tid + S::NT * u;
-            const int i = idx / (DV / 8);
-            const float bi = (idx < NVEC && i < L) ? cur.vb[u] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bv[u][e] = bi * cur.v[u].get(e);
+        for (int e = 0; e < 8; ++e) {
+            const bool ok = tv && (ch + e < DK);
+            const float gv = mode == KDA_GATE_CHANNEL ? (e < 4 ? cur.g0[e] : cur.g1[e - 4]) : cur.gt;
+            gl[e] = (ok && mode != KDA_GATE_NONE) ? gv * kLog2e : 0.f;   // log2 units
+            kv[e] = ok ? cur.k.get(e) : 0.f;
+            qv[e] = ok ? cur.q.get(e) * scale : 0.f;
         }
 
-        // ---- cumulative log-decay (in log2 units from here on, so that every
-        // decay factor is one 2^x).  Local running sums, then segment totals in
-        // LDS; every thread derives the references it needs from the totals with
-        // one left-to-right pass, so all threads obtain bit-identical values.
-        {
-            float run = 0.f;
+        // ---- cumulative log-decay, in log2 units from here on (every decay
+        // factor is one 2^x): inside the block by a scan over the row, the
+        // block totals through LDS.
 #pragma unroll
-            for (int u = 0; u < TPS; ++u) {
-                run += G[u];
-                G[u] = run;
-            }
-            segtot[seg][c] = run;
-            segfirst[seg][c] = G[0];
+        for (int e = 0; e < 8; ++e) gl[e] = row_scan16(gl[e]);
+        if (r == 0) {
+            *reinterpret_cast<f32x4*>(&bfirst[Ib][ch]) = (f32x4){gl[0], gl[1], gl[2], gl[3]};
+            *reinterpret_cast<f32x4*>(&bfirst[Ib][ch + 4]) = (f32x4){gl[4], gl[5], gl[6], gl[7]};
+        }
+        if (r == 15) {
+            *reinterpret_cast<f32x4*>(&btot[Ib][ch]) = (f32x4){gl[0], gl[1], gl[2], gl[3]};
+            *reinterpret_cast<f32x4*>(&btot[Ib][ch + 4]) = (f32x4){gl[4], gl[5], gl[6], gl[7]};
         }
         __syncthreads();
-        load_grp(nxt, 1);
-        const int Iblk = i0 >> 4;                     // this thread's 16-token block
-        const int s_first = (16 * Iblk) / TPS, s_last = (16 * Iblk + 15) / TPS;
-        // the block pair (pI, pJ), pJ < pI, whose cross factor this thread computes
-        const bool has_pair = seg < S::NPAIR;
-        int pI = 1, pJ = 0;
-        {
-            int base = 0;
-            while (base + pI <= seg) { base += pI; ++pI; }
-            pJ = seg - base;
-        }
-        const int p_first = (16 * pI) / TPS, p_last = (16 * pJ + 15) / TPS;
-        float off = 0.f, gs = 0.f, ge = 0.f, fgs = 0.f, fge = 0.f, acc = 0.f;
-        for (int s2 = 0; s2 < NSEG; ++s2) {
-            const float first = segfirst[s2][c];
-            if (s2 == seg) off = acc;
-            if (s2 == s_first) gs = acc + first;      // G at the block's first token
-            if (s2 == p_first) fgs = acc + first;
-            acc += segtot[s2][c];
-            if (s2 == s_last) ge = acc;               // G at the block's last token
-            if (s2 == p_last) fge = acc;
-        }
-        const float gL = acc;                         // G at the chunk's last token
+        load_in(nxt, nitem, tid, 0);
+        // ---- the factors of one (block I, channel c): a left-to-right pass
+        // over the block totals (the same order everywhere) gives G at the
+        // block boundaries; from them exp(G_s(I)), exp(G_last - G_e(I)), the
+        // cross-block factors exp(G_s(I) - G_e(J)), J < I, the range flag and,
+        // once per channel, the exp(G_last) record
+        for (int job = tid; job < NB * DKP; job += S::NT) {
+            const int I = job / DKP, c = job - I * DKP;
+            float acc = 0.f, off = 0.f, gend[NB];
 #pragma unroll
-        for (int u = 0; u < TPS; ++u) G[u] += off;
-        const float eS = exp2_fast(gs);               // exp(G_s(I)) <= 1
-        const float eL = exp2_fast(gL - ge);          // exp(G_last - G_e(I)) <= 1
-        const bool bad = (gs - ge) > kRangeMax * kLog2e;
-        if (seg == s_first) {
-            flag[Iblk][c] = bad ? 1 : 0;
-            if (bad) atomicOr(&anyflag, 1);
+            for (int J = 0; J < NB; ++J) {
+                if (J == I) off = acc;
+                acc += btot[J][c];
+                gend[J] = acc;
+            }
+            const float g0 = bfirst[I][c], gt = btot[I][c];
+            eSb[I][c] = exp2_fast(off + g0);
+            eLb[I][c] = exp2_fast(acc - (off + gt));
+            const bool bad = (g0 - gt) > kRangeMax * kLog2e;
+            flag[I][c] = bad ? 1 : 0;
+            if (bad) anyflag = 1;
+#pragma unroll
+            for (int J = 0; J < NB - 1; ++J)
+                if (J < I) fpair[I * (I - 1) / 2 + J][c] = exp2_fast(off + g0 - gend[J]);
+            if (I == 0 && c < DK) W.gl[rec * DK + c] = exp2_fast(acc);
         }
-        if (has_pair) fpair[seg][c] = exp2_fast(fgs - fge);   // exp(G_s(pI) - G_e(pJ)) <= 1
-        if (seg == 0 && c < DK) W.gl[rec * DK + c] = exp2_fast(gL);
+        __syncthreads();
+        load_in(nxt, nitem, tid, 1);
 
-        // ---- element-wise operands
-        float egreg[TPS], krv[TPS];
+        // ---- element-wise operands of token `it`, channels ch .. ch+7, each
+        // group stored as soon as it is formed
+        float gs[8], ge[8], eg[8];
+        unsigned int badbits = 0;
+        {
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(&bfirst[Ib][ch]);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(&bfirst[Ib][ch + 4]);
+            const f32x4 t0v = *reinterpret_cast<const f32x4*>(&btot[Ib][ch]);
+            const f32x4 t1v = *reinterpret_cast<const f32x4*>(&btot[Ib][ch + 4]);
+            const uint64_t fb = *reinterpret_cast<const uint64_t*>(&flag[Ib][ch]);
 #pragma unroll
-        for (int u = 0; u < TPS; ++u) {
-            const int i = i0 + u;
-            const float kv = kreg[u], qv = qreg[u];
-            const float x = exp2_fast(G[u] - gs);              // <= 1
-            const float kk = kv * exp2_fast(ge - G[u]);        // <= |k|
-            const float kd = bad ? 0.f : kv * exp2_fast(gs - G[u]);  // >= |k|, bounded
-            store_op(Qk + i * SK + c, kv * x);
-            store_p(Qq, i * SK + c, qv * x);
-            store_p(Kd, i * SK + c, kd);
-            Kk[i * SKF + c] = kk;
-            const float eg = x * eS;                           // exp(G_i) <= 1
-            egreg[u] = eg;
-            krv[u] = kk * eL;                                  // k exp(G_last - G_i) <= |k|
-            store_op(Wq + fragidx(i, c, DKP / 32), qv * eg);
-        }
-        // Kr^T row c, tokens i0 .. i0+TPS-1, four at a time (contiguous in the fragment layout)
-        if (c < DK) {
-            if constexpr (TPS >= 4) {
-#pragma unroll
-                for (int u = 0; u < TPS; u += 4)
-                    store4_p(Wkr, fragidx(c, i0 + u, CP / 32), (f32x4){krv[u], krv[u + 1], krv[u + 2], krv[u + 3]});
-            } else {
-#pragma unroll
-                for (int u = 0; u < TPS; ++u) store_p(Wkr, fragidx(c, i0 + u, CP / 32), krv[u]);
+            for (int e = 0; e < 8; ++e) {
+                gs[e] = e < 4 ? s0[e] : s1[e - 4];     // at the block's first token (local)
+                ge[e] = e < 4 ? t0v[e] : t1v[e - 4];   // at the block's last token (local)
+                badbits |= ((fb >> (8 * e)) & 1u) << e;
             }
         }
+        {
+            const f32x4 es0 = *reinterpret_cast<const f32x4*>(&eSb[Ib][ch]);
+            const f32x4 es1 = *reinterpret_cast<const f32x4*>(&eSb[Ib][ch + 4]);
+            float qk[8], qq[8], qg[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = exp2_fast(gl[e] - gs[e]);              // <= 1
+                eg[e] = x * (e < 4 ? es0[e] : es1[e - 4]);             // exp(G_i) <= 1
+                qk[e] = kv[e] * x;
+                qq[e] = qv[e] * x;
+                qg[e] = qv[e] * eg[e];
+            }
+            store_run<OT, 8>(Qk + it * SK + ch, qk);
+            store8_p(Qq, it * SK + ch, qq);
+            // Qg record: one 16-byte store per lane, a wave's tile is 1 KiB of
+            // contiguous record
+            store_run<OT, 8>(Wq + fragidx(it, ch, KSN), qg);
+        }
+        {
+            float kd[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                kd[e] = (badbits >> e) & 1u ? 0.f : kv[e] * exp2_fast(gs[e] - gl[e]);   // >= |k|, bounded
+            store8_p(Kd, it * SK + ch, kd);
+        }
+        {
+            const f32x4 el0 = *reinterpret_cast<const f32x4*>(&eLb[Ib][ch]);
+            const f32x4 el1 = *reinterpret_cast<const f32x4*>(&eLb[Ib][ch + 4]);
+            float kk[8], kr[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kk[e] = kv[e] * exp2_fast(ge[e] - gl[e]);              // <= |k|
+                kr[e] = kk[e] * (e < 4 ? el0[e] : el1[e - 4]);         // k exp(G_last - G_i)
+            }
+            *reinterpret_cast<f32x4*>(Kk + it * SKF + ch) = (f32x4){kk[0], kk[1], kk[2], kk[3]};
+            *reinterpret_cast<f32x4*>(Kk + it * SKF + ch + 4) = (f32x4){kk[4], kk[5], kk[6], kk[7]};
+            // Kr^T record, transposed on the matrix cores: a lane then holds
+            // four consecutive tokens of one channel
+            PFrag<OT> kf;
+            kf.from_f32(kr);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if (32 * ksl + 16 * hh < DK) {
+                    const Frag<OT> sel = select_frag<OT>(hh, lane);
+                    const int idx = fragidx(32 * ksl + 16 * hh + r, 16 * Ib + 4 * gq, CP / 32);
+                    Vec4<OT>::store(Wkr.h + idx, mma(kf.h, sel, zero4()));
+                    if constexpr (S::SPLIT) Vec4<OT>::store(Wkr.l + idx, mma(kf.l, sel, zero4()));
+                }
+            }
+        }
+        load_in(nxt, nitem, tid, 2);
+        // beta_i k_i exp(G_i), kept (in the plain operand type) for the
+        // right-hand side of the solve
+        Frag<OT> bk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bk.set(e, cur.b * kv[e] * eg[e]);
         if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
             for (int p = tid; p < DK * (CP - C); p += S::NT) {
                 const int cc = p / (CP - C), i = C + p % (CP - C);
@@ -438,7 +491,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             }
         }
         __syncthreads();
-        load_grp(nxt, 2);
+
 
         // ---- A^T and Aqk^T tiles on the matrix cores: tile (J, I), J <= I
         // lane result: A[i = 16I + r][j = 16J + 4gq + u]
@@ -483,20 +536,19 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             }
         }
         __syncthreads();   // stage-A operands are dead from here on
-        load_grp(nxt, 3);
+        load_in(nxt, nitem, tid, 3);
 
         // stage-B layout (aliases stage A)
-        OT* const XW = (OT*)big;                            // [DK][SC] beta_j k_j exp(G_j), plain
-        OT* const xu_h = XW + DK * SC;
-        const PArr<OT> XU{xu_h, xu_h + DV * SC};          // [DV][SC] beta_j v_j, precise, swizzled
-        OT* const m_h = xu_h + NP * DV * SC;
+        OT* const XW = (OT*)big;                            // [C][SK] beta_j k_j exp(G_j), plain
+        OT* const xu_h = XW + C * SK;
+        const PArr<OT> XU{xu_h, xu_h + C * SK};           // [C][SK] beta_j v_j, precise
+        OT* const m_h = xu_h + NP * C * SK;
         const PArr<OT> Mp{m_h, m_h + C * SC};             // [C][SC] A below the diagonal blocks, precise
-        float* const Ad = (float*)(m_h + NP * C * SC);    // [NB][16][20] diagonal blocks of A (float32)
-        OT* const tb_h = (OT*)((char*)Ad + S::AD_BYTES);
+        OT* const tb_h = m_h + NP * C * SC;
         const PArr<OT> Tb{tb_h, tb_h + C * SC};           // [C][SC] (I + A_II)^-1 on the diagonal blocks
         float* const Aq32 = (float*)tb_h;                  // [C][SA] Aqk staging of the exact fallback (dead before Tb)
         OT* const Wst = (OT*)((char*)tb_h + S::TB_BYTES);  // [C][SK] -W, plain, row-major (staging of the record)
-        auto ad = [&](int I, int ii, int jj) -> float& { return Ad[(I * 16 + ii) * 20 + jj]; };
+        auto ad = [&](int I, int ii, int jj) -> float& { return Ads[(I * 16 + ii) * 20 + jj]; };
         const bool fallback = anyflag != 0;
 
 #pragma unroll
@@ -538,34 +590,15 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                 }
             }
         }
-        // beta_j k_j exp(G_j) and beta_j v_j, transposed ([channel][token])
-        if (c < DK) {
-            float bk[TPS];
+        // beta_j k_j exp(G_j) and beta_j v_j, rows of 8 channels
+        bk.store(XW + it * SK + ch);
+        {
+            float bv[8];
 #pragma unroll
-            for (int u = 0; u < TPS; ++u) bk[u] = sb[i0 + u] * kreg[u] * egreg[u];
-            store_run<OT, TPS>(XW + c * SC + i0, bk);
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int idx = tid + S::NT * u;
-            if (idx < NVEC) {
-                const int i = idx / (DV / 8), n8 = 8 * (idx % (DV / 8));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) store_p(XU, (n8 + e) * SC + swz<CP>(n8 + e, i), bv[u][e]);
-            }
-        }
-        if (CP > C) {
-            for (int p = tid; p < DK * (CP - C); p += S::NT) {
-                const int row = p / (CP - C), i = C + p % (CP - C);
-                store_op(XW + row * SC + i, 0.f);
-            }
-            for (int p = tid; p < DV * (CP - C); p += S::NT) {
-                const int row = p / (CP - C), i = C + p % (CP - C);
-                store_p(XU, row * SC + swz<CP>(row, i), 0.f);
-            }
+            for (int e = 0; e < 8; ++e) bv[e] = (tv && ch + e < DK) ? cur.b * cur.v.get(e) : 0.f;
+            store8_p(XU, it * SK + ch, bv);
         }
         __syncthreads();
-        load_grp(nxt, 4);
 
         if (fallback) {
             // exact diagonal-block terms for key channels whose decay across the block
@@ -632,6 +665,14 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         // exactly the right operand of a 16-wide matrix-core product, so X_J
         // feeds the products with A_IJ and T_II without leaving the registers.
         {
+            // the right-hand side at tokens jb .. jb+3 of channel `row`
+            // (accumulator layout) from a [token][channel] array
+            auto col4 = [&](const OT* a, int jb, int row) {
+                f32x4 x;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x[u] = io<OT>::load(a + (jb + u) * SK + row);
+                return x;
+            };
             constexpr int MW = DK / 16, NTL = DK / 16 + DV / 16;
             for (int tix = wave; tix < NTL; tix += S::NW) {
                 const bool isw = tix < MW;
@@ -648,7 +689,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                         const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
                         f32x4 y;
                         if (isw) {
-                            f32x4 R = Vec4<OT>::load(XW + row * SC + jb);
+                            f32x4 R = col4(XW, jb, row);
 #pragma unroll
                             for (int J = 0; J < I; ++J)
                                 R = mma16(Mp.h + (16 * I + r) * SC + 16 * J + 4 * gq, negx[J], R);
@@ -657,7 +698,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 #pragma unroll
                             for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
                         } else {
-                            f32x4 R = XU.load4(row * SC + swz<CP>(row, jb));
+                            f32x4 R = col4(XU.h, jb, row) + col4(XU.l, jb, row);
 #pragma unroll
                             for (int J = 0; J < I; ++J) {
                                 const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
@@ -674,7 +715,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
                         const int jb = 16 * I + 4 * gq;
-                        f32x4 R = isw ? Vec4<OT>::load(XW + row * SC + jb) : XU.load4(row * SC + swz<CP>(row, jb));
+                        f32x4 R = col4(isw ? XW : XU.h, jb, row);
 #pragma unroll
                         for (int J = 0; J < I; ++J) {
                             const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
