@@ -877,32 +877,31 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                     else ea = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), ea);
                 }
             }
-#pragma unroll
-            for (int s = 0; s < MHW; ++s) {
-                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
-#pragma unroll
-                for (int ks = 0; ks < KC; ++ks) Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
-            }
             if (has_t) store4_p(ET, r * SC + 16 * wr + 4 * gq, ea + eb);
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, 1 + MHW * (1 + NP * KC), 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             __syncthreads();
-            // H = Diag(gl) H + Kr^T E
+            // H = Diag(gl) H + Kr^T E; the next Kr^T and gl are requested here,
+            // so that the record traffic of a step is spread over both of its
+            // phases (the load unit of the compute unit, not the matrix
+            // cores, bounds the step)
             f32x4 part[MHW];
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
                 if (ALLH || wr + 4 * s < MH) hacc[s] *= P.gl[s];
                 part[s] = zero4();
+                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
             }
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
                 const PFrag<OT> et = ET.frag(r * SC + 32 * ks + 8 * gq);
 #pragma unroll
                 for (int s = 0; s < MHW; ++s) {
+                    Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
                     if (ALLH || wr + 4 * s < MH) {
                         if (ks & 1) part[s] = mma3(P.kr[s][ks], et, part[s]);
                         else hacc[s] = mma3(P.kr[s][ks], et, hacc[s]);
@@ -919,7 +918,20 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
             __syncthreads();
         };
-        if (NC > 0) {
+        if (NC > 0 && S::SPLIT) {
+            // three operand sets in rotation: a chunk's operands are requested
+            // two steps before they are used (the records come from beyond the
+            // L2, whose latency one step does not cover)
+            Ops A, B, D;
+            load_ops(A, 0);
+            load_ops(B, min(1, NC - 1));
+            for (int cidx = 0; cidx < NC; cidx += 3) {
+                step(A, D, min(cidx + 2, NC - 1));
+                if (cidx + 1 < NC) step(B, A, min(cidx + 3, NC - 1));
+                if (cidx + 2 < NC) step(D, B, min(cidx + 4, NC - 1));
+            }
+        } else if (NC > 0) {
+            // float32 operands: two sets (a third does not fit the registers)
             Ops A, B;
             load_ops(A, 0);
             for (int cidx = 0; cidx < NC; cidx += 2) {
@@ -992,7 +1004,16 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
             __syncthreads();
         };
-        if (NC > 0) {
+        if (NC > 0 && S::SPLIT) {
+            Ops A, B, D;
+            load_ops(A, 0);
+            load_ops(B, min(1, NC - 1));
+            for (int cidx = 0; cidx < NC; cidx += 3) {
+                step(A, cidx, D, min(cidx + 2, NC - 1));
+                if (cidx + 1 < NC) step(B, cidx + 1, A, min(cidx + 3, NC - 1));
+                if (cidx + 2 < NC) step(D, cidx + 2, B, min(cidx + 4, NC - 1));
+            }
+        } else if (NC > 0) {
             Ops A, B;
             load_ops(A, 0);
             for (int cidx = 0; cidx < NC; cidx += 2) {
