@@ -60,10 +60,16 @@ def prefill_flops(B, H, T, D, C):
 
 
 def source_hash(*names):
+    """Hash of the kernel code: `//` comments, trailing blanks and empty lines
+    are left out, so an edit of comments alone does not mark the stored
+    counter figures as stale."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "gated_delta_rule_17_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_17_amd", "csrc", n), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

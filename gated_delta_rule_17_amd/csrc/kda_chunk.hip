@@ -15,10 +15,13 @@
 //   H'    = Diag(exp G_last) H + (K * exp(G_last - G))^T E
 //
 // Two kernels:
-//  chunk_prepare  one workgroup per (b, h, chunk), fully parallel.  Everything
-//                 that does not depend on the incoming state: G, A and Aqk on
-//                 the matrix cores, T by blocked forward substitution in LDS,
-//                 W and U on the matrix cores.  Writes one record per chunk.
+//  chunk_prepare  persistent workgroups striding over the (b, h, chunk) items,
+//                 fully parallel, one wavefront per 16-token x 32-channel tile.
+//                 Everything that does not depend on the incoming state: G,
+//                 A and Aqk on the matrix cores, the inverted diagonal blocks of
+//                 I + A by a column sweep, W and U by block forward
+//                 substitution carried in matrix-core accumulators.  Writes one
+//                 record per chunk.
 //  chunk_state    one workgroup per (b, h, 16 value columns), sequential over
 //                 the chunks.  The 16 state columns live in matrix-core
 //                 accumulators (float32) for the whole sequence; per chunk:
