@@ -684,30 +684,48 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                 if constexpr (S::SPLIT) {
                     // bf16 operands: U from precise products throughout; W (stored
                     // plain) from plain products with A_IJ and a precise one with
-                    // T_II; -X_J is split into bf16 parts once
-                    B16 negx[NB];                // -X_J, lane: X[16J + 4gq + u][16n + r]
+                    // T_II; -X_J is split into bf16 parts once.  Every LDS operand
+                    // of the recursion (right-hand sides, A_IJ, T_II) is read up
+                    // front, so that only the matrix-core chain remains serial.
+                    constexpr int NPR = NB * (NB - 1) / 2 > 0 ? NB * (NB - 1) / 2 : 1;
+                    auto ld4 = [&](const OT* p) { return *reinterpret_cast<const s16x4*>(p); };
+                    f32x4 R[NB];
+                    s16x4 th[NB], tl[NB], mh[NPR], ml[NPR];
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
                         const int jb = 16 * I + 4 * gq;
+                        R[I] = isw ? col4(XW, jb, row) : col4(XU.h, jb, row) + col4(XU.l, jb, row);
                         const int ti = (16 * I + r) * SC + 16 * I + 4 * gq;
-                        f32x4 y;
-                        if (isw) {
-                            f32x4 R = col4(XW, jb, row);
+                        th[I] = ld4(Tb.h + ti);
+                        tl[I] = ld4(Tb.l + ti);
 #pragma unroll
-                            for (int J = 0; J < I; ++J)
-                                R = mma16(Mp.h + (16 * I + r) * SC + 16 * J + 4 * gq, negx[J], R);
-                            y = mma16_p(Tb.h + ti, Tb.l + ti, B16::from(R), zero4());
+                        for (int J = 0; J < I; ++J) {
+                            const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
+                            mh[I * (I - 1) / 2 + J] = ld4(Mp.h + mi);
+                            if (!isw) ml[I * (I - 1) / 2 + J] = ld4(Mp.l + mi);
+                        }
+                    }
+                    B16 negx[NB];                // -X_J, lane: X[16J + 4gq + u][16n + r]
+                    if (isw) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            f32x4 x = R[I];
+#pragma unroll
+                            for (int J = 0; J < I; ++J) x = mma16v(mh[I * (I - 1) / 2 + J], negx[J].h, x);
+                            const f32x4 y = mma16v_p(th[I], tl[I], B16::from(x), zero4());
                             negx[I] = B16::plain(-y);
+                            const int jb = 16 * I + 4 * gq;
 #pragma unroll
                             for (int u = 0; u < 4; ++u) store_op(Wst + (jb + u) * SK + 16 * n + r, -y[u]);
-                        } else {
-                            f32x4 R = col4(XU.h, jb, row) + col4(XU.l, jb, row);
+                        }
+                    } else {
 #pragma unroll
-                            for (int J = 0; J < I; ++J) {
-                                const int mi = (16 * I + r) * SC + 16 * J + 4 * gq;
-                                R = mma16_p(Mp.h + mi, Mp.l + mi, negx[J], R);
-                            }
-                            y = mma16_p(Tb.h + ti, Tb.l + ti, B16::from(R), zero4());
+                        for (int I = 0; I < NB; ++I) {
+                            f32x4 x = R[I];
+#pragma unroll
+                            for (int J = 0; J < I; ++J)
+                                x = mma16v_p(mh[I * (I - 1) / 2 + J], ml[I * (I - 1) / 2 + J], negx[J], x);
+                            const f32x4 y = mma16v_p(th[I], tl[I], B16::from(x), zero4());
                             negx[I] = B16::from(-y);
                             // accumulator-major block (n, I) of the U^T record
                             Vec4<float>::store(Wut + accbase(n, I, NB, lane), y);

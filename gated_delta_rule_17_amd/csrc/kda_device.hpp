@@ -212,6 +212,15 @@ __device__ __forceinline__ f32x4 mma16_p(const bf16_t* ah, const bf16_t* al, con
     c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b.l, c, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_h, b.h, c, 0, 0, 0);
 }
+// the same with the left operand already in registers
+__device__ __forceinline__ f32x4 mma16v(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16v_p(s16x4 ah, s16x4 al, const B16& b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, b.h, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, b.l, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, b.h, c, 0, 0, 0);
+}
 // plain: one bf16 product (hi parts only)
 __device__ __forceinline__ f32x4 mma16(const bf16_t* a, const B16& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*reinterpret_cast<const s16x4*>(a), b.h, c, 0, 0, 0);
