@@ -11,6 +11,11 @@ Entry points (same names as the C ABI):
   kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None,
                 o=None, chunk=64, scale=None, mode=None, workspace=None)
   kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype)
+  kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None, scale=None, mode=None)
+  kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None,
+                       final_state=None, o=None, chunk=64, scale=None, mode=None,
+                       workspace=None)
+  kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype)
 """
 from __future__ import annotations
 
@@ -56,6 +61,13 @@ def lib():
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
+    L.kda_recurrent_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.kda_recurrent_varlen.restype = i
+    L.kda_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
+    L.kda_chunk_fwd_varlen_workspace_size.restype = sz
+    L.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp, i, i, i, i, i, i, f, i, i,
+                                       i, vp, sz, vp]
+    L.kda_chunk_fwd_varlen.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i
@@ -189,4 +201,102 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
                              m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length batches
+def _mode_of_packed(g, mode):
+    if mode is None:
+        if g is None:
+            return GATE_NONE
+        return GATE_CHANNEL if g.dim() == 3 else GATE_SCALAR
+    if isinstance(mode, str):
+        return _MODE_NAMES[mode]
+    return int(mode)
+
+
+def _check_cu(cu_seqlens):
+    torch = _torch()
+    _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+    return cu_seqlens.numel() - 1
+
+
+def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
+                         scale: Optional[float] = None, mode=None, out_dtype=None):
+    """Recurrent form over a packed batch; updates ``state`` in place.
+
+    q, k [T,H,Dk], v [T,H,Dv] (float32 or bfloat16), g [T,H,Dk] / [T,H] /
+    None, beta [T,H] float32, state [N,H,Dk,Dv] float32, cu_seqlens int32
+    [N+1] on the device.  Returns o [T,H,Dv].
+    """
+    torch = _torch()
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = _check_cu(cu_seqlens)
+    m = _mode_of_packed(g, mode)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (T, H))
+    _check_dev("state", state, torch.float32, (N, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    _check_dev("o", o, None, (T, H, Dv))
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_recurrent_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                    _ptr(o), _ptr(cu_seqlens), N, T, H, Dk, Dv, float(scale), m,
+                                    _dtype_code(q), _dtype_code(o), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_recurrent_varlen")
+    return o
+
+
+def kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype) -> int:
+    if isinstance(mode, str):
+        mode = _MODE_NAMES[mode]
+    return int(lib().kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, int(mode),
+                                                         int(dtype)))
+
+
+def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None,
+                         o=None, chunk: int = 64, scale: Optional[float] = None, mode=None,
+                         workspace=None, output_final_state: bool = True, out_dtype=None):
+    """Chunkwise form over a packed batch.  Returns (o, final_state).
+
+    Shapes as for :func:`kda_recurrent_varlen`; initial_state / final_state
+    are [N,H,Dk,Dv] float32 (final_state may be initial_state itself).
+    """
+    torch = _torch()
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    N = _check_cu(cu_seqlens)
+    m = _mode_of_packed(g, mode)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (T, H))
+    _check_dev("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    _check_dev("final_state", final_state, torch.float32, (N, H, Dk, Dv))
+    if o is None:
+        o = torch.empty((T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    _check_dev("o", o, None, (T, H, Dv))
+    dt = _dtype_code(q)
+    need = kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, m, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(initial_state), _ptr(final_state), _ptr(o),
+                                    _ptr(cu_seqlens), N, T, H, Dk, Dv, int(chunk), float(scale),
+                                    m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(),
+                                    _stream())
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_varlen")
     return o, final_state

@@ -64,7 +64,7 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     if (T == 0) return KDA_SUCCESS;
     if (!state) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(state)) return KDA_ERROR_MISALIGNED;
-    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, scale, mode, dtype, o_dtype};
+    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, scale, mode, dtype, o_dtype, nullptr};
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -102,7 +102,65 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     }
     if (T == 0 && !final_state) return KDA_SUCCESS;
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk,
-                     scale, mode, dtype, o_dtype, workspace, workspace_bytes};
+                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, nullptr, 0};
+    hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
+kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, float* state, void* o, const int* cu_seqlens,
+                                int N, int T, int H, int Dk, int Dv, float scale, kda_gate_mode mode,
+                                kda_dtype dtype, kda_dtype o_dtype, void* stream)
+{
+    if (N < 0) return KDA_ERROR_INVALID_VALUE;
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Dk, Dv, mode, dtype, o_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if ((double)N * H > 2.0e9) return KDA_ERROR_INVALID_VALUE;
+    if (N == 0 || T == 0) return KDA_SUCCESS;   // every sequence is empty: states unchanged
+    if (!state || !cu_seqlens) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned16(state) || ((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
+    kda::RecArgs a{q, k, v, g, beta, state, o, N, T, H, Dk, Dv, scale, mode, dtype, o_dtype, cu_seqlens};
+    hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, int chunk,
+                                           kda_gate_mode mode, kda_dtype dtype)
+{
+    (void)mode;
+    if (N < 1 || H < 1 || T < 0) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return kda::chunk_varlen_workspace_bytes(N, T, H, Dk, Dv, chunk, dtype);
+}
+
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* initial_state, float* final_state,
+                                void* o, const int* cu_seqlens, int N, int T, int H, int Dk, int Dv,
+                                int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
+                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream)
+{
+    if (N < 0) return KDA_ERROR_INVALID_VALUE;
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Dk, Dv, mode, dtype, o_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    if (Dk != Dv) return KDA_ERROR_NOT_SUPPORTED;
+    // chunk records and state workgroups are counted in 32-bit integers
+    const double gmax = (double)((T + chunk - 1) / chunk) + (double)N;
+    if (gmax * H > 1073741824.0 || (double)N * H * (Dv / 16) + 64.0 > 2147483647.0)
+        return KDA_ERROR_INVALID_VALUE;
+    if (N == 0) return KDA_SUCCESS;
+    if (!cu_seqlens) return KDA_ERROR_INVALID_VALUE;
+    if (((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERROR_MISALIGNED;
+    const size_t need = kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype);
+    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
+    if (T == 0 && !final_state) return KDA_SUCCESS;
+    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk,
+                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }

@@ -233,11 +233,36 @@ template <int C, int DK, int DV, typename OT>
 __global__ void __launch_bounds__((CS<C, DK, DV, OT>::NT))
 chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
-              int T, int H, int NC, int NITEM, float scale, int mode, void* __restrict__ ws, size_t nrec)
+              int T, int H, int NC, int NITEM, float scale, int mode, void* __restrict__ ws, size_t nrec,
+              const int2* __restrict__ ctab)
 {
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SKF = S::SKF, SC = S::SC,
                   SA = S::SA, NP = S::NP, KSN = S::KSN;
+
+    // Where an item's chunk lives: the token index of its first token (tokens
+    // are [*, H, D] rows) and its number of valid tokens.  Dense batches: item
+    // = (b*H + h) * NC + chunk over [B, T].  Packed variable-length batches
+    // (ctab != null): item = g * H + h over the chunk table, whose entry g is
+    // (first token, length); entries past the last chunk have length 0.
+    struct Loc { size_t tok0; int L, h; };
+    auto locate = [&](int item) {
+        Loc l;
+        if (ctab) {
+            const int gch = item / H;
+            l.h = item - gch * H;
+            const int2 e = ctab[gch];
+            l.tok0 = (size_t)e.x;
+            l.L = e.y;
+        } else {
+            const int bh = item / NC, c_idx = item - bh * NC;
+            const int b = bh / H;
+            l.h = bh - b * H;
+            l.tok0 = (size_t)b * T + (size_t)c_idx * C;
+            l.L = min(C, T - c_idx * C);
+        }
+        return l;
+    };
 
     __shared__ __align__(16) char big[S::BIG];
     __shared__ float sb[C];
@@ -270,12 +295,9 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         const int I = wv / KSN, ksl = wv - I * KSN;
         const int ch = 32 * ksl + 8 * (ln >> 4);
         const int chc = ch < DK ? ch : 0;                  // padded channels read channel 0
-        const int bh = item / NC, c_idx = item - bh * NC;
-        const int b = bh / H, h = bh - b * H;
-        const int t0 = c_idx * C;
-        const int L = min(C, T - t0);
+        const Loc l = locate(item);
         const int i = 16 * I + (ln & 15);
-        const size_t tok = ((size_t)b * T + t0 + (i < L ? i : L - 1)) * H + h;
+        const size_t tok = (l.tok0 + (size_t)(i < l.L ? i : max(l.L - 1, 0))) * H + l.h;
         // Both gate forms are loaded unconditionally, from valid addresses, so
         // that no branch joins loaded registers (a join would force a wait for
         // the loads right where they are issued); the unused form is never
@@ -345,10 +367,12 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         // the computation instead of stalling instruction issue in one burst
         In nxt;
 
-        const int bh = item / NC, c_idx = item - bh * NC;
-        const int t0 = c_idx * C;
-        const int b = bh / H, h = bh - b * H;
-        const int L = min(C, T - t0);       // valid tokens (>= 1)
+        const Loc loc = locate(item);
+        const int L = loc.L;                // valid tokens
+        const int h = loc.h;
+        // the chunk table ends in empty entries, and the items of one workgroup
+        // only grow: nothing is left for this workgroup (uniform)
+        if (L <= 0) break;
         const size_t rec = (size_t)item;
         OT* const Wq = W.qg_rec(rec);
         OT* const Wwn = W.wneg_rec(rec);
@@ -615,7 +639,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                     const int i = 16 * I + u;
                     float gv = 0.f, kv = 0.f, qv = 0.f;
                     if (i < L) {
-                        const size_t tok = ((size_t)b * T + t0 + i) * H + h;
+                        const size_t tok = (loc.tok0 + i) * H + h;
                         if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
                         else if (mode == KDA_GATE_SCALAR) gv = g[tok];
                         kv = io<OT>::load(k + tok * DK + cc);
@@ -787,7 +811,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 template <int C, int DK, int DV, typename OT, typename OUT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
-            int T, int H, int BH, int NC, const void* ws, size_t nrec)
+            int T, int H, int BH, int NC, const void* ws, size_t nrec, const int4* __restrict__ stab)
 {
     // (ws is deliberately not __restrict__: with it, the record loads count as
     // invariant and the compiler sinks the next chunk's operand loads past the
@@ -813,8 +837,29 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const int bh = (slot / NCT) * 8 + xcd;
     const int ct = slot % NCT;
     if (bh >= BH) return;
-    const int b = bh / H, h = bh - b * H;
+    const int h = bh - (bh / H) * H;
     const int n0 = 16 * ct;
+    // The sequence of this workgroup: its first token, its length, its number
+    // of chunks and where its chunk records start.  Dense batches: sequence b
+    // of [B, T], records (b*H + h) * NC + chunk.  Packed variable-length
+    // batches (stab != null): entry n = (first token, length, first chunk),
+    // records g * H + h for global chunk g.
+    size_t tokbase, recbase, recstride;
+    int seqlen, NCs;
+    if (stab) {
+        const int4 e = stab[bh / H];
+        tokbase = (size_t)e.x;
+        seqlen = e.y;
+        NCs = (seqlen + C - 1) / C;
+        recbase = (size_t)e.z * H + h;
+        recstride = (size_t)H;
+    } else {
+        tokbase = (size_t)(bh / H) * T;
+        seqlen = T;
+        NCs = NC;
+        recbase = (size_t)bh * NC;
+        recstride = 1;
+    }
     const WsLayout<C, DK, DV, OT> W(const_cast<void*>(ws), nrec);
 
     const int tid = threadIdx.x;
@@ -830,7 +875,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     for (int p = tid; p < NP * 16 * SC; p += 512) store_op(ETs + p, 0.f);
     __syncthreads();
 
-    auto rec_of = [&](int cidx) { return (size_t)bh * NC + cidx; };
+    auto rec_of = [&](int cidx) { return recbase + (size_t)cidx * recstride; };
 
     if (chain) {
         f32x4 hacc[MHW];
@@ -939,25 +984,25 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
             __syncthreads();
         };
-        if (NC > 0 && S::SPLIT) {
+        if (NCs > 0 && S::SPLIT) {
             // three operand sets in rotation: a chunk's operands are requested
             // two steps before they are used (the records come from beyond the
             // L2, whose latency one step does not cover)
             Ops A, B, D;
             load_ops(A, 0);
-            load_ops(B, min(1, NC - 1));
-            for (int cidx = 0; cidx < NC; cidx += 3) {
-                step(A, D, min(cidx + 2, NC - 1));
-                if (cidx + 1 < NC) step(B, A, min(cidx + 3, NC - 1));
-                if (cidx + 2 < NC) step(D, B, min(cidx + 4, NC - 1));
+            load_ops(B, min(1, NCs - 1));
+            for (int cidx = 0; cidx < NCs; cidx += 3) {
+                step(A, D, min(cidx + 2, NCs - 1));
+                if (cidx + 1 < NCs) step(B, A, min(cidx + 3, NCs - 1));
+                if (cidx + 2 < NCs) step(D, B, min(cidx + 4, NCs - 1));
             }
-        } else if (NC > 0) {
+        } else if (NCs > 0) {
             // float32 operands: two sets (a third does not fit the registers)
             Ops A, B;
             load_ops(A, 0);
-            for (int cidx = 0; cidx < NC; cidx += 2) {
-                step(A, B, min(cidx + 1, NC - 1));
-                if (cidx + 1 < NC) step(B, A, min(cidx + 2, NC - 1));
+            for (int cidx = 0; cidx < NCs; cidx += 2) {
+                step(A, B, min(cidx + 1, NCs - 1));
+                if (cidx + 1 < NCs) step(B, A, min(cidx + 2, NCs - 1));
             }
         }
         if (hT) {
@@ -1018,28 +1063,28 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 // lane holds o^T[n = 4gq + u][i = 16*wr + r]
                 const int t0 = cidx * C;
                 const int i = 16 * wr + r;
-                if (i < min(C, T - t0)) {
-                    OUT* op = o + (((size_t)b * T + t0 + i) * H + h) * DV + n0 + 4 * gq;
+                if (i < min(C, seqlen - t0)) {
+                    OUT* op = o + ((tokbase + t0 + i) * H + h) * DV + n0 + 4 * gq;
                     Vec4<OUT>::store(op, oacc);
                 }
             }
             __syncthreads();
         };
-        if (NC > 0 && S::SPLIT) {
+        if (NCs > 0 && S::SPLIT) {
             Ops A, B, D;
             load_ops(A, 0);
-            load_ops(B, min(1, NC - 1));
-            for (int cidx = 0; cidx < NC; cidx += 3) {
-                step(A, cidx, D, min(cidx + 2, NC - 1));
-                if (cidx + 1 < NC) step(B, cidx + 1, A, min(cidx + 3, NC - 1));
-                if (cidx + 2 < NC) step(D, cidx + 2, B, min(cidx + 4, NC - 1));
+            load_ops(B, min(1, NCs - 1));
+            for (int cidx = 0; cidx < NCs; cidx += 3) {
+                step(A, cidx, D, min(cidx + 2, NCs - 1));
+                if (cidx + 1 < NCs) step(B, cidx + 1, A, min(cidx + 3, NCs - 1));
+                if (cidx + 2 < NCs) step(D, cidx + 2, B, min(cidx + 4, NCs - 1));
             }
-        } else if (NC > 0) {
+        } else if (NCs > 0) {
             Ops A, B;
             load_ops(A, 0);
-            for (int cidx = 0; cidx < NC; cidx += 2) {
-                step(A, cidx, B, min(cidx + 1, NC - 1));
-                if (cidx + 1 < NC) step(B, cidx + 1, A, min(cidx + 2, NC - 1));
+            for (int cidx = 0; cidx < NCs; cidx += 2) {
+                step(A, cidx, B, min(cidx + 1, NCs - 1));
+                if (cidx + 1 < NCs) step(B, cidx + 1, A, min(cidx + 2, NCs - 1));
             }
         }
     }
@@ -1069,30 +1114,121 @@ static int resident_blocks(K kernel, int threads)
     return n;
 }
 
+// ---------------------------------------------------------------------------
+// Packed variable-length batches: the chunk and sequence tables (one
+// workgroup).  Sequence n covers tokens p_n .. p_{n+1}-1 with
+// p_m = max_{j <= m} clamp(cu[j], 0, Ttot): for a well-formed cu (0 = cu[0]
+// <= cu[1] <= ... <= cu[N] = Ttot) that is exactly [cu[n], cu[n+1]); for any
+// other content the sequences still tile a subrange of [0, Ttot] without
+// overlap, so no access leaves the buffers and at most
+// ceil(Ttot / C) + N chunks arise (the table's size, Gmax).  The sequence
+// table entry n is (first token, length, first chunk, 0); the chunk table
+// entry g is (first token, length), and the entries after the last chunk are
+// (0, 0).
+__global__ void __launch_bounds__(1024)
+varlen_tables(const int* __restrict__ cu, int N, int Ttot, int C, int Gmax,
+              int2* __restrict__ ctab, int4* __restrict__ stab)
+{
+    __shared__ int smax[1024], ssum[1024];
+    const int tid = threadIdx.x;
+    int pcarry = 0, ccarry = 0;    // boundary maximum and chunk count of the earlier tiles
+    for (int base = 0; base < N; base += 1024) {
+        const int n = base + tid;
+        int e0 = 0, e1 = 0;
+        if (n < N) {
+            e0 = min(max(cu[n], 0), Ttot);
+            e1 = min(max(cu[n + 1], 0), Ttot);
+        }
+        int x = e0;                // inclusive prefix maximum over the tile
+        smax[tid] = x;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int y = tid >= off ? smax[tid - off] : 0;
+            __syncthreads();
+            x = max(x, y);
+            smax[tid] = x;
+            __syncthreads();
+        }
+        const int start = max(x, pcarry);
+        const int len = n < N ? max(start, e1) - start : 0;
+        const int nch = (len + C - 1) / C;
+        int cs = nch;              // inclusive prefix sum of the chunk counts
+        ssum[tid] = cs;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {
+            const int y = tid >= off ? ssum[tid - off] : 0;
+            __syncthreads();
+            cs += y;
+            ssum[tid] = cs;
+            __syncthreads();
+        }
+        const int first = ccarry + cs - nch;
+        if (n < N) {
+            stab[n] = make_int4(start, len, first, 0);
+            for (int c = 0; c < nch && first + c < Gmax; ++c)
+                ctab[first + c] = make_int2(start + c * C, min(C, len - c * C));
+        }
+        pcarry = max(pcarry, smax[1023]);
+        ccarry += ssum[1023];
+        __syncthreads();           // smax / ssum are rewritten by the next tile
+    }
+    for (int gch = ccarry + tid; gch < Gmax; gch += 1024) ctab[gch] = make_int2(0, 0);
+}
+
+// Upper bound of the number of chunks of a packed batch, and the workspace
+// layout of the packed form: the records of Gmax * H chunks, then the chunk
+// table, then the sequence table.
+static size_t varlen_gmax(int N, int Ttot, int C) { return (size_t)(Ttot + C - 1) / C + (size_t)N; }
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
 template <int C, int DK, int DV, typename OT>
 static hipError_t launch3(const ChunkArgs& a, hipStream_t s)
 {
-    const int BH = a.B * a.H;
-    const int NC = (a.T + C - 1) / C;
-    const size_t nrec = (size_t)BH * NC;
-    if (NC > 0) {
+    const bool packed = a.cu != nullptr;
+    int BH, NC, nitem;
+    size_t nrec;
+    const int2* ctab = nullptr;
+    const int4* stab = nullptr;
+    if (packed) {
+        const size_t gmax = varlen_gmax(a.N, a.T, C);
+        BH = a.N * a.H;
+        NC = 0;
+        nrec = gmax * a.H;
+        nitem = (int)nrec;
+        char* t = (char*)a.ws + align_up(WsLayout<C, DK, DV, OT>::bytes(nrec), 256);
+        int2* ct = (int2*)t;
+        int4* st = (int4*)(t + align_up(gmax * sizeof(int2), 16));
+        if (a.N > 0) {
+            hipLaunchKernelGGL(varlen_tables, dim3(1), dim3(1024), 0, s, a.cu, a.N, a.T, C, (int)gmax, ct, st);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        ctab = ct;
+        stab = st;
+    } else {
+        BH = a.B * a.H;
+        NC = (a.T + C - 1) / C;
+        nrec = (size_t)BH * NC;
+        nitem = (int)nrec;
+    }
+    if (nitem > 0 && a.T > 0) {
         // persistent workgroups: as many as can be resident at once
-        const int nitem = (int)nrec;
         const int grid = min(nitem, resident_blocks(chunk_prepare<C, DK, DV, OT>, CS<C, DK, DV, OT>::NT));
         hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(grid), dim3(CS<C, DK, DV, OT>::NT), 0, s,
                            (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
-                           a.T, a.H, NC, nitem, a.scale, (int)a.mode, a.ws, nrec);
+                           a.T, a.H, NC, nitem, a.scale, (int)a.mode, a.ws, nrec, ctab);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (BH == 0) return hipSuccess;
     const int groups = (BH + 7) / 8;
     const dim3 grid(groups * 8 * (DV / 16));
     if (a.o_dtype == KDA_F32)
         hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
+                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
     else
         hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec);
+                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
     return hipGetLastError();
 }
 
@@ -1101,6 +1237,14 @@ static size_t ws3(int B, int T, int H)
 {
     const int NC = (T + C - 1) / C;
     return WsLayout<C, D, D, OT>::bytes((size_t)B * H * NC);
+}
+
+template <int C, int D, typename OT>
+static size_t ws3_varlen(int N, int Ttot, int H)
+{
+    const size_t gmax = varlen_gmax(N, Ttot, C);
+    return align_up(WsLayout<C, D, D, OT>::bytes(gmax * H), 256) + align_up(gmax * sizeof(int2), 16) +
+           (size_t)N * sizeof(int4);
 }
 
 template <typename OT>
@@ -1116,10 +1260,10 @@ static hipError_t dispatch_chunk(const ChunkArgs& a, hipStream_t s)
 }
 
 template <typename OT>
-static size_t ws_dispatch(int B, int T, int H, int D, int chunk)
+static size_t ws_dispatch(int B, int T, int H, int D, int chunk, bool packed)
 {
 #define KDA_CASE(CC, DD) \
-    if (chunk == CC && D == DD) return ws3<CC, DD, OT>(B, T, H);
+    if (chunk == CC && D == DD) return packed ? ws3_varlen<CC, DD, OT>(B, T, H) : ws3<CC, DD, OT>(B, T, H);
     KDA_CASE(16, 16) KDA_CASE(16, 32) KDA_CASE(16, 64) KDA_CASE(16, 128)
     KDA_CASE(32, 16) KDA_CASE(32, 32) KDA_CASE(32, 64) KDA_CASE(32, 128)
     KDA_CASE(64, 16) KDA_CASE(64, 32) KDA_CASE(64, 64) KDA_CASE(64, 128)
@@ -1130,8 +1274,15 @@ static size_t ws_dispatch(int B, int T, int H, int D, int chunk)
 size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype)
 {
     if (Dk != Dv) return 0;
-    if (dtype == KDA_BF16) return ws_dispatch<bf16_t>(B, T, H, Dk, chunk);
-    return ws_dispatch<float>(B, T, H, Dk, chunk);
+    if (dtype == KDA_BF16) return ws_dispatch<bf16_t>(B, T, H, Dk, chunk, false);
+    return ws_dispatch<float>(B, T, H, Dk, chunk, false);
+}
+
+size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype)
+{
+    if (Dk != Dv) return 0;
+    if (dtype == KDA_BF16) return ws_dispatch<bf16_t>(N, Ttot, H, Dk, chunk, true);
+    return ws_dispatch<float>(N, Ttot, H, Dk, chunk, true);
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s)

@@ -17,6 +17,9 @@ struct RecArgs {
     kda_gate_mode mode;
     kda_dtype dtype;      // q, k, v
     kda_dtype o_dtype;    // o
+    // packed variable-length batch: device offsets [N + 1] (B is N, T the
+    // packed token count), or null for a dense [B, T] batch
+    const int* cu;
 };
 
 struct ChunkArgs {
@@ -29,12 +32,17 @@ struct ChunkArgs {
     kda_dtype dtype;      // q, k, v
     kda_dtype o_dtype;    // o
     void* ws; size_t ws_bytes;
+    // packed variable-length batch: device offsets [N + 1] and N (T is the
+    // packed token count, B unused), or null for a dense [B, T] batch
+    const int* cu;
+    int N;
 };
 
 hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);
 
 // Workspace layout of the chunk path (bytes); 0 if unsupported.
 size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
+size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -42,12 +42,24 @@ __global__ void __launch_bounds__((RecShape<DK, DV>::NT))
 recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                  const float* __restrict__ g, const float* __restrict__ beta,
                  float* __restrict__ state, OUT* __restrict__ o,
-                 int T, int H, float scale, int mode)
+                 int T, int H, float scale, int mode, const int* __restrict__ cu)
 {
     using S = RecShape<DK, DV>;
     const int bh = blockIdx.x / S::NCT;
     const int c0 = (blockIdx.x - bh * S::NCT) * S::DVT;   // first column of the slab
     const int b = bh / H, h = bh - (bh / H) * H;
+    // the tokens of this sequence: [b*T, b*T + T) of a dense batch, or
+    // [cu[b], cu[b+1]) of a packed one (T is then the packed token count;
+    // the offsets are clamped into [0, T] and the end to at least the start,
+    // so no access leaves the buffers whatever they hold)
+    size_t tok0 = (size_t)b * T;
+    int Tn = T;
+    if (cu) {
+        const int s0 = min(max(cu[b], 0), T);
+        const int s1 = min(max(cu[b + 1], s0), T);
+        tok0 = (size_t)s0;
+        Tn = s1 - s0;
+    }
     const int tid = threadIdx.x;
     const int cx = tid % S::CX, rg = tid / S::CX;
     const int lane = tid & 63, wave = tid >> 6;
@@ -68,15 +80,15 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         }
         for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
     };
-    if (T > 0) token_inputs(((size_t)b * T) * H + h);
+    if (Tn > 0) token_inputs(tok0 * H + h);
     f32x4 hr[S::RPT];
 #pragma unroll
     for (int i = 0; i < S::RPT; ++i)
         hr[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
 
-    for (int t = 0; t < T; ++t) {
-        const size_t tok = ((size_t)b * T + t) * H + h;
+    for (int t = 0; t < Tn; ++t) {
+        const size_t tok = (tok0 + t) * H + h;
         if (t > 0) token_inputs(tok);
         __syncthreads();
 
@@ -147,11 +159,11 @@ static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
     if (a.o_dtype == KDA_F32)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (float*)a.o, a.T, a.H, a.scale, (int)a.mode);
+                           (float*)a.o, a.T, a.H, a.scale, (int)a.mode, a.cu);
     else
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (bf16_t*)a.o, a.T, a.H, a.scale, (int)a.mode);
+                           (bf16_t*)a.o, a.T, a.H, a.scale, (int)a.mode, a.cu);
     return hipGetLastError();
 }
 

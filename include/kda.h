@@ -78,7 +78,7 @@ typedef enum {
     KDA_SUCCESS = 0,
     KDA_ERROR_INVALID_VALUE = 1,  /* NULL required pointer, negative size, bad enum */
     KDA_ERROR_NOT_SUPPORTED = 2,  /* Dk, Dv or chunk outside the supported set     */
-    KDA_ERROR_MISALIGNED = 3,     /* a pointer is not 16-byte aligned               */
+    KDA_ERROR_MISALIGNED = 3,     /* a pointer is not 16-byte aligned (cu_seqlens: 4) */
     KDA_ERROR_WORKSPACE = 4,      /* workspace NULL or smaller than required        */
     KDA_ERROR_HIP = 5             /* the HIP runtime reported an error at launch    */
 } kda_status;
@@ -141,6 +141,75 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          int B, int T, int H, int Dk, int Dv, int chunk, float scale,
                          kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length batches
+ * ------------------------------
+ * N independent sequences of different lengths packed along one token axis
+ * (GeekNews #31925, section "Fused recurrent kernel for decode": the
+ * recurrent form serves decode, short sequences and stateful serving, and
+ * different sequences, heads and value tiles run independently).  Token
+ * tensors are [T, H, D] (the dense layout with B = 1), T the total number of
+ * packed tokens; beta is [T, H]; gates [T, H, Dk] or [T, H].  Sequence n holds
+ * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 and has its own state, entry n of
+ * a [N, H, Dk, Dv] float state.  Every sequence starts and ends its own
+ * recurrence: results equal separate calls, one per sequence.
+ *
+ * cu_seqlens is a DEVICE array of N + 1 int32, 4-byte aligned, with
+ * 0 = cu_seqlens[0] <= cu_seqlens[1] <= ... <= cu_seqlens[N] = T (empty
+ * sequences allowed).  Its contents cannot be checked on the host.  The
+ * kernels clamp every entry into [0, T], so no access leaves the buffers
+ * whatever the array holds. A malformed array gives defined but meaningless
+ * results.
+ */
+
+/*
+ * kda_recurrent_varlen -- kda_recurrent_step over a packed batch: for every
+ * sequence n and head h, the tokens of sequence n in order, starting from
+ * and updating state[n, h] IN PLACE (an empty sequence leaves it as is).
+ *
+ *   q, k   [T,H,Dk]  dtype   in         v, o  [T,H,Dv]  (o: o_dtype, out)
+ *   g, beta as above (float, in)       state [N,H,Dk,Dv] float in/out
+ *   cu_seqlens [N+1] int32 device      N >= 0 (N = 0 or T = 0: nothing to do)
+ */
+kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                float* state, void* o, const int* cu_seqlens,
+                                int N, int T, int H, int Dk, int Dv, float scale,
+                                kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                                void* stream);
+
+/*
+ * kda_chunk_fwd_varlen_workspace_size -- bytes of device workspace
+ * kda_chunk_fwd_varlen needs (0 for unsupported arguments or N = 0).  It
+ * depends on N and T only, not on the individual lengths: the chunks of every
+ * sequence start at its first token, and there are at most ceil(T/chunk) + N
+ * of them.
+ */
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, int chunk,
+                                           kda_gate_mode mode, kda_dtype dtype);
+
+/*
+ * kda_chunk_fwd_varlen -- kda_chunk_fwd over a packed batch: every sequence
+ * is cut into chunks from its own first token (the last one ragged) and
+ * carries its own state from chunk to chunk.
+ *
+ *   q, k, v, g, beta, o, cu_seqlens   as for kda_recurrent_varlen
+ *   initial_state  [N,H,Dk,Dv] float in, or NULL for zero states
+ *   final_state    [N,H,Dk,Dv] float out, or NULL; may equal initial_state
+ *   chunk, scale, mode, dtype, o_dtype   as for kda_chunk_fwd
+ *   workspace      at least kda_chunk_fwd_varlen_workspace_size(...) bytes,
+ *                  256-byte aligned, owned by the caller; contents are
+ *                  scratch (it also holds the chunk table built from
+ *                  cu_seqlens on the device, so the call stays asynchronous)
+ */
+kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
+                                const float* g, const float* beta,
+                                const float* initial_state, float* final_state, void* o,
+                                const int* cu_seqlens, int N, int T, int H, int Dk, int Dv,
+                                int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
+                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* kda_status_string(kda_status s);

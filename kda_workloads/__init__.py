@@ -232,3 +232,45 @@ def slice_heads(w: Workload, pairs):
         h0 = None if w.h0 is None else np.ascontiguousarray(w.h0[b:b + 1, h:h + 1])
         out.append((q, k, v, g, beta, h0))
     return out
+
+
+# --------------------------------------------------------------------------
+# packed variable-length batches
+# --------------------------------------------------------------------------
+def make_lengths(N: int, *, max_len: int, seed: int = 0, edge=()) -> np.ndarray:
+    """N sequence lengths: the given edge lengths first, the rest drawn
+    log-uniformly from [1, max_len] (many short sequences, a few long ones)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x7a11]))
+    n_draw = max(N - len(edge), 0)
+    drawn = np.exp(rng.uniform(0.0, math.log(max_len + 1), size=n_draw)).astype(np.int64)
+    drawn = np.clip(drawn, 1, max_len)
+    return np.concatenate([np.asarray(edge, np.int64)[:N], drawn]).astype(np.int64)
+
+
+@dataclasses.dataclass
+class VarlenWorkload:
+    """A packed batch: ``w`` holds the tokens of all sequences as one B = 1
+    workload of T = sum(lengths) tokens; ``cu`` [N+1] int32 are the sequence
+    offsets and ``h0`` [N,H,Dk,Dv] float32 (or None) the initial states."""
+    w: Workload
+    cu: np.ndarray
+    h0: Optional[np.ndarray]
+
+    @property
+    def N(self) -> int:
+        return len(self.cu) - 1
+
+
+def make_varlen(lengths, H, Dk, Dv, *, seed=0, h0_std=0.0, **kw) -> VarlenWorkload:
+    """Draw a packed batch with the given sequence lengths (same laws as
+    :func:`make_inputs`; keyword arguments are passed on to it)."""
+    lengths = np.asarray(lengths, np.int64)
+    cu = np.zeros(len(lengths) + 1, np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    w = make_inputs(1, T, H, Dk, Dv, seed=seed, h0_std=0.0, name="varlen", **kw)
+    h0 = None
+    if h0_std > 0.0:
+        rh = np.random.default_rng(np.random.SeedSequence([seed, 0x40]))
+        h0 = _normal(rh, (len(lengths), H, Dk, Dv), std=h0_std)
+    return VarlenWorkload(w=w, cu=cu.astype(np.int32), h0=h0)

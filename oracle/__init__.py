@@ -13,7 +13,11 @@ Two independent forms:
   (``chunkwise.py``), used to pin R on small inputs and to document the
   reading of the truncated chunkwise derivation.
 
+* :func:`recurrent_varlen` -- packed variable-length batches as one call
+  of oracle R per sequence (``varlen.py``).
+
 Both take the state transposed, ``H = S^T`` with shape ``[B, H, Dk, Dv]``.
 """
 from .recurrence import recurrent, build_oracle_library, oracle_threads  # noqa: F401
 from .chunkwise import chunkwise  # noqa: F401
+from .varlen import recurrent_varlen  # noqa: F401

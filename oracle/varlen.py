@@ -1,0 +1,56 @@
+"""Oracle for packed variable-length batches.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+GeekNews #31925, section "Fused recurrent kernel for decode": the recurrent
+form serves decode, short sequences and stateful serving, and different
+sequences run independently.  A packed batch is therefore nothing but N
+separate recurrences, one per sequence: sequence n takes tokens
+cu[n] .. cu[n+1]-1 of the packed [T, H, D] tensors, starts from its own
+state h0[n] and ends in hT[n].  This is that definition written out: a plain
+loop calling oracle R once per sequence.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+from .recurrence import recurrent
+
+
+def recurrent_varlen(q, k, v, g, beta, cu, h0=None, *, scale: Optional[float] = None,
+                     mode: str = "channel", threads: int = 0, mutant: int = 0):
+    """q, k [T,H,Dk]; v [T,H,Dv]; g [T,H,Dk] / [T,H] / None; beta [T,H];
+    cu [N+1] nondecreasing offsets with cu[0] = 0 and cu[N] = T;
+    h0 [N,H,Dk,Dv] or None.  Returns (o [T,H,Dv], hT [N,H,Dk,Dv]) in float64.
+
+    ``mutant`` > 0 plants a deliberate mistake (tests only): 1 starts every
+    sequence after the first one token late, 2 carries each final state into
+    the next sequence."""
+    cu = np.asarray(cu, np.int64)
+    N = len(cu) - 1
+    T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert N >= 0 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    o = np.zeros((T, H, Dv), np.float64)
+    hT = np.zeros((N, H, Dk, Dv), np.float64)
+    carry = None
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if mutant == 1 and n > 0 and s < e:
+            s += 1
+        hn = None if h0 is None else np.asarray(h0[n:n + 1], np.float64)
+        if mutant == 2 and carry is not None:
+            hn = carry
+        if e == s:                      # an empty sequence keeps its state
+            if hn is not None:
+                hT[n] = hn[0]
+            continue
+        sl = lambda x: None if x is None else np.asarray(x[s:e])[None]
+        on, hTn = recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), hn, scale=scale, mode=mode,
+                            threads=threads)
+        o[s:e] = on[0]
+        hT[n] = hTn[0]
+        carry = hTn
+    return o, hT

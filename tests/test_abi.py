@@ -19,7 +19,9 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = K.header_functions()
     assert set(names) >= {"kda_recurrent_step", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-                          "kda_status_string", "kda_version"}
+                          "kda_recurrent_varlen", "kda_chunk_fwd_varlen",
+                          "kda_chunk_fwd_varlen_workspace_size", "kda_status_string",
+                          "kda_version"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -87,3 +89,58 @@ def test_workspace_size(L):
     assert 0 < a < b == 2 * a
     assert f(2, 64, 3, 128, 128, 64, 0, 1) == 6 * a
     assert f(1, 64, 1, 128, 128, 64, 0, 0) >= a  # float32 records are no smaller
+
+
+# ---- packed variable-length batches (host validation only)
+CU = 0x20000          # a 4-byte aligned fake device address of the offsets
+
+
+def _rec_v(L, q=A, k=A, v=A, g=A, beta=A, state=A, o=A, cu=CU, N=2, T=10, H=1, Dk=128, Dv=128,
+           scale=1.0, mode=0, dtype=1, o_dtype=0):
+    return L.kda_recurrent_varlen(q, k, v, g, beta, state, o, cu, N, T, H, Dk, Dv, scale, mode,
+                                  dtype, o_dtype, None)
+
+
+def _chunk_v(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, cu=CU, N=2, T=64, H=1,
+             Dk=128, Dv=128, chunk=64, scale=1.0, mode=0, dtype=1, o_dtype=0, ws=A, wsb=None):
+    if wsb is None:
+        wsb = L.kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype)
+    return L.kda_chunk_fwd_varlen(q, k, v, g, beta, h0, hT, o, cu, N, T, H, Dk, Dv, chunk, scale,
+                                  mode, dtype, o_dtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(state=None), 1), (dict(cu=None), 1), (dict(N=-1), 1),
+    (dict(T=-1), 1), (dict(H=0), 1), (dict(g=None, mode=1), 1), (dict(Dk=48), 2),
+    (dict(cu=CU + 2), 3), (dict(state=MIS), 3), (dict(o=MIS), 3),
+])
+def test_recurrent_varlen_validation(L, kw, code):
+    assert _rec_v(L, **kw) == code
+
+
+def test_recurrent_varlen_nothing_to_do(L):
+    # no sequences, or no tokens: states unchanged, nothing enqueued
+    assert _rec_v(L, N=0, cu=None, state=None) == 0
+    assert _rec_v(L, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(cu=None), 1), (dict(N=-1), 1), (dict(mode=9), 1),
+    (dict(chunk=8), 2), (dict(Dk=64, Dv=128), 2), (dict(cu=CU + 1), 3), (dict(h0=MIS), 3),
+    (dict(hT=MIS), 3), (dict(ws=None), 4), (dict(wsb=64), 4), (dict(ws=A + 16), 3),
+])
+def test_chunk_varlen_validation(L, kw, code):
+    assert _chunk_v(L, **kw) == code
+
+
+def test_chunk_varlen_workspace_size(L):
+    f = L.kda_chunk_fwd_varlen_workspace_size
+    assert f(0, 64, 1, 128, 128, 64, 0, 1) == 0
+    assert f(1, 64, 1, 128, 128, 48, 0, 1) == 0
+    dense = L.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, 0, 1)
+    # room for ceil(T / chunk) + N chunk records plus the tables
+    one = f(1, 64, 1, 128, 128, 64, 0, 1)
+    assert one >= 2 * dense
+    assert f(3, 64, 1, 128, 128, 64, 0, 1) >= 4 * dense
+    # T = 0 still needs the tables (the final states are copied)
+    assert f(2, 0, 1, 128, 128, 64, 0, 1) > 0
