@@ -21,6 +21,9 @@ token-head plus 2 * d_k * d_v * 4 B of initial/final state per (b, h).
 ``traffic`` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE counter runs stored in
 profiles/traffic.json and is null when the kernel source changed since.
 ``cpu_baseline`` times the fp64 CPU oracle (test infrastructure) on the host.
+``varlen`` (outside the timed steps) times the packed variable-length entry
+points on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
+d=128, bf16, in both forms.
 """
 from __future__ import annotations
 
@@ -95,12 +98,69 @@ def cpu_baseline():
     oracle.recurrent(d.q, d.k, d.v, d.g, d.beta, d.h0, scale=d.scale, mode=d.mode)
     td = time.perf_counter() - t0
     state_bytes = d.B * d.H * d.Dk * d.Dv * 4 * 2
+    from kda_workloads import make_lengths, make_varlen
+    vw = make_varlen(make_lengths(64, max_len=2048, seed=17, edge=(1, 64, 2048)), 16, 128, 128,
+                     dtype="bf16", seed=17, h0_std=0.02)
+    vq = vw.w
+    t0 = time.perf_counter()
+    oracle.recurrent_varlen(vq.q[0], vq.k[0], vq.v[0], vq.g[0], vq.beta[0], vw.cu, vw.h0,
+                            scale=vq.scale, mode=vq.mode)
+    tv = time.perf_counter() - t0
     return {"value": w.B * w.T / tp, "unit": "tokens/s", "cores": oracle.oracle_threads(),
             "kind": "oracle",
             "sample": "fp64 oracle R over the whole prefill workload (B1 H16 T4096 d128, "
                       f"{tp:.2f} s) and one whole decode step (B256 H32 d128, {td:.2f} s)",
             "decode_state_GBps": state_bytes / td / 1e9,
+            "varlen_tokens_per_s": int(vw.cu[-1]) / tv,
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def bench_varlen(K, torch, dev, warmup, reps):
+    """Packed serving mix through kda_chunk_fwd_varlen and kda_recurrent_varlen
+    (each timed on its own, HIP events on the launch stream)."""
+    from kda_workloads import make_lengths, make_varlen
+    lengths = make_lengths(64, max_len=2048, seed=17, edge=(1, 64, 2048))
+    vw = make_varlen(lengths, 16, 128, 128, dtype="bf16", seed=17, h0_std=0.02)
+    w = vw.w
+    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    q, k, v = t(w.q[0], torch.bfloat16), t(w.k[0], torch.bfloat16), t(w.v[0], torch.bfloat16)
+    g, beta, h0 = t(w.g[0]), t(w.beta[0]), t(vw.h0)
+    cu = torch.from_numpy(vw.cu).to(dev)
+    N, T, H, D = vw.N, int(vw.cu[-1]), w.H, w.Dk
+    ws = torch.empty(K.kda_chunk_fwd_varlen_workspace_size(N, T, H, D, D, 64, 0, K.BF16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(h0)
+    st = h0.clone()
+
+    def chunk():
+        K.kda_chunk_fwd_varlen(q, k, v, g, beta, cu, initial_state=h0, final_state=hT, o=o,
+                               chunk=64, workspace=ws)
+
+    def rec():
+        K.kda_recurrent_varlen(q, k, v, g, beta, st, cu, o=o)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1e3
+
+    tc, tr = timed(chunk), timed(rec)
+    nbytes = T * H * (4 * D * 2 + D * 4 + 4) + N * H * 2 * D * D * 4
+    return {"workload": f"{N} sequences, log-uniform lengths 1..2048 (seed 17), {T} tokens, "
+                        "H16 d128 bf16, fp32 states",
+            "tokens": T, "sequences": N, "longest": int(lengths.max()),
+            "chunk_ms": tc * 1e3, "chunk_tokens_per_s": T / tc,
+            "chunk_hbm_frac": nbytes / tc / 1e9 / HBM_PEAK_GBPS,
+            "recurrent_ms": tr * 1e3, "recurrent_tokens_per_s": T / tr,
+            "algorithmic_bytes": nbytes}
 
 
 def main():
@@ -238,6 +298,7 @@ def main():
             "mfma_util_counters": mfma_util,
         },
     }
+    out["varlen"] = bench_varlen(K, torch, dev, args.warmup, max(args.steps // 2, 3))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
