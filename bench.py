@@ -23,7 +23,9 @@ profiles/traffic.json and is null when the kernel source changed since.
 ``cpu_baseline`` times the fp64 CPU oracle (test infrastructure) on the host.
 ``varlen`` (outside the timed steps) times the packed variable-length entry
 points on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
-d=128, bf16, in both forms.
+d=128, bf16, in both forms.  ``grouped_heads`` (4 query/key heads for the 16
+value heads) and ``mixed_dims`` (d_k 64, d_v 128) time kda_chunk_fwd on the
+prefill shape B1 T4096 H16, likewise outside the timed steps.
 """
 from __future__ import annotations
 
@@ -106,12 +108,22 @@ def cpu_baseline():
     oracle.recurrent_varlen(vq.q[0], vq.k[0], vq.v[0], vq.g[0], vq.beta[0], vw.cu, vw.h0,
                             scale=vq.scale, mode=vq.mode)
     tv = time.perf_counter() - t0
+    from kda_workloads import make_inputs
+    rows = {}
+    for name, Hqk, Dk, Dv in (("grouped_heads", 4, 128, 128), ("mixed_dims", 16, 64, 128)):
+        x = make_inputs(1, 4096, 16, Dk, Dv, dtype="bf16", seed=5, gate_shift=2.0, h0_std=0.01)
+        G = 16 // Hqk
+        t0 = time.perf_counter()
+        oracle.recurrent_grouped(x.q[:, :, ::G], x.k[:, :, ::G], x.v, x.g, x.beta, x.h0,
+                                 scale=x.scale, mode=x.mode)
+        rows[name + "_tokens_per_s"] = 4096 / (time.perf_counter() - t0)
     return {"value": w.B * w.T / tp, "unit": "tokens/s", "cores": oracle.oracle_threads(),
             "kind": "oracle",
             "sample": "fp64 oracle R over the whole prefill workload (B1 H16 T4096 d128, "
                       f"{tp:.2f} s) and one whole decode step (B256 H32 d128, {td:.2f} s)",
             "decode_state_GBps": state_bytes / td / 1e9,
             "varlen_tokens_per_s": int(vw.cu[-1]) / tv,
+            **rows,
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -163,12 +175,52 @@ def bench_varlen(K, torch, dev, warmup, reps):
             "algorithmic_bytes": nbytes}
 
 
+def bench_prefill_shape(K, torch, dev, warmup, reps, *, Hqk, Dk, Dv, H=16, T=4096):
+    """kda_chunk_fwd on B1 T4096 with H value heads, Hqk query/key heads and
+    (Dk, Dv); HIP events on the launch stream."""
+    from kda_workloads import make_inputs
+    w = make_inputs(1, T, H, Dk, Dv, dtype="bf16", seed=5, gate_shift=2.0, h0_std=0.01)
+    G = H // Hqk
+    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    q = t(w.q[:, :, ::G], torch.bfloat16)
+    k = t(w.k[:, :, ::G], torch.bfloat16)
+    v, g, beta, h0 = t(w.v, torch.bfloat16), t(w.g), t(w.beta), t(w.h0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(1, T, H, Dk, Dv, 64, 0, K.BF16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((1, T, H, Dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(h0)
+
+    def run():
+        K.kda_chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o, chunk=64,
+                        workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / reps / 1e3
+    # q, k per query/key head; v, o bf16, g fp32, beta per value head; states
+    nbytes = T * (Hqk * 2 * Dk * 2 + H * (2 * Dv * 2 + Dk * 4 + 4)) + H * 2 * Dk * Dv * 4
+    return {"workload": f"B1 T{T} H{H} value heads, {Hqk} query/key heads, d_k {Dk}, d_v {Dv}, "
+                        "chunk 64, bf16",
+            "ms": sec * 1e3, "tokens_per_s": T / sec, "algorithmic_bytes": nbytes,
+            "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-legs", action="store_true",
+                    help="skip the untimed legs after the steps (packed batches, grouped heads, "
+                         "mixed dims): profiling runs, whose launches would share kernel names "
+                         "with the prefill")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a float32 copy of exactly 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times, as the reference for HBM byte counters")
@@ -248,7 +300,7 @@ def main():
 
     traffic = load_traffic()
     rec_hash = source_hash("kda_recurrent.hip", "kda_device.hpp")
-    chk_hash = source_hash("kda_chunk.hip", "kda_device.hpp")
+    chk_hash = source_hash("kda_chunk.hpp", "kda_device.hpp")
     t_dec = traffic.get("decode")
     t_dec_bytes = t_dec["bytes_per_launch"] if t_dec and t_dec.get("source_hash") == rec_hash else None
     t_pre = traffic.get("prefill")
@@ -298,7 +350,11 @@ def main():
             "mfma_util_counters": mfma_util,
         },
     }
-    out["varlen"] = bench_varlen(K, torch, dev, args.warmup, max(args.steps // 2, 3))
+    if not args.no_extra_legs:
+        reps = max(args.steps // 2, 3)
+        out["varlen"] = bench_varlen(K, torch, dev, args.warmup, reps)
+        out["grouped_heads"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=4, Dk=128, Dv=128)
+        out["mixed_dims"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=16, Dk=64, Dv=128)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -54,19 +54,20 @@ def lib():
                            "`python -m gated_delta_rule_17_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i, vp]
     L.kda_recurrent_step.restype = i
     L.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd_workspace_size.restype = sz
-    L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i,
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, i, f, i, i, i,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
-    L.kda_recurrent_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    L.kda_recurrent_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, f, i, i, i,
+                                       vp]
     L.kda_recurrent_varlen.restype = i
     L.kda_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd_varlen_workspace_size.restype = sz
-    L.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp, i, i, i, i, i, i, f, i, i,
-                                       i, vp, sz, vp]
+    L.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp, i, i, i, i, i, i, i, f, i,
+                                       i, i, vp, sz, vp]
     L.kda_chunk_fwd_varlen.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -133,17 +134,21 @@ def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] =
                        mode=None, out_dtype=None):
     """Recurrent form over T >= 1 tokens; updates ``state`` in place.
 
-    q, k [B,T,H,Dk] and v [B,T,H,Dv] (float32 or bfloat16), g float32 log-gates
-    ([B,T,H,Dk] channel / [B,T,H] scalar / None), beta float32 [B,T,H],
-    state float32 [B,H,Dk,Dv].  Returns o [B,T,H,Dv] (``out_dtype``, default the
-    dtype of q; ignored when ``o`` is given).
+    q, k [B,T,Hqk,Dk] and v [B,T,H,Dv] (float32 or bfloat16; H a multiple of
+    Hqk: grouped value heads), g float32 log-gates ([B,T,H,Dk] channel /
+    [B,T,H] scalar / None), beta float32 [B,T,H], state float32 [B,H,Dk,Dv].
+    Returns o [B,T,H,Dv] (``out_dtype``, default the dtype of q; ignored when
+    ``o`` is given).
     """
     torch = _torch()
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    B, T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
     m = _mode_of(g, mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
     _check_dev("g", g, torch.float32)
     _check_dev("beta", beta, torch.float32, (B, T, H))
     _check_dev("state", state, torch.float32, (B, H, Dk, Dv))
@@ -153,7 +158,7 @@ def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] =
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                  _ptr(o), B, T, H, Dk, Dv, float(scale), m, _dtype_code(q),
+                                  _ptr(o), B, T, H, Hqk, Dk, Dv, float(scale), m, _dtype_code(q),
                                   _dtype_code(o), _stream())
     if st != 0:
         raise KDAError(st, "kda_recurrent_step")
@@ -174,13 +179,17 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
     ``final_state`` may be passed (it may be ``initial_state`` itself); if it
     is None and ``output_final_state`` is true a new float32 tensor is made.
     ``workspace`` (a uint8 device tensor) is allocated when not given.
+    Shapes as for :func:`kda_recurrent_step`.
     """
     torch = _torch()
-    B, T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    B, T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
     m = _mode_of(g, mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
     _check_dev("g", g, torch.float32)
     _check_dev("beta", beta, torch.float32, (B, T, H))
     _check_dev("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
@@ -197,7 +206,7 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                             _ptr(final_state), _ptr(o), B, T, H, Dk, Dv, int(chunk), float(scale),
+                             _ptr(final_state), _ptr(o), B, T, H, Hqk, Dk, Dv, int(chunk), float(scale),
                              m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
@@ -228,17 +237,20 @@ def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
                          scale: Optional[float] = None, mode=None, out_dtype=None):
     """Recurrent form over a packed batch; updates ``state`` in place.
 
-    q, k [T,H,Dk], v [T,H,Dv] (float32 or bfloat16), g [T,H,Dk] / [T,H] /
+    q, k [T,Hqk,Dk], v [T,H,Dv] (float32 or bfloat16), g [T,H,Dk] / [T,H] /
     None, beta [T,H] float32, state [N,H,Dk,Dv] float32, cu_seqlens int32
     [N+1] on the device.  Returns o [T,H,Dv].
     """
     torch = _torch()
-    T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
     N = _check_cu(cu_seqlens)
     m = _mode_of_packed(g, mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
     _check_dev("g", g, torch.float32)
     _check_dev("beta", beta, torch.float32, (T, H))
     _check_dev("state", state, torch.float32, (N, H, Dk, Dv))
@@ -248,7 +260,7 @@ def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_recurrent_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                                    _ptr(o), _ptr(cu_seqlens), N, T, H, Dk, Dv, float(scale), m,
+                                    _ptr(o), _ptr(cu_seqlens), N, T, H, Hqk, Dk, Dv, float(scale), m,
                                     _dtype_code(q), _dtype_code(o), _stream())
     if st != 0:
         raise KDAError(st, "kda_recurrent_varlen")
@@ -271,12 +283,15 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
     are [N,H,Dk,Dv] float32 (final_state may be initial_state itself).
     """
     torch = _torch()
-    T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
     N = _check_cu(cu_seqlens)
     m = _mode_of_packed(g, mode)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
     _check_dev("g", g, torch.float32)
     _check_dev("beta", beta, torch.float32, (T, H))
     _check_dev("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
@@ -294,7 +309,7 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
         scale = Dk ** -0.5
     st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                     _ptr(initial_state), _ptr(final_state), _ptr(o),
-                                    _ptr(cu_seqlens), N, T, H, Dk, Dv, int(chunk), float(scale),
+                                    _ptr(cu_seqlens), N, T, H, Hqk, Dk, Dv, int(chunk), float(scale),
                                     m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(),
                                     _stream())
     if st != 0:

@@ -12,10 +12,11 @@ bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 
 kda_status check_common(const void* q, const void* k, const void* v, const float* g,
-                        const float* beta, const void* o, int B, int T, int H, int Dk,
+                        const float* beta, const void* o, int B, int T, int H, int Hqk, int Dk,
                         int Dv, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype)
 {
     if (B < 1 || H < 1 || T < 0) return KDA_ERROR_INVALID_VALUE;
+    if (Hqk < 1 || Hqk > H || H % Hqk != 0) return KDA_ERROR_INVALID_VALUE;
     if (mode != KDA_GATE_CHANNEL && mode != KDA_GATE_SCALAR && mode != KDA_GATE_NONE)
         return KDA_ERROR_INVALID_VALUE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
@@ -52,19 +53,19 @@ const char* kda_status_string(kda_status s)
     return "KDA_ERROR_UNKNOWN";
 }
 
-int kda_version(void) { return 10000; }
+int kda_version(void) { return 10100; }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state, void* o, int B, int T, int H,
-                              int Dk, int Dv, float scale, kda_gate_mode mode, kda_dtype dtype,
-                              kda_dtype o_dtype, void* stream)
+                              int Hqk, int Dk, int Dv, float scale, kda_gate_mode mode,
+                              kda_dtype dtype, kda_dtype o_dtype, void* stream)
 {
-    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (T == 0) return KDA_SUCCESS;
     if (!state) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(state)) return KDA_ERROR_MISALIGNED;
-    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, scale, mode, dtype, o_dtype, nullptr};
+    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype, nullptr};
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -81,14 +82,13 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chu
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, float* final_state,
-                         void* o, int B, int T, int H, int Dk, int Dv, int chunk, float scale,
-                         kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                         void* o, int B, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                         float scale, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                          void* workspace, size_t workspace_bytes, void* stream)
 {
-    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
-    if (Dk != Dv) return KDA_ERROR_NOT_SUPPORTED;
     // chunk records and state workgroups are counted in 32-bit integers
     const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
     if (nrec > 1073741824.0 || (double)B * H * (Dv / 16) + 64.0 > 2147483647.0)
@@ -101,7 +101,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
         if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
     }
     if (T == 0 && !final_state) return KDA_SUCCESS;
-    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk,
+    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk, Hqk,
                      scale, mode, dtype, o_dtype, workspace, workspace_bytes, nullptr, 0};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
@@ -109,17 +109,19 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
 kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, float* state, void* o, const int* cu_seqlens,
-                                int N, int T, int H, int Dk, int Dv, float scale, kda_gate_mode mode,
-                                kda_dtype dtype, kda_dtype o_dtype, void* stream)
+                                int N, int T, int H, int Hqk, int Dk, int Dv, float scale,
+                                kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
+                                void* stream)
 {
     if (N < 0) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if ((double)N * H > 2.0e9) return KDA_ERROR_INVALID_VALUE;
     if (N == 0 || T == 0) return KDA_SUCCESS;   // every sequence is empty: states unchanged
     if (!state || !cu_seqlens) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(state) || ((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
-    kda::RecArgs a{q, k, v, g, beta, state, o, N, T, H, Dk, Dv, scale, mode, dtype, o_dtype, cu_seqlens};
+    kda::RecArgs a{q, k, v, g, beta, state, o, N, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype,
+                   cu_seqlens};
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -136,16 +138,15 @@ size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, 
 
 kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* g,
                                 const float* beta, const float* initial_state, float* final_state,
-                                void* o, const int* cu_seqlens, int N, int T, int H, int Dk, int Dv,
-                                int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
-                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
-                                void* stream)
+                                void* o, const int* cu_seqlens, int N, int T, int H, int Hqk,
+                                int Dk, int Dv, int chunk, float scale, kda_gate_mode mode,
+                                kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream)
 {
     if (N < 0) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
-    if (Dk != Dv) return KDA_ERROR_NOT_SUPPORTED;
     // chunk records and state workgroups are counted in 32-bit integers
     const double gmax = (double)((T + chunk - 1) / chunk) + (double)N;
     if (gmax * H > 1073741824.0 || (double)N * H * (Dv / 16) + 64.0 > 2147483647.0)
@@ -159,7 +160,7 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
     if (T == 0 && !final_state) return KDA_SUCCESS;
-    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk,
+    kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk, Hqk,
                      scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;

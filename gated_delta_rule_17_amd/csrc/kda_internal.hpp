@@ -13,6 +13,7 @@ struct RecArgs {
     const float* g; const float* beta;
     float* state; void* o;
     int B, T, H, Dk, Dv;
+    int Hq;               // query/key heads (H is a multiple; value head h reads h / (H / Hq))
     float scale;
     kda_gate_mode mode;
     kda_dtype dtype;      // q, k, v
@@ -27,6 +28,7 @@ struct ChunkArgs {
     const float* g; const float* beta;
     const float* h0; float* hT; void* o;
     int B, T, H, Dk, Dv, chunk;
+    int Hq;               // query/key heads (H is a multiple; value head h reads h / (H / Hq))
     float scale;
     kda_gate_mode mode;
     kda_dtype dtype;      // q, k, v
@@ -36,6 +38,10 @@ struct ChunkArgs {
     // packed token count, B unused), or null for a dense [B, T] batch
     const int* cu;
     int N;
+    // packed: the chunk and sequence tables in the workspace (set by the
+    // dispatcher after it has built them)
+    const void* ctab = nullptr;
+    const void* stab = nullptr;
 };
 
 hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);

@@ -42,7 +42,7 @@ __global__ void __launch_bounds__((RecShape<DK, DV>::NT))
 recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                  const float* __restrict__ g, const float* __restrict__ beta,
                  float* __restrict__ state, OUT* __restrict__ o,
-                 int T, int H, float scale, int mode, const int* __restrict__ cu)
+                 int T, int H, int HQ, float scale, int mode, const int* __restrict__ cu)
 {
     using S = RecShape<DK, DV>;
     const int bh = blockIdx.x / S::NCT;
@@ -69,10 +69,13 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
 
     float* st = state + (size_t)bh * DK * DV + c0;
     // the first token's inputs, requested before the state so that they arrive first
-    auto token_inputs = [&](size_t tok) {
+    // (value head h reads query/key head h / (H / HQ): grouped value heads)
+    const int hq = h / (H / HQ);
+    auto token_inputs = [&](size_t row) {
+        const size_t tok = row * H + h, tkq = row * HQ + hq;
         for (int c = tid; c < DK; c += S::NT) {
-            sk[c] = io<IO>::load(k + tok * DK + c);
-            sq[c] = io<IO>::load(q + tok * DK + c) * scale;
+            sk[c] = io<IO>::load(k + tkq * DK + c);
+            sq[c] = io<IO>::load(q + tkq * DK + c) * scale;
             float a = 1.f;
             if (mode == KDA_GATE_CHANNEL) a = expf(g[tok * DK + c]);
             else if (mode == KDA_GATE_SCALAR) a = expf(g[tok]);
@@ -80,7 +83,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         }
         for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
     };
-    if (Tn > 0) token_inputs(tok0 * H + h);
+    if (Tn > 0) token_inputs(tok0);
     f32x4 hr[S::RPT];
 #pragma unroll
     for (int i = 0; i < S::RPT; ++i)
@@ -89,7 +92,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
 
     for (int t = 0; t < Tn; ++t) {
         const size_t tok = (tok0 + t) * H + h;
-        if (t > 0) token_inputs(tok);
+        if (t > 0) token_inputs(tok0 + t);
         __syncthreads();
 
         f32x4 ak = zero4(), aq = zero4();
@@ -159,11 +162,11 @@ static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
     if (a.o_dtype == KDA_F32)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (float*)a.o, a.T, a.H, a.scale, (int)a.mode, a.cu);
+                           (float*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu);
     else
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (bf16_t*)a.o, a.T, a.H, a.scale, (int)a.mode, a.cu);
+                           (bf16_t*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu);
     return hipGetLastError();
 }
 

@@ -23,12 +23,17 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Layout.  Token tensors are contiguous [B, T, H, D]: q and k have D = Dk,
- *   v and o have D = Dv.  beta is [B, T, H] float.  Gates are log-gates
+ * Layout.  Token tensors are contiguous [B, T, heads, D]: q and k are
+ *   [B, T, Hqk, Dk], v and o [B, T, H, Dv].  H counts the value heads: every
+ *   (batch, value head) pair is one independent recurrence with its own
+ *   state, and value head h reads query/key head h / (H / Hqk) (grouped value
+ *   heads; GeekNews #31925, section "Fused recurrent kernel for decode":
+ *   programs run per sequence and value head).  Hqk = H is the ungrouped
+ *   case; H must be a multiple of Hqk.  beta is [B, T, H] float.  Gates are log-gates
  *   g = log(alpha) <= 0 (GeekNews #31925, section "Diagonal-plus-low-rank
  *   transition": implementations store g and use exp(g)) as float:
  *   [B, T, H, Dk] for KDA_GATE_CHANNEL, [B, T, H] for KDA_GATE_SCALAR, and
- *   NULL for KDA_GATE_NONE.  The recurrent state is stored transposed,
+ *   NULL for KDA_GATE_NONE (per value head).  The recurrent state is stored transposed,
  *   H = S^T, as contiguous float [B, H, Dk, Dv] (row = key channel, column =
  *   value channel), the d_k x d_v layout named in the same summary.
  * dtype.  q, k and v share one storage type `dtype`: KDA_F32 (float) or
@@ -45,8 +50,8 @@
  *   aligned.  Inputs are not modified except where stated.
  * Shapes.  B, H >= 1, T >= 0 (T = 0 leaves every output untouched except
  *   that kda_chunk_fwd copies the initial state to the final state).
- *   Dk, Dv in {16, 32, 64, 128} (kda_chunk_fwd: Dk == Dv); chunk in
- *   {16, 32, 64}; T need not be a multiple of chunk.
+ *   1 <= Hqk <= H with H % Hqk == 0.  Dk, Dv in {16, 32, 64, 128}, in any
+ *   combination; chunk in {16, 32, 64}; T need not be a multiple of chunk.
  * Values.  g must be finite (a hard forget is g = -30, say, not -inf).
  *   Keys are used as given: the article assumes unit keys, but nothing here
  *   normalises or checks them.  beta is not clamped.
@@ -93,7 +98,7 @@ typedef enum {
  * HBM, applies decay, prediction, correction, the rank-1 write and the read,
  * and writes it back once.
  *
- *   q, k   [B,T,H,Dk]  dtype        in
+ *   q, k   [B,T,Hqk,Dk] dtype       in
  *   v      [B,T,H,Dv]  dtype        in
  *   g      see "Layout" (float)     in   (NULL iff mode == KDA_GATE_NONE)
  *   beta   [B,T,H]     float        in
@@ -104,7 +109,7 @@ typedef enum {
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v,
                               const float* g, const float* beta,
                               float* state, void* o,
-                              int B, int T, int H, int Dk, int Dv, float scale,
+                              int B, int T, int H, int Hqk, int Dk, int Dv, float scale,
                               kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                               void* stream);
 
@@ -138,7 +143,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chu
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* g, const float* beta,
                          const float* initial_state, float* final_state, void* o,
-                         int B, int T, int H, int Dk, int Dv, int chunk, float scale,
+                         int B, int T, int H, int Hqk, int Dk, int Dv, int chunk, float scale,
                          kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
@@ -149,8 +154,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
  * (GeekNews #31925, section "Fused recurrent kernel for decode": the
  * recurrent form serves decode, short sequences and stateful serving, and
  * different sequences, heads and value tiles run independently).  Token
- * tensors are [T, H, D] (the dense layout with B = 1), T the total number of
- * packed tokens; beta is [T, H]; gates [T, H, Dk] or [T, H].  Sequence n holds
+ * tensors are [T, heads, D] (the dense layout with B = 1), T the total
+ * number of packed tokens: q, k [T, Hqk, Dk], v, o [T, H, Dv]; beta is
+ * [T, H]; gates [T, H, Dk] or [T, H].  Sequence n holds
  * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 and has its own state, entry n of
  * a [N, H, Dk, Dv] float state.  Every sequence starts and ends its own
  * recurrence: results equal separate calls, one per sequence.
@@ -168,14 +174,14 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
  * sequence n and head h, the tokens of sequence n in order, starting from
  * and updating state[n, h] IN PLACE (an empty sequence leaves it as is).
  *
- *   q, k   [T,H,Dk]  dtype   in         v, o  [T,H,Dv]  (o: o_dtype, out)
+ *   q, k   [T,Hqk,Dk] dtype  in         v, o  [T,H,Dv]  (o: o_dtype, out)
  *   g, beta as above (float, in)       state [N,H,Dk,Dv] float in/out
  *   cu_seqlens [N+1] int32 device      N >= 0 (N = 0 or T = 0: nothing to do)
  */
 kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v,
                                 const float* g, const float* beta,
                                 float* state, void* o, const int* cu_seqlens,
-                                int N, int T, int H, int Dk, int Dv, float scale,
+                                int N, int T, int H, int Hqk, int Dk, int Dv, float scale,
                                 kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                                 void* stream);
 
@@ -206,8 +212,8 @@ size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, 
 kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                 const float* g, const float* beta,
                                 const float* initial_state, float* final_state, void* o,
-                                const int* cu_seqlens, int N, int T, int H, int Dk, int Dv,
-                                int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
+                                const int* cu_seqlens, int N, int T, int H, int Hqk, int Dk,
+                                int Dv, int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
                                 kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
                                 void* stream);
 

@@ -13,6 +13,8 @@ Two independent forms:
   (``chunkwise.py``), used to pin R on small inputs and to document the
   reading of the truncated chunkwise derivation.
 
+* :func:`recurrent_grouped` -- grouped value heads: every query/key head
+  repeated over its value heads, then oracle R (``grouped.py``).
 * :func:`recurrent_varlen` -- packed variable-length batches as one call
   of oracle R per sequence (``varlen.py``).
 
@@ -20,4 +22,5 @@ Both take the state transposed, ``H = S^T`` with shape ``[B, H, Dk, Dv]``.
 """
 from .recurrence import recurrent, build_oracle_library, oracle_threads  # noqa: F401
 from .chunkwise import chunkwise  # noqa: F401
+from .grouped import recurrent_grouped  # noqa: F401
 from .varlen import recurrent_varlen  # noqa: F401

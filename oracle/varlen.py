@@ -16,12 +16,13 @@ from typing import Optional
 
 import numpy as np
 
-from .recurrence import recurrent
+from .grouped import recurrent_grouped
 
 
 def recurrent_varlen(q, k, v, g, beta, cu, h0=None, *, scale: Optional[float] = None,
                      mode: str = "channel", threads: int = 0, mutant: int = 0):
-    """q, k [T,H,Dk]; v [T,H,Dv]; g [T,H,Dk] / [T,H] / None; beta [T,H];
+    """q, k [T,Hqk,Dk]; v [T,H,Dv] (grouped value heads as in
+    :func:`oracle.recurrent_grouped`); g [T,H,Dk] / [T,H] / None; beta [T,H];
     cu [N+1] nondecreasing offsets with cu[0] = 0 and cu[N] = T;
     h0 [N,H,Dk,Dv] or None.  Returns (o [T,H,Dv], hT [N,H,Dk,Dv]) in float64.
 
@@ -30,8 +31,8 @@ def recurrent_varlen(q, k, v, g, beta, cu, h0=None, *, scale: Optional[float] = 
     the next sequence."""
     cu = np.asarray(cu, np.int64)
     N = len(cu) - 1
-    T, H, Dk = q.shape
-    Dv = v.shape[-1]
+    T, _, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
     assert N >= 0 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
     o = np.zeros((T, H, Dv), np.float64)
     hT = np.zeros((N, H, Dk, Dv), np.float64)
@@ -48,8 +49,8 @@ def recurrent_varlen(q, k, v, g, beta, cu, h0=None, *, scale: Optional[float] = 
                 hT[n] = hn[0]
             continue
         sl = lambda x: None if x is None else np.asarray(x[s:e])[None]
-        on, hTn = recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), hn, scale=scale, mode=mode,
-                            threads=threads)
+        on, hTn = recurrent_grouped(sl(q), sl(k), sl(v), sl(g), sl(beta), hn, scale=scale,
+                                    mode=mode, threads=threads)
         o[s:e] = on[0]
         hT[n] = hTn[0]
         carry = hTn
