@@ -211,6 +211,47 @@ def bench_prefill_shape(K, torch, dev, warmup, reps, *, Hqk, Dk, Dv, H=16, T=409
             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS}
 
 
+def bench_prologue(K, torch, dev, warmup, reps):
+    """The prefill and decode shapes with all three prologue transforms fused
+    (q, k L2-normalised; beta = sigmoid; g = log sigmoid of pre-activations)."""
+    from kda_workloads import make_inputs
+    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    flags = K.NORMALIZE_QK | K.BETA_SIGMOID | K.GATE_LOGSIGMOID
+    w = make_inputs(1, 4096, 16, 128, 128, dtype="bf16", seed=11, gate_shift=3.0, h0_std=0.01,
+                    preact=True)
+    q, k, v = t(w.q, torch.bfloat16), t(w.k, torch.bfloat16), t(w.v, torch.bfloat16)
+    g, beta, h0 = t(w.g), t(w.beta), t(w.h0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(1, 4096, 16, 128, 128, 64, 0, K.BF16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((1, 4096, 16, 128), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty_like(h0)
+    d = make_inputs(256, 1, 32, 128, 128, dtype="bf16", seed=12, gate_shift=3.0, h0_std=0.05,
+                    preact=True)
+    dq, dk, dv = t(d.q, torch.bfloat16), t(d.k, torch.bfloat16), t(d.v, torch.bfloat16)
+    dg, db, st = t(d.g), t(d.beta), t(d.h0)
+    od = torch.empty((256, 1, 32, 128), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    tp = timed(lambda: K.kda_chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o,
+                                       chunk=64, workspace=ws, prologue=flags))
+    td = timed(lambda: K.kda_recurrent_step(dq, dk, dv, dg, db, st, o=od, prologue=flags))
+    return {"workload": "prefill B1 H16 T4096 d128 and decode B256 H32 d128, bf16, "
+                        "pre-activations with all three transforms fused",
+            "prefill_ms": tp, "prefill_tokens_per_s": 4096 / (tp / 1e3),
+            "decode_ms": td, "decode_state_GBps": 256 * 32 * 128 * 128 * 8 / (td / 1e3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +396,7 @@ def main():
         out["varlen"] = bench_varlen(K, torch, dev, args.warmup, reps)
         out["grouped_heads"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=4, Dk=128, Dv=128)
         out["mixed_dims"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=16, Dk=64, Dv=128)
+        out["prologue"] = bench_prologue(K, torch, dev, args.warmup, reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

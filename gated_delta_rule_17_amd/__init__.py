@@ -16,6 +16,9 @@ Entry points (same names as the C ABI):
                        final_state=None, o=None, chunk=64, scale=None, mode=None,
                        workspace=None)
   kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype)
+
+Every compute call takes ``prologue``, a bitwise OR of NORMALIZE_QK,
+BETA_SIGMOID and GATE_LOGSIGMOID (0: inputs used as given).
 """
 from __future__ import annotations
 
@@ -29,6 +32,8 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 
 GATE_CHANNEL, GATE_SCALAR, GATE_NONE = 0, 1, 2
+# fused prologue flags (kda_prologue)
+NORMALIZE_QK, BETA_SIGMOID, GATE_LOGSIGMOID = 1, 2, 4
 F32, BF16 = 0, 1
 _MODE_NAMES = {"channel": GATE_CHANNEL, "scalar": GATE_SCALAR, "none": GATE_NONE}
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
@@ -54,20 +59,20 @@ def lib():
                            "`python -m gated_delta_rule_17_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]
     L.kda_recurrent_step.restype = i
     L.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd_workspace_size.restype = sz
-    L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, i, f, i, i, i,
+    L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
     L.kda_recurrent_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, f, i, i, i,
-                                       vp]
+                                       i, vp]
     L.kda_recurrent_varlen.restype = i
     L.kda_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i]
     L.kda_chunk_fwd_varlen_workspace_size.restype = sz
     L.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp, i, i, i, i, i, i, i, f, i,
-                                       i, i, vp, sz, vp]
+                                       i, i, i, vp, sz, vp]
     L.kda_chunk_fwd_varlen.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
@@ -131,7 +136,7 @@ def _stream():
 
 
 def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] = None,
-                       mode=None, out_dtype=None):
+                       mode=None, out_dtype=None, prologue: int = 0):
     """Recurrent form over T >= 1 tokens; updates ``state`` in place.
 
     q, k [B,T,Hqk,Dk] and v [B,T,H,Dv] (float32 or bfloat16; H a multiple of
@@ -159,7 +164,7 @@ def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] =
         scale = Dk ** -0.5
     st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                   _ptr(o), B, T, H, Hqk, Dk, Dv, float(scale), m, _dtype_code(q),
-                                  _dtype_code(o), _stream())
+                                  _dtype_code(o), int(prologue), _stream())
     if st != 0:
         raise KDAError(st, "kda_recurrent_step")
     return o
@@ -173,7 +178,7 @@ def kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype) -> int:
 
 def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None,
                   chunk: int = 64, scale: Optional[float] = None, mode=None, workspace=None,
-                  output_final_state: bool = True, out_dtype=None):
+                  output_final_state: bool = True, out_dtype=None, prologue: int = 0):
     """Chunkwise form.  Returns (o, final_state).
 
     ``final_state`` may be passed (it may be ``initial_state`` itself); if it
@@ -207,7 +212,8 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
         scale = Dk ** -0.5
     st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                              _ptr(final_state), _ptr(o), B, T, H, Hqk, Dk, Dv, int(chunk), float(scale),
-                             m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(), _stream())
+                             m, dt, _dtype_code(o), int(prologue), _ptr(workspace), workspace.numel(),
+                             _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
     return o, final_state
@@ -234,7 +240,8 @@ def _check_cu(cu_seqlens):
 
 
 def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
-                         scale: Optional[float] = None, mode=None, out_dtype=None):
+                         scale: Optional[float] = None, mode=None, out_dtype=None,
+                         prologue: int = 0):
     """Recurrent form over a packed batch; updates ``state`` in place.
 
     q, k [T,Hqk,Dk], v [T,H,Dv] (float32 or bfloat16), g [T,H,Dk] / [T,H] /
@@ -261,7 +268,7 @@ def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
         scale = Dk ** -0.5
     st = lib().kda_recurrent_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                                     _ptr(o), _ptr(cu_seqlens), N, T, H, Hqk, Dk, Dv, float(scale), m,
-                                    _dtype_code(q), _dtype_code(o), _stream())
+                                    _dtype_code(q), _dtype_code(o), int(prologue), _stream())
     if st != 0:
         raise KDAError(st, "kda_recurrent_varlen")
     return o
@@ -276,7 +283,8 @@ def kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype) -> 
 
 def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final_state=None,
                          o=None, chunk: int = 64, scale: Optional[float] = None, mode=None,
-                         workspace=None, output_final_state: bool = True, out_dtype=None):
+                         workspace=None, output_final_state: bool = True, out_dtype=None,
+                         prologue: int = 0):
     """Chunkwise form over a packed batch.  Returns (o, final_state).
 
     Shapes as for :func:`kda_recurrent_varlen`; initial_state / final_state
@@ -310,8 +318,8 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
     st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                     _ptr(initial_state), _ptr(final_state), _ptr(o),
                                     _ptr(cu_seqlens), N, T, H, Hqk, Dk, Dv, int(chunk), float(scale),
-                                    m, dt, _dtype_code(o), _ptr(workspace), workspace.numel(),
-                                    _stream())
+                                    m, dt, _dtype_code(o), int(prologue), _ptr(workspace),
+                                    workspace.numel(), _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd_varlen")
     return o, final_state

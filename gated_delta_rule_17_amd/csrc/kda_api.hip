@@ -58,14 +58,16 @@ int kda_version(void) { return 10100; }
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state, void* o, int B, int T, int H,
                               int Hqk, int Dk, int Dv, float scale, kda_gate_mode mode,
-                              kda_dtype dtype, kda_dtype o_dtype, void* stream)
+                              kda_dtype dtype, kda_dtype o_dtype, int prologue, void* stream)
 {
+    if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (T == 0) return KDA_SUCCESS;
     if (!state) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(state)) return KDA_ERROR_MISALIGNED;
-    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype, nullptr};
+    kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype, nullptr,
+                   prologue};
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -84,8 +86,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          const float* beta, const float* initial_state, float* final_state,
                          void* o, int B, int T, int H, int Hqk, int Dk, int Dv, int chunk,
                          float scale, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
-                         void* workspace, size_t workspace_bytes, void* stream)
+                         int prologue, void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
@@ -102,7 +105,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     }
     if (T == 0 && !final_state) return KDA_SUCCESS;
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk, Hqk,
-                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, nullptr, 0};
+                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, nullptr, 0, prologue};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -111,9 +114,9 @@ kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, con
                                 const float* beta, float* state, void* o, const int* cu_seqlens,
                                 int N, int T, int H, int Hqk, int Dk, int Dv, float scale,
                                 kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
-                                void* stream)
+                                int prologue, void* stream)
 {
-    if (N < 0) return KDA_ERROR_INVALID_VALUE;
+    if (N < 0 || (prologue & ~KDA_PROLOGUE_ALL)) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if ((double)N * H > 2.0e9) return KDA_ERROR_INVALID_VALUE;
@@ -121,7 +124,7 @@ kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, con
     if (!state || !cu_seqlens) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(state) || ((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
     kda::RecArgs a{q, k, v, g, beta, state, o, N, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype,
-                   cu_seqlens};
+                   cu_seqlens, prologue};
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -140,10 +143,10 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 const float* beta, const float* initial_state, float* final_state,
                                 void* o, const int* cu_seqlens, int N, int T, int H, int Hqk,
                                 int Dk, int Dv, int chunk, float scale, kda_gate_mode mode,
-                                kda_dtype dtype, kda_dtype o_dtype, void* workspace,
+                                kda_dtype dtype, kda_dtype o_dtype, int prologue, void* workspace,
                                 size_t workspace_bytes, void* stream)
 {
-    if (N < 0) return KDA_ERROR_INVALID_VALUE;
+    if (N < 0 || (prologue & ~KDA_PROLOGUE_ALL)) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
@@ -161,7 +164,7 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
     if (T == 0 && !final_state) return KDA_SUCCESS;
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk, Hqk,
-                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N};
+                     scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N, prologue};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }

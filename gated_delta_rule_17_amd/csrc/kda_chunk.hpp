@@ -52,6 +52,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (x in log2 units; underflows to 0)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// log(sigmoid(a)) = min(a, 0) - log(1 + exp(-|a|)), without overflow
+__device__ __forceinline__ float log_sigmoid(float a) { return fminf(a, 0.f) - log1pf(expf(-fabsf(a))); }
+
 template <int C, int DK, int DV, typename OT>
 struct CS {
     static constexpr int NB = C / 16;                 // 16-token blocks per chunk
@@ -236,12 +239,14 @@ __device__ __forceinline__ Frag<OT> select_frag(int hh, int lane) {
     return f;
 }
 
-template <int C, int DK, int DV, typename OT>
+// PRO: the fused prologue is compiled in (its flags are then read from
+// `pro`); without it the prologue code is absent and `pro` is ignored.
+template <int C, int DK, int DV, typename OT, bool PRO>
 __global__ void __launch_bounds__((CS<C, DK, DV, OT>::NT))
 chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
               int T, int H, int HQ, int NC, int NITEM, float scale, int mode, void* __restrict__ ws,
-              size_t nrec, const int2* __restrict__ ctab)
+              size_t nrec, const int2* __restrict__ ctab, int pro)
 {
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SKF = S::SKF, SC = S::SC,
@@ -279,6 +284,8 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
     __shared__ __align__(16) float bfirst[NB][DKP];     // and its first term
     __shared__ __align__(16) float eSb[NB][DKP];        // exp(G at the block's first token)
     __shared__ __align__(16) float eLb[NB][DKP];        // exp(G_last - G at the block's last token)
+    __shared__ float nrm[KSN][2][C];                    // partial sums of k^2, q^2 per slice
+    __shared__ float inrm[2][C];                        // 1 / norm of k and of q per token
     __shared__ __align__(16) float fpair[S::NPAIR > 0 ? S::NPAIR : 1][DKP];
     __shared__ __align__(8) unsigned char flag[NB][DKP];
     __shared__ int anyflag;
@@ -396,15 +403,36 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         float* Wut = W.ut + rec * S::U_N;
         if (tid == 0) anyflag = 0;
         const bool tv = it < L;
-        if (ksl == 0 && gq == 0) sb[it] = tv ? cur.b : 0.f;
+        // beta, or sigmoid of a pre-activation
+        const float bet = (PRO && (pro & KDA_BETA_SIGMOID)) ? 1.f / (1.f + expf(-cur.b)) : cur.b;
+        if (ksl == 0 && gq == 0) sb[it] = tv ? bet : 0.f;
         float gl[8], kv[8], qv[8];
+        float pk = 0.f, pq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const bool ok = tv && (ch + e < DK);
-            const float gv = mode == KDA_GATE_CHANNEL ? (e < 4 ? cur.g0[e] : cur.g1[e - 4]) : cur.gt;
+            float gv = mode == KDA_GATE_CHANNEL ? (e < 4 ? cur.g0[e] : cur.g1[e - 4]) : cur.gt;
+            if (PRO && (pro & KDA_GATE_LOGSIGMOID)) gv = log_sigmoid(gv);
             gl[e] = (ok && mode != KDA_GATE_NONE) ? gv * kLog2e : 0.f;   // log2 units
             kv[e] = ok ? cur.k.get(e) : 0.f;
             qv[e] = ok ? cur.q.get(e) * scale : 0.f;
+            if constexpr (PRO) {
+                pk += kv[e] * kv[e];
+                pq += qv[e] * qv[e];
+            }
+        }
+        // L2 normalisation of q and k: the sums of squares of token `it` over
+        // this wave's 32 channels (the four lanes holding them), one partial
+        // per slice to LDS; the scales are taken after the next barrier
+        if (PRO && (pro & KDA_NORMALIZE_QK)) {
+            pk += __shfl_xor(pk, 16);
+            pk += __shfl_xor(pk, 32);
+            pq += __shfl_xor(pq, 16);
+            pq += __shfl_xor(pq, 32);
+            if (gq == 0) {
+                nrm[ksl][0][it] = pk;
+                nrm[ksl][1][it] = pq;
+            }
         }
 
         // ---- cumulative log-decay, in log2 units from here on (every decay
@@ -422,6 +450,26 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         }
         __syncthreads();
         load_in(nxt, nitem, tid, 0);
+        if (PRO && (pro & KDA_NORMALIZE_QK)) {
+            float sk2 = 0.f, sq2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < KSN; ++j) {
+                sk2 += nrm[j][0][it];
+                sq2 += nrm[j][1][it];
+            }
+            const float fk = rsqrtf(sk2 + kNormEps);
+            // qv holds scale * q: its norm is taken over q itself
+            const float fq = scale != 0.f ? rsqrtf(sq2 / (scale * scale) + kNormEps) : 1.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kv[e] *= fk;
+                qv[e] *= fq;
+            }
+            if (ksl == 0 && gq == 0) {
+                inrm[0][it] = fk;
+                inrm[1][it] = fq;
+            }
+        }
         // ---- the factors of one (block I, channel c): a left-to-right pass
         // over the block totals (the same order everywhere) gives G at the
         // block boundaries; from them exp(G_s(I)), exp(G_last - G_e(I)), the
@@ -522,7 +570,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         // right-hand side of the solve
         Frag<OT> bk;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bk.set(e, cur.b * kv[e] * eg[e]);
+        for (int e = 0; e < 8; ++e) bk.set(e, bet * kv[e] * eg[e]);
         if (CP > C) {   // zero the padded token columns of Kr^T and Aqk
             for (int p = tid; p < DK * (CP - C); p += S::NT) {
                 const int cc = p / (CP - C), i = C + p % (CP - C);
@@ -641,7 +689,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
             if (vch < DVP) {
                 float bv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) bv[e] = (tv && vch + e < DV) ? cur.b * cur.v[j].get(e) : 0.f;
+                for (int e = 0; e < 8; ++e) bv[e] = (tv && vch + e < DV) ? bet * cur.v[j].get(e) : 0.f;
                 store8_p(XU, it * SV + vch, bv);
             }
         }
@@ -663,8 +711,13 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
                         const size_t tkq = (loc.tok0 + i) * HQ + h / GH;
                         if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
                         else if (mode == KDA_GATE_SCALAR) gv = g[tok];
+                        if (PRO && mode != KDA_GATE_NONE && (pro & KDA_GATE_LOGSIGMOID)) gv = log_sigmoid(gv);
                         kv = io<OT>::load(k + tkq * DK + cc);
                         qv = io<OT>::load(q + tkq * DK + cc) * scale;
+                        if (PRO && (pro & KDA_NORMALIZE_QK)) {
+                            kv *= inrm[0][i];
+                            qv *= inrm[1][i];
+                        }
                     }
                     run += gv;
                     gi[u] = run; ki[u] = kv; qi[u] = qv;
@@ -1165,10 +1218,19 @@ hipError_t launch3(const ChunkArgs& a, hipStream_t s)
     }
     if (nitem > 0 && a.T > 0) {
         // persistent workgroups: as many as can be resident at once
-        const int grid = min(nitem, resident_blocks(chunk_prepare<C, DK, DV, OT>, CS<C, DK, DV, OT>::NT));
-        hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT>), dim3(grid), dim3(CS<C, DK, DV, OT>::NT), 0, s,
-                           (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
-                           a.T, a.H, a.Hq, NC, nitem, a.scale, (int)a.mode, a.ws, nrec, ctab);
+        constexpr int NT = CS<C, DK, DV, OT>::NT;
+        if (a.prologue) {
+            const int grid = min(nitem, resident_blocks(chunk_prepare<C, DK, DV, OT, true>, NT));
+            hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT, true>), dim3(grid), dim3(NT), 0, s,
+                               (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
+                               a.T, a.H, a.Hq, NC, nitem, a.scale, (int)a.mode, a.ws, nrec, ctab,
+                               a.prologue);
+        } else {
+            const int grid = min(nitem, resident_blocks(chunk_prepare<C, DK, DV, OT, false>, NT));
+            hipLaunchKernelGGL((chunk_prepare<C, DK, DV, OT, false>), dim3(grid), dim3(NT), 0, s,
+                               (const OT*)a.q, (const OT*)a.k, (const OT*)a.v, a.g, a.beta,
+                               a.T, a.H, a.Hq, NC, nitem, a.scale, (int)a.mode, a.ws, nrec, ctab, 0);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -8,6 +8,9 @@
 
 namespace kda {
 
+// epsilon of the fused L2 normalisation: x / sqrt(sum x^2 + eps)
+constexpr float kNormEps = 1e-6f;
+
 struct RecArgs {
     const void* q; const void* k; const void* v;
     const float* g; const float* beta;
@@ -21,6 +24,7 @@ struct RecArgs {
     // packed variable-length batch: device offsets [N + 1] (B is N, T the
     // packed token count), or null for a dense [B, T] batch
     const int* cu;
+    int prologue;         // kda_prologue flags
 };
 
 struct ChunkArgs {
@@ -38,6 +42,7 @@ struct ChunkArgs {
     // packed token count, B unused), or null for a dense [B, T] batch
     const int* cu;
     int N;
+    int prologue;         // kda_prologue flags
     // packed: the chunk and sequence tables in the workspace (set by the
     // dispatcher after it has built them)
     const void* ctab = nullptr;

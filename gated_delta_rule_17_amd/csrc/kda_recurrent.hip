@@ -42,7 +42,7 @@ __global__ void __launch_bounds__((RecShape<DK, DV>::NT))
 recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                  const float* __restrict__ g, const float* __restrict__ beta,
                  float* __restrict__ state, OUT* __restrict__ o,
-                 int T, int H, int HQ, float scale, int mode, const int* __restrict__ cu)
+                 int T, int H, int HQ, float scale, int mode, const int* __restrict__ cu, int pro)
 {
     using S = RecShape<DK, DV>;
     const int bh = blockIdx.x / S::NCT;
@@ -65,7 +65,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     const int lane = tid & 63, wave = tid >> 6;
 
     __shared__ float sk[DK], sq[DK], sa[DK], sv[S::DVT];
-    __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][9];
+    __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][11];
 
     float* st = state + (size_t)bh * DK * DV + c0;
     // the first token's inputs, requested before the state so that they arrive first
@@ -77,8 +77,11 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             sk[c] = io<IO>::load(k + tkq * DK + c);
             sq[c] = io<IO>::load(q + tkq * DK + c) * scale;
             float a = 1.f;
-            if (mode == KDA_GATE_CHANNEL) a = expf(g[tok * DK + c]);
-            else if (mode == KDA_GATE_SCALAR) a = expf(g[tok]);
+            if (mode != KDA_GATE_NONE) {
+                const float gv = mode == KDA_GATE_CHANNEL ? g[tok * DK + c] : g[tok];
+                // the retention alpha = exp(g), or sigmoid(a) from a pre-activation
+                a = (pro & KDA_GATE_LOGSIGMOID) ? 1.f / (1.f + expf(-gv)) : expf(gv);
+            }
             sa[c] = a;
         }
         for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
@@ -96,7 +99,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         __syncthreads();
 
         f32x4 ak = zero4(), aq = zero4();
-        float kq = 0.f;
+        float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
         for (int i = 0; i < S::RPT; ++i) {
             const int r = rg + S::RG * i;
@@ -105,6 +108,8 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             ak += hr[i] * kr;
             aq += hr[i] * qr;
             kq += kr * qr;
+            kk += kr * kr;
+            qq += qr * qr;
         }
         // reduce over the row groups held by this wavefront
 #pragma unroll
@@ -115,6 +120,8 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                 aq[u] += __shfl_xor(aq[u], off);
             }
             kq += __shfl_xor(kq, off);
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
         }
         if constexpr (S::NW > 1) {
             if (lane < S::CX) {
@@ -124,9 +131,11 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                     red[wave][cx][4 + u] = aq[u];
                 }
                 red[wave][cx][8] = kq;
+                red[wave][cx][9] = kk;
+                red[wave][cx][10] = qq;
             }
             __syncthreads();
-            ak = zero4(); aq = zero4(); kq = 0.f;
+            ak = zero4(); aq = zero4(); kq = 0.f; kk = 0.f; qq = 0.f;
 #pragma unroll
             for (int w = 0; w < S::NW; ++w) {
 #pragma unroll
@@ -135,14 +144,28 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                     aq[u] += red[w][cx][4 + u];
                 }
                 kq += red[w][cx][8];
+                kk += red[w][cx][9];
+                qq += red[w][cx][10];
             }
         }
-        const float bt = beta[tok];
+        // L2-normalised q and k: every product with them is linear, so the
+        // norms are applied to the reduced sums (sq holds scale * q)
+        float fk = 1.f, fq = 1.f;
+        if (pro & KDA_NORMALIZE_QK) {
+            fk = rsqrtf(kk + kNormEps);
+            fq = scale != 0.f ? rsqrtf(qq / (scale * scale) + kNormEps) : 1.f;
+            ak *= fk;
+            aq *= fq;
+            kq *= fk * fq;
+        }
+        float bt = beta[tok];
+        if (pro & KDA_BETA_SIGMOID) bt = 1.f / (1.f + expf(-bt));
         f32x4 e;
 #pragma unroll
         for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
+        const f32x4 ek = e * fk;
 #pragma unroll
-        for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * e;
+        for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * ek;
         if (rg == 0) {
             Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
         }
@@ -162,11 +185,11 @@ static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
     if (a.o_dtype == KDA_F32)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (float*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu);
+                           (float*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu, a.prologue);
     else
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
-                           (bf16_t*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu);
+                           (bf16_t*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu, a.prologue);
     return hipGetLastError();
 }
 

@@ -53,8 +53,9 @@
  *   1 <= Hqk <= H with H % Hqk == 0.  Dk, Dv in {16, 32, 64, 128}, in any
  *   combination; chunk in {16, 32, 64}; T need not be a multiple of chunk.
  * Values.  g must be finite (a hard forget is g = -30, say, not -inf).
- *   Keys are used as given: the article assumes unit keys, but nothing here
- *   normalises or checks them.  beta is not clamped.
+ *   Keys are used as given unless KDA_NORMALIZE_QK is passed: the article
+ *   assumes unit keys, but nothing else here normalises or checks them.
+ *   beta is not clamped.
  * Errors.  Arguments are validated on the host before any HIP call; a bad
  *   argument returns a status and enqueues nothing.  A failed launch returns
  *   KDA_ERROR_HIP.  Nothing is printed and nothing aborts.
@@ -78,6 +79,30 @@ typedef enum {
     KDA_F32 = 0,
     KDA_BF16 = 1
 } kda_dtype;
+
+/*
+ * Fused prologue (the `prologue` argument, a bitwise OR of these flags; 0
+ * uses q, k, beta and g as given).  Each flag moves one input transform into
+ * the kernels, applied to the values as they are loaded:
+ *   KDA_NORMALIZE_QK     q and k of every token and query/key head are
+ *                        L2-normalised over Dk, x / sqrt(sum x^2 + 1e-6)
+ *                        ("You could have come up with Kimi Delta
+ *                        Attention", notation note: keys are assumed
+ *                        normalised); the query scale applies after it.
+ *   KDA_BETA_SIGMOID     beta holds pre-activations b; the write strength
+ *                        is sigmoid(b), inside [0, 1] (GeekNews #31925,
+ *                        section "DeltaNet: write the error, not the value").
+ *   KDA_GATE_LOGSIGMOID  g holds pre-activations a; the retention is
+ *                        alpha = sigmoid(a), i.e. g = log(sigmoid(a)) <= 0
+ *                        (GeekNews #31925, section "Diagonal-plus-low-rank
+ *                        transition": implementations keep g = log alpha).
+ */
+typedef enum {
+    KDA_NORMALIZE_QK = 1,
+    KDA_BETA_SIGMOID = 2,
+    KDA_GATE_LOGSIGMOID = 4,
+    KDA_PROLOGUE_ALL = 7
+} kda_prologue;
 
 typedef enum {
     KDA_SUCCESS = 0,
@@ -105,13 +130,14 @@ typedef enum {
  *   state  [B,H,Dk,Dv] float        in/out (S_{t0-1} on entry, S_{t0+T-1} on exit)
  *   o      [B,T,H,Dv]  o_dtype      out  (must not alias any input)
  *   scale  query scale (pass 1/sqrt(Dk) for the article's d_k^-1/2)
+ *   prologue  kda_prologue flags (0: inputs used as given)
  */
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v,
                               const float* g, const float* beta,
                               float* state, void* o,
                               int B, int T, int H, int Hqk, int Dk, int Dv, float scale,
                               kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
-                              void* stream);
+                              int prologue, void* stream);
 
 /*
  * kda_chunk_fwd_workspace_size -- bytes of device workspace kda_chunk_fwd
@@ -145,7 +171,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const float* initial_state, float* final_state, void* o,
                          int B, int T, int H, int Hqk, int Dk, int Dv, int chunk, float scale,
                          kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int prologue, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Packed variable-length batches
@@ -183,7 +209,7 @@ kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v,
                                 float* state, void* o, const int* cu_seqlens,
                                 int N, int T, int H, int Hqk, int Dk, int Dv, float scale,
                                 kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
-                                void* stream);
+                                int prologue, void* stream);
 
 /*
  * kda_chunk_fwd_varlen_workspace_size -- bytes of device workspace
@@ -214,8 +240,8 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                 const float* initial_state, float* final_state, void* o,
                                 const int* cu_seqlens, int N, int T, int H, int Hqk, int Dk,
                                 int Dv, int chunk, float scale, kda_gate_mode mode, kda_dtype dtype,
-                                kda_dtype o_dtype, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                kda_dtype o_dtype, int prologue, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* kda_status_string(kda_status s);

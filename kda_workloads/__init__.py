@@ -117,7 +117,7 @@ def _normal(rng, shape, std=1.0, mean=0.0):
 def make_inputs(B, T, H, Dk, Dv, *, mode=CHANNEL, dtype="bf16", chunk=64,
                 seed=0, gate_law="softplus", gate_shift=0.0, beta_law="sigmoid",
                 h0_std=0.0, normalise_k=True, scale=None, name="custom",
-                scalar_gate_per_head=True):
+                scalar_gate_per_head=True, preact=False):
     """Draw one workload.
 
     gate_law:
@@ -129,16 +129,20 @@ def make_inputs(B, T, H, Dk, Dv, *, mode=CHANNEL, dtype="bf16", chunk=64,
       "zero"       log a = 0
     beta_law: "sigmoid" (sigmoid(N(0,1))) or "uniform" (U[0.1, 1]).
     In scalar mode one gate value is drawn per (b, t, h).
+    preact: draw pre-activations for the fused prologue instead: q, k ~ N(0,1)
+    unnormalised, beta ~ N(0,1), g ~ N(gate_shift, 1) (gate_law ignored).
     """
     if mode not in GATE_MODES:
         raise ValueError(mode)
     rq, rk, rv, rb, rg, rh = _children(seed)
     q = _normal(rq, (B, T, H, Dk))
     k = _normal(rk, (B, T, H, Dk))
-    if normalise_k:
+    if normalise_k and not preact:
         k = _l2_normalise_last(k)
     v = _normal(rv, (B, T, H, Dv))
-    if beta_law == "sigmoid":
+    if preact:
+        beta = _normal(rb, (B, T, H))
+    elif beta_law == "sigmoid":
         beta = _sigmoid(_normal(rb, (B, T, H)))
     elif beta_law == "uniform":
         beta = rb.uniform(0.1, 1.0, size=(B, T, H)).astype(np.float32)
@@ -147,6 +151,9 @@ def make_inputs(B, T, H, Dk, Dv, *, mode=CHANNEL, dtype="bf16", chunk=64,
 
     if mode == NONE:
         g = None
+    elif preact:
+        gshape = (B, T, H, Dk) if mode == CHANNEL else (B, T, H)
+        g = _normal(rg, gshape, mean=float(gate_shift))
     else:
         gshape = (B, T, H, Dk) if mode == CHANNEL else (B, T, H)
         if gate_law == "softplus":

@@ -17,6 +17,9 @@ Two independent forms:
   repeated over its value heads, then oracle R (``grouped.py``).
 * :func:`recurrent_varlen` -- packed variable-length batches as one call
   of oracle R per sequence (``varlen.py``).
+* :func:`apply_prologue` -- the optional input transforms (L2-normalised
+  q/k, sigmoid beta, log-sigmoid gates), applied before the others
+  (``prologue.py``).
 
 Both take the state transposed, ``H = S^T`` with shape ``[B, H, Dk, Dv]``.
 """
@@ -24,3 +27,4 @@ from .recurrence import recurrent, build_oracle_library, oracle_threads  # noqa:
 from .chunkwise import chunkwise  # noqa: F401
 from .grouped import recurrent_grouped  # noqa: F401
 from .varlen import recurrent_varlen  # noqa: F401
+from .prologue import apply_prologue  # noqa: F401

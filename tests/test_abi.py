@@ -34,19 +34,20 @@ def test_status_strings(L):
 
 
 def _rec(L, q=A, k=A, v=A, g=A, beta=A, state=A, o=A, B=1, T=1, H=1, Hqk=None, Dk=128, Dv=128,
-         scale=1.0, mode=0, dtype=1, o_dtype=0):
+         scale=1.0, mode=0, dtype=1, o_dtype=0, pro=0):
     Hqk = H if Hqk is None else Hqk
     return L.kda_recurrent_step(q, k, v, g, beta, state, o, B, T, H, Hqk, Dk, Dv, scale, mode,
-                                dtype, o_dtype, None)
+                                dtype, o_dtype, pro, None)
 
 
 def _chunk(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, B=1, T=64, H=1, Hqk=None,
-           Dk=128, Dv=128, chunk=64, scale=1.0, mode=0, dtype=1, o_dtype=0, ws=A, wsb=None):
+           Dk=128, Dv=128, chunk=64, scale=1.0, mode=0, dtype=1, o_dtype=0, ws=A, wsb=None,
+           pro=0):
     Hqk = H if Hqk is None else Hqk
     if wsb is None:
         wsb = L.kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype)
     return L.kda_chunk_fwd(q, k, v, g, beta, h0, hT, o, B, T, H, Hqk, Dk, Dv, chunk, scale, mode,
-                           dtype, o_dtype, ws, wsb, None)
+                           dtype, o_dtype, pro, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -54,7 +55,8 @@ def _chunk(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, B=1, T=64, H=1,
     (dict(o=None), 1), (dict(state=None), 1), (dict(g=None, mode=0), 1),
     (dict(g=None, mode=1), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
     (dict(mode=3), 1), (dict(dtype=2), 1), (dict(o_dtype=-1), 1), (dict(Dk=48), 2), (dict(Dv=256), 2),
-    (dict(H=4, Hqk=3), 1), (dict(H=2, Hqk=4), 1), (dict(Hqk=0), 1),
+    (dict(H=4, Hqk=3), 1), (dict(H=2, Hqk=4), 1), (dict(Hqk=0), 1), (dict(pro=8), 1),
+    (dict(pro=-1), 1),
     (dict(Dk=8), 2), (dict(q=MIS), 3), (dict(state=MIS), 3), (dict(g=MIS), 3),
     (dict(o=MIS), 3),
 ])
@@ -66,7 +68,7 @@ def test_recurrent_validation(L, kw, code):
     (dict(q=None), 1), (dict(g=None, mode=0), 1), (dict(B=0), 1), (dict(mode=7), 1),
     (dict(o_dtype=5), 1),
     (dict(chunk=48), 2), (dict(chunk=128), 2), (dict(Dk=256, Dv=256), 2), (dict(Dv=256), 2),
-    (dict(H=6, Hqk=4), 1),
+    (dict(H=6, Hqk=4), 1), (dict(pro=16), 1),
     (dict(q=MIS), 3), (dict(h0=MIS), 3), (dict(hT=MIS), 3), (dict(ws=None), 4),
     (dict(wsb=16), 4), (dict(ws=A + 16), 3),
 ])
@@ -103,25 +105,25 @@ CU = 0x20000          # a 4-byte aligned fake device address of the offsets
 
 
 def _rec_v(L, q=A, k=A, v=A, g=A, beta=A, state=A, o=A, cu=CU, N=2, T=10, H=1, Hqk=None,
-           Dk=128, Dv=128, scale=1.0, mode=0, dtype=1, o_dtype=0):
+           Dk=128, Dv=128, scale=1.0, mode=0, dtype=1, o_dtype=0, pro=0):
     Hqk = H if Hqk is None else Hqk
     return L.kda_recurrent_varlen(q, k, v, g, beta, state, o, cu, N, T, H, Hqk, Dk, Dv, scale,
-                                  mode, dtype, o_dtype, None)
+                                  mode, dtype, o_dtype, pro, None)
 
 
 def _chunk_v(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, cu=CU, N=2, T=64, H=1,
              Hqk=None, Dk=128, Dv=128, chunk=64, scale=1.0, mode=0, dtype=1, o_dtype=0, ws=A,
-             wsb=None):
+             wsb=None, pro=0):
     Hqk = H if Hqk is None else Hqk
     if wsb is None:
         wsb = L.kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype)
     return L.kda_chunk_fwd_varlen(q, k, v, g, beta, h0, hT, o, cu, N, T, H, Hqk, Dk, Dv, chunk,
-                                  scale, mode, dtype, o_dtype, ws, wsb, None)
+                                  scale, mode, dtype, o_dtype, pro, ws, wsb, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(state=None), 1), (dict(cu=None), 1), (dict(N=-1), 1),
-    (dict(H=4, Hqk=8), 1),
+    (dict(H=4, Hqk=8), 1), (dict(pro=9), 1),
     (dict(T=-1), 1), (dict(H=0), 1), (dict(g=None, mode=1), 1), (dict(Dk=48), 2),
     (dict(cu=CU + 2), 3), (dict(state=MIS), 3), (dict(o=MIS), 3),
 ])
@@ -137,7 +139,7 @@ def test_recurrent_varlen_nothing_to_do(L):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(cu=None), 1), (dict(N=-1), 1), (dict(mode=9), 1),
-    (dict(H=3, Hqk=2), 1), (dict(chunk=8), 2), (dict(Dv=512), 2), (dict(cu=CU + 1), 3), (dict(h0=MIS), 3),
+    (dict(H=3, Hqk=2), 1), (dict(pro=32), 1), (dict(chunk=8), 2), (dict(Dv=512), 2), (dict(cu=CU + 1), 3), (dict(h0=MIS), 3),
     (dict(hT=MIS), 3), (dict(ws=None), 4), (dict(wsb=64), 4), (dict(ws=A + 16), 3),
 ])
 def test_chunk_varlen_validation(L, kw, code):
