@@ -238,6 +238,19 @@ __device__ __forceinline__ Frag<OT> select_frag(int hh, int lane) {
     for (int e = 0; e < 8; ++e) f.set(e, (8 * g + e == 16 * hh + r) ? 1.f : 0.f);
     return f;
 }
+// bf16: the single one (0x3f80) is placed into its 32-bit word directly
+template <>
+__device__ __forceinline__ Frag<bf16_t> select_frag<bf16_t>(int hh, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const int e = 16 * hh + r - 8 * g;                       // position of the one, if in [0, 8)
+    const uint32_t one = (unsigned)e < 8u ? (0x3f80u << (16 * (e & 1))) : 0u;
+    const int d = e >> 1;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 w = {d == 0 ? one : 0u, d == 1 ? one : 0u, d == 2 ? one : 0u, d == 3 ? one : 0u};
+    Frag<bf16_t> f;
+    f.v = __builtin_bit_cast(u16x8, w);
+    return f;
+}
 
 // PRO: the fused prologue is compiled in (its flags are then read from
 // `pro`); without it the prologue code is absent and `pro` is ignored.
@@ -410,7 +423,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         float pk = 0.f, pq = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const bool ok = tv && (ch + e < DK);
+            const bool ok = tv && (DK % 32 == 0 || ch + e < DK);   // (padded channels only when DK < 32)
             float gv = mode == KDA_GATE_CHANNEL ? (e < 4 ? cur.g0[e] : cur.g1[e - 4]) : cur.gt;
             if (PRO && (pro & KDA_GATE_LOGSIGMOID)) gv = log_sigmoid(gv);
             gl[e] = (ok && mode != KDA_GATE_NONE) ? gv * kLog2e : 0.f;   // log2 units
