@@ -20,6 +20,8 @@
 //   o    = H^T q~ = r + e * kq                      (no second pass needed)
 // The partial sums are reduced across the rows a wavefront holds with lane
 // shuffles, then across wavefronts through LDS.
+#include <atomic>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -37,7 +39,10 @@ struct RecShape {
     static_assert(NT % 64 == 0 && RPT >= 1 && RG * RPT == DK && CX <= 64, "shape");
 };
 
-template <int DK, int DV, typename IO, typename OUT>
+// MULTI: sequences of more than one token (the next token's inputs are
+// prefetched during the current one); without it every sequence has at most
+// one token (a decode step), and the state's rows are used as they arrive.
+template <int DK, int DV, typename IO, typename OUT, bool MULTI>
 __global__ void __launch_bounds__((RecShape<DK, DV>::NT))
 recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                  const float* __restrict__ g, const float* __restrict__ beta,
@@ -68,108 +73,147 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][11];
 
     float* st = state + (size_t)bh * DK * DV + c0;
-    // the first token's inputs, requested before the state so that they arrive first
     // (value head h reads query/key head h / (H / HQ): grouped value heads)
     const int hq = h / (H / HQ);
-    auto token_inputs = [&](size_t row) {
+    // The inputs of one token as this thread reads them (thread c < DK owns key
+    // channel c, thread j < DVT value column j; every thread reads beta).  The
+    // loads are unconditional, from clamped indices, so that no branch joins
+    // loaded registers; commit() moves them to LDS.  Token t+1's inputs are
+    // requested while token t is computed.
+    // (raw storage values: converted only in commit(), so that nothing waits
+    // for the loads before then)
+    struct TokIn { IO k, q, v; float g, b; };
+    const int ck = tid < DK ? tid : DK - 1, cv = tid < S::DVT ? tid : S::DVT - 1;
+    // gate address of a row: g[row][h][ck] (channel), g[row][h] (scalar); without
+    // a gate beta stands in (a valid address; the value is unused)
+    const float* gbase = mode == KDA_GATE_NONE ? beta : g;
+    const size_t gstride = mode == KDA_GATE_CHANNEL ? (size_t)H * DK : (size_t)H;
+    const size_t goff = mode == KDA_GATE_CHANNEL ? (size_t)h * DK + ck : (size_t)h;
+    auto fetch = [&](size_t row, TokIn& x) {
         const size_t tok = row * H + h, tkq = row * HQ + hq;
-        for (int c = tid; c < DK; c += S::NT) {
-            sk[c] = io<IO>::load(k + tkq * DK + c);
-            sq[c] = io<IO>::load(q + tkq * DK + c) * scale;
-            float a = 1.f;
-            if (mode != KDA_GATE_NONE) {
-                const float gv = mode == KDA_GATE_CHANNEL ? g[tok * DK + c] : g[tok];
-                // the retention alpha = exp(g), or sigmoid(a) from a pre-activation
-                a = (pro & KDA_GATE_LOGSIGMOID) ? 1.f / (1.f + expf(-gv)) : expf(gv);
-            }
-            sa[c] = a;
-        }
-        for (int j = tid; j < S::DVT; j += S::NT) sv[j] = io<IO>::load(v + tok * DV + c0 + j);
+        x.k = k[tkq * DK + ck];
+        x.q = q[tkq * DK + ck];
+        x.g = gbase[row * gstride + goff];
+        x.v = v[tok * DV + c0 + cv];
+        x.b = beta[tok];
     };
-    if (Tn > 0) token_inputs(tok0);
+    auto commit = [&](const TokIn& x) {
+        if (tid < DK) {
+            sk[tid] = io<IO>::load(&x.k);
+            sq[tid] = io<IO>::load(&x.q) * scale;
+            // the retention alpha = exp(g), or sigmoid(a) from a pre-activation
+            float a = 1.f;
+            if (mode != KDA_GATE_NONE)
+                a = (pro & KDA_GATE_LOGSIGMOID) ? 1.f / (1.f + expf(-x.g)) : expf(x.g);
+            sa[tid] = a;
+        }
+        if (tid < S::DVT) sv[tid] = io<IO>::load(&x.v);
+    };
+    // the first token's inputs, requested before the state so that they arrive first
+    TokIn cur;
+    if (Tn > 0) fetch(tok0, cur);
     f32x4 hr[S::RPT];
 #pragma unroll
     for (int i = 0; i < S::RPT; ++i)
         hr[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
 
-    for (int t = 0; t < Tn; ++t) {
-        const size_t tok = (tok0 + t) * H + h;
-        if (t > 0) token_inputs(tok0 + t);
-        __syncthreads();
-
-        f32x4 ak = zero4(), aq = zero4();
-        float kq = 0.f, kk = 0.f, qq = 0.f;
-#pragma unroll
-        for (int i = 0; i < S::RPT; ++i) {
-            const int r = rg + S::RG * i;
-            const float a = sa[r], kr = sk[r], qr = sq[r];
-            hr[i] *= a;
-            ak += hr[i] * kr;
-            aq += hr[i] * qr;
-            kq += kr * qr;
-            kk += kr * kr;
-            qq += qr * qr;
-        }
-        // reduce over the row groups held by this wavefront
-#pragma unroll
-        for (int off = S::CX; off < 64; off <<= 1) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                ak[u] += __shfl_xor(ak[u], off);
-                aq[u] += __shfl_xor(aq[u], off);
+    if (Tn > 0) commit(cur);
+    float bcur = cur.b;
+    // one token: decay, the two reductions over the rows, correction, rank-1
+    // write and read (inputs in LDS, beta in bcur)
+    auto token = [&](size_t tok) {
+            f32x4 ak = zero4(), aq = zero4();
+            float kq = 0.f, kk = 0.f, qq = 0.f;
+    #pragma unroll
+            for (int i = 0; i < S::RPT; ++i) {
+                const int r = rg + S::RG * i;
+                const float a = sa[r], kr = sk[r], qr = sq[r];
+                hr[i] *= a;
+                ak += hr[i] * kr;
+                aq += hr[i] * qr;
+                kq += kr * qr;
+                kk += kr * kr;
+                qq += qr * qr;
             }
-            kq += __shfl_xor(kq, off);
-            kk += __shfl_xor(kk, off);
-            qq += __shfl_xor(qq, off);
-        }
-        if constexpr (S::NW > 1) {
-            if (lane < S::CX) {
-#pragma unroll
+            // reduce over the row groups held by this wavefront
+    #pragma unroll
+            for (int off = S::CX; off < 64; off <<= 1) {
+    #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    red[wave][cx][u] = ak[u];
-                    red[wave][cx][4 + u] = aq[u];
+                    ak[u] += __shfl_xor(ak[u], off);
+                    aq[u] += __shfl_xor(aq[u], off);
                 }
-                red[wave][cx][8] = kq;
-                red[wave][cx][9] = kk;
-                red[wave][cx][10] = qq;
+                kq += __shfl_xor(kq, off);
+                kk += __shfl_xor(kk, off);
+                qq += __shfl_xor(qq, off);
             }
+            if constexpr (S::NW > 1) {
+                if (lane < S::CX) {
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        red[wave][cx][u] = ak[u];
+                        red[wave][cx][4 + u] = aq[u];
+                    }
+                    red[wave][cx][8] = kq;
+                    red[wave][cx][9] = kk;
+                    red[wave][cx][10] = qq;
+                }
+                __syncthreads();
+                ak = zero4(); aq = zero4(); kq = 0.f; kk = 0.f; qq = 0.f;
+    #pragma unroll
+                for (int w = 0; w < S::NW; ++w) {
+    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        ak[u] += red[w][cx][u];
+                        aq[u] += red[w][cx][4 + u];
+                    }
+                    kq += red[w][cx][8];
+                    kk += red[w][cx][9];
+                    qq += red[w][cx][10];
+                }
+            }
+            // L2-normalised q and k: every product with them is linear, so the
+            // norms are applied to the reduced sums (sq holds scale * q)
+            float fk = 1.f, fq = 1.f;
+            if (pro & KDA_NORMALIZE_QK) {
+                fk = rsqrtf(kk + kNormEps);
+                fq = scale != 0.f ? rsqrtf(qq / (scale * scale) + kNormEps) : 1.f;
+                ak *= fk;
+                aq *= fq;
+                kq *= fk * fq;
+            }
+            float bt = bcur;
+            if (pro & KDA_BETA_SIGMOID) bt = 1.f / (1.f + expf(-bt));
+            f32x4 e;
+    #pragma unroll
+            for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
+            const f32x4 ek = e * fk;
+    #pragma unroll
+            for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * ek;
+            if (rg == 0) {
+                Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
+            }
+    };
+    if constexpr (!MULTI) {
+        // a decode step: the state's rows are used as they arrive
+        if (Tn == 1) {
             __syncthreads();
-            ak = zero4(); aq = zero4(); kq = 0.f; kk = 0.f; qq = 0.f;
-#pragma unroll
-            for (int w = 0; w < S::NW; ++w) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    ak[u] += red[w][cx][u];
-                    aq[u] += red[w][cx][4 + u];
-                }
-                kq += red[w][cx][8];
-                kk += red[w][cx][9];
-                qq += red[w][cx][10];
-            }
+            token(tok0 * H + h);
         }
-        // L2-normalised q and k: every product with them is linear, so the
-        // norms are applied to the reduced sums (sq holds scale * q)
-        float fk = 1.f, fq = 1.f;
-        if (pro & KDA_NORMALIZE_QK) {
-            fk = rsqrtf(kk + kNormEps);
-            fq = scale != 0.f ? rsqrtf(qq / (scale * scale) + kNormEps) : 1.f;
-            ak *= fk;
-            aq *= fq;
-            kq *= fk * fq;
+    } else {
+        for (int t = 0; t < Tn; ++t) {
+            __syncthreads();   // token t's inputs are in LDS
+            // token t+1's inputs (the last token's once more at the end),
+            // requested unconditionally so that every wait for the state's
+            // rows in the first step counts them as younger loads
+            TokIn nxt;
+            fetch(tok0 + min(t + 1, Tn - 1), nxt);
+            token((tok0 + t) * H + h);
+            __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
+            commit(nxt);
+            bcur = nxt.b;
         }
-        float bt = beta[tok];
-        if (pro & KDA_BETA_SIGMOID) bt = 1.f / (1.f + expf(-bt));
-        f32x4 e;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
-        const f32x4 ek = e * fk;
-#pragma unroll
-        for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * ek;
-        if (rg == 0) {
-            Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
-        }
-        __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
     }
 #pragma unroll
     for (int i = 0; i < S::RPT; ++i)
@@ -178,19 +222,56 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
 }
 
 
-template <int DK, int DV, typename IO>
-static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
+// Dynamic LDS the decode launch reserves so that at most two of its
+// workgroups share a compute unit: with three (the registers would allow it)
+// the state stream measured 7% slower (190 us against 177 us for the B256 H32
+// d128 step).  Two fit when each workgroup takes 2/5 of the unit's LDS.
+static size_t decode_lds_reserve(size_t static_bytes)
+{
+    static std::atomic<long long> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    long long per_cu = cache[slot].load(std::memory_order_relaxed);
+    if (per_cu <= 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            v <= 0)
+            v = 65536;
+        per_cu = v;
+        cache[slot].store(per_cu, std::memory_order_relaxed);
+    }
+    const size_t want = (size_t)per_cu * 2 / 5;
+    return want > static_bytes ? want - static_bytes : 0;
+}
+
+template <int DK, int DV, typename IO, bool MULTI>
+static hipError_t launch_rec2(const RecArgs& a, hipStream_t s)
 {
     using S = RecShape<DK, DV>;
+    size_t dyn = 0;
+    if constexpr (!MULTI) {
+        // the kernel's own LDS: sk, sq, sa, sv and the reduction array
+        const size_t static_bytes = (3 * DK + S::DVT) * 4 + (S::NW > 1 ? S::NW : 1) * S::CX * 11 * 4;
+        dyn = decode_lds_reserve(static_bytes);
+    }
     if (a.o_dtype == KDA_F32)
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, float, MULTI>), dim3(a.B * a.H * S::NCT), dim3(S::NT), dyn, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
                            (float*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu, a.prologue);
     else
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t>), dim3(a.B * a.H * S::NCT), dim3(S::NT), 0, s,
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, IO, bf16_t, MULTI>), dim3(a.B * a.H * S::NCT), dim3(S::NT), dyn, s,
                            (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.state,
                            (bf16_t*)a.o, a.T, a.H, a.Hq, a.scale, (int)a.mode, a.cu, a.prologue);
     return hipGetLastError();
+}
+
+template <int DK, int DV, typename IO>
+static hipError_t launch_rec(const RecArgs& a, hipStream_t s)
+{
+    // one token per sequence (a dense T = 1 call): the decode kernel
+    if (a.cu == nullptr && a.T == 1) return launch_rec2<DK, DV, IO, false>(a, s);
+    return launch_rec2<DK, DV, IO, true>(a, s);
 }
 
 template <int DK, typename IO>
