@@ -1,4 +1,5 @@
-"""ctypes wrapper of oracle R (``kda_recurrence.c``).
+"""ctypes wrapper of oracle R (``kda_recurrence.c``) and of its gradient
+(``kda_backward.c``).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
@@ -18,6 +19,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_recurrence.c")
+_SRC_BWD = os.path.join(_HERE, "kda_backward.c")
 _BUILD = os.path.join(_HERE, "_build")
 _MODES = {"channel": 0, "scalar": 1, "none": 2}
 
@@ -34,12 +36,13 @@ def build_oracle_library(out_path: Optional[str] = None, mutant: int = 0,
         name = "libkda_oracle.so" if mutant == 0 else f"libkda_oracle_m{mutant}.so"
         out_path = os.path.join(_BUILD, name)
     if not force and os.path.exists(out_path) and \
-            os.path.getmtime(out_path) >= os.path.getmtime(_SRC):
+            os.path.getmtime(out_path) >= max(os.path.getmtime(_SRC),
+                                              os.path.getmtime(_SRC_BWD)):
         return out_path
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     tmp = out_path + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-           f"-DKDA_MUTANT={int(mutant)}", _SRC, "-o", tmp, "-lm"]
+           f"-DKDA_MUTANT={int(mutant)}", _SRC, _SRC_BWD, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out_path)
     return out_path
@@ -55,6 +58,9 @@ def _load(mutant: int = 0):
     lib.kda_oracle_recurrent.argtypes = [dp] * 8 + [ctypes.c_long] * 5 + \
         [ctypes.c_double, ctypes.c_int, ctypes.c_int]
     lib.kda_oracle_recurrent.restype = ctypes.c_int
+    lib.kda_oracle_recurrent_bwd.argtypes = [dp] * 14 + [ctypes.c_long] * 5 + \
+        [ctypes.c_double, ctypes.c_int, ctypes.c_int]
+    lib.kda_oracle_recurrent_bwd.restype = ctypes.c_int
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     _libs[mutant] = lib
     return lib
@@ -112,3 +118,48 @@ def recurrent(q, k, v, g, beta, h0=None, *, scale: Optional[float] = None,
     if rc != 0:
         raise RuntimeError(f"oracle R failed with code {rc}")
     return o, hT
+
+
+def recurrent_bwd(q, k, v, g, beta, h0, do, dhT=None, *, scale: Optional[float] = None,
+                  mode: str = "channel", threads: int = 0, mutant: int = 0):
+    """Gradients of oracle R (``kda_backward.c``).
+
+    Inputs as for :func:`recurrent`, plus ``do`` = dL/do [B,T,H,Dv] and
+    ``dhT`` = dL/dH_T [B,H,Dk,Dv] or None (zero).  Returns a dict of float64
+    arrays: dq, dk [B,T,H,Dk]; dv [B,T,H,Dv]; dg (shape of g, None in the
+    ungated mode); dbeta [B,T,H]; dh0 [B,H,Dk,Dv] (the gradient of the
+    initial state, also when ``h0`` is None, i.e. zero).
+    """
+    q, k, v, beta = _f64(q), _f64(k), _f64(v), _f64(beta)
+    g, h0, do, dhT = _f64(g), _f64(h0), _f64(do), _f64(dhT)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and v.shape == (B, T, H, Dv)
+    assert do.shape == (B, T, H, Dv) and beta.shape == (B, T, H)
+    if mode == "channel":
+        assert g is not None and g.shape == (B, T, H, Dk)
+    elif mode == "scalar":
+        assert g is not None and g.shape == (B, T, H)
+    elif mode == "none":
+        g = None
+    else:
+        raise ValueError(mode)
+    for x in (h0, dhT):
+        if x is not None:
+            assert x.shape == (B, H, Dk, Dv)
+    if scale is None:
+        scale = Dk ** -0.5
+    out = {
+        "dq": np.zeros((B, T, H, Dk)), "dk": np.zeros((B, T, H, Dk)),
+        "dv": np.zeros((B, T, H, Dv)), "dbeta": np.zeros((B, T, H)),
+        "dg": None if g is None else np.zeros(g.shape),
+        "dh0": np.zeros((B, H, Dk, Dv)),
+    }
+    rc = _load(mutant).kda_oracle_recurrent_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(do), _ptr(dhT),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+        _ptr(out["dbeta"]), _ptr(out["dh0"]),
+        B, T, H, Dk, Dv, float(scale), _MODES[mode], int(threads))
+    if rc != 0:
+        raise RuntimeError(f"oracle R-bwd failed with code {rc}")
+    return out
