@@ -16,6 +16,9 @@ Entry points (same names as the C ABI):
                        final_state=None, o=None, chunk=64, scale=None, mode=None,
                        workspace=None)
   kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, mode, dtype)
+  kda_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
+                chunk=64, scale=None, mode=None, workspace=None, out=None)
+  kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype)
 
 Every compute call takes ``prologue``, a bitwise OR of NORMALIZE_QK,
 BETA_SIGMOID and GATE_LOGSIGMOID (0: inputs used as given).
@@ -74,6 +77,11 @@ def lib():
     L.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, vp, i, i, i, i, i, i, i, f, i,
                                        i, i, i, vp, sz, vp]
     L.kda_chunk_fwd_varlen.restype = i
+    L.kda_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
+    L.kda_chunk_bwd_workspace_size.restype = sz
+    L.kda_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
+                                i, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    L.kda_chunk_bwd.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i
@@ -323,3 +331,83 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd_varlen")
     return o, final_state
+
+
+# ---------------------------------------------------------------------------
+# gradients of the chunkwise form
+def kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype) -> int:
+    if isinstance(mode, str):
+        mode = _MODE_NAMES[mode]
+    return int(lib().kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, int(mode),
+                                                  int(dtype)))
+
+
+def kda_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
+                  chunk: int = 64, scale: Optional[float] = None, mode=None, workspace=None,
+                  out=None, want_d_initial_state: bool = True, grad_dtype=None):
+    """Gradients of :func:`kda_chunk_fwd` for the same inputs.
+
+    ``d_o`` [B,T,H,Dv] has the dtype of q; ``d_final_state`` float32
+    [B,H,Dk,Dv] or None (zero).  Returns a dict with dq, dk (shape of q),
+    dv (shape of v), all of ``grad_dtype`` (default the dtype of q), dg
+    (shape of g, None in the ungated mode), dbeta [B,T,H] and
+    d_initial_state [B,H,Dk,Dv] (None when ``want_d_initial_state`` is
+    false).  ``out`` may hold preallocated tensors under those keys (their
+    dtype then sets the gradient storage type).
+    """
+    torch = _torch()
+    B, T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
+    m = _mode_of(g, mode)
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
+    _check_dev("d_o", d_o, q.dtype, v.shape)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (B, T, H))
+    _check_dev("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
+    _check_dev("d_final_state", d_final_state, torch.float32, (B, H, Dk, Dv))
+    out = dict(out or {})
+    dev = q.device
+    if out.get("dq") is not None:
+        grad_dtype = out["dq"].dtype
+    gdt = grad_dtype or q.dtype
+    if out.get("dq") is None:
+        out["dq"] = torch.empty(q.shape, dtype=gdt, device=dev)
+    if out.get("dk") is None:
+        out["dk"] = torch.empty(k.shape, dtype=gdt, device=dev)
+    if out.get("dv") is None:
+        out["dv"] = torch.empty(v.shape, dtype=gdt, device=dev)
+    if m == GATE_NONE:
+        out["dg"] = None
+    elif out.get("dg") is None:
+        out["dg"] = torch.empty_like(g)
+    if out.get("dbeta") is None:
+        out["dbeta"] = torch.empty_like(beta)
+    if want_d_initial_state and out.get("d_initial_state") is None:
+        out["d_initial_state"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    if not want_d_initial_state:
+        out["d_initial_state"] = None
+    _check_dev("dq", out["dq"], gdt, q.shape)
+    _check_dev("dk", out["dk"], gdt, q.shape)
+    _check_dev("dv", out["dv"], gdt, v.shape)
+    _check_dev("dg", out["dg"], torch.float32, None if g is None else g.shape)
+    _check_dev("dbeta", out["dbeta"], torch.float32, (B, T, H))
+    _check_dev("d_initial_state", out["d_initial_state"], torch.float32, (B, H, Dk, Dv))
+    dt = _dtype_code(q)
+    need = kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, m, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                             _ptr(d_o), _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]),
+                             _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                             _ptr(out["d_initial_state"]), B, T, H, Hqk, Dk, Dv, int(chunk),
+                             float(scale), m, dt, _dtype_code(out["dq"]), _ptr(workspace),
+                             workspace.numel(), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd")
+    return out

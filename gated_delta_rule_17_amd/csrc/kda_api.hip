@@ -53,7 +53,7 @@ const char* kda_status_string(kda_status s)
     return "KDA_ERROR_UNKNOWN";
 }
 
-int kda_version(void) { return 10100; }
+int kda_version(void) { return 10200; }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state, void* o, int B, int T, int H,
@@ -166,6 +166,54 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk, Hqk,
                      scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N, prologue};
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                                    kda_gate_mode mode, kda_dtype dtype)
+{
+    (void)mode;
+    if (B < 1 || H < 1 || T <= 0) return 0;
+    if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return kda::chunk_bwd_workspace_bytes(B, T, H, Hqk, Dk, Dv, chunk);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* d_o,
+                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, float* d_initial_state, int B, int T, int H, int Hqk,
+                         int Dk, int Dv, int chunk, float scale, kda_gate_mode mode,
+                         kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, d_o, B, T, H, Hqk, Dk, Dv, mode, dtype, grad_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
+    if (nrec > 1073741824.0 || (double)B * H * 2.0 > 65535.0 * 1024.0)
+        return KDA_ERROR_INVALID_VALUE;
+    if (T > 0) {
+        if (!dq || !dk || !dv || !dbeta) return KDA_ERROR_INVALID_VALUE;
+        if (mode != KDA_GATE_NONE && !dg) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbeta))
+            return KDA_ERROR_MISALIGNED;
+        if (dg && !aligned16(dg)) return KDA_ERROR_MISALIGNED;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
+        (d_initial_state && !aligned16(d_initial_state)))
+        return KDA_ERROR_MISALIGNED;
+    const size_t need = kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype);
+    if (T > 0) {
+        if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
+    }
+    if (T == 0 && !d_initial_state) return KDA_SUCCESS;
+    kda::ChunkBwdArgs a{q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                        d_initial_state, B, T, H, Hqk, Dk, Dv, chunk, scale, mode, dtype,
+                        grad_dtype, workspace, workspace_bytes};
+    hipError_t e = kda::launch_chunk_bwd(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
 

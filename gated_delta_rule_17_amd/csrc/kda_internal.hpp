@@ -49,11 +49,29 @@ struct ChunkArgs {
     const void* stab = nullptr;
 };
 
+struct ChunkBwdArgs {
+    const void* q; const void* k; const void* v;
+    const float* g; const float* beta; const float* h0;
+    const void* dO; const float* dhT;
+    void* dq; void* dk; void* dv;
+    float* dg; float* dbeta; float* dh0;
+    int B, T, H, Hq, Dk, Dv, chunk;
+    float scale;
+    kda_gate_mode mode;
+    kda_dtype dtype;      // q, k, v, dO
+    kda_dtype grad_dtype; // dq, dk, dv
+    void* ws; size_t ws_bytes;
+};
+
 hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);
 
 // Workspace layout of the chunk path (bytes); 0 if unsupported.
 size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
 size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
+
+// Gradient of the chunk path: workspace bytes and launch.
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Hq, int Dk, int Dv, int chunk);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
 
 }  // namespace kda

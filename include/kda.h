@@ -243,6 +243,66 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v,
                                 kda_dtype o_dtype, int prologue, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * Gradients (training backward)
+ * -----------------------------
+ * The pages train the method with the chunkwise algorithm (F29 course
+ * outline, "Paper: Gated DeltaNet -> Kimi Delta Attention"; GeekNews #31925,
+ * section "Fused recurrent kernel for decode": the chunkwise form serves
+ * training and prefill).  kda_chunk_bwd returns the gradients of a scalar
+ * loss with respect to every input of kda_chunk_fwd, given the gradients of
+ * that loss with respect to its outputs, i.e. reverse mode through the same
+ * recurrence (results equal, up to rounding, the gradient of the token loop
+ * of kda_recurrent_step).  It recomputes what it needs from the inputs (no
+ * tensors are saved by the forward call).
+ */
+
+/*
+ * kda_chunk_bwd_workspace_size -- bytes of device workspace kda_chunk_bwd
+ * needs (0 when T == 0 or the arguments are unsupported).  About
+ * 4 (2 Dk Dv + 4 chunk Dk + 3 chunk Dv + 3 chunk^2) bytes per (b, h, chunk),
+ * plus 8 B T H Dk bytes when Hqk < H.
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                                    kda_gate_mode mode, kda_dtype dtype);
+
+/*
+ * kda_chunk_bwd -- gradients of the chunkwise form.
+ *
+ *   q, k, v, g, beta, initial_state   the inputs of the forward call (same
+ *                  layouts; initial_state NULL = zero state)
+ *   d_o            [B,T,H,Dv] dtype      dL/do, in
+ *   d_final_state  [B,H,Dk,Dv] float     dL/d(final state), in, or NULL (zero)
+ *   dq, dk         [B,T,Hqk,Dk] grad_dtype  out (grouped value heads: the sum
+ *                  over the value heads that read the query/key head)
+ *   dv             [B,T,H,Dv] grad_dtype    out
+ *   dg             shape of g, float     out (NULL iff mode == KDA_GATE_NONE;
+ *                  scalar mode: one value per token and head)
+ *   dbeta          [B,T,H] float         out
+ *   d_initial_state [B,H,Dk,Dv] float    out, or NULL (not stored); with
+ *                  T = 0 it receives d_final_state (zero if NULL)
+ *   chunk, scale, mode   as for kda_chunk_fwd (chunk 16, 32 or 64)
+ *   dtype          storage type of q, k, v and d_o
+ *   grad_dtype     storage type of dq, dk and dv (either one, independently;
+ *                  a bf16 gradient is the float32 result rounded to
+ *                  nearest-even at the final store)
+ *   workspace      at least kda_chunk_bwd_workspace_size(...) bytes,
+ *                  256-byte aligned, caller-owned scratch
+ *
+ * Outputs must not alias inputs or each other.  The fused prologue and
+ * packed batches are forward-only: pass the transformed inputs.  Within a
+ * chunk the kernels split decays at 16-token boundaries, so results stay
+ * finite while no key channel's log gates sum below about -80 over 16
+ * consecutive tokens (a per-token g above about -5).
+ */
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, const void* d_o,
+                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, float* d_initial_state, int B, int T, int H, int Hqk,
+                         int Dk, int Dv, int chunk, float scale, kda_gate_mode mode,
+                         kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* kda_status_string(kda_status s);
 

@@ -187,6 +187,30 @@ def make_inputs(B, T, H, Dk, Dv, *, mode=CHANNEL, dtype="bf16", chunk=64,
 
 
 # --------------------------------------------------------------------------
+# gradients of a loss with respect to the forward outputs (backward inputs)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Cotangents:
+    """Seeded gradients dL/do [B,T,H,Dv] (bf16-rounded for a bf16 workload,
+    like o) and dL/dH_T [B,H,Dk,Dv] float32 or None (zero)."""
+    do: np.ndarray
+    dhT: Optional[np.ndarray]
+
+
+def make_cotangents(w: Workload, *, seed: int = 0, do_std: float = 1.0,
+                    dhT_std: float = 0.0) -> Cotangents:
+    """Draw dL/do ~ N(0, do_std^2) and dL/dH_T ~ N(0, dhT_std^2) (None when
+    dhT_std is 0) from their own seed sequence, independent of the inputs."""
+    rd, rh = [np.random.Generator(np.random.PCG64(s))
+              for s in np.random.SeedSequence([seed, 0xD0]).spawn(2)]
+    do = _normal(rd, (w.B, w.T, w.H, w.Dv), std=do_std)
+    if w.dtype == "bf16":
+        do = bf16_round(do)
+    dhT = _normal(rh, (w.B, w.H, w.Dk, w.Dv), std=dhT_std) if dhT_std > 0.0 else None
+    return Cotangents(do=np.ascontiguousarray(do), dhT=dhT)
+
+
+# --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
 CONFIGS = {

@@ -21,7 +21,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"kda_recurrent_step", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
                           "kda_recurrent_varlen", "kda_chunk_fwd_varlen",
                           "kda_chunk_fwd_varlen_workspace_size", "kda_status_string",
-                          "kda_version"}
+                          "kda_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -157,3 +157,53 @@ def test_chunk_varlen_workspace_size(L):
     assert f(3, 64, 1, 128, 128, 64, 0, 1) >= 4 * dense
     # T = 0 still needs the tables (the final states are copied)
     assert f(2, 0, 1, 128, 128, 64, 0, 1) > 0
+
+
+# ---- gradients of the chunk path (host validation only)
+def _bwd(L, q=A, k=A, v=A, g=A, beta=A, h0=None, do=A, dhT=None, dq=A, dk=A, dv=A, dg=A,
+         dbeta=A, dh0=None, B=1, T=64, H=1, Hqk=None, Dk=128, Dv=128, chunk=64, scale=1.0,
+         mode=0, dtype=1, gdtype=0, ws=A, wsb=None):
+    Hqk = H if Hqk is None else Hqk
+    if wsb is None:
+        wsb = L.kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype)
+    return L.kda_chunk_bwd(q, k, v, g, beta, h0, do, dhT, dq, dk, dv, dg, dbeta, dh0, B, T, H,
+                           Hqk, Dk, Dv, chunk, scale, mode, dtype, gdtype, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(beta=None), 1),
+    (dict(do=None), 1), (dict(dq=None), 1), (dict(dk=None), 1), (dict(dv=None), 1),
+    (dict(dbeta=None), 1), (dict(dg=None), 1), (dict(dg=None, mode=1), 1),
+    (dict(g=None, mode=0), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
+    (dict(mode=3), 1), (dict(dtype=2), 1), (dict(gdtype=2), 1), (dict(H=6, Hqk=4), 1),
+    (dict(Hqk=0), 1),
+    (dict(chunk=48), 2), (dict(chunk=128), 2), (dict(Dk=256), 2), (dict(Dv=8), 2),
+    (dict(q=MIS), 3), (dict(do=MIS), 3), (dict(dq=MIS), 3), (dict(dk=MIS), 3), (dict(dv=MIS), 3),
+    (dict(dg=MIS), 3), (dict(dbeta=MIS), 3), (dict(h0=MIS), 3), (dict(dhT=MIS), 3),
+    (dict(dh0=MIS), 3), (dict(ws=None), 4), (dict(wsb=64), 4), (dict(ws=A + 16), 3),
+])
+def test_chunk_bwd_validation(L, kw, code):
+    assert _bwd(L, **kw) == code
+
+
+def test_chunk_bwd_none_mode_accepts_null_gates(L):
+    # only the workspace check remains to fail: g = dg = NULL passed validation
+    assert _bwd(L, g=None, dg=None, mode=2, ws=None) == 4
+
+
+def test_chunk_bwd_zero_length_without_state_gradient_is_a_no_op(L):
+    assert _bwd(L, T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None,
+                dv=None, dg=None, dbeta=None, ws=None) == 0
+
+
+def test_chunk_bwd_workspace_size(L):
+    f = L.kda_chunk_bwd_workspace_size
+    assert f(1, 0, 1, 1, 128, 128, 64, 0, 1) == 0
+    assert f(1, 64, 1, 1, 128, 128, 48, 0, 1) == 0
+    assert f(1, 64, 4, 3, 128, 128, 64, 0, 1) == 0
+    one = f(1, 64, 1, 1, 128, 128, 64, 0, 1)
+    # per chunk: 2 Dk Dv + 4 C Dk + 3 C Dv + 3 C^2 floats (each record 256-byte aligned)
+    assert one >= 4 * (2 * 128 * 128 + 7 * 64 * 128 + 3 * 64 * 64)
+    assert f(1, 65, 1, 1, 128, 128, 64, 0, 1) >= 2 * one - 16 * 256
+    # grouped heads add float partials of dq and dk per value head
+    assert f(1, 64, 4, 2, 128, 128, 64, 0, 1) >= 4 * one + 2 * 4 * 64 * 4 * 128 - 16 * 256

@@ -1,0 +1,180 @@
+"""Parity of the chunkwise gradient (kda_chunk_bwd) with the gradient oracle
+(GPU).
+
+The reference is oracle R-bwd, reverse mode through the token recurrence in
+double precision, pinned to finite differences of the forward oracle
+(tests/test_oracle_backward.py).  Every gradient (dq, dk, dv, dg, dbeta and
+the initial-state gradient) is compared element by element with the
+max|delta| / rms measure of the forward tests, at the forward tolerances:
+1e-4 for float32 inputs, 2e-2 for bf16 inputs.
+"""
+import numpy as np
+import pytest
+
+import gated_delta_rule_17_amd as K
+import oracle
+from kda_workloads import make_config, make_cotangents, make_inputs, slice_heads
+from tests.conftest import rel_err
+from tests.gpu_util import TOL, say
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _t(x, dt=None):
+    import torch
+    if x is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dt or torch.float32)
+
+
+def _run(w, cot, chunk, q=None, k=None, grad="f32"):
+    """Run the gradient path; parity is measured on float32 gradients (a
+    bf16 gradient is that float32 result rounded, see
+    test_bf16_gradients_are_the_rounded_float32_ones)."""
+    import torch
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gd = torch.bfloat16 if grad == "bf16" else torch.float32
+    q = w.q if q is None else q
+    k = w.k if k is None else k
+    out = K.kda_chunk_bwd(_t(q, dt), _t(k, dt), _t(w.v, dt), _t(w.g), _t(w.beta), _t(cot.do, dt),
+                          initial_state=_t(w.h0), d_final_state=_t(cot.dhT), chunk=chunk,
+                          scale=w.scale, mode=w.mode, grad_dtype=gd)
+    torch.cuda.synchronize()
+    res = {}
+    for name, key in zip(NAMES, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")):
+        x = out[key]
+        res[name] = None if x is None else x.float().cpu().numpy()
+    return res
+
+
+def _compare(label, got, ref, tol):
+    errs = {}
+    for name in NAMES:
+        if ref[name] is None:
+            assert got[name] is None, name
+            continue
+        assert np.isfinite(got[name]).all(), (label, name)
+        errs[name] = rel_err(got[name], ref[name])
+    print(f"[parity] bwd {label} " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()),
+          flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, (label, bad)
+
+
+def _oracle(w, cot, q=None, k=None):
+    q = w.q if q is None else q
+    k = w.k if k is None else k
+    if q.shape[2] != w.H:
+        return oracle.recurrent_grouped_bwd(q, k, w.v, w.g, w.beta, w.h0, cot.do, cot.dhT,
+                                            scale=w.scale, mode=w.mode)
+    return oracle.recurrent_bwd(q, k, w.v, w.g, w.beta, w.h0, cot.do, cot.dhT, scale=w.scale,
+                                mode=w.mode)
+
+
+@pytest.mark.parametrize("mode", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("chunk,T", [(16, 64), (32, 100), (64, 200), (64, 64)])
+def test_bwd_f32_small(mode, chunk, T):
+    w = make_inputs(2, T, 2, 32, 32, mode=mode, dtype="f32", seed=T + chunk, h0_std=0.2,
+                    gate_law="softplus" if mode != "none" else "zero")
+    cot = make_cotangents(w, seed=1, dhT_std=0.3)
+    say("bwd f32", mode, chunk, T)
+    _compare(f"f32 {mode} C{chunk} T{T}", _run(w, cot, chunk), _oracle(w, cot), TOL["f32"])
+
+
+@pytest.mark.parametrize("Dk,Dv", [(16, 16), (16, 128), (128, 16), (64, 32), (128, 128)])
+def test_bwd_f32_dims(Dk, Dv):
+    w = make_inputs(1, 150, 2, Dk, Dv, mode="channel", dtype="f32", seed=Dk + 3 * Dv,
+                    h0_std=0.2)
+    cot = make_cotangents(w, seed=2, dhT_std=0.3)
+    say("bwd f32 dims", Dk, Dv)
+    _compare(f"f32 Dk{Dk} Dv{Dv}", _run(w, cot, 64), _oracle(w, cot), TOL["f32"])
+
+
+def test_bwd_without_initial_state_or_final_gradient():
+    w = make_inputs(1, 90, 3, 64, 64, mode="channel", dtype="f32", seed=9, h0_std=0.0)
+    cot = make_cotangents(w, seed=3)
+    assert w.h0 is None and cot.dhT is None
+    say("bwd zero state")
+    _compare("f32 zero state", _run(w, cot, 32), _oracle(w, cot), TOL["f32"])
+
+
+@pytest.mark.parametrize("Hqk,G", [(2, 2), (1, 4)])
+def test_bwd_grouped_heads(Hqk, G):
+    w = make_inputs(1, 130, Hqk * G, 64, 32, mode="channel", dtype="f32", seed=40 + G,
+                    h0_std=0.1)
+    q = np.ascontiguousarray(w.q[:, :, ::G])
+    k = np.ascontiguousarray(w.k[:, :, ::G])
+    cot = make_cotangents(w, seed=4, dhT_std=0.2)
+    say("bwd grouped", Hqk, G)
+    _compare(f"grouped Hqk{Hqk} G{G}", _run(w, cot, 64, q, k), _oracle(w, cot, q, k), TOL["f32"])
+
+
+def test_bwd_zero_length_copies_the_final_state_gradient():
+    import torch
+    w = make_inputs(1, 0, 2, 32, 32, dtype="f32", seed=5)
+    cot = make_cotangents(w, seed=5, dhT_std=1.0)
+    say("bwd T=0")
+    got = _run(w, cot, 64)
+    np.testing.assert_array_equal(got["dh0"], cot.dhT)
+    assert got["dq"].size == 0
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", ["channel", "scalar", "none"])
+def test_bwd_bf16_mid(mode):
+    w = make_inputs(1, 512, 2, 128, 128, mode=mode, dtype="bf16", seed=77, h0_std=0.01,
+                    gate_law="softplus" if mode != "none" else "zero", gate_shift=2.0)
+    cot = make_cotangents(w, seed=6, dhT_std=0.1)
+    say("bwd bf16", mode)
+    _compare(f"bf16 {mode} T512", _run(w, cot, 64), _oracle(w, cot), TOL["bf16"])
+
+
+@pytest.mark.parametrize("Hqk,G", [(4, 1), (2, 2)])
+def test_bf16_gradients_are_the_rounded_float32_ones(Hqk, G):
+    from kda_workloads import bf16_round
+    w = make_inputs(1, 200, Hqk * G, 64, 64, mode="channel", dtype="bf16", seed=8, h0_std=0.01)
+    q = np.ascontiguousarray(w.q[:, :, ::G])
+    k = np.ascontiguousarray(w.k[:, :, ::G])
+    cot = make_cotangents(w, seed=8, dhT_std=0.1)
+    say("bwd bf16 gradient storage", Hqk, G)
+    g32 = _run(w, cot, 64, q, k, grad="f32")
+    g16 = _run(w, cot, 64, q, k, grad="bf16")
+    for name in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(g16[name], bf16_round(g32[name].astype(np.float32)))
+    for name in ("dg", "dbeta", "dh0"):
+        np.testing.assert_array_equal(g16[name], g32[name])
+
+
+def test_bwd_strong_gates_within_range():
+    # per-token log gates down to -4.5 on half the channels: 16-token decays
+    # reach e^-70, inside the range the kernels support
+    w = make_inputs(1, 192, 2, 64, 64, mode="channel", dtype="f32", seed=12, h0_std=0.1)
+    g = w.g.copy()
+    g[..., ::2] = -4.5 * np.random.default_rng(0).uniform(0.5, 1.0, g[..., ::2].shape)
+    w.g = g.astype(np.float32)
+    cot = make_cotangents(w, seed=7, dhT_std=0.2)
+    say("bwd strong gates")
+    _compare("f32 strong gates", _run(w, cot, 64), _oracle(w, cot), TOL["f32"])
+
+
+def test_bwd_full_size_prefill_sampled_heads():
+    """The prefill workload at full size (B1 H16 T4096 d128, bf16), in the
+    launch configuration the benchmark times; the oracle runs on three of
+    the sixteen heads."""
+    w = make_config("prefill_h16_t4096")
+    cot = make_cotangents(w, seed=0, dhT_std=0.01)
+    say("bwd full size prefill")
+    got = _run(w, cot, 64)
+    heads = [0, 7, 15]
+    sl = slice_heads(w, [(0, h) for h in heads])
+    cat = lambda i: None if sl[0][i] is None else np.concatenate([x[i] for x in sl], axis=2)
+    q, k, v, g, beta, h0 = (cat(i) for i in range(6))
+    h0 = None if h0 is None else np.concatenate([x[5] for x in sl], axis=1)
+    do = np.ascontiguousarray(cot.do[:, :, heads])
+    dhT = np.ascontiguousarray(cot.dhT[:, heads])
+    ref = oracle.recurrent_bwd(q, k, v, g, beta, h0, do, dhT, scale=w.scale, mode=w.mode)
+    sub = {n: None if got[n] is None else
+           (got[n][:, heads] if n == "dh0" else got[n][:, :, heads]) for n in NAMES}
+    _compare("full size prefill heads 0,7,15", sub, ref, TOL["bf16"])

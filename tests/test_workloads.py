@@ -55,3 +55,16 @@ def test_bf16_workloads_hold_exact_bf16_values():
         assert np.array_equal(bf16_round(x), x)
     assert set(CONFIGS) >= {"tiny_f32", "prefill_h16_t4096", "decode_b256_h32",
                             "train_b8_h32_t8192", "long_t65536_channel"}
+
+
+def test_cotangents_shapes_rounding_and_independence():
+    from kda_workloads import make_cotangents, bf16_round
+    w = make_inputs(2, 5, 3, 16, 32, dtype="bf16", seed=1)
+    c = make_cotangents(w, seed=4, dhT_std=0.5)
+    assert c.do.shape == (2, 5, 3, 32) and c.dhT.shape == (2, 3, 16, 32)
+    np.testing.assert_array_equal(c.do, bf16_round(c.do))
+    assert abs(float(c.dhT.std()) - 0.5) < 0.1
+    c2 = make_cotangents(w, seed=4, dhT_std=0.5)
+    np.testing.assert_array_equal(c.do, c2.do)
+    assert make_cotangents(w, seed=5).dhT is None
+    assert not np.array_equal(make_cotangents(w, seed=5).do, c.do)
