@@ -25,7 +25,10 @@ profiles/traffic.json and is null when the kernel source changed since.
 points on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
 d=128, bf16, in both forms.  ``grouped_heads`` (4 query/key heads for the 16
 value heads) and ``mixed_dims`` (d_k 64, d_v 128) time kda_chunk_fwd on the
-prefill shape B1 T4096 H16, likewise outside the timed steps.
+prefill shape B1 T4096 H16, likewise outside the timed steps.  ``backward``
+(also outside them) times kda_chunk_bwd, the gradients of the prefill
+call, on the prefill workload with seeded output gradients, against the
+float32 matrix-core peak (its products run on float32 operands).
 """
 from __future__ import annotations
 
@@ -43,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix, published
 
 PREFILL = dict(B=1, H=16, T=4096, D=128, chunk=64)
 DECODE = dict(B=256, H=32, D=128)
@@ -62,6 +66,24 @@ def prefill_flops(B, H, T, D, C):
     # triangle-exploiting count per token-head: 6 d^2 + (C-1) d + (C+1)(2d + 2d) + C^2/3
     per = 6 * D * D + (C - 1) * D + (C + 1) * (4 * D) + C * C / 3.0
     return B * H * T * per
+
+
+def backward_flops(B, H, T, Dk, Dv, C):
+    """Matrix products of the chunkwise gradient per chunk, 2 m n k each and
+    half that for a triangular factor: 16 C Dk Dv (Qg^T dO, the two state
+    carries at two products each, the three products with the state and its
+    gradient) + 7 C^2 Dk (both couplings, W, and the four decayed sums of the
+    key/query gradients) + 5 C^2 Dv (U, Aqk^T dO, T^T dE and the two C x C
+    products with E)."""
+    nc = B * H * ((T + C - 1) // C)
+    return nc * (16 * C * Dk * Dv + 7 * C * C * Dk + 5 * C * C * Dv)
+
+
+def backward_bytes(B, H, T, Dk, Dv):
+    # in: q, k, v, dO bf16, g fp32, beta; out: dq, dk, dv bf16, dg fp32, dbeta;
+    # initial state, final-state gradient and initial-state gradient fp32
+    per = (2 * Dk + 2 * Dv) * 2 + Dk * 4 + 4 + (2 * Dk + Dv) * 2 + Dk * 4 + 4
+    return B * H * T * per + 3 * B * H * Dk * Dv * 4
 
 
 def source_hash(*names):
@@ -117,6 +139,12 @@ def cpu_baseline():
         oracle.recurrent_grouped(x.q[:, :, ::G], x.k[:, :, ::G], x.v, x.g, x.beta, x.h0,
                                  scale=x.scale, mode=x.mode)
         rows[name + "_tokens_per_s"] = 4096 / (time.perf_counter() - t0)
+    from kda_workloads import make_cotangents
+    cot = make_cotangents(w, seed=0, dhT_std=0.01)
+    t0 = time.perf_counter()
+    oracle.recurrent_bwd(w.q, w.k, w.v, w.g, w.beta, w.h0, cot.do, cot.dhT, scale=w.scale,
+                         mode=w.mode)
+    rows["backward_tokens_per_s"] = w.B * w.T / (time.perf_counter() - t0)
     return {"value": w.B * w.T / tp, "unit": "tokens/s", "cores": oracle.oracle_threads(),
             "kind": "oracle",
             "sample": "fp64 oracle R over the whole prefill workload (B1 H16 T4096 d128, "
@@ -211,6 +239,50 @@ def bench_prefill_shape(K, torch, dev, warmup, reps, *, Hqk, Dk, Dv, H=16, T=409
             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS}
 
 
+def bench_backward(K, torch, dev, warmup, reps):
+    """kda_chunk_bwd on the prefill workload (B1 H16 T4096 d128, chunk 64,
+    bf16 q/k/v and output gradient, bf16 input gradients), HIP events on the
+    launch stream."""
+    from kda_workloads import make_config, make_cotangents
+    w = make_config("prefill_h16_t4096")
+    cot = make_cotangents(w, seed=0, dhT_std=0.01)
+    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    bf = torch.bfloat16
+    q, k, v, do = t(w.q, bf), t(w.k, bf), t(w.v, bf), t(cot.do, bf)
+    g, beta, h0, dhT = t(w.g), t(w.beta), t(w.h0), t(cot.dhT)
+    B, T, H, Dk, Dv, C = w.B, w.T, w.H, w.Dk, w.Dv, 64
+    ws = torch.empty(K.kda_chunk_bwd_workspace_size(B, T, H, H, Dk, Dv, C, 0, K.BF16),
+                     dtype=torch.uint8, device=dev)
+    out = K.kda_chunk_bwd(q, k, v, g, beta, do, initial_state=h0, d_final_state=dhT, chunk=C,
+                          workspace=ws)
+
+    def run():
+        K.kda_chunk_bwd(q, k, v, g, beta, do, initial_state=h0, d_final_state=dhT, chunk=C,
+                        workspace=ws, out=out)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / reps / 1e3
+    flops = backward_flops(B, H, T, Dk, Dv, C)
+    nbytes = backward_bytes(B, H, T, Dk, Dv)
+    return {"workload": "gradients of the prefill call: B1 H16 T4096 d128, chunk 64, bf16 "
+                        "q/k/v/dO and input gradients, fp32 gates/beta/states",
+            "ms": sec * 1e3, "tokens_per_s": B * T / sec,
+            "roofline": {"kernel": "kda_chunk_bwd (bwd_prep + bwd_states + bwd_grad)",
+                         "bound": "mfma", "achieved": flops / sec / 1e12,
+                         "peak": F32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": flops / sec / 1e12 / F32_MFMA_PEAK_TFLOPS,
+                         "algorithmic_flops_per_launch": flops},
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
+            "workspace_bytes": int(ws.numel())}
+
+
 def bench_prologue(K, torch, dev, warmup, reps):
     """The prefill and decode shapes with all three prologue transforms fused
     (q, k L2-normalised; beta = sigmoid; g = log sigmoid of pre-activations)."""
@@ -265,6 +337,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a float32 copy of exactly 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times, as the reference for HBM byte counters")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="run only the gradient leg (kda_chunk_bwd on the prefill workload) "
+                         "and print its JSON object: profiling runs of the gradient kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -275,6 +350,17 @@ def main():
     import gated_delta_rule_17_amd as K
     from kda_workloads import make_config
     dev = torch.device("cuda:0")
+    if args.backward_only:
+        if args.calibrate_copy:
+            src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        print(json.dumps({"backward": bench_backward(K, torch, dev, args.warmup, args.steps)}),
+              flush=True)
+        return
 
     def dev_inputs(w):
         dt = torch.bfloat16
@@ -397,6 +483,7 @@ def main():
         out["grouped_heads"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=4, Dk=128, Dv=128)
         out["mixed_dims"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=16, Dk=64, Dv=128)
         out["prologue"] = bench_prologue(K, torch, dev, args.warmup, reps)
+        out["backward"] = bench_backward(K, torch, dev, args.warmup, reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

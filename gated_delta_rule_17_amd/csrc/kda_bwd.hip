@@ -10,7 +10,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Byte offsets of the per-chunk records (see bwd::Records) and of the
 // grouped-head partials inside the caller's workspace.
 struct BwdLayout {
-    size_t G, W, Kr, Qg, U, Tm, Aq, Ap, Hs, E, dH, dE, dqp, dkp, total;
+    size_t G, W, WT, Kr, KrT, U, Ut, P, Tm, Ap, Hs, E, dH, dE, dqp, dkp, total;
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
@@ -23,11 +23,13 @@ BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
     auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
     l.G = take(R * C * Dk * f);
     l.W = take(R * C * Dk * f);
+    l.WT = take(R * C * Dk * f);
     l.Kr = take(R * C * Dk * f);
-    l.Qg = take(R * C * Dk * f);
+    l.KrT = take(R * C * Dk * f);
     l.U = take(R * C * Dv * f);
+    l.Ut = take(R * C * Dv * f);
+    l.P = take(R * Dk * Dv * f);
     l.Tm = take(R * C * C * f);
-    l.Aq = take(R * C * C * f);
     l.Ap = take(R * C * C * f);
     l.Hs = take(R * Dk * Dv * f);
     l.E = take(R * C * Dv * f);
@@ -64,11 +66,13 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
     if (h.T > 0) {
         a.r.G = (float*)(ws + l.G);
         a.r.W = (float*)(ws + l.W);
+        a.r.WT = (float*)(ws + l.WT);
         a.r.Kr = (float*)(ws + l.Kr);
-        a.r.Qg = (float*)(ws + l.Qg);
+        a.r.KrT = (float*)(ws + l.KrT);
         a.r.U = (float*)(ws + l.U);
+        a.r.Ut = (float*)(ws + l.Ut);
+        a.r.P = (float*)(ws + l.P);
         a.r.Tm = (float*)(ws + l.Tm);
-        a.r.Aq = (float*)(ws + l.Aq);
         a.r.Ap = (float*)(ws + l.Ap);
         a.r.Hs = (float*)(ws + l.Hs);
         a.r.E = (float*)(ws + l.E);

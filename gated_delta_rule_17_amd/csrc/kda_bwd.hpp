@@ -59,16 +59,18 @@ namespace bwd {
 struct Records {
     float* G;    // [C][DK]  inclusive prefix of the log gates
     float* W;    // [C][DK]
+    float* WT;   // [DK][C]  W transposed
     float* Kr;   // [C][DK]  K e^{G_last - G}
-    float* Qg;   // [C][DK]  scale Q e^G
-    float* U;    // [C][DV]
+    float* KrT;  // [DK][C]  Kr transposed
+    float* U;    // [DV][C]  U transposed
+    float* Ut;   // [DV][C]  (Aqk^T dO) transposed
+    float* P;    // [DV][DK] ((scale Q e^G)^T dO) transposed
     float* Tm;   // [C][C]   (I + A)^-1
-    float* Aq;   // [C][C]   Aqk (inclusive lower)
     float* Ap;   // [C][C]   A before the beta scaling (strict lower)
-    float* Hs;   // [DK][DV] state entering the chunk
-    float* E;    // [C][DV]  pseudo-values
-    float* dH;   // [DK][DV] gradient of the state leaving the chunk
-    float* dE;   // [C][DV]
+    float* Hs;   // [DV][DK] state entering the chunk, transposed (= S)
+    float* E;    // [DV][C]  pseudo-values, transposed
+    float* dH;   // [DV][DK] gradient of the state leaving the chunk, transposed
+    float* dE;   // [DV][C]  transposed
 };
 
 struct Args {
@@ -108,21 +110,46 @@ __device__ __forceinline__ void lower_tile(int n, int& I, int& J) {
 // ---------------------------------------------------------------------------
 // 1. per-chunk preparation
 // ---------------------------------------------------------------------------
+template <int C, int DK, int DV>
+struct PrepLds {
+    static constexpr int NB = C / 16;
+    static constexpr int DM = DK > DV ? DK : DV;
+    static constexpr int LS = DM + 2, LK = DK + 2, LC = C + 2, LQ = C + 16;
+    static constexpr int LO = DV + 16, LG = DK + 16;
+    // phase 1: couplings, inverse, W, U
+    static constexpr int oS = 0, oAk = oS + C * LS, oAq = oAk + 16 * LK, oAp = oAq + 16 * LK,
+                         oT = oAp + C * LC, P1_END = oT + C * LC;
+    // phase 2: Aqk^T dO and (scale Q e^G)^T dO, over the phase-1 buffers
+    static constexpr int odO = 0, oQg = odO + C * LO, P2_END = oQg + C * LG;
+    // Aqk lives through both phases
+    static constexpr int oAqk = P1_END > P2_END ? P1_END : P2_END;
+    static constexpr int SIZE = oAqk + C * LQ;
+};
+
+template <int C, int DK, int DV>
+constexpr int prep_threads() { return (C * DK >= 512 && C * DV >= 512) ? 512 : 256; }
+
 template <int C, int DK, int DV, typename IO>
-__global__ void __launch_bounds__(256) bwd_prep(Args a)
+__global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 {
-    constexpr int NB = C / 16;
-    constexpr int LK = DK + 2;
-    constexpr int DM = DK > DV ? DK : DV;
-    constexpr int LS = DM + 2;
-    constexpr int LC = C + 2;
-    __shared__ float sG[C][LK];
-    __shared__ float sS[C][LS];
-    __shared__ float sAk[16][LK];
-    __shared__ float sAq[16][LK];
-    __shared__ float sAp[C][LC];
-    __shared__ float sT[C][LC];
+    using S = PrepLds<C, DK, DV>;
+    constexpr int NB = S::NB, LS = S::LS, LK = S::LK, LC = S::LC, LQ = S::LQ, LO = S::LO,
+                  LG = S::LG;
+    constexpr int NT = prep_threads<C, DK, DV>(), NW = NT / 64;
+    constexpr int TPC = NT / DK, RPT = C / TPC;    // threads per key channel, rows per thread
+    constexpr int TPV = NT / DV, RPV = C / TPV;    // the same for value channels
+    __shared__ __align__(16) float smem[S::SIZE];
+    __shared__ float sGref[NB + 1][DK];             // G at rows 16 I and at the last row
+    __shared__ float sSeg[TPC][DK];
     __shared__ float sBeta[C];
+    float* const sS = smem + S::oS;
+    float* const sAk = smem + S::oAk;
+    float* const sAq = smem + S::oAq;
+    float* const sAp = smem + S::oAp;
+    float* const sT = smem + S::oT;
+    float* const sdO = smem + S::odO;
+    float* const sQg = smem + S::oQg;
+    float* const sAqk = smem + S::oAqk;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
@@ -134,313 +161,406 @@ __global__ void __launch_bounds__(256) bwd_prep(Args a)
     const IO* q = (const IO*)a.q;
     const IO* k = (const IO*)a.k;
     const IO* v = (const IO*)a.v;
+    const IO* dO = (const IO*)a.dO;
     const size_t R = (size_t)rec;
-    float* const gG = a.r.G + R * C * DK;
 
-    // G: inclusive prefix of the log gates per key channel (zero past the end)
-    for (int c = tid; c < DK; c += 256) {
-        float acc = 0.f;
-        for (int i = 0; i < C; ++i) {
-            float gi = 0.f;
-            if (i < L) {
-                if (a.mode == KDA_GATE_CHANNEL) gi = a.g[tok_v(a, b, t0 + i, h) * DK + c];
-                else if (a.mode == KDA_GATE_SCALAR) gi = a.g[tok_v(a, b, t0 + i, h)];
-            }
-            acc += gi;
-            sG[i][c] = acc;
-            gG[i * DK + c] = acc;
+    // this thread's elements: key channel c, rows r0 .. r0 + RPT - 1
+    const int c = tid % DK, seg = tid / DK, r0 = seg * RPT;
+    float kr[RPT], qr[RPT], Gr[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = r0 + m;
+        float kv = 0.f, qv = 0.f, gv = 0.f;
+        if (i < L) {
+            const size_t o = tok_qk(a, b, t0 + i, hq) * DK + c;
+            kv = io<IO>::load(k + o);
+            qv = io<IO>::load(q + o);
+            if (a.mode == KDA_GATE_CHANNEL) gv = a.g[tok_v(a, b, t0 + i, h) * DK + c];
+            else if (a.mode == KDA_GATE_SCALAR) gv = a.g[tok_v(a, b, t0 + i, h)];
+        }
+        kr[m] = kv;
+        qr[m] = qv;
+        Gr[m] = gv;
+    }
+    // G: inclusive prefix per channel (segment scans, then segment offsets)
+#pragma unroll
+    for (int m = 1; m < RPT; ++m) Gr[m] += Gr[m - 1];
+    sSeg[seg][c] = Gr[RPT - 1];
+    for (int i = tid; i < C; i += NT) sBeta[i] = i < L ? a.beta[tok_v(a, b, t0 + i, h)] : 0.f;
+    __syncthreads();
+    {
+        float off = 0.f;
+        for (int s2 = 0; s2 < seg; ++s2) off += sSeg[s2][c];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            Gr[m] += off;
+            const int i = r0 + m;
+            a.r.G[R * C * DK + i * DK + c] = Gr[m];
+            if (i % 16 == 0) sGref[i / 16][c] = Gr[m];
+            if (i == C - 1) sGref[NB][c] = Gr[m];
         }
     }
-    for (int i = tid; i < C; i += 256) sBeta[i] = i < L ? a.beta[tok_v(a, b, t0 + i, h)] : 0.f;
     __syncthreads();
 
-    // coupling before beta (strict lower) and Aqk (inclusive lower), one
-    // 16-row block I at a time, reference row 16 I
+    // couplings, one 16-row block I at a time with reference row 16 I:
+    // Ap = strict lower K Gamma K^T (before beta), Aqk = inclusive lower Q~ Gamma K^T
     for (int I = 0; I < NB; ++I) {
-        const int rows = 16 * (I + 1);
-        for (int e = tid; e < rows * DK; e += 256) {
-            const int j = e / DK, c = e % DK;
-            const float kv = j < L ? io<IO>::load(k + tok_qk(a, b, t0 + j, hq) * DK + c) : 0.f;
-            sS[j][c] = kv * ex(sG[16 * I][c] - sG[j][c]);
-        }
-        for (int e = tid; e < 16 * DK; e += 256) {
-            const int m = e / DK, c = e % DK, i = 16 * I + m;
-            const float f = ex(sG[i][c] - sG[16 * I][c]);
-            float kv = 0.f, qv = 0.f;
-            if (i < L) {
-                kv = io<IO>::load(k + tok_qk(a, b, t0 + i, hq) * DK + c);
-                qv = io<IO>::load(q + tok_qk(a, b, t0 + i, hq) * DK + c);
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int j = r0 + m;
+            if (j < 16 * (I + 1)) sS[j * LS + c] = kr[m] * ex(sGref[I][c] - Gr[m]);
+            if (j >= 16 * I && j < 16 * (I + 1)) {
+                const float f = ex(Gr[m] - sGref[I][c]);
+                sAk[(j - 16 * I) * LK + c] = kr[m] * f;
+                sAq[(j - 16 * I) * LK + c] = a.scale * qr[m] * f;
             }
-            sAk[m][c] = kv * f;
-            sAq[m][c] = a.scale * qv * f;
         }
         __syncthreads();
-        for (int job = w; job < 2 * (I + 1); job += 4) {
+        for (int job = w; job < 2 * (I + 1); job += NW) {
             const int which = job & 1, J = job >> 1;
-            const float* A = which ? &sAq[0][0] : &sAk[0][0];
+            const float* A = which ? sAq : sAk;
             f32x4 acc = zero4();
 #pragma unroll 8
             for (int kk = 0; kk < DK; kk += 4)
-                acc = mma4(A[r16 * LK + kk + q4], sS[16 * J + r16][kk + q4], acc);
+                acc = mma4(A[r16 * LK + kk + q4], sS[(16 * J + r16) * LS + kk + q4], acc);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * I + 4 * q4 + ii, j = 16 * J + r16;
                 if (which == 0) {
                     const float val = j < i ? acc[ii] : 0.f;
-                    sAp[i][j] = val;
+                    sAp[i * LC + j] = val;
                     a.r.Ap[R * C * C + i * C + j] = val;
                 } else {
-                    a.r.Aq[R * C * C + i * C + j] = j <= i ? acc[ii] : 0.f;
+                    sAqk[i * LQ + j] = j <= i ? acc[ii] : 0.f;
                 }
-            }
-        }
-        if (rows < C) {
-            for (int e = tid; e < 16 * (C - rows); e += 256) {
-                const int i = 16 * I + e / (C - rows), j = rows + e % (C - rows);
-                sAp[i][j] = 0.f;
-                a.r.Ap[R * C * C + i * C + j] = 0.f;
-                a.r.Aq[R * C * C + i * C + j] = 0.f;
             }
         }
         __syncthreads();
     }
 
-    // T = (I + A)^-1 by forward substitution, one column per thread:
-    // T[i][c] = delta_ic - beta_i sum_{c <= j < i} Ap[i][j] T[j][c]
-    if (tid < C) {
-        const int cc = tid;
-        for (int i = 0; i < C; ++i) {
+    // T = (I + A)^-1, A = Diag(beta) Ap: diagonal 16 x 16 blocks by column
+    // substitution, then T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ by block
+    // distance on the matrix cores
+    if (tid < 16 * NB) {
+        const int base = 16 * (tid / 16), col = tid % 16;
+        for (int m = 0; m < 16; ++m) {
             float t;
-            if (i < cc) {
+            if (m < col) {
                 t = 0.f;
-            } else if (i == cc) {
+            } else if (m == col) {
                 t = 1.f;
             } else {
                 float s = 0.f;
-                for (int j = cc; j < i; ++j) s += sAp[i][j] * sT[j][cc];
-                t = -sBeta[i] * s;
+                for (int j = col; j < m; ++j) s += sAp[(base + m) * LC + base + j] * sT[(base + j) * LC + base + col];
+                t = -sBeta[base + m] * s;
             }
-            sT[i][cc] = t;
+            sT[(base + m) * LC + base + col] = t;
         }
     }
     __syncthreads();
-    for (int e = tid; e < C * C; e += 256) a.r.Tm[R * C * C + e] = sT[e / C][e % C];
+    for (int d = 1; d < NB; ++d) {
+        if (w < NB - d) {
+            const int J = w, I = w + d;
+            const int i = 16 * I + r16;
+            f32x4 M = zero4();
+            for (int K = J; K < I; ++K) {
+#pragma unroll
+                for (int kk = 0; kk < 16; kk += 4)
+                    M = mma4(sBeta[i] * sAp[i * LC + 16 * K + kk + q4],
+                             sT[(16 * K + kk + q4) * LC + 16 * J + r16], M);
+            }
+            // M is the right operand as it stands: lane (r16, q4) holds M[4 q4 + s][r16]
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2)
+                acc = mma4(sT[(16 * I + r16) * LC + 16 * I + 4 * q4 + s2], M[s2], acc);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sT[(16 * I + 4 * q4 + ii) * LC + 16 * J + r16] = -acc[ii];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < C * C; e += NT) {
+        const int i = e / C, j = e % C;
+        a.r.Tm[R * C * C + e] = (j >> 4) <= (i >> 4) ? sT[i * LC + j] : 0.f;
+    }
 
-    // W = T Diag(beta) (K e^G)
-    for (int e = tid; e < C * DK; e += 256) {
-        const int j = e / DK, c = e % DK;
-        const float kv = j < L ? io<IO>::load(k + tok_qk(a, b, t0 + j, hq) * DK + c) : 0.f;
-        sS[j][c] = sBeta[j] * kv * ex(sG[j][c]);
+    // W = T Diag(beta) (K e^G), stored as [C][DK] and transposed [DK][C]
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int j = r0 + m;
+        sS[j * LS + c] = sBeta[j] * kr[m] * ex(Gr[m]);
     }
     __syncthreads();
-    for (int job = w; job < NB * (DK / 16); job += 4) {
+    for (int job = w; job < NB * (DK / 16); job += NW) {
         const int I = job / (DK / 16), Rc = job % (DK / 16);
         f32x4 acc = zero4();
         for (int kk = 0; kk < 16 * (I + 1); kk += 4)
-            acc = mma4(sT[16 * I + r16][kk + q4], sS[kk + q4][16 * Rc + r16], acc);
+            acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
             a.r.W[R * C * DK + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
+        *reinterpret_cast<f32x4*>(a.r.WT + R * DK * C + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
     }
     __syncthreads();
 
     // U = T Diag(beta) V
-    for (int e = tid; e < C * DV; e += 256) {
-        const int j = e / DV, c = e % DV;
-        const float vv = j < L ? io<IO>::load(v + tok_v(a, b, t0 + j, h) * DV + c) : 0.f;
-        sS[j][c] = sBeta[j] * vv;
+    {
+        const int cv = tid % DV, r0v = (tid / DV) * RPV;
+#pragma unroll
+        for (int m = 0; m < RPV; ++m) {
+            const int j = r0v + m;
+            const float vv = j < L ? io<IO>::load(v + tok_v(a, b, t0 + j, h) * DV + cv) : 0.f;
+            sS[j * LS + cv] = sBeta[j] * vv;
+        }
     }
     __syncthreads();
-    for (int job = w; job < NB * (DV / 16); job += 4) {
+    for (int job = w; job < NB * (DV / 16); job += NW) {
         const int I = job / (DV / 16), Rc = job % (DV / 16);
         f32x4 acc = zero4();
         for (int kk = 0; kk < 16 * (I + 1); kk += 4)
-            acc = mma4(sT[16 * I + r16][kk + q4], sS[kk + q4][16 * Rc + r16], acc);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            a.r.U[R * C * DV + (16 * I + 4 * q4 + ii) * DV + 16 * Rc + r16] = acc[ii];
+            acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
+        *reinterpret_cast<f32x4*>(a.r.U + R * C * DV + (size_t)(16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
     }
 
-    // Kr = K e^{G_last - G}, Qg = scale Q e^G
-    for (int e = tid; e < C * DK; e += 256) {
-        const int i = e / DK, c = e % DK;
-        float kv = 0.f, qv = 0.f;
-        if (i < L) {
-            kv = io<IO>::load(k + tok_qk(a, b, t0 + i, hq) * DK + c);
-            qv = io<IO>::load(q + tok_qk(a, b, t0 + i, hq) * DK + c);
+    // Kr = K e^{G_last - G}, stored as [C][DK] and transposed [DK][C]
+    {
+        float kx[RPT];
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            kx[m] = kr[m] * ex(sGref[NB][c] - Gr[m]);
+            a.r.Kr[R * C * DK + (r0 + m) * DK + c] = kx[m];
         }
-        a.r.Kr[R * C * DK + e] = kv * ex(sG[C - 1][c] - sG[i][c]);
-        a.r.Qg[R * C * DK + e] = a.scale * qv * ex(sG[i][c]);
+        float* kt = a.r.KrT + R * DK * C + (size_t)c * C + r0;
+        if constexpr (RPT % 4 == 0) {
+#pragma unroll
+            for (int m = 0; m < RPT; m += 4)
+                *reinterpret_cast<f32x4*>(kt + m) = (f32x4){kx[m], kx[m + 1], kx[m + 2], kx[m + 3]};
+        } else {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) kt[m] = kx[m];
+        }
+    }
+    __syncthreads();
+
+    // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV]
+    {
+        const int cv = tid % DV, r0v = (tid / DV) * RPV;
+#pragma unroll
+        for (int m = 0; m < RPV; ++m) {
+            const int j = r0v + m;
+            sdO[j * LO + cv] = j < L ? io<IO>::load(dO + tok_v(a, b, t0 + j, h) * DV + cv) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) sQg[(r0 + m) * LG + c] = a.scale * qr[m] * ex(Gr[m]);
+    __syncthreads();
+    constexpr int NJU = NB * (DV / 16), NJP = (DK / 16) * (DV / 16);
+    for (int job = w; job < NJU + NJP; job += NW) {
+        f32x4 acc = zero4();
+        if (job < NJU) {
+            const int J = job / (DV / 16), Vt = job % (DV / 16);
+            for (int kk = 16 * J; kk < C; kk += 4)
+                acc = mma4(sAqk[(kk + q4) * LQ + 16 * J + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
+            *reinterpret_cast<f32x4*>(a.r.Ut + R * C * DV + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
+        } else {
+            const int jp = job - NJU, Rc = jp / (DV / 16), Vt = jp % (DV / 16);
+#pragma unroll 8
+            for (int kk = 0; kk < C; kk += 4)
+                acc = mma4(sQg[(kk + q4) * LG + 16 * Rc + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
+            *reinterpret_cast<f32x4*>(a.r.P + R * DK * DV + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // 2. sequential state passes (forward carry and reverse gradient carry)
 // ---------------------------------------------------------------------------
-template <int C, int DK, int DV>
-struct StateLds {
-    static constexpr int VT = 16;
-    static constexpr int LW = DK + 2;    // rows read along the row index (normal A operand)
-    static constexpr int LX = DK + 16;   // rows read along the column index (transposed A)
-    static constexpr int LA = C + 16;
-    // forward role
-    static constexpr int fH = 0, fW = fH + DK * VT, fKr = fW + C * LW, fE = fKr + C * LX,
-                         fGam = fE + C * VT, F_END = fGam + DK;
-    // reverse role
-    static constexpr int rdH = 0, rAq = rdH + DK * VT, rKr = rAq + C * LA, rQg = rKr + C * LW,
-                         rW = rQg + C * LX, rdO = rW + C * LX, rdE = rdO + C * VT,
-                         rGam = rdE + C * VT, R_END = rGam + DK;
-    static constexpr int SIZE = F_END > R_END ? F_END : R_END;
+// Workgroup = (head, 16-column value tile); wave w owns key channels
+// [w CPW, (w + 1) CPW) and keeps their 16-column state strip in registers
+// for the whole pass: lane (r16, q4) holds rows w CPW + q4 SQ + s, s < SQ,
+// of column r16.  A product over key channels (E = U - W H, or
+// dE = Ut + Kr dH) is a partial sum per wave, exchanged through LDS; the
+// update of the wave's own rows (H' = Diag(gamma) H + Kr^T E, or
+// dH = Diag(gamma) dH' + P - W^T dE) contracts over the chunk's rows with the
+// output rows ordered so that each accumulator element lands on the lane
+// and slot that holds that row of the strip.
+template <int C, int DK>
+struct StateShape {
+    static constexpr int NB = C / 16;
+    static constexpr int NWS = DK >= 64 ? 4 : DK / 16;   // waves
+    static constexpr int CPW = DK / NWS;                  // key channels per wave: 16 or 32
+    static constexpr int SQ = CPW / 4;                    // strip slots per lane
+    static constexpr int TPW = CPW / 16;                  // 16-row tiles per wave
+    static constexpr int CQ = C / 4;                      // chunk rows per lane group
+    static constexpr int LP = C + 4;
 };
-
-// copy a [rows][cols] float record into LDS rows of stride ld
-template <int ROWS, int COLS, int NT>
-__device__ __forceinline__ void stage(float* dst, int ld, const float* src, int tid) {
-    for (int e4 = tid; e4 < ROWS * COLS / 4; e4 += NT) {
-        const int row = e4 / (COLS / 4), c4 = (e4 % (COLS / 4)) * 4;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + row * COLS + c4);
-        float* d = dst + row * ld + c4;
-        d[0] = x[0]; d[1] = x[1]; d[2] = x[2]; d[3] = x[3];
-    }
-}
 
 template <int C, int DK, int DV, typename IO>
 __global__ void __launch_bounds__(256) bwd_states(Args a)
 {
-    using S = StateLds<C, DK, DV>;
-    constexpr int NB = C / 16, VT = S::VT;
-    __shared__ __align__(16) float smem[S::SIZE];
+    using S = StateShape<C, DK>;
+    constexpr int NB = S::NB, NWS = S::NWS, CPW = S::CPW, SQ = S::SQ, TPW = S::TPW, CQ = S::CQ,
+                  LP = S::LP;
+    __shared__ __align__(16) float sPart[NWS][16][LP];   // per-wave partial sums, [column][row]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const int units = a.B * a.H;
-    const bool reverse = (int)blockIdx.y >= units;
-    const int u = reverse ? blockIdx.y - units : blockIdx.y;
-    const int b = u / a.H, h = u % a.H;
-    const int v0 = blockIdx.x * VT;
+    // Workgroups are handed to the eight XCDs round-robin by id; the DV / 16
+    // value tiles of one (role, head) take ids 8 apart, so they share an XCD
+    // and its L2, which then serves the records they all read.
+    constexpr int NVT = DV / 16;
+    const int L8 = blockIdx.x, xcd = L8 % 8, slot = L8 / 8;
+    const int ur = (slot / NVT) * 8 + xcd, vt = slot % NVT;
+    if (ur >= 2 * units) return;
+    const bool reverse = ur >= units;
+    const int u = reverse ? ur - units : ur;
+    const int v0 = vt * 16;
     const size_t DD = (size_t)DK * DV;
+    const int cw0 = w * CPW;
+    const int NC = a.NC;
+    // channel of strip slot s of this lane, and of row m of output tile t
+    const int crow = cw0 + q4 * SQ;                       // + s
+    const int ctile = cw0 + (r16 >> 2) * SQ + (r16 & 3);  // + 4 t
 
-    if (!reverse) {
-        float* sH = smem + S::fH;
-        float* sW = smem + S::fW;
-        float* sKr = smem + S::fKr;
-        float* sE = smem + S::fE;
-        float* sGam = smem + S::fGam;
-        for (int e = tid; e < DK * VT; e += 256) {
-            const int c = e / VT, n = e % VT;
-            sH[e] = a.h0 ? a.h0[(size_t)u * DD + c * DV + v0 + n] : 0.f;
-        }
-        for (int ch = 0; ch < a.NC; ++ch) {
-            const size_t R = (size_t)u * a.NC + ch;
-            stage<C, DK, 256>(sW, S::LW, a.r.W + R * C * DK, tid);
-            stage<C, DK, 256>(sKr, S::LX, a.r.Kr + R * C * DK, tid);
-            for (int c = tid; c < DK; c += 256) sGam[c] = ex(a.r.G[R * C * DK + (C - 1) * DK + c]);
-            __syncthreads();
-            for (int e = tid; e < DK * VT; e += 256) {
-                const int c = e / VT, n = e % VT;
-                a.r.Hs[R * DD + c * DV + v0 + n] = sH[e];
-            }
-            if (w < NB) {
-                const int I = w;
-                f32x4 acc = zero4();
-#pragma unroll 8
-                for (int kk = 0; kk < DK; kk += 4)
-                    acc = mma4(sW[(16 * I + r16) * S::LW + kk + q4], sH[(kk + q4) * VT + r16], acc);
+    float st[SQ];
+    {
+        const float* init = reverse ? a.dhT : a.h0;
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int i = 16 * I + 4 * q4 + ii;
-                    const float e = a.r.U[R * C * DV + i * DV + v0 + r16] - acc[ii];
-                    sE[i * VT + r16] = e;
-                    a.r.E[R * C * DV + i * DV + v0 + r16] = e;
-                }
-            }
-            __syncthreads();
-            for (int Rt = w; Rt < DK / 16; Rt += 4) {
-                f32x4 acc = zero4();
-#pragma unroll 8
-                for (int kk = 0; kk < C; kk += 4)
-                    acc = mma4(sKr[(kk + q4) * S::LX + 16 * Rt + r16], sE[(kk + q4) * VT + r16], acc);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int c = 16 * Rt + 4 * q4 + ii;
-                    sH[c * VT + r16] = sGam[c] * sH[c * VT + r16] + acc[ii];
-                }
-            }
-            __syncthreads();
-        }
-        return;
+        for (int s = 0; s < SQ; ++s)
+            st[s] = init ? init[(size_t)u * DD + (size_t)(crow + s) * DV + v0 + r16] : 0.f;
     }
 
-    // reverse role
-    const IO* dO = (const IO*)a.dO;
-    float* sdH = smem + S::rdH;
-    float* sAq = smem + S::rAq;
-    float* sKr = smem + S::rKr;
-    float* sQg = smem + S::rQg;
-    float* sW = smem + S::rW;
-    float* sdO = smem + S::rdO;
-    float* sdE = smem + S::rdE;
-    float* sGam = smem + S::rGam;
-    for (int e = tid; e < DK * VT; e += 256) {
-        const int c = e / VT, n = e % VT;
-        sdH[e] = a.dhT ? a.dhT[(size_t)u * DD + c * DV + v0 + n] : 0.f;
-    }
-    for (int ch = a.NC - 1; ch >= 0; --ch) {
-        const size_t R = (size_t)u * a.NC + ch;
-        const int t0 = ch * C;
-        const int L = min(C, a.T - t0);
-        stage<C, C, 256>(sAq, S::LA, a.r.Aq + R * C * C, tid);
-        stage<C, DK, 256>(sKr, S::LW, a.r.Kr + R * C * DK, tid);
-        stage<C, DK, 256>(sQg, S::LX, a.r.Qg + R * C * DK, tid);
-        stage<C, DK, 256>(sW, S::LX, a.r.W + R * C * DK, tid);
-        for (int e = tid; e < C * VT; e += 256) {
-            const int i = e / VT, n = e % VT;
-            sdO[e] = i < L ? io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n) : 0.f;
+    // operands of one chunk step
+    struct Ops {
+        float A1[NB][SQ];      // W (forward) or Kr (reverse) rows 16 I + r16, this wave's channels
+        float A2[TPW][CQ];     // Kr^T (forward) or W^T (reverse) rows of this wave's output tiles
+        float add[NB][4];      // U (forward) or Ut (reverse) at the accumulator positions (wave 0)
+        float gam[SQ];         // e^{G_last} of the strip rows
+        float P[SQ];           // reverse: P at the strip positions
+    };
+    auto load = [&](Ops& o, int ch) {
+        const size_t R = (size_t)u * NC + ch;
+        const float* A1 = (reverse ? a.r.Kr : a.r.W) + R * C * DK;
+        const float* A2 = (reverse ? a.r.WT : a.r.KrT) + R * DK * C;
+        const float* AD = (reverse ? a.r.Ut : a.r.U) + R * C * DV + (size_t)(v0 + r16) * C;
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            const float* p = A1 + (16 * I + r16) * DK + crow;
+#pragma unroll
+            for (int s = 0; s < SQ; s += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
+                o.A1[I][s] = x[0]; o.A1[I][s + 1] = x[1]; o.A1[I][s + 2] = x[2]; o.A1[I][s + 3] = x[3];
+            }
+            if (w == 0) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(AD + 16 * I + 4 * q4);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) o.add[I][ii] = x[ii];
+            }
         }
-        for (int c = tid; c < DK; c += 256) sGam[c] = ex(a.r.G[R * C * DK + (C - 1) * DK + c]);
-        __syncthreads();
-        for (int e = tid; e < DK * VT; e += 256) {
-            const int c = e / VT, n = e % VT;
-            a.r.dH[R * DD + c * DV + v0 + n] = sdH[e];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const float* p = A2 + (size_t)(ctile + 4 * t) * C + q4 * CQ;
+#pragma unroll
+            for (int s = 0; s < CQ; s += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
+                o.A2[t][s] = x[0]; o.A2[t][s + 1] = x[1]; o.A2[t][s + 2] = x[2]; o.A2[t][s + 3] = x[3];
+            }
         }
-        if (w < NB) {
-            const int I = w;
+        const float* Gl = a.r.G + R * C * DK + (C - 1) * DK + crow;
+        const float* P = a.r.P + R * DD + (size_t)(v0 + r16) * DK + crow;
+#pragma unroll
+        for (int s = 0; s < SQ; s += 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Gl + s);
+            o.gam[s] = x[0]; o.gam[s + 1] = x[1]; o.gam[s + 2] = x[2]; o.gam[s + 3] = x[3];
+            if (reverse) {
+                const f32x4 y = *reinterpret_cast<const f32x4*>(P + s);
+                o.P[s] = y[0]; o.P[s + 1] = y[1]; o.P[s + 2] = y[2]; o.P[s + 3] = y[3];
+            }
+        }
+    };
+
+    // one chunk step with the operands in `cur`
+    auto step = [&](const Ops& cur, int n) {
+        const int ch = reverse ? NC - 1 - n : n;
+        const size_t R = (size_t)u * NC + ch;
+
+        // the state entering the chunk (forward) or the gradient leaving it (reverse)
+        float* rec = (reverse ? a.r.dH : a.r.Hs) + R * DD + (size_t)(v0 + r16) * DK + crow;
+#pragma unroll
+        for (int s = 0; s < SQ; s += 4)
+            *reinterpret_cast<f32x4*>(rec + s) = (f32x4){st[s], st[s + 1], st[s + 2], st[s + 3]};
+
+        // partial sums over this wave's channels
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
             f32x4 acc = zero4();
-            for (int kk = 16 * I; kk < C; kk += 4)
-                acc = mma4(sAq[(kk + q4) * S::LA + 16 * I + r16], sdO[(kk + q4) * VT + r16], acc);
-#pragma unroll 8
-            for (int kk = 0; kk < DK; kk += 4)
-                acc = mma4(sKr[(16 * I + r16) * S::LW + kk + q4], sdH[(kk + q4) * VT + r16], acc);
+#pragma unroll
+            for (int s = 0; s < SQ; ++s) acc = mma4(cur.A1[I][s], st[s], acc);
+            f32x4 part;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const int i = 16 * I + 4 * q4 + ii;
-                sdE[i * VT + r16] = acc[ii];
-                a.r.dE[R * C * DV + i * DV + v0 + r16] = acc[ii];
+                // forward: E = U - sum_w (W H)_w ; reverse: dE = Ut + sum_w (Kr dH)_w
+                const float x = reverse ? acc[ii] : -acc[ii];
+                part[ii] = w == 0 ? cur.add[I][ii] + x : x;
+            }
+            *reinterpret_cast<f32x4*>(&sPart[w][r16][16 * I + 4 * q4]) = part;
+        }
+        __syncthreads();
+        f32x4 pv[NWS][CQ / 4];
+#pragma unroll
+        for (int ww = 0; ww < NWS; ++ww) {
+#pragma unroll
+            for (int s = 0; s < CQ / 4; ++s)
+                pv[ww][s] = *reinterpret_cast<const f32x4*>(&sPart[ww][r16][q4 * CQ + 4 * s]);
+        }
+        float e[CQ];
+#pragma unroll
+        for (int s = 0; s < CQ / 4; ++s) {
+            f32x4 x = pv[0][s];
+#pragma unroll
+            for (int ww = 1; ww < NWS; ++ww) x += pv[ww][s];
+            e[4 * s] = x[0]; e[4 * s + 1] = x[1]; e[4 * s + 2] = x[2]; e[4 * s + 3] = x[3];
+        }
+        if (w == 0) {
+            float* er = (reverse ? a.r.dE : a.r.E) + R * C * DV + (size_t)(v0 + r16) * C + q4 * CQ;
+#pragma unroll
+            for (int s = 0; s < CQ; s += 4)
+                *reinterpret_cast<f32x4*>(er + s) = (f32x4){e[s], e[s + 1], e[s + 2], e[s + 3]};
+        }
+        // update of this wave's strip
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < CQ; ++s) acc = mma4(cur.A2[t][s], e[s], acc);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int s = 4 * t + ii;
+                const float gm = ex(cur.gam[s]);
+                st[s] = reverse ? gm * st[s] + cur.P[s] - acc[ii] : gm * st[s] + acc[ii];
             }
         }
         __syncthreads();
-        for (int Rt = w; Rt < DK / 16; Rt += 4) {
-            f32x4 pos = zero4(), neg = zero4();
-#pragma unroll 8
-            for (int kk = 0; kk < C; kk += 4) {
-                pos = mma4(sQg[(kk + q4) * S::LX + 16 * Rt + r16], sdO[(kk + q4) * VT + r16], pos);
-                neg = mma4(sW[(kk + q4) * S::LX + 16 * Rt + r16], sdE[(kk + q4) * VT + r16], neg);
-            }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int c = 16 * Rt + 4 * q4 + ii;
-                sdH[c * VT + r16] = sGam[c] * sdH[c * VT + r16] + pos[ii] - neg[ii];
-            }
+    };
+    auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
+
+    // two operand buffers in turn, so a prefetch is consumed a whole step
+    // after it was issued and never copied
+    Ops bufA, bufB;
+    if (NC > 0) load(bufA, chunk_of(0));
+    for (int n = 0; n < NC; n += 2) {
+        load(bufB, chunk_of(n + 1));
+        step(bufA, n);
+        if (n + 1 < NC) {
+            load(bufA, chunk_of(n + 2));
+            step(bufB, n + 1);
         }
-        __syncthreads();
     }
-    if (a.dh0) {
-        for (int e = tid; e < DK * VT; e += 256) {
-            const int c = e / VT, n = e % VT;
-            a.dh0[(size_t)u * DD + c * DV + v0 + n] = sdH[e];
-        }
+    if (reverse && a.dh0) {
+#pragma unroll
+        for (int s = 0; s < SQ; ++s) a.dh0[(size_t)u * DD + (size_t)(crow + s) * DV + v0 + r16] = st[s];
     }
 }
-
 // ---------------------------------------------------------------------------
 // 3. per-chunk gradients
 // ---------------------------------------------------------------------------
@@ -448,11 +568,15 @@ template <int C, int DK, int DV>
 struct GradLds {
     static constexpr int NB = C / 16, NW = DK / 16;
     static constexpr int VS = DV < 32 ? DV : 32;
-    static constexpr int LT = C + 16, LV = VS + 2, LE = VS + 16, LA = C + 2;
-    // value-slice phase
-    static constexpr int oT = 0, oH = oT + C * LT, odH = oH + DK * LV, oE = odH + DK * LV,
-                         odO = oE + C * LV, odU = odO + C * LV, oV = odU + C * LV,
-                         odE = oV + C * LV, S_END = odE + C * LE;
+    // row strides (floats): 16 mod 32 where lanes run along a row, 2 mod 32
+    // where they run down a column
+    static constexpr int LT = C + 16, LV = VS + 2, LA = C + 2;
+    static constexpr int LHT = (DK + 31) / 32 * 32 + 16, LET = (C + 31) / 32 * 32 + 16, LDE = C + 2;
+    // value-slice phase; the state, its gradient and E are kept transposed
+    // ([value column][row]) as the records hold them
+    static constexpr int oT = 0, oH = oT + C * LT, odH = oH + VS * LHT, oE = odH + VS * LHT,
+                         odO = oE + VS * LET, odU = odO + C * LV, oV = odU + C * LV,
+                         odE = oV + C * LV, S_END = odE + VS * LDE;
     // output phase
     static constexpr int oAq = 0, oAb = oAq + C * LA, oSrc = oAb + C * LA,
                          oRow = oSrc + NW * 2 * C * 16, oRowG = oRow + NW * C,
@@ -466,7 +590,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     using S = GradLds<C, DK, DV>;
     constexpr int NB = S::NB, NW = S::NW, NT = 64 * NW;
     constexpr int VS = S::VS, NS = DV / VS;
-    constexpr int LT = S::LT, LV = S::LV, LE = S::LE, LA = S::LA;
+    constexpr int LT = S::LT, LV = S::LV, LA = S::LA, LHT = S::LHT, LET = S::LET, LDE = S::LDE;
     constexpr int NY = NB * (NB + 1) / 2;
     constexpr int NYS = (2 * NY + NW - 1) / NW;
     __shared__ __align__(16) float smem[S::SIZE];
@@ -512,15 +636,22 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     for (int s = 0; s < NS; ++s) {
         const int v0 = s * VS;
         __syncthreads();
-        for (int e = tid; e < DK * VS; e += NT) {
-            const int c = e / VS, n = e % VS;
-            sH[c * LV + n] = a.r.Hs[R * DD + c * DV + v0 + n];
-            sdH[c * LV + n] = a.r.dH[R * DD + c * DV + v0 + n];
+        for (int e = tid; e < DK * VS / 4; e += NT) {
+            const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
+            const size_t o = R * DD + (size_t)(v0 + n) * DK + c;
+            *reinterpret_cast<f32x4*>(sH + n * LHT + c) = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
+            *reinterpret_cast<f32x4*>(sdH + n * LHT + c) = *reinterpret_cast<const f32x4*>(a.r.dH + o);
+        }
+        for (int e = tid; e < C * VS / 4; e += NT) {
+            const int n = e / (C / 4), i = 4 * (e % (C / 4));
+            const size_t o = R * C * DV + (size_t)(v0 + n) * C + i;
+            *reinterpret_cast<f32x4*>(sE + n * LET + i) = *reinterpret_cast<const f32x4*>(a.r.E + o);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(a.r.dE + o);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) sdE[n * LDE + i + z] = y[z];
         }
         for (int e = tid; e < C * VS; e += NT) {
             const int i = e / VS, n = e % VS;
-            sE[i * LV + n] = a.r.E[R * C * DV + i * DV + v0 + n];
-            sdE[i * LE + n] = a.r.dE[R * C * DV + i * DV + v0 + n];
             float dov = 0.f, vv = 0.f;
             if (i < L) {
                 dov = io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n);
@@ -535,7 +666,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             const int I = job / (VS / 16), Vt = job % (VS / 16);
             f32x4 acc = zero4();
             for (int kk = 16 * I; kk < C; kk += 4)
-                acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdE[(kk + q4) * LE + 16 * Vt + r16], acc);
+                acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdE[(16 * Vt + r16) * LDE + kk + q4], acc);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * I + 4 * q4 + ii, n = 16 * Vt + r16;
@@ -549,17 +680,17 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             for (int n = 0; n < VS; ++n) zacc += sdU[tid * LV + n] * sV[tid * LV + n];
         }
         if (tid < DK) {
-            for (int n = 0; n < VS; ++n) gacc += sH[tid * LV + n] * sdH[tid * LV + n];
+            for (int n = 0; n < VS; ++n) gacc += sH[n * LHT + tid] * sdH[n * LHT + tid];
         }
         // products with the state and its gradient for this wave's 16 channels
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
 #pragma unroll
             for (int kk = 0; kk < VS; kk += 4) {
-                const float bH = sH[(16 * w + r16) * LV + kk + q4];
-                const float bdH = sdH[(16 * w + r16) * LV + kk + q4];
+                const float bH = sH[(kk + q4) * LHT + 16 * w + r16];
+                const float bdH = sdH[(kk + q4) * LHT + 16 * w + r16];
                 X1[I] = mma4(sdO[(16 * I + r16) * LV + kk + q4], bH, X1[I]);
-                X2[I] = mma4(sE[(16 * I + r16) * LV + kk + q4], bdH, X2[I]);
+                X2[I] = mma4(sE[(kk + q4) * LET + 16 * I + r16], bdH, X2[I]);
                 X3[I] = mma4(sdU[(16 * I + r16) * LV + kk + q4], bH, X3[I]);
             }
         }
@@ -573,7 +704,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 const float* A = job >= NY ? sdU : sdO;
 #pragma unroll
                 for (int kk = 0; kk < VS; kk += 4)
-                    Y[sl] = mma4(A[(16 * I + r16) * LV + kk + q4], sE[(16 * J + r16) * LV + kk + q4], Y[sl]);
+                    Y[sl] = mma4(A[(16 * I + r16) * LV + kk + q4], sE[(kk + q4) * LET + 16 * J + r16], Y[sl]);
             }
         }
     }
@@ -826,11 +957,14 @@ hipError_t launch3(const Args& a, hipStream_t s)
     const int units = a.B * a.H;
     const unsigned nrec = (unsigned)units * (unsigned)a.NC;
     if (nrec > 0) {
-        hipLaunchKernelGGL((bwd_prep<C, DK, DV, IO>), dim3(nrec), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_prep<C, DK, DV, IO>), dim3(nrec), dim3(prep_threads<C, DK, DV>()), 0, s,
+                           a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_states<C, DK, DV, IO>), dim3(DV / 16, 2 * units), dim3(256), 0, s, a);
+    const unsigned ur8 = (unsigned)((2 * units + 7) / 8) * 8;
+    hipLaunchKernelGGL((bwd_states<C, DK, DV, IO>), dim3(ur8 * (DV / 16)),
+                       dim3(64 * StateShape<C, DK>::NWS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nrec > 0) {
