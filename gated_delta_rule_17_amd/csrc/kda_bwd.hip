@@ -7,10 +7,14 @@ namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Byte offsets of the per-chunk records (see bwd::Records) and of the
-// grouped-head partials inside the caller's workspace.
+// Layout of the workspace: one float block per (sequence, head, chunk)
+// record holding all of its fields (see bwd::Records) one after another, so
+// that a workgroup working on a chunk touches one contiguous region; then
+// the grouped-head partials.  Every field is a multiple of 1 KiB.
 struct BwdLayout {
-    size_t G, W, WT, Kr, KrT, U, Ut, P, Tm, Ap, Hs, E, dH, dE, dqp, dkp, total;
+    size_t G, W, WT, Kr, KrT, U, Ut, P, Tm, Ap, Hs, E, dH, dE;   // float offsets in a record
+    size_t rs;                                                  // floats per record
+    size_t dqp, dkp, total;                                     // bytes
 };
 
 BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
@@ -18,27 +22,30 @@ BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
     BwdLayout l{};
     const size_t NC = (size_t)((T + C - 1) / C);
     const size_t R = (size_t)B * H * NC;
-    const size_t f = sizeof(float);
     size_t o = 0;
-    auto take = [&](size_t bytes) { const size_t at = o; o = align256(o + bytes); return at; };
-    l.G = take(R * C * Dk * f);
-    l.W = take(R * C * Dk * f);
-    l.WT = take(R * C * Dk * f);
-    l.Kr = take(R * C * Dk * f);
-    l.KrT = take(R * C * Dk * f);
-    l.U = take(R * C * Dv * f);
-    l.Ut = take(R * C * Dv * f);
-    l.P = take(R * Dk * Dv * f);
-    l.Tm = take(R * C * C * f);
-    l.Ap = take(R * C * C * f);
-    l.Hs = take(R * Dk * Dv * f);
-    l.E = take(R * C * Dv * f);
-    l.dH = take(R * Dk * Dv * f);
-    l.dE = take(R * C * Dv * f);
-    const size_t part = Hq < H ? (size_t)B * T * H * Dk * f : 0;
-    l.dqp = take(part);
-    l.dkp = take(part);
-    l.total = o;
+    auto take = [&](size_t floats) { const size_t at = o; o += floats; return at; };
+    l.G = take((size_t)C * Dk);
+    l.W = take((size_t)C * Dk);
+    l.WT = take((size_t)C * Dk);
+    l.Kr = take((size_t)C * Dk);
+    l.KrT = take((size_t)C * Dk);
+    l.U = take((size_t)C * Dv);
+    l.Ut = take((size_t)C * Dv);
+    l.P = take((size_t)Dk * Dv);
+    l.Tm = take((size_t)C * C);
+    l.Ap = take((size_t)C * C);
+    l.Hs = take((size_t)Dk * Dv);
+    l.E = take((size_t)C * Dv);
+    l.dH = take((size_t)Dk * Dv);
+    l.dE = take((size_t)C * Dv);
+    l.rs = o;
+    size_t b = align256(R * l.rs * sizeof(float));
+    const size_t part = Hq < H ? (size_t)B * T * H * Dk * sizeof(float) : 0;
+    l.dqp = b;
+    b = align256(b + part);
+    l.dkp = b;
+    b = align256(b + part);
+    l.total = b;
     return l;
 }
 
@@ -64,20 +71,22 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
     a.dqp = grouped ? (float*)(ws + l.dqp) : nullptr;
     a.dkp = grouped ? (float*)(ws + l.dkp) : nullptr;
     if (h.T > 0) {
-        a.r.G = (float*)(ws + l.G);
-        a.r.W = (float*)(ws + l.W);
-        a.r.WT = (float*)(ws + l.WT);
-        a.r.Kr = (float*)(ws + l.Kr);
-        a.r.KrT = (float*)(ws + l.KrT);
-        a.r.U = (float*)(ws + l.U);
-        a.r.Ut = (float*)(ws + l.Ut);
-        a.r.P = (float*)(ws + l.P);
-        a.r.Tm = (float*)(ws + l.Tm);
-        a.r.Ap = (float*)(ws + l.Ap);
-        a.r.Hs = (float*)(ws + l.Hs);
-        a.r.E = (float*)(ws + l.E);
-        a.r.dH = (float*)(ws + l.dH);
-        a.r.dE = (float*)(ws + l.dE);
+        float* f = (float*)ws;
+        a.r.G = f + l.G;
+        a.r.W = f + l.W;
+        a.r.WT = f + l.WT;
+        a.r.Kr = f + l.Kr;
+        a.r.KrT = f + l.KrT;
+        a.r.U = f + l.U;
+        a.r.Ut = f + l.Ut;
+        a.r.P = f + l.P;
+        a.r.Tm = f + l.Tm;
+        a.r.Ap = f + l.Ap;
+        a.r.Hs = f + l.Hs;
+        a.r.E = f + l.E;
+        a.r.dH = f + l.dH;
+        a.r.dE = f + l.dE;
+        a.r.rs = l.rs;
     }
     a.B = h.B; a.T = h.T; a.H = h.H; a.Hq = h.Hq;
     a.NC = (h.T + C - 1) / C;

@@ -71,6 +71,8 @@ struct Records {
     float* E;    // [DV][C]  pseudo-values, transposed
     float* dH;   // [DV][DK] gradient of the state leaving the chunk, transposed
     float* dE;   // [DV][C]  transposed
+    size_t rs;   // floats from one record to the next: the fields of one
+                 // (sequence, head, chunk) lie together in one block
 };
 
 struct Args {
@@ -99,6 +101,39 @@ __device__ __forceinline__ size_t tok_v(const Args& a, int b, int t, int h) {
 }
 
 __device__ __forceinline__ float ex(float x) { return __expf(x); }
+
+// Workgroup barrier that orders LDS only: LDS writes before it are visible to
+// LDS reads after it, while global loads and stores stay in flight.
+// __syncthreads() also waits for every outstanding global access, and since
+// the vector-memory counter retires in order, a record store issued after a
+// prefetch then holds the barrier until the prefetch has landed.  Every
+// exchange between the waves of these kernels goes through LDS.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Loads of a chunk's rows are issued unconditionally from a clamped row
+// (every chunk has at least one row) and zeroed past the end afterwards: a
+// load under a per-row branch is waited for at the branch join, which
+// serialises the loads of a thread.
+__device__ __forceinline__ int clamp_row(int i, int L) { return i < L ? i : L - 1; }
+__device__ __forceinline__ float keep(float x, int i, int L) { return i < L ? x : 0.f; }
+
+// The gate of row i as base[i * stride], branch-free over the three modes
+// (the ungated mode reads beta and scales it by zero).
+struct GatePtr {
+    const float* base;
+    size_t stride;
+    float mul;
+};
+__device__ __forceinline__ GatePtr gate_ptr(const Args& a, int b, int t0, int h, int c, int DK) {
+    const size_t row0 = ((size_t)b * a.T + t0) * a.H + h;
+    if (a.mode == KDA_GATE_CHANNEL) return {a.g + row0 * DK + c, (size_t)a.H * DK, 1.f};
+    if (a.mode == KDA_GATE_SCALAR) return {a.g + row0, (size_t)a.H, 1.f};
+    return {a.beta + row0, (size_t)a.H, 0.f};
+}
 
 // Index of the n-th lower block tile (I, J), J <= I, of an NB x NB grid.
 __device__ __forceinline__ void lower_tile(int n, int& I, int& J) {
@@ -167,27 +202,29 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     // this thread's elements: key channel c, rows r0 .. r0 + RPT - 1
     const int c = tid % DK, seg = tid / DK, r0 = seg * RPT;
     float kr[RPT], qr[RPT], Gr[RPT];
+    {
+        const GatePtr gp = gate_ptr(a, b, t0, h, c, DK);
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int i = r0 + m;
-        float kv = 0.f, qv = 0.f, gv = 0.f;
-        if (i < L) {
-            const size_t o = tok_qk(a, b, t0 + i, hq) * DK + c;
-            kv = io<IO>::load(k + o);
-            qv = io<IO>::load(q + o);
-            if (a.mode == KDA_GATE_CHANNEL) gv = a.g[tok_v(a, b, t0 + i, h) * DK + c];
-            else if (a.mode == KDA_GATE_SCALAR) gv = a.g[tok_v(a, b, t0 + i, h)];
+        for (int m = 0; m < RPT; ++m) {
+            const int ic = clamp_row(r0 + m, L);
+            const size_t o = tok_qk(a, b, t0 + ic, hq) * DK + c;
+            kr[m] = io<IO>::load(k + o);
+            qr[m] = io<IO>::load(q + o);
+            Gr[m] = gp.base[ic * gp.stride] * gp.mul;
         }
-        kr[m] = kv;
-        qr[m] = qv;
-        Gr[m] = gv;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            kr[m] = keep(kr[m], r0 + m, L);
+            qr[m] = keep(qr[m], r0 + m, L);
+            Gr[m] = keep(Gr[m], r0 + m, L);
+        }
     }
     // G: inclusive prefix per channel (segment scans, then segment offsets)
 #pragma unroll
     for (int m = 1; m < RPT; ++m) Gr[m] += Gr[m - 1];
     sSeg[seg][c] = Gr[RPT - 1];
     for (int i = tid; i < C; i += NT) sBeta[i] = i < L ? a.beta[tok_v(a, b, t0 + i, h)] : 0.f;
-    __syncthreads();
+    lds_barrier();
     {
         float off = 0.f;
         for (int s2 = 0; s2 < seg; ++s2) off += sSeg[s2][c];
@@ -195,12 +232,12 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
         for (int m = 0; m < RPT; ++m) {
             Gr[m] += off;
             const int i = r0 + m;
-            a.r.G[R * C * DK + i * DK + c] = Gr[m];
+            a.r.G[R * a.r.rs + i * DK + c] = Gr[m];
             if (i % 16 == 0) sGref[i / 16][c] = Gr[m];
             if (i == C - 1) sGref[NB][c] = Gr[m];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // couplings, one 16-row block I at a time with reference row 16 I:
     // Ap = strict lower K Gamma K^T (before beta), Aqk = inclusive lower Q~ Gamma K^T
@@ -215,7 +252,7 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
                 sAq[(j - 16 * I) * LK + c] = a.scale * qr[m] * f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int job = w; job < 2 * (I + 1); job += NW) {
             const int which = job & 1, J = job >> 1;
             const float* A = which ? sAq : sAk;
@@ -229,35 +266,34 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
                 if (which == 0) {
                     const float val = j < i ? acc[ii] : 0.f;
                     sAp[i * LC + j] = val;
-                    a.r.Ap[R * C * C + i * C + j] = val;
+                    a.r.Ap[R * a.r.rs + i * C + j] = val;
                 } else {
                     sAqk[i * LQ + j] = j <= i ? acc[ii] : 0.f;
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     // T = (I + A)^-1, A = Diag(beta) Ap: diagonal 16 x 16 blocks by column
     // substitution, then T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ by block
     // distance on the matrix cores
     if (tid < 16 * NB) {
+        // column `col` of the block, kept in registers; rows above the
+        // diagonal come out zero by themselves
         const int base = 16 * (tid / 16), col = tid % 16;
+        float t[16];
+#pragma unroll
         for (int m = 0; m < 16; ++m) {
-            float t;
-            if (m < col) {
-                t = 0.f;
-            } else if (m == col) {
-                t = 1.f;
-            } else {
-                float s = 0.f;
-                for (int j = col; j < m; ++j) s += sAp[(base + m) * LC + base + j] * sT[(base + j) * LC + base + col];
-                t = -sBeta[base + m] * s;
-            }
-            sT[(base + m) * LC + base + col] = t;
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < m; ++j) s += sAp[(base + m) * LC + base + j] * t[j];
+            t[m] = (m == col ? 1.f : 0.f) - sBeta[base + m] * s;
         }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) sT[(base + m) * LC + base + col] = t[m];
     }
-    __syncthreads();
+    lds_barrier();
     for (int d = 1; d < NB; ++d) {
         if (w < NB - d) {
             const int J = w, I = w + d;
@@ -277,11 +313,11 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) sT[(16 * I + 4 * q4 + ii) * LC + 16 * J + r16] = -acc[ii];
         }
-        __syncthreads();
+        lds_barrier();
     }
     for (int e = tid; e < C * C; e += NT) {
         const int i = e / C, j = e % C;
-        a.r.Tm[R * C * C + e] = (j >> 4) <= (i >> 4) ? sT[i * LC + j] : 0.f;
+        a.r.Tm[R * a.r.rs + e] = (j >> 4) <= (i >> 4) ? sT[i * LC + j] : 0.f;
     }
 
     // W = T Diag(beta) (K e^G), stored as [C][DK] and transposed [DK][C]
@@ -290,7 +326,7 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
         const int j = r0 + m;
         sS[j * LS + c] = sBeta[j] * kr[m] * ex(Gr[m]);
     }
-    __syncthreads();
+    lds_barrier();
     for (int job = w; job < NB * (DK / 16); job += NW) {
         const int I = job / (DK / 16), Rc = job % (DK / 16);
         f32x4 acc = zero4();
@@ -298,28 +334,31 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            a.r.W[R * C * DK + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
-        *reinterpret_cast<f32x4*>(a.r.WT + R * DK * C + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+            a.r.W[R * a.r.rs + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
+        *reinterpret_cast<f32x4*>(a.r.WT + R * a.r.rs + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
     }
-    __syncthreads();
+    lds_barrier();
 
     // U = T Diag(beta) V
     {
         const int cv = tid % DV, r0v = (tid / DV) * RPV;
+        float vv[RPV];
+#pragma unroll
+        for (int m = 0; m < RPV; ++m)
+            vv[m] = io<IO>::load(v + tok_v(a, b, t0 + clamp_row(r0v + m, L), h) * DV + cv);
 #pragma unroll
         for (int m = 0; m < RPV; ++m) {
             const int j = r0v + m;
-            const float vv = j < L ? io<IO>::load(v + tok_v(a, b, t0 + j, h) * DV + cv) : 0.f;
-            sS[j * LS + cv] = sBeta[j] * vv;
+            sS[j * LS + cv] = sBeta[j] * keep(vv[m], j, L);
         }
     }
-    __syncthreads();
+    lds_barrier();
     for (int job = w; job < NB * (DV / 16); job += NW) {
         const int I = job / (DV / 16), Rc = job % (DV / 16);
         f32x4 acc = zero4();
         for (int kk = 0; kk < 16 * (I + 1); kk += 4)
             acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
-        *reinterpret_cast<f32x4*>(a.r.U + R * C * DV + (size_t)(16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+        *reinterpret_cast<f32x4*>(a.r.U + R * a.r.rs + (size_t)(16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
     }
 
     // Kr = K e^{G_last - G}, stored as [C][DK] and transposed [DK][C]
@@ -328,9 +367,9 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
             kx[m] = kr[m] * ex(sGref[NB][c] - Gr[m]);
-            a.r.Kr[R * C * DK + (r0 + m) * DK + c] = kx[m];
+            a.r.Kr[R * a.r.rs + (r0 + m) * DK + c] = kx[m];
         }
-        float* kt = a.r.KrT + R * DK * C + (size_t)c * C + r0;
+        float* kt = a.r.KrT + R * a.r.rs + (size_t)c * C + r0;
         if constexpr (RPT % 4 == 0) {
 #pragma unroll
             for (int m = 0; m < RPT; m += 4)
@@ -340,20 +379,21 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             for (int m = 0; m < RPT; ++m) kt[m] = kx[m];
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV]
     {
         const int cv = tid % DV, r0v = (tid / DV) * RPV;
+        float dv_[RPV];
 #pragma unroll
-        for (int m = 0; m < RPV; ++m) {
-            const int j = r0v + m;
-            sdO[j * LO + cv] = j < L ? io<IO>::load(dO + tok_v(a, b, t0 + j, h) * DV + cv) : 0.f;
-        }
+        for (int m = 0; m < RPV; ++m)
+            dv_[m] = io<IO>::load(dO + tok_v(a, b, t0 + clamp_row(r0v + m, L), h) * DV + cv);
+#pragma unroll
+        for (int m = 0; m < RPV; ++m) sdO[(r0v + m) * LO + cv] = keep(dv_[m], r0v + m, L);
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) sQg[(r0 + m) * LG + c] = a.scale * qr[m] * ex(Gr[m]);
-    __syncthreads();
+    lds_barrier();
     constexpr int NJU = NB * (DV / 16), NJP = (DK / 16) * (DV / 16);
     for (int job = w; job < NJU + NJP; job += NW) {
         f32x4 acc = zero4();
@@ -361,13 +401,13 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             const int J = job / (DV / 16), Vt = job % (DV / 16);
             for (int kk = 16 * J; kk < C; kk += 4)
                 acc = mma4(sAqk[(kk + q4) * LQ + 16 * J + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
-            *reinterpret_cast<f32x4*>(a.r.Ut + R * C * DV + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
+            *reinterpret_cast<f32x4*>(a.r.Ut + R * a.r.rs + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
         } else {
             const int jp = job - NJU, Rc = jp / (DV / 16), Vt = jp % (DV / 16);
 #pragma unroll 8
             for (int kk = 0; kk < C; kk += 4)
                 acc = mma4(sQg[(kk + q4) * LG + 16 * Rc + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
-            *reinterpret_cast<f32x4*>(a.r.P + R * DK * DV + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
+            *reinterpret_cast<f32x4*>(a.r.P + R * a.r.rs + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
         }
     }
 }
@@ -430,62 +470,71 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
             st[s] = init ? init[(size_t)u * DD + (size_t)(crow + s) * DV + v0 + r16] : 0.f;
     }
 
-    // operands of one chunk step
-    struct Ops {
-        float A1[NB][SQ];      // W (forward) or Kr (reverse) rows 16 I + r16, this wave's channels
-        float A2[TPW][CQ];     // Kr^T (forward) or W^T (reverse) rows of this wave's output tiles
-        float add[NB][4];      // U (forward) or Ut (reverse) at the accumulator positions (wave 0)
-        float gam[SQ];         // e^{G_last} of the strip rows
-        float P[SQ];           // reverse: P at the strip positions
+    // record bases of this role
+    const float* const A1b = reverse ? a.r.Kr : a.r.W;     // rows 16 I + r16, this wave's channels
+    const float* const A2b = reverse ? a.r.WT : a.r.KrT;   // rows of this wave's output tiles
+    const float* const ADb = reverse ? a.r.Ut : a.r.U;     // added to the partial sums (wave 0)
+    float* const recb = reverse ? a.r.dH : a.r.Hs;
+    float* const erb = reverse ? a.r.dE : a.r.E;
+
+    // operands used at the start of a step: requested one step ahead, in two
+    // sets that alternate (registers are scarce: the strip update's operands
+    // are requested at the start of their own step instead)
+    struct Pre {
+        float A1[NB][SQ];
+        float add[NB][4];
     };
-    auto load = [&](Ops& o, int ch) {
+    auto load_pre = [&](Pre& o, int ch) {
         const size_t R = (size_t)u * NC + ch;
-        const float* A1 = (reverse ? a.r.Kr : a.r.W) + R * C * DK;
-        const float* A2 = (reverse ? a.r.WT : a.r.KrT) + R * DK * C;
-        const float* AD = (reverse ? a.r.Ut : a.r.U) + R * C * DV + (size_t)(v0 + r16) * C;
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
-            const float* p = A1 + (16 * I + r16) * DK + crow;
+            const float* p = A1b + R * a.r.rs + (16 * I + r16) * DK + crow;
 #pragma unroll
             for (int s = 0; s < SQ; s += 4) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
                 o.A1[I][s] = x[0]; o.A1[I][s + 1] = x[1]; o.A1[I][s + 2] = x[2]; o.A1[I][s + 3] = x[3];
             }
             if (w == 0) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(AD + 16 * I + 4 * q4);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(ADb + R * a.r.rs + (size_t)(v0 + r16) * C + 16 * I + 4 * q4);
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) o.add[I][ii] = x[ii];
             }
         }
+    };
+
+    // one chunk step with its early operands in `cur`
+    auto step = [&](const Pre& cur, int n) {
+        const int ch = reverse ? NC - 1 - n : n;
+        const size_t R = (size_t)u * NC + ch;
+        // operands of the strip update, first used after the exchange
+        float A2[TPW][CQ], gam[SQ], Pv[SQ];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const float* p = A2 + (size_t)(ctile + 4 * t) * C + q4 * CQ;
+            const float* p = A2b + R * a.r.rs + (size_t)(ctile + 4 * t) * C + q4 * CQ;
 #pragma unroll
             for (int s = 0; s < CQ; s += 4) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
-                o.A2[t][s] = x[0]; o.A2[t][s + 1] = x[1]; o.A2[t][s + 2] = x[2]; o.A2[t][s + 3] = x[3];
+                A2[t][s] = x[0]; A2[t][s + 1] = x[1]; A2[t][s + 2] = x[2]; A2[t][s + 3] = x[3];
             }
         }
-        const float* Gl = a.r.G + R * C * DK + (C - 1) * DK + crow;
-        const float* P = a.r.P + R * DD + (size_t)(v0 + r16) * DK + crow;
+        {
+            const float* Gl = a.r.G + R * a.r.rs + (C - 1) * DK + crow;
+            const float* P = a.r.P + R * a.r.rs + (size_t)(v0 + r16) * DK + crow;
 #pragma unroll
-        for (int s = 0; s < SQ; s += 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(Gl + s);
-            o.gam[s] = x[0]; o.gam[s + 1] = x[1]; o.gam[s + 2] = x[2]; o.gam[s + 3] = x[3];
-            if (reverse) {
-                const f32x4 y = *reinterpret_cast<const f32x4*>(P + s);
-                o.P[s] = y[0]; o.P[s + 1] = y[1]; o.P[s + 2] = y[2]; o.P[s + 3] = y[3];
+            for (int s = 0; s < SQ; s += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(Gl + s);
+                gam[s] = x[0]; gam[s + 1] = x[1]; gam[s + 2] = x[2]; gam[s + 3] = x[3];
+                if (reverse) {
+                    const f32x4 y = *reinterpret_cast<const f32x4*>(P + s);
+                    Pv[s] = y[0]; Pv[s + 1] = y[1]; Pv[s + 2] = y[2]; Pv[s + 3] = y[3];
+                } else {
+                    Pv[s] = Pv[s + 1] = Pv[s + 2] = Pv[s + 3] = 0.f;
+                }
             }
         }
-    };
-
-    // one chunk step with the operands in `cur`
-    auto step = [&](const Ops& cur, int n) {
-        const int ch = reverse ? NC - 1 - n : n;
-        const size_t R = (size_t)u * NC + ch;
 
         // the state entering the chunk (forward) or the gradient leaving it (reverse)
-        float* rec = (reverse ? a.r.dH : a.r.Hs) + R * DD + (size_t)(v0 + r16) * DK + crow;
+        float* rec = recb + R * a.r.rs + (size_t)(v0 + r16) * DK + crow;
 #pragma unroll
         for (int s = 0; s < SQ; s += 4)
             *reinterpret_cast<f32x4*>(rec + s) = (f32x4){st[s], st[s + 1], st[s + 2], st[s + 3]};
@@ -505,24 +554,29 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
             }
             *reinterpret_cast<f32x4*>(&sPart[w][r16][16 * I + 4 * q4]) = part;
         }
-        __syncthreads();
-        f32x4 pv[NWS][CQ / 4];
-#pragma unroll
-        for (int ww = 0; ww < NWS; ++ww) {
-#pragma unroll
-            for (int s = 0; s < CQ / 4; ++s)
-                pv[ww][s] = *reinterpret_cast<const f32x4*>(&sPart[ww][r16][q4 * CQ + 4 * s]);
-        }
+        lds_barrier();
         float e[CQ];
+        constexpr int HB = CQ / 4 > 1 ? CQ / 8 : 1;     // f32x4 groups read per batch
 #pragma unroll
-        for (int s = 0; s < CQ / 4; ++s) {
-            f32x4 x = pv[0][s];
+        for (int s0 = 0; s0 < CQ / 4; s0 += HB) {
+            f32x4 pv[NWS][HB];
 #pragma unroll
-            for (int ww = 1; ww < NWS; ++ww) x += pv[ww][s];
-            e[4 * s] = x[0]; e[4 * s + 1] = x[1]; e[4 * s + 2] = x[2]; e[4 * s + 3] = x[3];
+            for (int ww = 0; ww < NWS; ++ww) {
+#pragma unroll
+                for (int s = 0; s < HB; ++s)
+                    pv[ww][s] = *reinterpret_cast<const f32x4*>(&sPart[ww][r16][q4 * CQ + 4 * (s0 + s)]);
+            }
+#pragma unroll
+            for (int s = 0; s < HB; ++s) {
+                f32x4 x = pv[0][s];
+#pragma unroll
+                for (int ww = 1; ww < NWS; ++ww) x += pv[ww][s];
+                const int b4 = 4 * (s0 + s);
+                e[b4] = x[0]; e[b4 + 1] = x[1]; e[b4 + 2] = x[2]; e[b4 + 3] = x[3];
+            }
         }
         if (w == 0) {
-            float* er = (reverse ? a.r.dE : a.r.E) + R * C * DV + (size_t)(v0 + r16) * C + q4 * CQ;
+            float* er = erb + R * a.r.rs + (size_t)(v0 + r16) * C + q4 * CQ;
 #pragma unroll
             for (int s = 0; s < CQ; s += 4)
                 *reinterpret_cast<f32x4*>(er + s) = (f32x4){e[s], e[s + 1], e[s + 2], e[s + 3]};
@@ -532,27 +586,27 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         for (int t = 0; t < TPW; ++t) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < CQ; ++s) acc = mma4(cur.A2[t][s], e[s], acc);
+            for (int s = 0; s < CQ; ++s) acc = mma4(A2[t][s], e[s], acc);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int s = 4 * t + ii;
-                const float gm = ex(cur.gam[s]);
-                st[s] = reverse ? gm * st[s] + cur.P[s] - acc[ii] : gm * st[s] + acc[ii];
+                const float gm = ex(gam[s]);
+                st[s] = reverse ? gm * st[s] + Pv[s] - acc[ii] : gm * st[s] + acc[ii];
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
     auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
 
-    // two operand buffers in turn, so a prefetch is consumed a whole step
-    // after it was issued and never copied
-    Ops bufA, bufB;
-    if (NC > 0) load(bufA, chunk_of(0));
+    // two sets of early operands in turn, so a prefetch is consumed a whole
+    // step after it was issued and never copied
+    Pre bufA, bufB;
+    if (NC > 0) load_pre(bufA, chunk_of(0));
     for (int n = 0; n < NC; n += 2) {
-        load(bufB, chunk_of(n + 1));
+        load_pre(bufB, chunk_of(n + 1));
         step(bufA, n);
         if (n + 1 < NC) {
-            load(bufA, chunk_of(n + 2));
+            load_pre(bufA, chunk_of(n + 2));
             step(bufB, n + 1);
         }
     }
@@ -622,7 +676,18 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     float* sV = smem + S::oV;
     float* sdE = smem + S::odE;
 
-    for (int e = tid; e < C * C; e += NT) sT[(e / C) * LT + e % C] = a.r.Tm[R * C * C + e];
+    {
+        constexpr int NTT = (C * C / 4 + NT - 1) / NT;
+        f32x4 tv[NTT];
+#pragma unroll
+        for (int j = 0; j < NTT; ++j)
+            tv[j] = *reinterpret_cast<const f32x4*>(a.r.Tm + R * a.r.rs + 4 * min(tid + j * NT, C * C / 4 - 1));
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+            const int e = 4 * (tid + j * NT);
+            if (e < C * C) *reinterpret_cast<f32x4*>(sT + (e / C) * LT + e % C) = tv[j];
+        }
+    }
     for (int i = tid; i < C; i += NT) sBeta[i] = i < L ? a.beta[tok_v(a, b, t0 + i, h)] : 0.f;
     for (int e = tid; e < C * NB; e += NT) sPart[e / NB][e % NB] = 0.f;
 
@@ -633,34 +698,81 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     for (int s = 0; s < NYS; ++s) Y[s] = zero4();
     float zacc = 0.f, gacc = 0.f;
 
+    // One value slice of the records and inputs, requested into registers
+    // while the previous slice is being used and written to LDS at the start
+    // of its own turn.  Indices past the end are clamped for the loads (which
+    // are then unconditional) and skipped for the LDS writes.
+    constexpr int NHS = DK * VS / 4, NES = C * VS / 4, NOS = C * VS;
+    constexpr int NH = (NHS + NT - 1) / NT, NE = (NES + NT - 1) / NT, NO = (NOS + NT - 1) / NT;
+    struct Slice {
+        f32x4 hh[NH], dh[NH], ee[NE], de[NE];
+        float oo[NO], vv[NO];
+    };
+    auto load_slice = [&](Slice& x, int s) {
+        const int v0 = s * VS;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+            const int e = min(tid + j * NT, NHS - 1);
+            const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
+            const size_t o = R * a.r.rs + (size_t)(v0 + n) * DK + c;
+            x.hh[j] = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
+            x.dh[j] = *reinterpret_cast<const f32x4*>(a.r.dH + o);
+        }
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int e = min(tid + j * NT, NES - 1);
+            const int n = e / (C / 4), i = 4 * (e % (C / 4));
+            const size_t o = R * a.r.rs + (size_t)(v0 + n) * C + i;
+            x.ee[j] = *reinterpret_cast<const f32x4*>(a.r.E + o);
+            x.de[j] = *reinterpret_cast<const f32x4*>(a.r.dE + o);
+        }
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int e = min(tid + j * NT, NOS - 1);
+            const int i = clamp_row(e / VS, L), n = e % VS;
+            x.oo[j] = io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n);
+            x.vv[j] = io<IO>::load(v + tok_v(a, b, t0 + i, h) * DV + v0 + n);
+        }
+    };
+    auto store_slice = [&](const Slice& x) {
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+            const int e = tid + j * NT;
+            if (e < NHS) {
+                const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
+                *reinterpret_cast<f32x4*>(sH + n * LHT + c) = x.hh[j];
+                *reinterpret_cast<f32x4*>(sdH + n * LHT + c) = x.dh[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int e = tid + j * NT;
+            if (e < NES) {
+                const int n = e / (C / 4), i = 4 * (e % (C / 4));
+                *reinterpret_cast<f32x4*>(sE + n * LET + i) = x.ee[j];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) sdE[n * LDE + i + z] = x.de[j][z];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NO; ++j) {
+            const int e = tid + j * NT;
+            if (e < NOS) {
+                const int i = e / VS, n = e % VS;
+                sdO[i * LV + n] = keep(x.oo[j], i, L);
+                sV[i * LV + n] = keep(x.vv[j], i, L);
+            }
+        }
+    };
+
+    Slice nx;
+    load_slice(nx, 0);
     for (int s = 0; s < NS; ++s) {
         const int v0 = s * VS;
-        __syncthreads();
-        for (int e = tid; e < DK * VS / 4; e += NT) {
-            const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
-            const size_t o = R * DD + (size_t)(v0 + n) * DK + c;
-            *reinterpret_cast<f32x4*>(sH + n * LHT + c) = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
-            *reinterpret_cast<f32x4*>(sdH + n * LHT + c) = *reinterpret_cast<const f32x4*>(a.r.dH + o);
-        }
-        for (int e = tid; e < C * VS / 4; e += NT) {
-            const int n = e / (C / 4), i = 4 * (e % (C / 4));
-            const size_t o = R * C * DV + (size_t)(v0 + n) * C + i;
-            *reinterpret_cast<f32x4*>(sE + n * LET + i) = *reinterpret_cast<const f32x4*>(a.r.E + o);
-            const f32x4 y = *reinterpret_cast<const f32x4*>(a.r.dE + o);
-#pragma unroll
-            for (int z = 0; z < 4; ++z) sdE[n * LDE + i + z] = y[z];
-        }
-        for (int e = tid; e < C * VS; e += NT) {
-            const int i = e / VS, n = e % VS;
-            float dov = 0.f, vv = 0.f;
-            if (i < L) {
-                dov = io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n);
-                vv = io<IO>::load(v + tok_v(a, b, t0 + i, h) * DV + v0 + n);
-            }
-            sdO[i * LV + n] = dov;
-            sV[i * LV + n] = vv;
-        }
-        __syncthreads();
+        lds_barrier();
+        store_slice(nx);
+        if (s + 1 < NS) load_slice(nx, s + 1);
+        lds_barrier();
         // dUt = T^T dE (upper triangular: rows i take j >= 16 I), dv = beta dUt
         for (int job = w; job < NB * (VS / 16); job += NW) {
             const int I = job / (VS / 16), Vt = job % (VS / 16);
@@ -675,7 +787,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                     store_grad(a.dv, tok_v(a, b, t0 + i, h) * DV + v0 + n, sBeta[i] * acc[ii], a.gdt);
             }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < C) {
             for (int n = 0; n < VS; ++n) zacc += sdU[tid * LV + n] * sV[tid * LV + n];
         }
@@ -708,13 +820,22 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // dAqk (inclusive lower) and beta_i dA_ij, dA = -(strict lower of dUt E^T);
     // the dbeta term sum_j dA_ij Ap_ij per tile goes to sPart
     float* sdAq = smem + S::oAq;
     float* sdAb = smem + S::oAb;
     if (tid < DK) sDgam[tid] = gacc;
+    float apv[NYS][4];
+#pragma unroll
+    for (int sl = 0; sl < NYS; ++sl) {
+        int I, J;
+        lower_tile(min(w + sl * NW, 2 * NY - 1) % NY, I, J);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            apv[sl][ii] = a.r.Ap[R * a.r.rs + (16 * I + 4 * q4 + ii) * C + 16 * J + r16];
+    }
 #pragma unroll
     for (int sl = 0; sl < NYS; ++sl) {
         const int job = w + sl * NW;
@@ -732,7 +853,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 for (int ii = 0; ii < 4; ++ii) {
                     const int i = 16 * I + 4 * q4 + ii, j = 16 * J + r16;
                     const float dA = j < i ? -Y[sl][ii] : 0.f;
-                    float part = dA * a.r.Ap[R * C * C + i * C + j];
+                    float part = dA * apv[sl][ii];
                     part += __shfl_xor(part, 1);
                     part += __shfl_xor(part, 2);
                     part += __shfl_xor(part, 4);
@@ -743,7 +864,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < C) {
         float s = zacc;
         for (int J = 0; J < NB; ++J) s += sPart[tid][J];
@@ -763,14 +884,19 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = 16 * I + 4 * q4 + ii;
-            Gd[I][ii] = a.r.G[R * C * DK + i * DK + c];
-            float kv = 0.f, qv = 0.f;
-            if (i < L) {
-                kv = io<IO>::load(k + tok_qk(a, b, t0 + i, hq) * DK + c);
-                qv = io<IO>::load(q + tok_qk(a, b, t0 + i, hq) * DK + c);
-            }
-            kd[I][ii] = kv;
-            qd[I][ii] = qv;
+            Gd[I][ii] = a.r.G[R * a.r.rs + i * DK + c];
+            const size_t o = tok_qk(a, b, t0 + clamp_row(i, L), hq) * DK + c;
+            kd[I][ii] = io<IO>::load(k + o);
+            qd[I][ii] = io<IO>::load(q + o);
+        }
+    }
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * I + 4 * q4 + ii;
+            kd[I][ii] = keep(kd[I][ii], i, L);
+            qd[I][ii] = keep(qd[I][ii], i, L);
         }
     }
     f32x4 dq[NB], Pg[NB], Pinv[NB];
@@ -784,7 +910,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             for (int ii = 0; ii < 4; ++ii)
                 src0[(16 * J + 4 * q4 + ii) * 16 + r16] = kd[J][ii] * ex(Gs - Gd[J][ii]);
         }
-        __syncthreads();
+        lds_barrier();
         f32x4 ra = zero4(), rb = zero4();
         for (int kk = 0; kk < 16 * (I + 1); kk += 4) {
             const float bs = src0[(kk + q4) * 16 + r16];
@@ -798,7 +924,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             dq[I][ii] = a.scale * (eg * X1[I][ii] + f * ra[ii]);
             Pg[I][ii] = -sBeta[i] * eg * X3[I][ii] + f * rb[ii];
         }
-        __syncthreads();
+        lds_barrier();
     }
     // sums over later tokens i >= j, reference row 16 J + 15
 #pragma unroll
@@ -814,7 +940,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 src1[row * 16 + r16] = a.scale * qd[I][ii] * f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         f32x4 acc = zero4();
         for (int kk = 16 * J; kk < C; kk += 4) {
             acc = mma4(sdAb[(kk + q4) * LA + 16 * J + r16], src0[(kk + q4) * 16 + r16], acc);
@@ -822,7 +948,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) Pinv[J][ii] = ex(Ge - Gd[J][ii]) * acc[ii];
-        __syncthreads();
+        lds_barrier();
     }
 
     // dk, dq, dG; the dbeta term -sum_c (dUt H^T)_ic k_ic e^G_ic
@@ -869,7 +995,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) src0[(16 * I + 4 * q4 + ii) * 16 + r16] = dG[I][ii];
         }
-        __syncthreads();
+        lds_barrier();
         float seg[16];
         float tot = 0.f;
         if (16 * q4 < C) {
@@ -902,7 +1028,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (a.mode == KDA_GATE_SCALAR && w == 0) {
         float x = 0.f;
         if (lane < C) {
