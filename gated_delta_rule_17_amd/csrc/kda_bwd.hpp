@@ -458,16 +458,20 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     const size_t DD = (size_t)DK * DV;
     const int cw0 = w * CPW;
     const int NC = a.NC;
-    // channel of strip slot s of this lane, and of row m of output tile t
-    const int crow = cw0 + q4 * SQ;                       // + s
-    const int ctile = cw0 + (r16 >> 2) * SQ + (r16 & 3);  // + 4 t
+    // Strip slot s = 4 j + z of lane (r16, q4) holds key channel
+    // cw0 + 16 j + 4 q4 + z, and output tile t of the strip update covers
+    // channels cw0 + 16 t .. + 15 in order: the accumulator element ii of
+    // tile t is then slot 4 t + ii, and every per-lane vector access below
+    // reads 16 bytes of a 64-byte run shared with the three other lane groups.
+    const int cbase = cw0 + 4 * q4;
+    auto chan = [&](int s) { return cbase + 16 * (s >> 2) + (s & 3); };
 
     float st[SQ];
     {
         const float* init = reverse ? a.dhT : a.h0;
 #pragma unroll
         for (int s = 0; s < SQ; ++s)
-            st[s] = init ? init[(size_t)u * DD + (size_t)(crow + s) * DV + v0 + r16] : 0.f;
+            st[s] = init ? init[(size_t)u * DD + (size_t)chan(s) * DV + v0 + r16] : 0.f;
     }
 
     // record bases of this role
@@ -488,10 +492,10 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         const size_t R = (size_t)u * NC + ch;
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
-            const float* p = A1b + R * a.r.rs + (16 * I + r16) * DK + crow;
+            const float* p = A1b + R * a.r.rs + (16 * I + r16) * DK + cbase;
 #pragma unroll
             for (int s = 0; s < SQ; s += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * s);
                 o.A1[I][s] = x[0]; o.A1[I][s + 1] = x[1]; o.A1[I][s + 2] = x[2]; o.A1[I][s + 3] = x[3];
             }
             if (w == 0) {
@@ -510,22 +514,22 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         float A2[TPW][CQ], gam[SQ], Pv[SQ];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const float* p = A2b + R * a.r.rs + (size_t)(ctile + 4 * t) * C + q4 * CQ;
+            const float* p = A2b + R * a.r.rs + (size_t)(cw0 + 16 * t + r16) * C + 4 * q4;
 #pragma unroll
             for (int s = 0; s < CQ; s += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(p + s);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * s);
                 A2[t][s] = x[0]; A2[t][s + 1] = x[1]; A2[t][s + 2] = x[2]; A2[t][s + 3] = x[3];
             }
         }
         {
-            const float* Gl = a.r.G + R * a.r.rs + (C - 1) * DK + crow;
-            const float* P = a.r.P + R * a.r.rs + (size_t)(v0 + r16) * DK + crow;
+            const float* Gl = a.r.G + R * a.r.rs + (C - 1) * DK + cbase;
+            const float* P = a.r.P + R * a.r.rs + (size_t)(v0 + r16) * DK + cbase;
 #pragma unroll
             for (int s = 0; s < SQ; s += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(Gl + s);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(Gl + 4 * s);
                 gam[s] = x[0]; gam[s + 1] = x[1]; gam[s + 2] = x[2]; gam[s + 3] = x[3];
                 if (reverse) {
-                    const f32x4 y = *reinterpret_cast<const f32x4*>(P + s);
+                    const f32x4 y = *reinterpret_cast<const f32x4*>(P + 4 * s);
                     Pv[s] = y[0]; Pv[s + 1] = y[1]; Pv[s + 2] = y[2]; Pv[s + 3] = y[3];
                 } else {
                     Pv[s] = Pv[s + 1] = Pv[s + 2] = Pv[s + 3] = 0.f;
@@ -534,10 +538,10 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         }
 
         // the state entering the chunk (forward) or the gradient leaving it (reverse)
-        float* rec = recb + R * a.r.rs + (size_t)(v0 + r16) * DK + crow;
+        float* rec = recb + R * a.r.rs + (size_t)(v0 + r16) * DK + cbase;
 #pragma unroll
         for (int s = 0; s < SQ; s += 4)
-            *reinterpret_cast<f32x4*>(rec + s) = (f32x4){st[s], st[s + 1], st[s + 2], st[s + 3]};
+            *reinterpret_cast<f32x4*>(rec + 4 * s) = (f32x4){st[s], st[s + 1], st[s + 2], st[s + 3]};
 
         // partial sums over this wave's channels
 #pragma unroll
@@ -564,7 +568,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
             for (int ww = 0; ww < NWS; ++ww) {
 #pragma unroll
                 for (int s = 0; s < HB; ++s)
-                    pv[ww][s] = *reinterpret_cast<const f32x4*>(&sPart[ww][r16][q4 * CQ + 4 * (s0 + s)]);
+                    pv[ww][s] = *reinterpret_cast<const f32x4*>(&sPart[ww][r16][16 * (s0 + s) + 4 * q4]);
             }
 #pragma unroll
             for (int s = 0; s < HB; ++s) {
@@ -576,10 +580,10 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
             }
         }
         if (w == 0) {
-            float* er = erb + R * a.r.rs + (size_t)(v0 + r16) * C + q4 * CQ;
+            float* er = erb + R * a.r.rs + (size_t)(v0 + r16) * C + 4 * q4;
 #pragma unroll
             for (int s = 0; s < CQ; s += 4)
-                *reinterpret_cast<f32x4*>(er + s) = (f32x4){e[s], e[s + 1], e[s + 2], e[s + 3]};
+                *reinterpret_cast<f32x4*>(er + 4 * s) = (f32x4){e[s], e[s + 1], e[s + 2], e[s + 3]};
         }
         // update of this wave's strip
 #pragma unroll
@@ -612,7 +616,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     }
     if (reverse && a.dh0) {
 #pragma unroll
-        for (int s = 0; s < SQ; ++s) a.dh0[(size_t)u * DD + (size_t)(crow + s) * DV + v0 + r16] = st[s];
+        for (int s = 0; s < SQ; ++s) a.dh0[(size_t)u * DD + (size_t)chan(s) * DV + v0 + r16] = st[s];
     }
 }
 // ---------------------------------------------------------------------------
@@ -795,12 +799,12 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             for (int n = 0; n < VS; ++n) gacc += sH[n * LHT + tid] * sdH[n * LHT + tid];
         }
         // products with the state and its gradient for this wave's 16 channels
+#pragma unroll 2
+        for (int kk = 0; kk < VS; kk += 4) {
+            const float bH = sH[(kk + q4) * LHT + 16 * w + r16];
+            const float bdH = sdH[(kk + q4) * LHT + 16 * w + r16];
 #pragma unroll
-        for (int I = 0; I < NB; ++I) {
-#pragma unroll
-            for (int kk = 0; kk < VS; kk += 4) {
-                const float bH = sH[(kk + q4) * LHT + 16 * w + r16];
-                const float bdH = sdH[(kk + q4) * LHT + 16 * w + r16];
+            for (int I = 0; I < NB; ++I) {
                 X1[I] = mma4(sdO[(16 * I + r16) * LV + kk + q4], bH, X1[I]);
                 X2[I] = mma4(sE[(kk + q4) * LET + 16 * I + r16], bdH, X2[I]);
                 X3[I] = mma4(sdU[(16 * I + r16) * LV + kk + q4], bH, X3[I]);
@@ -814,7 +818,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 int I, J;
                 lower_tile(job % NY, I, J);
                 const float* A = job >= NY ? sdU : sdO;
-#pragma unroll
+#pragma unroll 4
                 for (int kk = 0; kk < VS; kk += 4)
                     Y[sl] = mma4(A[(16 * I + r16) * LV + kk + q4], sE[(kk + q4) * LET + 16 * J + r16], Y[sl]);
             }
@@ -899,34 +903,8 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             qd[I][ii] = keep(qd[I][ii], i, L);
         }
     }
-    f32x4 dq[NB], Pg[NB], Pinv[NB];
-    // sums over earlier tokens j <= i, reference row 16 I
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-        const float Gs = __shfl(Gd[I][0], r16);
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                src0[(16 * J + 4 * q4 + ii) * 16 + r16] = kd[J][ii] * ex(Gs - Gd[J][ii]);
-        }
-        lds_barrier();
-        f32x4 ra = zero4(), rb = zero4();
-        for (int kk = 0; kk < 16 * (I + 1); kk += 4) {
-            const float bs = src0[(kk + q4) * 16 + r16];
-            ra = mma4(sdAq[(16 * I + r16) * LA + kk + q4], bs, ra);
-            rb = mma4(sdAb[(16 * I + r16) * LA + kk + q4], bs, rb);
-        }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int i = 16 * I + 4 * q4 + ii;
-            const float f = ex(Gd[I][ii] - Gs), eg = ex(Gd[I][ii]);
-            dq[I][ii] = a.scale * (eg * X1[I][ii] + f * ra[ii]);
-            Pg[I][ii] = -sBeta[i] * eg * X3[I][ii] + f * rb[ii];
-        }
-        lds_barrier();
-    }
     // sums over later tokens i >= j, reference row 16 J + 15
+    f32x4 Pinv[NB];
 #pragma unroll
     for (int J = NB - 1; J >= 0; --J) {
         const float Ge = __shfl(Gd[J][3], 48 + r16);
@@ -951,21 +929,39 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         lds_barrier();
     }
 
-    // dk, dq, dG; the dbeta term -sum_c (dUt H^T)_ic k_ic e^G_ic
+    // sums over earlier tokens j <= i (reference row 16 I), and with them each
+    // 16-row block's dq, dk and dG (staged in src1 for the suffix sums); the
+    // dbeta term -sum_c (dUt H^T)_ic k_ic e^G_ic goes to sRow
     const float Gl = __shfl(Gd[NB - 1][3], 48 + r16);
     const bool grouped = a.dqp != nullptr;
-    float dG[NB][4];
     float colPr = 0.f;
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
+        const float Gs = __shfl(Gd[I][0], r16);
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                src0[(16 * J + 4 * q4 + ii) * 16 + r16] = kd[J][ii] * ex(Gs - Gd[J][ii]);
+        }
+        lds_barrier();
+        f32x4 ra = zero4(), rb = zero4();
+        for (int kk = 0; kk < 16 * (I + 1); kk += 4) {
+            const float bs = src0[(kk + q4) * 16 + r16];
+            ra = mma4(sdAq[(16 * I + r16) * LA + kk + q4], bs, ra);
+            rb = mma4(sdAb[(16 * I + r16) * LA + kk + q4], bs, rb);
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = 16 * I + 4 * q4 + ii;
+            const float f = ex(Gd[I][ii] - Gs), eg = ex(Gd[I][ii]);
+            const float dqv = a.scale * (eg * X1[I][ii] + f * ra[ii]);
+            const float pg = -sBeta[i] * eg * X3[I][ii] + f * rb[ii];
             const float pr = ex(Gl - Gd[I][ii]) * X2[I][ii];
-            const float dkv = Pg[I][ii] + Pinv[I][ii] + pr;
-            dG[I][ii] = kd[I][ii] * (Pg[I][ii] - Pinv[I][ii] - pr) + qd[I][ii] * dq[I][ii];
+            const float dkv = pg + Pinv[I][ii] + pr;
+            src1[i * 16 + r16] = kd[I][ii] * (pg - Pinv[I][ii] - pr) + qd[I][ii] * dqv;
             colPr += pr * kd[I][ii];
-            float x3 = X3[I][ii] * kd[I][ii] * ex(Gd[I][ii]);
+            float x3 = X3[I][ii] * kd[I][ii] * eg;
             x3 += __shfl_xor(x3, 1);
             x3 += __shfl_xor(x3, 2);
             x3 += __shfl_xor(x3, 4);
@@ -974,34 +970,30 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             if (i < L) {
                 if (grouped) {
                     const size_t o = tok_v(a, b, t0 + i, h) * DK + c;
-                    a.dqp[o] = dq[I][ii];
+                    a.dqp[o] = dqv;
                     a.dkp[o] = dkv;
                 } else {
                     const size_t o = tok_qk(a, b, t0 + i, hq) * DK + c;
-                    store_grad(a.dq, o, dq[I][ii], a.gdt);
+                    store_grad(a.dq, o, dqv, a.gdt);
                     store_grad(a.dk, o, dkv, a.gdt);
                 }
             }
         }
+        lds_barrier();
     }
     colPr += __shfl_xor(colPr, 16);
     colPr += __shfl_xor(colPr, 32);
-    if (q4 == 3) dG[NB - 1][3] += colPr + sDgam[c] * ex(Gl);
+    if (q4 == 3) src1[(C - 1) * 16 + r16] += colPr + sDgam[c] * ex(Gl);
+    lds_barrier();
 
     if (a.mode == KDA_GATE_CHANNEL) {
         // dg = suffix sums of dG over the rows of the chunk, per channel
-#pragma unroll
-        for (int I = 0; I < NB; ++I) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) src0[(16 * I + 4 * q4 + ii) * 16 + r16] = dG[I][ii];
-        }
-        lds_barrier();
         float seg[16];
         float tot = 0.f;
         if (16 * q4 < C) {
 #pragma unroll
             for (int m = 15; m >= 0; --m) {
-                tot += src0[(16 * q4 + m) * 16 + r16];
+                tot += src1[(16 * q4 + m) * 16 + r16];
                 seg[m] = tot;
             }
         }
@@ -1015,17 +1007,12 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             }
         }
     } else if (a.mode == KDA_GATE_SCALAR) {
+        // row sums of dG over this wave's 16 channels
+        if (lane < C) {
+            float x = 0.f;
 #pragma unroll
-        for (int I = 0; I < NB; ++I) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                float x = dG[I][ii];
-                x += __shfl_xor(x, 1);
-                x += __shfl_xor(x, 2);
-                x += __shfl_xor(x, 4);
-                x += __shfl_xor(x, 8);
-                if (r16 == 0) sRowG[w * C + 16 * I + 4 * q4 + ii] = x;
-            }
+            for (int cc = 0; cc < 16; ++cc) x += src1[lane * 16 + cc];
+            sRowG[w * C + lane] = x;
         }
     }
     lds_barrier();
