@@ -22,7 +22,7 @@ token-head plus 2 * d_k * d_v * 4 B of initial/final state per (b, h).
 profiles/traffic.json and is null when the kernel source changed since.
 ``cpu_baseline`` times the fp64 CPU oracle (test infrastructure) on the host.
 ``varlen`` (outside the timed steps) times the packed variable-length entry
-points on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
+points (both forward forms and the gradient) on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
 d=128, bf16, in both forms.  ``grouped_heads`` (4 query/key heads for the 16
 value heads) and ``mixed_dims`` (d_k 64, d_v 128) time kda_chunk_fwd on the
 prefill shape B1 T4096 H16, likewise outside the timed steps.  ``backward``
@@ -180,6 +180,17 @@ def bench_varlen(K, torch, dev, warmup, reps):
     def rec():
         K.kda_recurrent_varlen(q, k, v, g, beta, st, cu, o=o)
 
+    do = t(np.random.default_rng(np.random.SeedSequence([17, 0xD0])).standard_normal(
+        (T, H, D), dtype=np.float32), torch.bfloat16)
+    wsb = torch.empty(K.kda_chunk_bwd_varlen_workspace_size(N, T, H, H, D, D, 64, 0, K.BF16),
+                      dtype=torch.uint8, device=dev)
+    grads = K.kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu, initial_state=h0, chunk=64,
+                                   workspace=wsb)
+
+    def bwd():
+        K.kda_chunk_bwd_varlen(q, k, v, g, beta, do, cu, initial_state=h0, chunk=64,
+                               workspace=wsb, out=grads)
+
     def timed(fn):
         for _ in range(warmup):
             fn()
@@ -192,7 +203,7 @@ def bench_varlen(K, torch, dev, warmup, reps):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps / 1e3
 
-    tc, tr = timed(chunk), timed(rec)
+    tc, tr, tb = timed(chunk), timed(rec), timed(bwd)
     nbytes = T * H * (4 * D * 2 + D * 4 + 4) + N * H * 2 * D * D * 4
     return {"workload": f"{N} sequences, log-uniform lengths 1..2048 (seed 17), {T} tokens, "
                         "H16 d128 bf16, fp32 states",
@@ -200,6 +211,7 @@ def bench_varlen(K, torch, dev, warmup, reps):
             "chunk_ms": tc * 1e3, "chunk_tokens_per_s": T / tc,
             "chunk_hbm_frac": nbytes / tc / 1e9 / HBM_PEAK_GBPS,
             "recurrent_ms": tr * 1e3, "recurrent_tokens_per_s": T / tr,
+            "backward_ms": tb * 1e3, "backward_tokens_per_s": T / tb,
             "algorithmic_bytes": nbytes}
 
 

@@ -19,6 +19,9 @@ Entry points (same names as the C ABI):
   kda_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
                 chunk=64, scale=None, mode=None, workspace=None, out=None)
   kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype)
+  kda_chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, initial_state=None,
+                       d_final_state=None, chunk=64, scale=None, mode=None, workspace=None)
+  kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, mode, dtype)
 
 Every compute call takes ``prologue``, a bitwise OR of NORMALIZE_QK,
 BETA_SIGMOID and GATE_LOGSIGMOID (0: inputs used as given).
@@ -82,6 +85,11 @@ def lib():
     L.kda_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp,
                                 i, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     L.kda_chunk_bwd.restype = i
+    L.kda_chunk_bwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i]
+    L.kda_chunk_bwd_varlen_workspace_size.restype = sz
+    L.kda_chunk_bwd_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp, vp,
+                                       i, i, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    L.kda_chunk_bwd_varlen.restype = i
     L.kda_status_string.argtypes = [i]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_version.restype = i
@@ -410,4 +418,79 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
                              workspace.numel(), _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_bwd")
+    return out
+
+
+def kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, mode, dtype) -> int:
+    if isinstance(mode, str):
+        mode = _MODE_NAMES[mode]
+    return int(lib().kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, int(mode),
+                                                         int(dtype)))
+
+
+def kda_chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, initial_state=None,
+                         d_final_state=None, chunk: int = 64, scale: Optional[float] = None,
+                         mode=None, workspace=None, out=None, want_d_initial_state: bool = True,
+                         grad_dtype=None):
+    """Gradients of :func:`kda_chunk_fwd_varlen` for the same packed inputs.
+
+    Token tensors are packed [T, heads, D] as for the packed forward;
+    ``cu_seqlens`` is an int32 device tensor [N + 1]; ``initial_state`` and
+    ``d_final_state`` are float32 [N, H, Dk, Dv] or None.  Returns the dict of
+    :func:`kda_chunk_bwd` (d_initial_state [N, H, Dk, Dv]).
+    """
+    torch = _torch()
+    T, Hqk, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
+    m = _mode_of_packed(g, mode)
+    _check_cu(cu_seqlens)
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("k", k, q.dtype, q.shape)
+    if v.shape[0] != T:
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
+    _check_dev("d_o", d_o, q.dtype, v.shape)
+    _check_dev("g", g, torch.float32)
+    _check_dev("beta", beta, torch.float32, (T, H))
+    _check_dev("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
+    _check_dev("d_final_state", d_final_state, torch.float32, (N, H, Dk, Dv))
+    out = dict(out or {})
+    dev = q.device
+    if out.get("dq") is not None:
+        grad_dtype = out["dq"].dtype
+    gdt = grad_dtype or q.dtype
+    for name, ref in (("dq", q), ("dk", k), ("dv", v)):
+        if out.get(name) is None:
+            out[name] = torch.empty(ref.shape, dtype=gdt, device=dev)
+    if m == GATE_NONE:
+        out["dg"] = None
+    elif out.get("dg") is None:
+        out["dg"] = torch.empty_like(g)
+    if out.get("dbeta") is None:
+        out["dbeta"] = torch.empty_like(beta)
+    if want_d_initial_state and out.get("d_initial_state") is None:
+        out["d_initial_state"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    if not want_d_initial_state:
+        out["d_initial_state"] = None
+    _check_dev("dq", out["dq"], gdt, q.shape)
+    _check_dev("dk", out["dk"], gdt, q.shape)
+    _check_dev("dv", out["dv"], gdt, v.shape)
+    _check_dev("dg", out["dg"], torch.float32, None if g is None else g.shape)
+    _check_dev("dbeta", out["dbeta"], torch.float32, (T, H))
+    _check_dev("d_initial_state", out["d_initial_state"], torch.float32, (N, H, Dk, Dv))
+    dt = _dtype_code(q)
+    need = kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, m, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_chunk_bwd_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(d_o),
+        _ptr(d_final_state), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+        _ptr(out["dbeta"]), _ptr(out["d_initial_state"]), _ptr(cu_seqlens), N, T, H, Hqk, Dk, Dv,
+        int(chunk), float(scale), m, dt, _dtype_code(out["dq"]), _ptr(workspace),
+        workspace.numel(), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_chunk_bwd_varlen")
     return out

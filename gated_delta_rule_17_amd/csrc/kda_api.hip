@@ -217,4 +217,55 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
 
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                                           kda_gate_mode mode, kda_dtype dtype)
+{
+    (void)mode;
+    if (N < 1 || H < 1 || T < 0) return 0;
+    if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
+    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    return kda::chunk_bwd_varlen_workspace_bytes(N, T, H, Hqk, Dk, Dv, chunk);
+}
+
+kda_status kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* initial_state, const void* d_o,
+                                const float* d_final_state, void* dq, void* dk, void* dv,
+                                float* dg, float* dbeta, float* d_initial_state,
+                                const int* cu_seqlens, int N, int T, int H, int Hqk, int Dk,
+                                int Dv, int chunk, float scale, kda_gate_mode mode,
+                                kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    if (N < 0) return KDA_ERROR_INVALID_VALUE;
+    kda_status st = check_common(q, k, v, g, beta, d_o, 1, T, H, Hqk, Dk, Dv, mode, dtype, grad_dtype);
+    if (st != KDA_SUCCESS) return st;
+    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    const double gmax = (double)((T + chunk - 1) / chunk) + (double)N;
+    if (gmax * H > 1073741824.0 || (double)N * H * 2.0 > 65535.0 * 1024.0)
+        return KDA_ERROR_INVALID_VALUE;
+    if (N == 0) return KDA_SUCCESS;
+    if (!cu_seqlens) return KDA_ERROR_INVALID_VALUE;
+    if (((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
+    if (T > 0) {
+        if (!dq || !dk || !dv || !dbeta) return KDA_ERROR_INVALID_VALUE;
+        if (mode != KDA_GATE_NONE && !dg) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(dbeta))
+            return KDA_ERROR_MISALIGNED;
+        if (dg && !aligned16(dg)) return KDA_ERROR_MISALIGNED;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
+        (d_initial_state && !aligned16(d_initial_state)))
+        return KDA_ERROR_MISALIGNED;
+    const size_t need = kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, mode, dtype);
+    if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return KDA_ERROR_MISALIGNED;
+    if (T == 0 && !d_initial_state) return KDA_SUCCESS;
+    kda::ChunkBwdArgs a{q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                        d_initial_state, 1, T, H, Hqk, Dk, Dv, chunk, scale, mode, dtype,
+                        grad_dtype, workspace, workspace_bytes, cu_seqlens, N};
+    hipError_t e = kda::launch_chunk_bwd(a, (hipStream_t)stream);
+    return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
+}
+
 }  // extern "C"

@@ -14,14 +14,19 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct BwdLayout {
     size_t G, W, WT, Kr, KrT, U, Ut, P, Tm, Ap, Hs, E, dH, dE;   // float offsets in a record
     size_t rs;                                                  // floats per record
-    size_t dqp, dkp, total;                                     // bytes
+    size_t dqp, dkp, ctab, stab, total;                         // bytes
+    size_t gmax;                                                // packed: chunk slots
 };
 
-BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
+// Dense batch: B * H * ceil(T / C) records.  Packed batch (N > 0, B = 1):
+// H * gmax records, gmax = ceil(T / C) + N chunk slots, then the chunk and
+// sequence tables.
+BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C, int N = 0)
 {
     BwdLayout l{};
     const size_t NC = (size_t)((T + C - 1) / C);
-    const size_t R = (size_t)B * H * NC;
+    l.gmax = N > 0 ? packed_chunk_slots(N, T, C) : 0;
+    const size_t R = N > 0 ? (size_t)H * l.gmax : (size_t)B * H * NC;
     size_t o = 0;
     auto take = [&](size_t floats) { const size_t at = o; o += floats; return at; };
     l.G = take((size_t)C * Dk);
@@ -45,6 +50,12 @@ BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C)
     b = align256(b + part);
     l.dkp = b;
     b = align256(b + part);
+    if (N > 0) {
+        l.ctab = b;
+        b = align256(b + l.gmax * sizeof(int2));
+        l.stab = b;
+        b = align256(b + (size_t)N * sizeof(int4));
+    }
     l.total = b;
     return l;
 }
@@ -57,10 +68,17 @@ size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Hq, int Dk, int Dv, in
     return bwd_layout(B, T, H, Hq, Dk, Dv, chunk).total;
 }
 
+size_t chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int Hq, int Dk, int Dv, int chunk)
+{
+    if (N <= 0) return 0;
+    return bwd_layout(1, T, H, Hq, Dk, Dv, chunk, N).total;
+}
+
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
 {
     const int C = h.chunk;
-    const BwdLayout l = bwd_layout(h.B, h.T, h.H, h.Hq, h.Dk, h.Dv, C);
+    const bool packed = h.cu != nullptr;
+    const BwdLayout l = bwd_layout(h.B, h.T, h.H, h.Hq, h.Dk, h.Dv, C, packed ? h.N : 0);
     char* ws = (char*)h.ws;
     bwd::Args a{};
     a.q = h.q; a.k = h.k; a.v = h.v; a.dO = h.dO;
@@ -90,6 +108,20 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
     }
     a.B = h.B; a.T = h.T; a.H = h.H; a.Hq = h.Hq;
     a.NC = (h.T + C - 1) / C;
+    a.ctab = nullptr;
+    a.stab = nullptr;
+    a.N = 0;
+    a.Gmax = 0;
+    if (packed) {
+        if (h.N == 0) return hipSuccess;
+        a.B = 1;
+        a.N = h.N;
+        a.Gmax = (int)l.gmax;
+        a.ctab = (const int2*)(ws + l.ctab);
+        a.stab = (const int4*)(ws + l.stab);
+        hipError_t e = build_varlen_tables(h.cu, h.N, h.T, C, l.gmax, ws + l.ctab, ws + l.stab, s);
+        if (e != hipSuccess) return e;
+    }
     a.mode = (int)h.mode;
     a.gdt = (int)h.grad_dtype;
     a.scale = h.scale;

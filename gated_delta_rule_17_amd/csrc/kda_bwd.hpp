@@ -54,7 +54,8 @@ namespace kda {
 namespace bwd {
 
 // Per-chunk float32 records in the workspace; record r = unit * NC + chunk,
-// unit = b * H + h.  Rows of a ragged last chunk beyond its length are zero
+// unit = b * H + h (dense batch), or r = h * Gmax + g for chunk slot g of a
+// packed batch (the chunks of one sequence are consecutive slots).  Rows of a ragged last chunk beyond its length are zero
 // (G repeats its last valid row).
 struct Records {
     float* G;    // [C][DK]  inclusive prefix of the log gates
@@ -83,6 +84,12 @@ struct Args {
     float* dqp; float* dkp;   // grouped heads: float partials per value head, else null
     Records r;
     int B, T, H, Hq, NC, mode;
+    // packed batch: chunk table (first token, length) of Gmax slots, sequence
+    // table (first token, length, first slot, 0) of N sequences; B = 1 and T
+    // the packed token count.  Null for a dense batch.
+    const int2* ctab;
+    const int4* stab;
+    int N, Gmax;
     int gdt;                  // storage type of dq, dk, dv (kda_dtype)
     float scale;
 };
@@ -133,6 +140,30 @@ __device__ __forceinline__ GatePtr gate_ptr(const Args& a, int b, int t0, int h,
     if (a.mode == KDA_GATE_CHANNEL) return {a.g + row0 * DK + c, (size_t)a.H * DK, 1.f};
     if (a.mode == KDA_GATE_SCALAR) return {a.g + row0, (size_t)a.H, 1.f};
     return {a.beta + row0, (size_t)a.H, 0.f};
+}
+
+// The chunk of a per-chunk workgroup: batch entry, value head, first token
+// and length (0 for an empty slot of a packed batch).
+struct ChunkLoc {
+    int b, h, t0, L;
+};
+template <int C>
+__device__ __forceinline__ ChunkLoc locate_chunk(const Args& a, int rec) {
+    ChunkLoc l;
+    if (a.ctab) {
+        l.b = 0;
+        l.h = rec / a.Gmax;
+        const int2 e = a.ctab[rec % a.Gmax];
+        l.t0 = e.x;
+        l.L = e.y;
+    } else {
+        const int u = rec / a.NC, ch = rec % a.NC;
+        l.b = u / a.H;
+        l.h = u % a.H;
+        l.t0 = ch * C;
+        l.L = min(C, a.T - l.t0);
+    }
+    return l;
 }
 
 // Index of the n-th lower block tile (I, J), J <= I, of an NB x NB grid.
@@ -189,10 +220,11 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const int rec = blockIdx.x;
-    const int u = rec / a.NC, ch = rec % a.NC;
-    const int b = u / a.H, h = u % a.H, hq = h / (a.H / a.Hq);
-    const int t0 = ch * C;
-    const int L = min(C, a.T - t0);
+    const ChunkLoc loc = locate_chunk<C>(a, rec);
+    if (loc.L <= 0) return;                  // empty slot of a packed batch
+    const int b = loc.b, h = loc.h, hq = h / (a.H / a.Hq);
+    const int t0 = loc.t0;
+    const int L = loc.L;
     const IO* q = (const IO*)a.q;
     const IO* k = (const IO*)a.k;
     const IO* v = (const IO*)a.v;
@@ -444,7 +476,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     __shared__ __align__(16) float sPart[NWS][16][LP];   // per-wave partial sums, [column][row]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
-    const int units = a.B * a.H;
+    const int units = (a.stab ? a.N : a.B) * a.H;   // (sequence, head) pairs
     // Workgroups are handed to the eight XCDs round-robin by id; the DV / 16
     // value tiles of one (role, head) take ids 8 apart, so they share an XCD
     // and its L2, which then serves the records they all read.
@@ -457,7 +489,19 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     const int v0 = vt * 16;
     const size_t DD = (size_t)DK * DV;
     const int cw0 = w * CPW;
-    const int NC = a.NC;
+    // chunks of this (sequence, head): records R = rbase + rstep * chunk
+    int NC;
+    size_t rbase, rstep;
+    if (a.stab) {
+        const int4 sq = a.stab[u / a.H];
+        NC = (sq.y + C - 1) / C;
+        rbase = (size_t)(u % a.H) * a.Gmax + sq.z;
+        rstep = 1;
+    } else {
+        NC = a.NC;
+        rbase = (size_t)u * a.NC;
+        rstep = 1;
+    }
     // Strip slot s = 4 j + z of lane (r16, q4) holds key channel
     // cw0 + 16 j + 4 q4 + z, and output tile t of the strip update covers
     // channels cw0 + 16 t .. + 15 in order: the accumulator element ii of
@@ -489,7 +533,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         float add[NB][4];
     };
     auto load_pre = [&](Pre& o, int ch) {
-        const size_t R = (size_t)u * NC + ch;
+        const size_t R = rbase + rstep * ch;
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
             const float* p = A1b + R * a.r.rs + (16 * I + r16) * DK + cbase;
@@ -509,7 +553,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     // one chunk step with its early operands in `cur`
     auto step = [&](const Pre& cur, int n) {
         const int ch = reverse ? NC - 1 - n : n;
-        const size_t R = (size_t)u * NC + ch;
+        const size_t R = rbase + rstep * ch;
         // operands of the strip update, first used after the exchange
         float A2[TPW][CQ], gam[SQ], Pv[SQ];
 #pragma unroll
@@ -660,10 +704,11 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r16 = lane & 15, q4 = lane >> 4;
     const int rec = blockIdx.x;
-    const int u = rec / a.NC, ch = rec % a.NC;
-    const int b = u / a.H, h = u % a.H, hq = h / (a.H / a.Hq);
-    const int t0 = ch * C;
-    const int L = min(C, a.T - t0);
+    const ChunkLoc loc = locate_chunk<C>(a, rec);
+    if (loc.L <= 0) return;                  // empty slot of a packed batch
+    const int b = loc.b, h = loc.h, hq = h / (a.H / a.Hq);
+    const int t0 = loc.t0;
+    const int L = loc.L;
     const size_t R = (size_t)rec;
     const size_t DD = (size_t)DK * DV;
     const IO* q = (const IO*)a.q;
@@ -1067,8 +1112,8 @@ namespace bwd {
 template <int C, int DK, int DV, typename IO>
 hipError_t launch3(const Args& a, hipStream_t s)
 {
-    const int units = a.B * a.H;
-    const unsigned nrec = (unsigned)units * (unsigned)a.NC;
+    const int units = (a.stab ? a.N : a.B) * a.H;
+    const unsigned nrec = a.ctab ? (unsigned)a.H * (unsigned)a.Gmax : (unsigned)units * (unsigned)a.NC;
     if (nrec > 0) {
         hipLaunchKernelGGL((bwd_prep<C, DK, DV, IO>), dim3(nrec), dim3(prep_threads<C, DK, DV>()), 0, s,
                            a);

@@ -102,6 +102,16 @@ size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int 
     return packed_layout(N, Ttot, H, Dk, Dv, chunk, dtype).total;
 }
 
+size_t packed_chunk_slots(int N, int T, int chunk) { return varlen_gmax(N, T, chunk); }
+
+hipError_t build_varlen_tables(const int* cu, int N, int T, int chunk, size_t gmax, void* ctab,
+                               void* stab, hipStream_t s)
+{
+    hipLaunchKernelGGL(varlen_tables, dim3(1), dim3(1024), 0, s, cu, N, T, chunk, (int)gmax,
+                       (int2*)ctab, (int4*)stab);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk(const ChunkArgs& a0, hipStream_t s)
 {
     ChunkArgs a = a0;

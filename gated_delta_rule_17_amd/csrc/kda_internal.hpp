@@ -61,6 +61,10 @@ struct ChunkBwdArgs {
     kda_dtype dtype;      // q, k, v, dO
     kda_dtype grad_dtype; // dq, dk, dv
     void* ws; size_t ws_bytes;
+    // packed variable-length batch: device offsets [N + 1] (T is the packed
+    // token count, B is 1), or null for a dense [B, T] batch
+    const int* cu = nullptr;
+    int N = 0;
 };
 
 hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);
@@ -70,8 +74,16 @@ size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda
 size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
 hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 
+// Chunk and sequence tables of a packed batch (one workgroup, asynchronous):
+// gmax chunk slots of (first token, length) and N sequences of (first token,
+// length, first slot, 0), from device offsets cu[N + 1].
+size_t packed_chunk_slots(int N, int T, int chunk);
+hipError_t build_varlen_tables(const int* cu, int N, int T, int chunk, size_t gmax, void* ctab,
+                               void* stab, hipStream_t s);
+
 // Gradient of the chunk path: workspace bytes and launch.
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Hq, int Dk, int Dv, int chunk);
+size_t chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int Hq, int Dk, int Dv, int chunk);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs& a, hipStream_t s);
 
 }  // namespace kda

@@ -289,8 +289,9 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv
  *   workspace      at least kda_chunk_bwd_workspace_size(...) bytes,
  *                  256-byte aligned, caller-owned scratch
  *
- * Outputs must not alias inputs or each other.  The fused prologue and
- * packed batches are forward-only: pass the transformed inputs.  Within a
+ * Outputs must not alias inputs or each other.  The fused prologue is
+ * forward-only: pass the transformed inputs (and take the prologue's own
+ * gradients outside).  Within a
  * chunk the kernels split decays at 16-token boundaries, so results stay
  * finite while no key channel's log gates sum below about -80 over 16
  * consecutive tokens (a per-token g above about -5).
@@ -302,6 +303,39 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          int Dk, int Dv, int chunk, float scale, kda_gate_mode mode,
                          kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_bwd_varlen_workspace_size -- bytes of device workspace
+ * kda_chunk_bwd_varlen needs (0 for unsupported arguments or N = 0): records
+ * for ceil(T / chunk) + N chunks per head, the chunk and sequence tables,
+ * and 8 T H Dk bytes when Hqk < H.
+ */
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                                           kda_gate_mode mode, kda_dtype dtype);
+
+/*
+ * kda_chunk_bwd_varlen -- kda_chunk_bwd over a packed batch (see "Packed
+ * variable-length batches"): the gradients of kda_chunk_fwd_varlen.  Every
+ * sequence is cut into chunks from its own first token and carries its own
+ * state and state gradient; results equal separate kda_chunk_bwd calls, one
+ * per sequence.
+ *
+ *   q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta   packed [T, heads, ...]
+ *                  as for kda_recurrent_varlen (no batch axis)
+ *   initial_state, d_final_state, d_initial_state   [N,H,Dk,Dv] float or NULL
+ *   cu_seqlens     [N+1] int32 device offsets (clamped as for the forward)
+ *   the rest       as for kda_chunk_bwd; the workspace holds at least
+ *                  kda_chunk_bwd_varlen_workspace_size(...) bytes, 256-byte
+ *                  aligned, and also the tables built on the device
+ */
+kda_status kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* initial_state, const void* d_o,
+                                const float* d_final_state, void* dq, void* dk, void* dv,
+                                float* dg, float* dbeta, float* d_initial_state,
+                                const int* cu_seqlens, int N, int T, int H, int Hqk, int Dk,
+                                int Dv, int chunk, float scale, kda_gate_mode mode,
+                                kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* kda_status_string(kda_status s);

@@ -22,6 +22,7 @@ Two independent forms:
 * :func:`chunkwise_bwd` -- the same gradient in the chunkwise matrix form,
   NumPy (``chunkwise_bwd.py``), pinned to R-bwd.
 * :func:`recurrent_grouped_bwd` -- R-bwd for grouped value heads.
+* :func:`recurrent_varlen_bwd` -- R-bwd per sequence of a packed batch.
 * :func:`apply_prologue` -- the optional input transforms (L2-normalised
   q/k, sigmoid beta, log-sigmoid gates), applied before the others
   (``prologue.py``).
@@ -32,5 +33,5 @@ from .recurrence import recurrent, recurrent_bwd, build_oracle_library, oracle_t
 from .chunkwise import chunkwise  # noqa: F401
 from .grouped import recurrent_grouped, recurrent_grouped_bwd  # noqa: F401
 from .chunkwise_bwd import chunkwise_bwd  # noqa: F401
-from .varlen import recurrent_varlen  # noqa: F401
+from .varlen import recurrent_varlen, recurrent_varlen_bwd  # noqa: F401
 from .prologue import apply_prologue  # noqa: F401

@@ -55,3 +55,39 @@ def recurrent_varlen(q, k, v, g, beta, cu, h0=None, *, scale: Optional[float] = 
         hT[n] = hTn[0]
         carry = hTn
     return o, hT
+
+
+def recurrent_varlen_bwd(q, k, v, g, beta, cu, h0, do, dhT=None, *,
+                         scale: Optional[float] = None, mode: str = "channel",
+                         threads: int = 0):
+    """Gradients of :func:`recurrent_varlen`: one call of the grouped
+    gradient oracle per sequence (the sequences share nothing, so neither do
+    their gradients).  ``do`` [T,H,Dv]; ``dhT`` [N,H,Dk,Dv] or None.  Returns
+    the dict of :func:`oracle.recurrent_bwd` with packed token tensors (no
+    batch axis) and dh0 [N,H,Dk,Dv]; an empty sequence passes dhT[n] through."""
+    from .grouped import recurrent_grouped_bwd
+    cu = np.asarray(cu, np.int64)
+    N = len(cu) - 1
+    T, Hq, Dk = q.shape
+    H, Dv = v.shape[-2], v.shape[-1]
+    assert N >= 0 and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    out = {"dq": np.zeros((T, Hq, Dk)), "dk": np.zeros((T, Hq, Dk)), "dv": np.zeros((T, H, Dv)),
+           "dbeta": np.zeros((T, H)), "dg": None if mode == "none" else np.zeros(np.shape(g)),
+           "dh0": np.zeros((N, H, Dk, Dv))}
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        if e == s:
+            if dhT is not None:
+                out["dh0"][n] = dhT[n]
+            continue
+        sl = lambda x: None if x is None else np.asarray(x[s:e])[None]
+        hn = None if h0 is None else np.asarray(h0[n:n + 1], np.float64)
+        dn = None if dhT is None else np.asarray(dhT[n:n + 1], np.float64)
+        r = recurrent_grouped_bwd(sl(q), sl(k), sl(v), sl(g), sl(beta), hn, sl(do), dn,
+                                  scale=scale, mode=mode, threads=threads)
+        for name in ("dq", "dk", "dv", "dbeta"):
+            out[name][s:e] = r[name][0]
+        if out["dg"] is not None:
+            out["dg"][s:e] = r["dg"][0]
+        out["dh0"][n] = r["dh0"][0]
+    return out

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) >= {"kda_recurrent_step", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
                           "kda_recurrent_varlen", "kda_chunk_fwd_varlen",
                           "kda_chunk_fwd_varlen_workspace_size", "kda_status_string",
-                          "kda_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size"}
+                          "kda_version", "kda_chunk_bwd", "kda_chunk_bwd_workspace_size",
+                          "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_size"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -207,3 +208,41 @@ def test_chunk_bwd_workspace_size(L):
     assert f(1, 65, 1, 1, 128, 128, 64, 0, 1) >= 2 * one - 16 * 256
     # grouped heads add float partials of dq and dk per value head
     assert f(1, 64, 4, 2, 128, 128, 64, 0, 1) >= 4 * one + 2 * 4 * 64 * 4 * 128 - 16 * 256
+
+
+def _bwd_v(L, q=A, k=A, v=A, g=A, beta=A, h0=None, do=A, dhT=None, dq=A, dk=A, dv=A, dg=A,
+           dbeta=A, dh0=None, cu=CU, N=2, T=64, H=1, Hqk=None, Dk=128, Dv=128, chunk=64,
+           scale=1.0, mode=0, dtype=1, gdtype=0, ws=A, wsb=None):
+    Hqk = H if Hqk is None else Hqk
+    if wsb is None:
+        wsb = L.kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, mode, dtype)
+    return L.kda_chunk_bwd_varlen(q, k, v, g, beta, h0, do, dhT, dq, dk, dv, dg, dbeta, dh0, cu,
+                                  N, T, H, Hqk, Dk, Dv, chunk, scale, mode, dtype, gdtype, ws, wsb,
+                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(do=None), 1), (dict(cu=None), 1), (dict(N=-1), 1),
+    (dict(dq=None), 1), (dict(dg=None), 1), (dict(mode=5), 1), (dict(gdtype=3), 1),
+    (dict(H=4, Hqk=3), 1), (dict(chunk=24), 2), (dict(Dk=8), 2), (dict(cu=CU + 2), 3),
+    (dict(dq=MIS), 3), (dict(h0=MIS), 3), (dict(dh0=MIS), 3), (dict(ws=None), 4),
+    (dict(wsb=100), 4), (dict(ws=A + 64), 3),
+])
+def test_chunk_bwd_varlen_validation(L, kw, code):
+    assert _bwd_v(L, **kw) == code
+
+
+def test_chunk_bwd_varlen_nothing_to_do(L):
+    assert _bwd_v(L, N=0, cu=None) == 0
+    assert _bwd_v(L, T=0, q=None, k=None, v=None, g=None, beta=None, do=None, dq=None, dk=None,
+                  dv=None, dg=None, dbeta=None) == 0
+
+
+def test_chunk_bwd_varlen_workspace_size(L):
+    f = L.kda_chunk_bwd_varlen_workspace_size
+    assert f(0, 64, 1, 1, 128, 128, 64, 0, 1) == 0
+    dense = L.kda_chunk_bwd_workspace_size(1, 64, 1, 1, 128, 128, 64, 0, 1)
+    # room for ceil(T / chunk) + N chunk records plus the tables
+    assert f(1, 64, 1, 1, 128, 128, 64, 0, 1) >= 2 * dense
+    assert f(3, 64, 1, 1, 128, 128, 64, 0, 1) >= 4 * dense
+    assert f(2, 0, 1, 1, 128, 128, 64, 0, 1) > 0

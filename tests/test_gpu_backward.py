@@ -178,3 +178,119 @@ def test_bwd_full_size_prefill_sampled_heads():
     sub = {n: None if got[n] is None else
            (got[n][:, heads] if n == "dh0" else got[n][:, :, heads]) for n in NAMES}
     _compare("full size prefill heads 0,7,15", sub, ref, TOL["bf16"])
+
+
+# ---- packed variable-length batches ----------------------------------------
+from kda_workloads import make_lengths, make_varlen  # noqa: E402
+
+EDGE = (0, 1, 2, 15, 16, 17, 63, 64, 65, 130)
+
+
+def _varlen_cot(vw, seed, dhT_std):
+    import numpy as _np
+    w = vw.w
+    cot = make_cotangents(w, seed=seed)
+    do = cot.do[0]
+    dhT = None
+    if dhT_std > 0:
+        r = _np.random.default_rng(_np.random.SeedSequence([seed, 0xD1]))
+        dhT = (dhT_std * r.standard_normal((vw.N, w.H, w.Dk, w.Dv))).astype(_np.float32)
+    return do, dhT
+
+
+def _run_varlen(vw, do, dhT, chunk, q=None, k=None):
+    import torch
+    w = vw.w
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q = w.q[0] if q is None else q
+    k = w.k[0] if k is None else k
+    g = None if w.g is None else w.g[0]
+    cu = torch.from_numpy(vw.cu).cuda()
+    out = K.kda_chunk_bwd_varlen(_t(q, dt), _t(k, dt), _t(w.v[0], dt), _t(g), _t(w.beta[0]),
+                                 _t(do, dt), cu, initial_state=_t(vw.h0), d_final_state=_t(dhT),
+                                 chunk=chunk, scale=w.scale, mode=w.mode,
+                                 grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return {n: None if out[key] is None else out[key].float().cpu().numpy()
+            for n, key in zip(NAMES, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"))}
+
+
+def _oracle_varlen(vw, do, dhT, q=None, k=None):
+    w = vw.w
+    q = w.q[0] if q is None else q
+    k = w.k[0] if k is None else k
+    return oracle.recurrent_varlen_bwd(q, k, w.v[0], None if w.g is None else w.g[0], w.beta[0],
+                                       vw.cu, vw.h0, do, dhT, scale=w.scale, mode=w.mode)
+
+
+@pytest.mark.parametrize("mode", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bwd_varlen_ragged_f32(mode, chunk):
+    lengths = make_lengths(14, max_len=200, seed=chunk, edge=EDGE)
+    vw = make_varlen(lengths, 2, 32, 32, mode=mode, dtype="f32", seed=7 + chunk, h0_std=0.2,
+                     gate_law="softplus" if mode != "none" else "zero")
+    do, dhT = _varlen_cot(vw, 3, 0.3)
+    say("bwd varlen f32", mode, chunk, list(lengths))
+    _compare(f"varlen f32 {mode} C{chunk}", _run_varlen(vw, do, dhT, chunk),
+             _oracle_varlen(vw, do, dhT), TOL["f32"])
+
+
+def test_bwd_varlen_grouped_heads_bf16():
+    lengths = make_lengths(10, max_len=300, seed=4, edge=(0, 1, 64, 65))
+    vw = make_varlen(lengths, 4, 64, 32, dtype="bf16", seed=12, h0_std=0.05)
+    q = np.ascontiguousarray(vw.w.q[0][:, ::2])
+    k = np.ascontiguousarray(vw.w.k[0][:, ::2])
+    do, dhT = _varlen_cot(vw, 5, 0.1)
+    say("bwd varlen grouped bf16", list(lengths))
+    _compare("varlen grouped bf16", _run_varlen(vw, do, dhT, 64, q, k),
+             _oracle_varlen(vw, do, dhT, q, k), TOL["bf16"])
+
+
+def test_bwd_varlen_equal_lengths_match_dense_bitwise():
+    import torch
+    N, L, H, D = 3, 150, 2, 64
+    vw = make_varlen([L] * N, H, D, D, dtype="bf16", seed=5, h0_std=0.05)
+    do, dhT = _varlen_cot(vw, 6, 0.1)
+    say("bwd varlen = dense")
+    got = _run_varlen(vw, do, dhT, 64)
+    w = vw.w
+    r = lambda x: None if x is None else np.ascontiguousarray(x[0].reshape((N, L) + x.shape[2:]))
+    bf = torch.bfloat16
+    dense = K.kda_chunk_bwd(_t(r(w.q), bf), _t(r(w.k), bf), _t(r(w.v), bf), _t(r(w.g)),
+                            _t(r(w.beta)), _t(np.ascontiguousarray(do.reshape(N, L, H, D)), bf),
+                            initial_state=_t(vw.h0), d_final_state=_t(dhT), chunk=64,
+                            scale=w.scale, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for name, key in zip(NAMES, ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")):
+        x = dense[key].cpu().numpy()
+        np.testing.assert_array_equal(got[name], x.reshape(got[name].shape), err_msg=name)
+
+
+def test_bwd_varlen_empty_sequences_pass_the_state_gradient():
+    vw = make_varlen([0, 5, 0], 2, 32, 32, dtype="f32", seed=9, h0_std=0.3)
+    do, dhT = _varlen_cot(vw, 7, 1.0)
+    say("bwd varlen empty")
+    got = _run_varlen(vw, do, dhT, 64)
+    np.testing.assert_array_equal(got["dh0"][0], dhT[0])
+    np.testing.assert_array_equal(got["dh0"][2], dhT[2])
+    _compare("varlen empty", got, _oracle_varlen(vw, do, dhT), TOL["f32"])
+
+
+def test_bwd_varlen_serving_mix_sampled():
+    """The serving mix (64 sequences, lengths log-uniform in [1, 2048], H16
+    d128 bf16) through one call; the oracle runs on eight of the sequences."""
+    lengths = make_lengths(64, max_len=2048, seed=17, edge=(1, 64, 2048))
+    vw = make_varlen(lengths, 16, 128, 128, dtype="bf16", seed=17, h0_std=0.02)
+    do, dhT = _varlen_cot(vw, 8, 0.02)
+    say("bwd varlen serving mix")
+    got = _run_varlen(vw, do, dhT, 64)
+    w = vw.w
+    for n in (0, 1, 2, 7, 19, 33, 48, 63):
+        s, e = int(vw.cu[n]), int(vw.cu[n + 1])
+        sl = lambda x: None if x is None else np.ascontiguousarray(x[0][s:e])[None]
+        ref = oracle.recurrent_bwd(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta),
+                                   vw.h0[n:n + 1], np.ascontiguousarray(do[s:e])[None],
+                                   dhT[n:n + 1], scale=w.scale, mode=w.mode)
+        sub = {name: (got[name][n:n + 1] if name == "dh0" else got[name][s:e][None])
+               for name in NAMES}
+        _compare(f"varlen serving seq {n} len {e - s}", sub, ref, TOL["bf16"])

@@ -8,7 +8,8 @@ how the gradient is derived, so a dropped term, a wrong sign or a
 transposed operand anywhere in R-bwd fails it; the planted mistakes below
 show that it does.  The chunkwise gradient (oracle C-bwd) and the grouped
 gradient are then pinned to R-bwd, and the grouped one to finite
-differences of the grouped forward as well.
+differences of the grouped forward as well; the packed-batch gradient to
+finite differences of the packed forward and to the dense batch.
 """
 import functools
 
@@ -175,3 +176,48 @@ def test_grouped_bwd_sums_over_the_group():
         np.testing.assert_allclose(got[name], summed, rtol=1e-12, atol=1e-12)
     for name in ("dv", "dbeta", "dg", "dh0"):
         np.testing.assert_array_equal(got[name], ref[name])
+
+
+def _packed_case(seed, lengths, H=2, Hq=2, Dk=3, Dv=2, mode="channel"):
+    r = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T, N = int(cu[-1]), len(lengths)
+    q = r.standard_normal((T, Hq, Dk))
+    k = r.standard_normal((T, Hq, Dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((T, H, Dv))
+    beta = r.uniform(0.1, 1.0, (T, H))
+    g = -r.uniform(0, 1, (T, H, Dk)) if mode == "channel" else \
+        (-r.uniform(0, 1, (T, H)) if mode == "scalar" else None)
+    h0 = 0.5 * r.standard_normal((N, H, Dk, Dv))
+    do = r.standard_normal((T, H, Dv))
+    dhT = r.standard_normal((N, H, Dk, Dv))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, h0=h0), do, dhT, cu
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_varlen_bwd_matches_finite_differences(mode):
+    inputs, do, dhT, cu = _packed_case(31, [3, 0, 4, 1], H=2, Hq=1, mode=mode)
+    fwd = lambda q, k, v, g, beta, h0, scale, mode: oracle.recurrent_varlen(
+        q, k, v, g, beta, cu, h0, scale=scale, mode=mode)
+    got = oracle.recurrent_varlen_bwd(inputs["q"], inputs["k"], inputs["v"], inputs["g"],
+                                      inputs["beta"], cu, inputs["h0"], do, dhT, scale=0.6,
+                                      mode=mode)
+    fd = _finite_differences(fwd, inputs, do, dhT, mode, 0.6)
+    for name, ref in fd.items():
+        err = np.max(np.abs(got[name] - ref)) / max(1.0, np.max(np.abs(ref)))
+        assert err < 2e-7, (name, err)
+    # the empty sequence passes its final-state gradient through
+    np.testing.assert_array_equal(got["dh0"][1], dhT[1])
+
+
+def test_varlen_bwd_equal_lengths_equal_the_dense_batch():
+    inputs, do, dhT, cu = _packed_case(32, [5, 5, 5], H=2, Hq=2, Dk=4, Dv=3)
+    got = oracle.recurrent_varlen_bwd(inputs["q"], inputs["k"], inputs["v"], inputs["g"],
+                                      inputs["beta"], cu, inputs["h0"], do, dhT)
+    r = lambda x: x.reshape((3, 5) + x.shape[1:])
+    ref = oracle.recurrent_bwd(r(inputs["q"]), r(inputs["k"]), r(inputs["v"]), r(inputs["g"]),
+                               r(inputs["beta"]), inputs["h0"], r(do), dhT)
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        np.testing.assert_array_equal(got[name], ref[name].reshape(got[name].shape))
+    np.testing.assert_array_equal(got["dh0"], ref["dh0"])
