@@ -121,6 +121,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders this wave's LDS writes before its later LDS reads, for lanes of one
+// wave that exchange values through a buffer of their own (no other wave
+// takes part, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Loads of a chunk's rows are issued unconditionally from a clamped row
 // (every chunk has at least one row) and zeroed past the end afterwards: a
 // load under a per-row branch is waited for at the branch join, which
@@ -963,7 +972,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 src1[row * 16 + r16] = a.scale * qd[I][ii] * f;
             }
         }
-        lds_barrier();
+        wave_lds_sync();
         f32x4 acc = zero4();
         for (int kk = 16 * J; kk < C; kk += 4) {
             acc = mma4(sdAb[(kk + q4) * LA + 16 * J + r16], src0[(kk + q4) * 16 + r16], acc);
@@ -971,7 +980,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) Pinv[J][ii] = ex(Ge - Gd[J][ii]) * acc[ii];
-        lds_barrier();
+        wave_lds_sync();
     }
 
     // sums over earlier tokens j <= i (reference row 16 I), and with them each
@@ -989,7 +998,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             for (int ii = 0; ii < 4; ++ii)
                 src0[(16 * J + 4 * q4 + ii) * 16 + r16] = kd[J][ii] * ex(Gs - Gd[J][ii]);
         }
-        lds_barrier();
+        wave_lds_sync();
         f32x4 ra = zero4(), rb = zero4();
         for (int kk = 0; kk < 16 * (I + 1); kk += 4) {
             const float bs = src0[(kk + q4) * 16 + r16];
@@ -1024,12 +1033,12 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 }
             }
         }
-        lds_barrier();
+        wave_lds_sync();
     }
     colPr += __shfl_xor(colPr, 16);
     colPr += __shfl_xor(colPr, 32);
     if (q4 == 3) src1[(C - 1) * 16 + r16] += colPr + sDgam[c] * ex(Gl);
-    lds_barrier();
+    wave_lds_sync();
 
     if (a.mode == KDA_GATE_CHANNEL) {
         // dg = suffix sums of dG over the rows of the chunk, per channel
