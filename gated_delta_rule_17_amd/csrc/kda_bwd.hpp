@@ -34,9 +34,11 @@
 //   4. bwd_group_sum (grouped value heads only) adds the query/key gradients
 //                 of the value heads that share a query/key head.
 //
-// Every product runs on v_mfma_f32_16x16x4_f32 with float32 operands from
-// LDS.  Operand convention of that instruction (lane l, r = l % 16,
-// g = l / 16): A[r][g], B[g][r]; accumulator element i is D[4g + i][r].
+// Products run on v_mfma_f32_16x16x4_f32 with float32 operands from LDS
+// (operand convention, lane l, r = l % 16, g = l / 16: A[r][g], B[g][r];
+// accumulator element i is D[4g + i][r]), except the products over the value
+// dimension in bwd_grad, which take v_mfma_f32_16x16x32_bf16 over bf16 parts
+// (hi + mid + lo) of their float32 operands.
 //
 // Decays inside a chunk come from differences of G.  Products that sum
 // over the tokens of a chunk with a decay between the two tokens are split
@@ -46,6 +48,8 @@
 // stays finite while no key channel decays by more than about e^-80 across
 // 16 consecutive tokens.
 #pragma once
+
+#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -688,12 +692,33 @@ struct GradLds {
     static constexpr int oT = 0, oH = oT + C * LT, odH = oH + VS * LHT, oE = odH + VS * LHT,
                          odO = oE + VS * LET, odU = odO + C * LV, oV = odU + C * LV,
                          odE = oV + C * LV, S_END = odE + VS * LDE;
+    // value-slice phase with split bf16 operands (slices of 32 columns):
+    // float T, V and dE (transposed), then bf16 planes [row][SB] of the
+    // hi, mid and lo parts of the state, its gradient, E, dO and dUt
+    // (offsets in floats)
+    static constexpr bool HL = VS == 32;
+    static constexpr int SB = VS + 8;
+    static constexpr int hT = 0, hV = hT + C * LT, hdE = hV + C * LV, hP = hdE + VS * LDE;
+    static constexpr int pH = DK * SB / 2, pC = C * SB / 2;   // floats per plane
+    static constexpr int hH = hP, hdH = hH + 3 * pH, hE = hdH + 3 * pH, hO = hE + 3 * pC,
+                         hU = hO + 3 * pC, H_END = hU + 3 * pC;
+    static constexpr int SL_END = HL ? H_END : S_END;
     // output phase
     static constexpr int oAq = 0, oAb = oAq + C * LA, oSrc = oAb + C * LA,
                          oRow = oSrc + NW * 2 * C * 16, oRowG = oRow + NW * C,
                          E_END = oRowG + NW * C;
-    static constexpr int SIZE = S_END > E_END ? S_END : E_END;
+    static constexpr int SIZE = SL_END > E_END ? SL_END : E_END;
 };
+
+// x = hi + mid + lo in bf16 parts (each the nearest bf16 to what the
+// previous parts leave; the differences are exact in float32), good to
+// about 2^-24 of x
+__device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    hi = f32_to_bf16(x);
+    const float r = x - bf16_to_f32(hi);
+    mid = f32_to_bf16(r);
+    lo = f32_to_bf16(r - bf16_to_f32(mid));
+}
 
 template <int C, int DK, int DV, typename IO>
 __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
@@ -756,125 +781,380 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     for (int s = 0; s < NYS; ++s) Y[s] = zero4();
     float zacc = 0.f, gacc = 0.f;
 
-    // One value slice of the records and inputs, requested into registers
-    // while the previous slice is being used and written to LDS at the start
-    // of its own turn.  Indices past the end are clamped for the loads (which
-    // are then unconditional) and skipped for the LDS writes.
-    constexpr int NHS = DK * VS / 4, NES = C * VS / 4, NOS = C * VS;
-    constexpr int NH = (NHS + NT - 1) / NT, NE = (NES + NT - 1) / NT, NO = (NOS + NT - 1) / NT;
-    struct Slice {
-        f32x4 hh[NH], dh[NH], ee[NE], de[NE];
-        float oo[NO], vv[NO];
-    };
-    auto load_slice = [&](Slice& x, int s) {
-        const int v0 = s * VS;
-#pragma unroll
-        for (int j = 0; j < NH; ++j) {
-            const int e = min(tid + j * NT, NHS - 1);
-            const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
-            const size_t o = R * a.r.rs + (size_t)(v0 + n) * DK + c;
-            x.hh[j] = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
-            x.dh[j] = *reinterpret_cast<const f32x4*>(a.r.dH + o);
-        }
-#pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int e = min(tid + j * NT, NES - 1);
-            const int n = e / (C / 4), i = 4 * (e % (C / 4));
-            const size_t o = R * a.r.rs + (size_t)(v0 + n) * C + i;
-            x.ee[j] = *reinterpret_cast<const f32x4*>(a.r.E + o);
-            x.de[j] = *reinterpret_cast<const f32x4*>(a.r.dE + o);
-        }
-#pragma unroll
-        for (int j = 0; j < NO; ++j) {
-            const int e = min(tid + j * NT, NOS - 1);
-            const int i = clamp_row(e / VS, L), n = e % VS;
-            x.oo[j] = io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n);
-            x.vv[j] = io<IO>::load(v + tok_v(a, b, t0 + i, h) * DV + v0 + n);
-        }
-    };
-    auto store_slice = [&](const Slice& x) {
-#pragma unroll
-        for (int j = 0; j < NH; ++j) {
-            const int e = tid + j * NT;
-            if (e < NHS) {
-                const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
-                *reinterpret_cast<f32x4*>(sH + n * LHT + c) = x.hh[j];
-                *reinterpret_cast<f32x4*>(sdH + n * LHT + c) = x.dh[j];
+    if constexpr (S::HL) {
+        // Slices of 32 value columns: every product of the slice is a sum of
+        // 32-deep steps of v_mfma_f32_16x16x32_bf16 over bf16 parts of the
+        // float32 operands, x = x_h + x_m + x_l.  A product keeps the parts
+        // down to 2^-24 of the operands (hh + hm + mh + hl + lh + mm, six
+        // steps); dO of a bf16 batch is exact in bf16 and takes three steps
+        // (h against h, m, l).  dUt H^T keeps hh + hm + mh: its error
+        // (2^-16 of the products) only reaches dk and dG through Pg, where
+        // it stays far below the float32 tolerance.  Operand convention of
+        // that instruction (lane l, r = l % 16, g = l / 16): A[r][8g..8g+7],
+        // B[8g..8g+7][r]; the accumulator is laid out as for the float32
+        // instruction.  Planes hold bf16 rows of 32 columns (stride SB); the
+        // state, its gradient and E are transposed on the way in, two value
+        // columns per 32-bit write.
+        constexpr int SB = S::SB, SW = SB / 2, PH = S::pH, PC = S::pC;
+        constexpr bool OEX = std::is_same<IO, bf16_t>::value;
+        uint32_t* pH = reinterpret_cast<uint32_t*>(smem + S::hH);     // + m * PH
+        uint32_t* pdH = reinterpret_cast<uint32_t*>(smem + S::hdH);
+        uint32_t* pE = reinterpret_cast<uint32_t*>(smem + S::hE);     // + m * PC
+        uint32_t* pO = reinterpret_cast<uint32_t*>(smem + S::hO);
+        uint32_t* pU = reinterpret_cast<uint32_t*>(smem + S::hU);
+        float* sVh = smem + S::hV;
+        float* sdEh = smem + S::hdE;
+        auto pack = [](uint16_t x0, uint16_t x1) -> uint32_t {
+            return (uint32_t)x0 | ((uint32_t)x1 << 16);
+        };
+        // the three parts of a pair of values into three planes of PS floats
+        auto put3 = [&](uint32_t* plane, int PS, int o, float x0, float x1) {
+            uint16_t h0, m0, l0, h1, m1, l1;
+            split3(x0, h0, m0, l0);
+            split3(x1, h1, m1, l1);
+            plane[o] = pack(h0, h1);
+            plane[PS + o] = pack(m0, m1);
+            plane[2 * PS + o] = pack(l0, l1);
+        };
+        auto frag = [&](const uint32_t* plane, int row) -> u16x8 {
+            return *reinterpret_cast<const u16x8*>(plane + row * SW + 4 * q4);
+        };
+        struct F3 { u16x8 h, m, l; };
+        auto frag3 = [&](const uint32_t* plane, int PS, int row) -> F3 {
+            return F3{frag(plane, row), frag(plane + PS, row), frag(plane + 2 * PS, row)};
+        };
+        auto mmb = [](const u16x8& x, const u16x8& y, f32x4 acc) -> f32x4 {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                           __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+        };
+        auto mm6 = [&](const F3& x, const F3& y, f32x4 acc) -> f32x4 {
+            acc = mmb(x.m, y.m, acc);
+            acc = mmb(x.l, y.h, acc);
+            acc = mmb(x.h, y.l, acc);
+            acc = mmb(x.m, y.h, acc);
+            acc = mmb(x.h, y.m, acc);
+            return mmb(x.h, y.h, acc);
+        };
+        auto mm3x = [&](const u16x8& x, const F3& y, f32x4 acc) -> f32x4 {   // x exact
+            acc = mmb(x, y.l, acc);
+            acc = mmb(x, y.m, acc);
+            return mmb(x, y.h, acc);
+        };
+        // element maps (tid-based, 64-lane groups): a state or E element is
+        // (column quad cq, value-column pair p), with four consecutive quads
+        // per 64 bytes of a record row; a dO / v element is (row i, pair p)
+        constexpr int NEP = 4 * C, NOP = 16 * C;
+        constexpr int NEJ = (NEP + NT - 1) / NT, NOJ = (NOP + NT - 1) / NT;
+        constexpr int NES = C * VS / 4, NE = (NES + NT - 1) / NT;
+        static_assert(4 * DK == NT, "one state element pair per thread");
+        const int hcq = 4 * (tid >> 6) + (tid & 3), hp = (tid >> 2) & 15;
+        float gpart[4] = {0.f, 0.f, 0.f, 0.f};     // sum_n H dH of channels 4 hcq + z
+        struct SliceHL {
+            f32x4 h0, h1, d0, d1, e0[NEJ], e1[NEJ], de[NE];
+            float o0[NOJ], o1[NOJ], v0[NOJ], v1[NOJ];
+        };
+        auto load_slice = [&](SliceHL& x, int s) {
+            const int v0 = s * VS;
+            {
+                const size_t o = R * a.r.rs + (size_t)(v0 + 2 * hp) * DK + 4 * hcq;
+                x.h0 = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
+                x.h1 = *reinterpret_cast<const f32x4*>(a.r.Hs + o + DK);
+                x.d0 = *reinterpret_cast<const f32x4*>(a.r.dH + o);
+                x.d1 = *reinterpret_cast<const f32x4*>(a.r.dH + o + DK);
             }
-        }
 #pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int e = tid + j * NT;
-            if (e < NES) {
+            for (int j = 0; j < NEJ; ++j) {
+                const int e = min(tid + j * NT, NEP - 1);
+                const int iq = 4 * (e >> 6) + (e & 3), p = (e >> 2) & 15;
+                const size_t o = R * a.r.rs + (size_t)(v0 + 2 * p) * C + 4 * iq;
+                x.e0[j] = *reinterpret_cast<const f32x4*>(a.r.E + o);
+                x.e1[j] = *reinterpret_cast<const f32x4*>(a.r.E + o + C);
+            }
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int e = min(tid + j * NT, NES - 1);
                 const int n = e / (C / 4), i = 4 * (e % (C / 4));
-                *reinterpret_cast<f32x4*>(sE + n * LET + i) = x.ee[j];
-#pragma unroll
-                for (int z = 0; z < 4; ++z) sdE[n * LDE + i + z] = x.de[j][z];
+                x.de[j] = *reinterpret_cast<const f32x4*>(a.r.dE + R * a.r.rs + (size_t)(v0 + n) * C + i);
             }
-        }
 #pragma unroll
-        for (int j = 0; j < NO; ++j) {
-            const int e = tid + j * NT;
-            if (e < NOS) {
-                const int i = e / VS, n = e % VS;
-                sdO[i * LV + n] = keep(x.oo[j], i, L);
-                sV[i * LV + n] = keep(x.vv[j], i, L);
+            for (int j = 0; j < NOJ; ++j) {
+                const int e = min(tid + j * NT, NOP - 1);
+                const int i = clamp_row(e >> 4, L), p = e & 15;
+                const size_t o = tok_v(a, b, t0 + i, h) * DV + v0 + 2 * p;
+                if constexpr (OEX) {
+                    // the bf16 pair stays packed until it is stored
+                    x.o0[j] = __uint_as_float(*reinterpret_cast<const uint32_t*>(dO + o));
+                    x.v0[j] = __uint_as_float(*reinterpret_cast<const uint32_t*>(v + o));
+                } else {
+                    const float2 fo = *reinterpret_cast<const float2*>(dO + o);
+                    const float2 fv = *reinterpret_cast<const float2*>(v + o);
+                    x.o0[j] = fo.x; x.o1[j] = fo.y;
+                    x.v0[j] = fv.x; x.v1[j] = fv.y;
+                }
             }
-        }
-    };
+        };
+        auto store_slice = [&](const SliceHL& x) {
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const int o = (4 * hcq + z) * SW + hp;
+                put3(pH, PH, o, x.h0[z], x.h1[z]);
+                put3(pdH, PH, o, x.d0[z], x.d1[z]);
+                gpart[z] += x.h0[z] * x.d0[z] + x.h1[z] * x.d1[z];
+            }
+#pragma unroll
+            for (int j = 0; j < NEJ; ++j) {
+                const int e = tid + j * NT;
+                if (e < NEP) {
+                    const int iq = 4 * (e >> 6) + (e & 3), p = (e >> 2) & 15;
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) put3(pE, PC, (4 * iq + z) * SW + p, x.e0[j][z], x.e1[j][z]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int e = tid + j * NT;
+                if (e < NES) {
+                    const int n = e / (C / 4), i = 4 * (e % (C / 4));
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) sdEh[n * LDE + i + z] = x.de[j][z];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NOJ; ++j) {
+                const int e = tid + j * NT;
+                if (e < NOP) {
+                    const int i = e >> 4, p = e & 15;
+                    if constexpr (OEX) {
+                        const uint32_t uo = i < L ? __float_as_uint(x.o0[j]) : 0u;
+                        const uint32_t uv = i < L ? __float_as_uint(x.v0[j]) : 0u;
+                        pO[i * SW + p] = uo;
+                        sVh[i * LV + 2 * p] = __uint_as_float(uv << 16);
+                        sVh[i * LV + 2 * p + 1] = __uint_as_float(uv & 0xffff0000u);
+                    } else {
+                        put3(pO, PC, i * SW + p, keep(x.o0[j], i, L), keep(x.o1[j], i, L));
+                        sVh[i * LV + 2 * p] = keep(x.v0[j], i, L);
+                        sVh[i * LV + 2 * p + 1] = keep(x.v1[j], i, L);
+                    }
+                }
+            }
+        };
 
-    Slice nx;
-    load_slice(nx, 0);
-    for (int s = 0; s < NS; ++s) {
-        const int v0 = s * VS;
-        lds_barrier();
-        store_slice(nx);
-        if (s + 1 < NS) load_slice(nx, s + 1);
-        lds_barrier();
-        // dUt = T^T dE (upper triangular: rows i take j >= 16 I), dv = beta dUt
-        for (int job = w; job < NB * (VS / 16); job += NW) {
-            const int I = job / (VS / 16), Vt = job % (VS / 16);
-            f32x4 acc = zero4();
-            for (int kk = 16 * I; kk < C; kk += 4)
-                acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdE[(16 * Vt + r16) * LDE + kk + q4], acc);
+        SliceHL nx;
+        load_slice(nx, 0);
+        uint16_t* pU16 = reinterpret_cast<uint16_t*>(pU);
+        for (int s = 0; s < NS; ++s) {
+            const int v0 = s * VS;
+            lds_barrier();
+            store_slice(nx);
+            if (s + 1 < NS) load_slice(nx, s + 1);
+            lds_barrier();
+            // dUt = T^T dE (upper triangular: rows i take j >= 16 I), dv = beta dUt
+            for (int job = w; job < NB * (VS / 16); job += NW) {
+                const int I = job / (VS / 16), Vt = job % (VS / 16);
+                f32x4 acc = zero4();
+                for (int kk = 16 * I; kk < C; kk += 4)
+                    acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdEh[(16 * Vt + r16) * LDE + kk + q4], acc);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int i = 16 * I + 4 * q4 + ii, n = 16 * Vt + r16;
-                sdU[i * LV + n] = acc[ii];
-                if (i < L)
-                    store_grad(a.dv, tok_v(a, b, t0 + i, h) * DV + v0 + n, sBeta[i] * acc[ii], a.gdt);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int i = 16 * I + 4 * q4 + ii, n = 16 * Vt + r16;
+                    uint16_t hi, mid, lo;
+                    split3(acc[ii], hi, mid, lo);
+                    pU16[i * SB + n] = hi;
+                    pU16[2 * PC + i * SB + n] = mid;
+                    pU16[4 * PC + i * SB + n] = lo;
+                    if (i < L)
+                        store_grad(a.dv, tok_v(a, b, t0 + i, h) * DV + v0 + n, sBeta[i] * acc[ii], a.gdt);
+                }
+            }
+            lds_barrier();
+            if (tid < C) {
+                for (int p = 0; p < VS / 2; ++p) {
+                    const uint32_t uh = pU[tid * SW + p], um = pU[PC + tid * SW + p],
+                                   ul = pU[2 * PC + tid * SW + p];
+                    const float u0 = __uint_as_float(uh << 16) + __uint_as_float(um << 16) +
+                                     __uint_as_float(ul << 16);
+                    const float u1 = __uint_as_float(uh & 0xffff0000u) + __uint_as_float(um & 0xffff0000u) +
+                                     __uint_as_float(ul & 0xffff0000u);
+                    zacc += u0 * sVh[tid * LV + 2 * p] + u1 * sVh[tid * LV + 2 * p + 1];
+                }
+            }
+            // products with the state and its gradient for this wave's 16 channels
+            {
+                const F3 fH = frag3(pH, PH, 16 * w + r16);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const int row = 16 * I + r16;
+                    if constexpr (OEX)
+                        X1[I] = mm3x(frag(pO, row), fH, X1[I]);
+                    else
+                        X1[I] = mm6(frag3(pO, PC, row), fH, X1[I]);
+                    const u16x8 fUh = frag(pU, row), fUm = frag(pU + PC, row);
+                    X3[I] = mmb(fUm, fH.h, X3[I]);
+                    X3[I] = mmb(fUh, fH.m, X3[I]);
+                    X3[I] = mmb(fUh, fH.h, X3[I]);
+                }
+            }
+            {
+                const F3 fdH = frag3(pdH, PH, 16 * w + r16);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) X2[I] = mm6(frag3(pE, PC, 16 * I + r16), fdH, X2[I]);
+            }
+            // C x C products dO E^T and dUt E^T on the lower block tiles
+#pragma unroll
+            for (int sl = 0; sl < NYS; ++sl) {
+                const int job = w + sl * NW;
+                if (job < 2 * NY) {
+                    int I, J;
+                    lower_tile(job % NY, I, J);
+                    const F3 fB = frag3(pE, PC, 16 * J + r16);
+                    if (job >= NY)
+                        Y[sl] = mm6(frag3(pU, PC, 16 * I + r16), fB, Y[sl]);
+                    else if constexpr (OEX)
+                        Y[sl] = mm3x(frag(pO, 16 * I + r16), fB, Y[sl]);
+                    else
+                        Y[sl] = mm6(frag3(pO, PC, 16 * I + r16), fB, Y[sl]);
+                }
             }
         }
+        // sum_n H dH per channel: lanes of one column quad differ in bits 2..5
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            float t = gpart[z];
+            t += __shfl_xor(t, 4);
+            t += __shfl_xor(t, 8);
+            t += __shfl_xor(t, 16);
+            t += __shfl_xor(t, 32);
+            gpart[z] = t;
+        }
+        // handed to the channel's own thread through LDS after the loop
         lds_barrier();
-        if (tid < C) {
-            for (int n = 0; n < VS; ++n) zacc += sdU[tid * LV + n] * sV[tid * LV + n];
-        }
-        if (tid < DK) {
-            for (int n = 0; n < VS; ++n) gacc += sH[n * LHT + tid] * sdH[n * LHT + tid];
-        }
-        // products with the state and its gradient for this wave's 16 channels
-#pragma unroll 2
-        for (int kk = 0; kk < VS; kk += 4) {
-            const float bH = sH[(kk + q4) * LHT + 16 * w + r16];
-            const float bdH = sdH[(kk + q4) * LHT + 16 * w + r16];
+        if (hp == 0) {
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                X1[I] = mma4(sdO[(16 * I + r16) * LV + kk + q4], bH, X1[I]);
-                X2[I] = mma4(sE[(kk + q4) * LET + 16 * I + r16], bdH, X2[I]);
-                X3[I] = mma4(sdU[(16 * I + r16) * LV + kk + q4], bH, X3[I]);
+            for (int z = 0; z < 4; ++z) sDgam[4 * hcq + z] = gpart[z];
+        }
+        lds_barrier();
+        if (tid < DK) gacc = sDgam[tid];
+    } else {
+        // One value slice of the records and inputs, requested into registers
+        // while the previous slice is being used and written to LDS at the start
+        // of its own turn.  Indices past the end are clamped for the loads (which
+        // are then unconditional) and skipped for the LDS writes.
+        constexpr int NHS = DK * VS / 4, NES = C * VS / 4, NOS = C * VS;
+        constexpr int NH = (NHS + NT - 1) / NT, NE = (NES + NT - 1) / NT, NO = (NOS + NT - 1) / NT;
+        struct Slice {
+            f32x4 hh[NH], dh[NH], ee[NE], de[NE];
+            float oo[NO], vv[NO];
+        };
+        auto load_slice = [&](Slice& x, int s) {
+            const int v0 = s * VS;
+    #pragma unroll
+            for (int j = 0; j < NH; ++j) {
+                const int e = min(tid + j * NT, NHS - 1);
+                const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
+                const size_t o = R * a.r.rs + (size_t)(v0 + n) * DK + c;
+                x.hh[j] = *reinterpret_cast<const f32x4*>(a.r.Hs + o);
+                x.dh[j] = *reinterpret_cast<const f32x4*>(a.r.dH + o);
             }
-        }
-        // C x C products dO E^T and dUt E^T on the lower block tiles
-#pragma unroll
-        for (int sl = 0; sl < NYS; ++sl) {
-            const int job = w + sl * NW;
-            if (job < 2 * NY) {
-                int I, J;
-                lower_tile(job % NY, I, J);
-                const float* A = job >= NY ? sdU : sdO;
-#pragma unroll 4
-                for (int kk = 0; kk < VS; kk += 4)
-                    Y[sl] = mma4(A[(16 * I + r16) * LV + kk + q4], sE[(kk + q4) * LET + 16 * J + r16], Y[sl]);
+    #pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int e = min(tid + j * NT, NES - 1);
+                const int n = e / (C / 4), i = 4 * (e % (C / 4));
+                const size_t o = R * a.r.rs + (size_t)(v0 + n) * C + i;
+                x.ee[j] = *reinterpret_cast<const f32x4*>(a.r.E + o);
+                x.de[j] = *reinterpret_cast<const f32x4*>(a.r.dE + o);
+            }
+    #pragma unroll
+            for (int j = 0; j < NO; ++j) {
+                const int e = min(tid + j * NT, NOS - 1);
+                const int i = clamp_row(e / VS, L), n = e % VS;
+                x.oo[j] = io<IO>::load(dO + tok_v(a, b, t0 + i, h) * DV + v0 + n);
+                x.vv[j] = io<IO>::load(v + tok_v(a, b, t0 + i, h) * DV + v0 + n);
+            }
+        };
+        auto store_slice = [&](const Slice& x) {
+    #pragma unroll
+            for (int j = 0; j < NH; ++j) {
+                const int e = tid + j * NT;
+                if (e < NHS) {
+                    const int n = e / (DK / 4), c = 4 * (e % (DK / 4));
+                    *reinterpret_cast<f32x4*>(sH + n * LHT + c) = x.hh[j];
+                    *reinterpret_cast<f32x4*>(sdH + n * LHT + c) = x.dh[j];
+                }
+            }
+    #pragma unroll
+            for (int j = 0; j < NE; ++j) {
+                const int e = tid + j * NT;
+                if (e < NES) {
+                    const int n = e / (C / 4), i = 4 * (e % (C / 4));
+                    *reinterpret_cast<f32x4*>(sE + n * LET + i) = x.ee[j];
+    #pragma unroll
+                    for (int z = 0; z < 4; ++z) sdE[n * LDE + i + z] = x.de[j][z];
+                }
+            }
+    #pragma unroll
+            for (int j = 0; j < NO; ++j) {
+                const int e = tid + j * NT;
+                if (e < NOS) {
+                    const int i = e / VS, n = e % VS;
+                    sdO[i * LV + n] = keep(x.oo[j], i, L);
+                    sV[i * LV + n] = keep(x.vv[j], i, L);
+                }
+            }
+        };
+
+        Slice nx;
+        load_slice(nx, 0);
+        for (int s = 0; s < NS; ++s) {
+            const int v0 = s * VS;
+            lds_barrier();
+            store_slice(nx);
+            if (s + 1 < NS) load_slice(nx, s + 1);
+            lds_barrier();
+            // dUt = T^T dE (upper triangular: rows i take j >= 16 I), dv = beta dUt
+            for (int job = w; job < NB * (VS / 16); job += NW) {
+                const int I = job / (VS / 16), Vt = job % (VS / 16);
+                f32x4 acc = zero4();
+                for (int kk = 16 * I; kk < C; kk += 4)
+                    acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdE[(16 * Vt + r16) * LDE + kk + q4], acc);
+    #pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int i = 16 * I + 4 * q4 + ii, n = 16 * Vt + r16;
+                    sdU[i * LV + n] = acc[ii];
+                    if (i < L)
+                        store_grad(a.dv, tok_v(a, b, t0 + i, h) * DV + v0 + n, sBeta[i] * acc[ii], a.gdt);
+                }
+            }
+            lds_barrier();
+            if (tid < C) {
+                for (int n = 0; n < VS; ++n) zacc += sdU[tid * LV + n] * sV[tid * LV + n];
+            }
+            if (tid < DK) {
+                for (int n = 0; n < VS; ++n) gacc += sH[n * LHT + tid] * sdH[n * LHT + tid];
+            }
+            // products with the state and its gradient for this wave's 16 channels
+    #pragma unroll 2
+            for (int kk = 0; kk < VS; kk += 4) {
+                const float bH = sH[(kk + q4) * LHT + 16 * w + r16];
+                const float bdH = sdH[(kk + q4) * LHT + 16 * w + r16];
+    #pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    X1[I] = mma4(sdO[(16 * I + r16) * LV + kk + q4], bH, X1[I]);
+                    X2[I] = mma4(sE[(kk + q4) * LET + 16 * I + r16], bdH, X2[I]);
+                    X3[I] = mma4(sdU[(16 * I + r16) * LV + kk + q4], bH, X3[I]);
+                }
+            }
+            // C x C products dO E^T and dUt E^T on the lower block tiles
+    #pragma unroll
+            for (int sl = 0; sl < NYS; ++sl) {
+                const int job = w + sl * NW;
+                if (job < 2 * NY) {
+                    int I, J;
+                    lower_tile(job % NY, I, J);
+                    const float* A = job >= NY ? sdU : sdO;
+    #pragma unroll 4
+                    for (int kk = 0; kk < VS; kk += 4)
+                        Y[sl] = mma4(A[(16 * I + r16) * LV + kk + q4], sE[(kk + q4) * LET + 16 * J + r16], Y[sl]);
+                }
             }
         }
     }
