@@ -286,15 +286,34 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 
     // couplings, one 16-row block I at a time with reference row 16 I:
     // Ap = strict lower K Gamma K^T (before beta), Aqk = inclusive lower Q~ Gamma K^T
-    for (int I = 0; I < NB; ++I) {
+    // v and dO rows of this thread's value channel for U, Ut and P, requested
+    // here so that they arrive during the coupling phase
+    const int cv = tid % DV, r0v = (tid / DV) * RPV;
+    float vv[RPV], dv_[RPV];
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) {
-            const int j = r0 + m;
-            if (j < 16 * (I + 1)) sS[j * LS + c] = kr[m] * ex(sGref[I][c] - Gr[m]);
-            if (j >= 16 * I && j < 16 * (I + 1)) {
-                const float f = ex(Gr[m] - sGref[I][c]);
-                sAk[(j - 16 * I) * LK + c] = kr[m] * f;
-                sAq[(j - 16 * I) * LK + c] = a.scale * qr[m] * f;
+    for (int m = 0; m < RPV; ++m) {
+        const size_t o = tok_v(a, b, t0 + clamp_row(r0v + m, L), h) * DV + cv;
+        vv[m] = io<IO>::load(v + o);
+        dv_[m] = io<IO>::load(dO + o);
+    }
+
+    // (a thread's RPT <= 16 rows lie in one 16-row block, Ib, so the row
+    // conditions are uniform per thread and the reference is read once)
+    static_assert(RPT <= 16 && 16 % RPT == 0, "a thread's rows within one block");
+    const int Ib = r0 / 16;
+    for (int I = 0; I < NB; ++I) {
+        const float gref = sGref[I][c];
+        if (Ib <= I) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) sS[(r0 + m) * LS + c] = kr[m] * ex(gref - Gr[m]);
+        }
+        if (Ib == I) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int jl = r0 + m - 16 * I;
+                const float f = ex(Gr[m] - gref);
+                sAk[jl * LK + c] = kr[m] * f;
+                sAq[jl * LK + c] = a.scale * qr[m] * f;
             }
         }
         lds_barrier();
@@ -385,17 +404,10 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     lds_barrier();
 
     // U = T Diag(beta) V
-    {
-        const int cv = tid % DV, r0v = (tid / DV) * RPV;
-        float vv[RPV];
 #pragma unroll
-        for (int m = 0; m < RPV; ++m)
-            vv[m] = io<IO>::load(v + tok_v(a, b, t0 + clamp_row(r0v + m, L), h) * DV + cv);
-#pragma unroll
-        for (int m = 0; m < RPV; ++m) {
-            const int j = r0v + m;
-            sS[j * LS + cv] = sBeta[j] * keep(vv[m], j, L);
-        }
+    for (int m = 0; m < RPV; ++m) {
+        const int j = r0v + m;
+        sS[j * LS + cv] = sBeta[j] * keep(vv[m], j, L);
     }
     lds_barrier();
     for (int job = w; job < NB * (DV / 16); job += NW) {
@@ -427,15 +439,8 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     lds_barrier();
 
     // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV]
-    {
-        const int cv = tid % DV, r0v = (tid / DV) * RPV;
-        float dv_[RPV];
 #pragma unroll
-        for (int m = 0; m < RPV; ++m)
-            dv_[m] = io<IO>::load(dO + tok_v(a, b, t0 + clamp_row(r0v + m, L), h) * DV + cv);
-#pragma unroll
-        for (int m = 0; m < RPV; ++m) sdO[(r0v + m) * LO + cv] = keep(dv_[m], r0v + m, L);
-    }
+    for (int m = 0; m < RPV; ++m) sdO[(r0v + m) * LO + cv] = keep(dv_[m], r0v + m, L);
 #pragma unroll
     for (int m = 0; m < RPT; ++m) sQg[(r0 + m) * LG + c] = a.scale * qr[m] * ex(Gr[m]);
     lds_barrier();
