@@ -134,6 +134,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Inclusive prefix sum over the 16 lanes of a DPP row (row_shr 1, 2, 4, 8;
+// lanes shifted in from outside the row contribute zero): lane 15 of the row
+// ends with the row's total.  Pure VALU, no LDS round trip.
+__device__ __forceinline__ float row16_scan(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, false));
+    return x;
+}
+
 // Loads of a chunk's rows are issued unconditionally from a clamped row
 // (every chunk has at least one row) and zeroed past the end afterwards: a
 // load under a per-row branch is waited for at the branch join, which
@@ -1170,6 +1181,21 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     float* sdAq = smem + S::oAq;
     float* sdAb = smem + S::oAb;
     if (tid < DK) sDgam[tid] = gacc;
+    // the output phase's G, k and q (wave w: key channel c = 16 w + r16, rows
+    // 16 I + 4 q4 + ii), requested before the staging below
+    const int c = 16 * w + r16;
+    float Gd[NB][4], kd[NB][4], qd[NB][4];
+#pragma unroll
+    for (int I = 0; I < NB; ++I) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * I + 4 * q4 + ii;
+            Gd[I][ii] = a.r.G[R * a.r.rs + i * DK + c];
+            const size_t o = tok_qk(a, b, t0 + clamp_row(i, L), hq) * DK + c;
+            kd[I][ii] = io<IO>::load(k + o);
+            qd[I][ii] = io<IO>::load(q + o);
+        }
+    }
     float apv[NYS][4];
 #pragma unroll
     for (int sl = 0; sl < NYS; ++sl) {
@@ -1196,12 +1222,8 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 for (int ii = 0; ii < 4; ++ii) {
                     const int i = 16 * I + 4 * q4 + ii, j = 16 * J + r16;
                     const float dA = j < i ? -Y[sl][ii] : 0.f;
-                    float part = dA * apv[sl][ii];
-                    part += __shfl_xor(part, 1);
-                    part += __shfl_xor(part, 2);
-                    part += __shfl_xor(part, 4);
-                    part += __shfl_xor(part, 8);
-                    if (r16 == 0) sPart[i][J] = part;
+                    const float part = row16_scan(dA * apv[sl][ii]);
+                    if (r16 == 15) sPart[i][J] = part;
                     sdAb[i * LA + j] = sBeta[i] * dA;
                 }
             }
@@ -1216,23 +1238,10 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
 
     // output phase: wave w owns key channels 16 w .. 16 w + 15; lane (r16, q4)
     // holds rows 16 I + 4 q4 + ii of channel 16 w + r16
-    const int c = 16 * w + r16;
     float* src0 = smem + S::oSrc + w * 2 * C * 16;
     float* src1 = src0 + C * 16;
     float* sRow = smem + S::oRow;
     float* sRowG = smem + S::oRowG;
-    float Gd[NB][4], kd[NB][4], qd[NB][4];
-#pragma unroll
-    for (int I = 0; I < NB; ++I) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int i = 16 * I + 4 * q4 + ii;
-            Gd[I][ii] = a.r.G[R * a.r.rs + i * DK + c];
-            const size_t o = tok_qk(a, b, t0 + clamp_row(i, L), hq) * DK + c;
-            kd[I][ii] = io<IO>::load(k + o);
-            qd[I][ii] = io<IO>::load(q + o);
-        }
-    }
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
 #pragma unroll
@@ -1300,12 +1309,8 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             const float dkv = pg + Pinv[I][ii] + pr;
             src1[i * 16 + r16] = kd[I][ii] * (pg - Pinv[I][ii] - pr) + qd[I][ii] * dqv;
             colPr += pr * kd[I][ii];
-            float x3 = X3[I][ii] * kd[I][ii] * eg;
-            x3 += __shfl_xor(x3, 1);
-            x3 += __shfl_xor(x3, 2);
-            x3 += __shfl_xor(x3, 4);
-            x3 += __shfl_xor(x3, 8);
-            if (r16 == 0) sRow[w * C + i] = x3;
+            const float x3 = row16_scan(X3[I][ii] * kd[I][ii] * eg);
+            if (r16 == 15) sRow[w * C + i] = x3;
             if (i < L) {
                 if (grouped) {
                     const size_t o = tok_v(a, b, t0 + i, h) * DK + c;
