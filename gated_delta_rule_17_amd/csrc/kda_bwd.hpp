@@ -37,8 +37,10 @@
 // Products run on v_mfma_f32_16x16x4_f32 with float32 operands from LDS
 // (operand convention, lane l, r = l % 16, g = l / 16: A[r][g], B[g][r];
 // accumulator element i is D[4g + i][r]), except the products over the value
-// dimension in bwd_grad, which take v_mfma_f32_16x16x32_bf16 over bf16 parts
-// (hi + mid + lo) of their float32 operands.
+// dimension in bwd_grad and, for bf16 inputs, the products with T, Aqk and
+// scale Q e^G in bwd_prep: those take v_mfma_f32_16x16x32_bf16 over bf16
+// parts (hi + mid + lo) of their float32 operands, which keeps them good to
+// about 2^-24 of each operand.
 //
 // Decays inside a chunk come from differences of G.  Products that sum
 // over the tokens of a chunk with a decay between the two tokens are split
@@ -197,6 +199,75 @@ __device__ __forceinline__ void lower_tile(int n, int& I, int& J) {
     J = n;
 }
 
+// ---- products over bf16 parts of float32 operands ---------------------------
+// x = hi + mid + lo in bf16 parts (each the nearest bf16 to what the
+// previous parts leave; the differences are exact in float32), good to
+// about 2^-24 of x.
+__device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+    hi = f32_to_bf16(x);
+    const float r = x - bf16_to_f32(hi);
+    mid = f32_to_bf16(r);
+    lo = f32_to_bf16(r - bf16_to_f32(mid));
+}
+
+// Planes of bf16 rows (pw 32-bit words per row); a fragment is the 8
+// consecutive values at columns 8 q4 .. 8 q4 + 7 of one row, which is the
+// operand of lane (r, q4) of v_mfma_f32_16x16x32_bf16 (A[r][8g..8g+7] and
+// B[8g..8g+7][r]; the accumulator is laid out as for the float32
+// instruction).  The three parts of a split operand sit in three planes ps
+// words apart.
+struct F3 { u16x8 h, m, l; };
+__device__ __forceinline__ u16x8 pfrag(const uint32_t* plane, int pw, int row, int q4) {
+    return *reinterpret_cast<const u16x8*>(plane + row * pw + 4 * q4);
+}
+__device__ __forceinline__ F3 pfrag3(const uint32_t* plane, int ps, int pw, int row, int q4) {
+    return F3{pfrag(plane, pw, row, q4), pfrag(plane + ps, pw, row, q4), pfrag(plane + 2 * ps, pw, row, q4)};
+}
+__device__ __forceinline__ f32x4 mmb(const u16x8& x, const u16x8& y, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y),
+                                                   acc, 0, 0, 0);
+}
+// both operands split: hh + hm + mh + hl + lh + mm (smallest terms first)
+__device__ __forceinline__ f32x4 mm6(const F3& x, const F3& y, f32x4 acc) {
+    acc = mmb(x.m, y.m, acc);
+    acc = mmb(x.l, y.h, acc);
+    acc = mmb(x.h, y.l, acc);
+    acc = mmb(x.m, y.h, acc);
+    acc = mmb(x.h, y.m, acc);
+    return mmb(x.h, y.h, acc);
+}
+// one operand exact in bf16
+__device__ __forceinline__ f32x4 mm3a(const u16x8& x, const F3& y, f32x4 acc) {
+    acc = mmb(x, y.l, acc);
+    acc = mmb(x, y.m, acc);
+    return mmb(x, y.h, acc);
+}
+__device__ __forceinline__ f32x4 mm3b(const F3& x, const u16x8& y, f32x4 acc) {
+    acc = mmb(x.l, y, acc);
+    acc = mmb(x.m, y, acc);
+    return mmb(x.h, y, acc);
+}
+// eight consecutive values of a row into the three part planes
+__device__ __forceinline__ void put3x8(uint32_t* plane, int ps, int off, const float* x) {
+    u16x8 h, m, l;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) {
+        uint16_t a, b, c;
+        split3(x[z], a, b, c);
+        h[z] = a; m[z] = b; l[z] = c;
+    }
+    *reinterpret_cast<u16x8*>(plane + off) = h;
+    *reinterpret_cast<u16x8*>(plane + ps + off) = m;
+    *reinterpret_cast<u16x8*>(plane + 2 * ps + off) = l;
+}
+// eight values exact in bf16 into one plane
+__device__ __forceinline__ void put1x8(uint32_t* plane, int off, const float* x) {
+    u16x8 h;
+#pragma unroll
+    for (int z = 0; z < 8; ++z) h[z] = f32_to_bf16(x[z]);
+    *reinterpret_cast<u16x8*>(plane + off) = h;
+}
+
 // ---------------------------------------------------------------------------
 // 1. per-chunk preparation
 // ---------------------------------------------------------------------------
@@ -214,6 +285,16 @@ struct PrepLds {
     // Aqk lives through both phases
     static constexpr int oAqk = P1_END > P2_END ? P1_END : P2_END;
     static constexpr int SIZE = oAqk + C * LQ;
+    // split path (bf16 inputs): bf16 planes whose rows hold C + 8 values along
+    // the chunk (PW words per row).  (K e^G)^T and V^T overlay phase 1 once T
+    // has been read; T Diag(beta) sits past phase 1; (scale Q e^G)^T and dO^T
+    // overlay both; Aqk^T lives past everything from the coupling phase on.
+    static constexpr int PW = (C + 8) / 2;
+    static constexpr int xKG = 0, xVT = xKG + 3 * DK * PW, X2_END = xVT + DV * PW;
+    static constexpr int xTB = P1_END > X2_END ? P1_END : X2_END, XT_END = xTB + 3 * C * PW;
+    static constexpr int yQG = 0, ydO = yQG + 3 * DK * PW, Y_END = ydO + DV * PW;
+    static constexpr int oAqkP = XT_END > Y_END ? XT_END : Y_END;
+    static constexpr int SIZE_S = oAqkP + 3 * C * PW;
 };
 
 template <int C, int DK, int DV>
@@ -228,7 +309,11 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     constexpr int NT = prep_threads<C, DK, DV>(), NW = NT / 64;
     constexpr int TPC = NT / DK, RPT = C / TPC;    // threads per key channel, rows per thread
     constexpr int TPV = NT / DV, RPV = C / TPV;    // the same for value channels
-    __shared__ __align__(16) float smem[S::SIZE];
+    // bf16 inputs: the products with T, Aqk and (scale Q e^G) run on bf16
+    // matrix cores over split operands (v and dO are exact in bf16)
+    constexpr bool SPLIT = std::is_same<IO, bf16_t>::value && C % 32 == 0 && RPT % 8 == 0 && RPV % 8 == 0;
+    constexpr int PW = S::PW;
+    __shared__ __align__(16) float smem[SPLIT ? S::SIZE_S : S::SIZE];
     __shared__ float sGref[NB + 1][DK];             // G at rows 16 I and at the last row
     __shared__ float sSeg[TPC][DK];
     __shared__ float sBeta[C];
@@ -297,6 +382,16 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 
     // couplings, one 16-row block I at a time with reference row 16 I:
     // Ap = strict lower K Gamma K^T (before beta), Aqk = inclusive lower Q~ Gamma K^T
+    if constexpr (SPLIT) {
+        // Aqk^T blocks (rows 16 (I + 1) .., columns 16 I ..) above the
+        // diagonal are read by the 32-wide steps of the Ut products: zero
+        uint32_t* pAq = reinterpret_cast<uint32_t*>(smem + S::oAqkP);
+        for (int e = tid; e < 3 * (NB - 1) * 32; e += NT) {
+            const int part = e / ((NB - 1) * 32), r = e % ((NB - 1) * 32), I = r / 32;
+            const int row = 16 * (I + 1) + (r % 32) / 2, col = 16 * I + 8 * (r % 2);
+            *reinterpret_cast<u16x8*>(pAq + part * C * PW + row * PW + col / 2) = (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
     // v and dO rows of this thread's value channel for U, Ut and P, requested
     // here so that they arrive during the coupling phase
     const int cv = tid % DV, r0v = (tid / DV) * RPV;
@@ -342,8 +437,25 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
                     const float val = j < i ? acc[ii] : 0.f;
                     sAp[i * LC + j] = val;
                     a.r.Ap[R * a.r.rs + i * C + j] = val;
-                } else {
+                } else if (!SPLIT) {
                     sAqk[i * LQ + j] = j <= i ? acc[ii] : 0.f;
+                }
+            }
+            if constexpr (SPLIT) {
+                if (which == 1) {
+                    // Aqk^T in bf16 parts: row j, the four columns i = 16 I + 4 q4 + ii
+                    u16x4 h4, m4, l4;
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        uint16_t x0, x1, x2;
+                        split3(16 * J + r16 <= 16 * I + 4 * q4 + ii ? acc[ii] : 0.f, x0, x1, x2);
+                        h4[ii] = x0; m4[ii] = x1; l4[ii] = x2;
+                    }
+                    uint16_t* pq = reinterpret_cast<uint16_t*>(smem + S::oAqkP);
+                    const int o = (16 * J + r16) * (2 * PW) + 16 * I + 4 * q4;
+                    *reinterpret_cast<u16x4*>(pq + o) = h4;
+                    *reinterpret_cast<u16x4*>(pq + 2 * C * PW + o) = m4;
+                    *reinterpret_cast<u16x4*>(pq + 4 * C * PW + o) = l4;
                 }
             }
         }
@@ -395,38 +507,90 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
         a.r.Tm[R * a.r.rs + e] = (j >> 4) <= (i >> 4) ? sT[i * LC + j] : 0.f;
     }
 
-    // W = T Diag(beta) (K e^G), stored as [C][DK] and transposed [DK][C]
+    if constexpr (SPLIT) {
+        // TB = T Diag(beta) in bf16 parts, rows of C values (blocks above the
+        // diagonal zero); then (K e^G)^T in parts and V^T (exact)
+        uint32_t* pTB = reinterpret_cast<uint32_t*>(smem + S::xTB);
+        uint32_t* pKG = reinterpret_cast<uint32_t*>(smem + S::xKG);
+        uint32_t* pVT = reinterpret_cast<uint32_t*>(smem + S::xVT);
+        for (int g = tid; g < C * C / 8; g += NT) {
+            const int i = g / (C / 8), j0 = 8 * (g % (C / 8));
+            float x[8];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int j = r0 + m;
-        sS[j * LS + c] = sBeta[j] * kr[m] * ex(Gr[m]);
-    }
-    lds_barrier();
-    for (int job = w; job < NB * (DK / 16); job += NW) {
-        const int I = job / (DK / 16), Rc = job % (DK / 16);
-        f32x4 acc = zero4();
-        for (int kk = 0; kk < 16 * (I + 1); kk += 4)
-            acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
+            for (int z = 0; z < 8; ++z)
+                x[z] = (j0 >> 4) <= (i >> 4) ? sT[i * LC + j0 + z] * sBeta[j0 + z] : 0.f;
+            put3x8(pTB, C * PW, i * PW + j0 / 2, x);
+        }
+        lds_barrier();
+        {
+            float x[RPT];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            a.r.W[R * a.r.rs + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
-        *reinterpret_cast<f32x4*>(a.r.WT + R * a.r.rs + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
-    }
-    lds_barrier();
+            for (int m = 0; m < RPT; ++m) x[m] = kr[m] * ex(Gr[m]);
+#pragma unroll
+            for (int g = 0; g < RPT; g += 8) put3x8(pKG, DK * PW, c * PW + (r0 + g) / 2, x + g);
+            float y[RPV];
+#pragma unroll
+            for (int m = 0; m < RPV; ++m) y[m] = keep(vv[m], r0v + m, L);
+#pragma unroll
+            for (int g = 0; g < RPV; g += 8) put1x8(pVT, cv * PW + (r0v + g) / 2, y + g);
+        }
+        lds_barrier();
+        // W = TB (K e^G), stored as [C][DK] and transposed [DK][C]; U = TB V
+        constexpr int NJW = NB * (DK / 16);
+        for (int job = w; job < NJW + NB * (DV / 16); job += NW) {
+            f32x4 acc = zero4();
+            if (job < NJW) {
+                const int I = job / (DK / 16), Rc = job % (DK / 16);
+                for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
+                    acc = mm6(pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4),
+                              pfrag3(pKG + k0 / 2, DK * PW, PW, 16 * Rc + r16, q4), acc);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    a.r.W[R * a.r.rs + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
+                *reinterpret_cast<f32x4*>(a.r.WT + R * a.r.rs + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+            } else {
+                const int ju = job - NJW, I = ju / (DV / 16), Vt = ju % (DV / 16);
+                for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
+                    acc = mm3b(pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4),
+                               pfrag(pVT + k0 / 2, PW, 16 * Vt + r16, q4), acc);
+                *reinterpret_cast<f32x4*>(a.r.U + R * a.r.rs + (size_t)(16 * Vt + r16) * C + 16 * I + 4 * q4) = acc;
+            }
+        }
+    } else {
+        // W = T Diag(beta) (K e^G), stored as [C][DK] and transposed [DK][C]
+    #pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int j = r0 + m;
+            sS[j * LS + c] = sBeta[j] * kr[m] * ex(Gr[m]);
+        }
+        lds_barrier();
+        for (int job = w; job < NB * (DK / 16); job += NW) {
+            const int I = job / (DK / 16), Rc = job % (DK / 16);
+            f32x4 acc = zero4();
+            for (int kk = 0; kk < 16 * (I + 1); kk += 4)
+                acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
+    #pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                a.r.W[R * a.r.rs + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
+            *reinterpret_cast<f32x4*>(a.r.WT + R * a.r.rs + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+        }
+        lds_barrier();
 
-    // U = T Diag(beta) V
-#pragma unroll
-    for (int m = 0; m < RPV; ++m) {
-        const int j = r0v + m;
-        sS[j * LS + cv] = sBeta[j] * keep(vv[m], j, L);
-    }
-    lds_barrier();
-    for (int job = w; job < NB * (DV / 16); job += NW) {
-        const int I = job / (DV / 16), Rc = job % (DV / 16);
-        f32x4 acc = zero4();
-        for (int kk = 0; kk < 16 * (I + 1); kk += 4)
-            acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
-        *reinterpret_cast<f32x4*>(a.r.U + R * a.r.rs + (size_t)(16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+        // U = T Diag(beta) V
+    #pragma unroll
+        for (int m = 0; m < RPV; ++m) {
+            const int j = r0v + m;
+            sS[j * LS + cv] = sBeta[j] * keep(vv[m], j, L);
+        }
+        lds_barrier();
+        for (int job = w; job < NB * (DV / 16); job += NW) {
+            const int I = job / (DV / 16), Rc = job % (DV / 16);
+            f32x4 acc = zero4();
+            for (int kk = 0; kk < 16 * (I + 1); kk += 4)
+                acc = mma4(sT[(16 * I + r16) * LC + kk + q4], sS[(kk + q4) * LS + 16 * Rc + r16], acc);
+            *reinterpret_cast<f32x4*>(a.r.U + R * a.r.rs + (size_t)(16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+        }
+
     }
 
     // Kr = K e^{G_last - G}, stored as [C][DK] and transposed [DK][C]
@@ -449,26 +613,66 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     }
     lds_barrier();
 
-    // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV]
+    if constexpr (SPLIT) {
+        // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV] over
+        // (scale Q e^G)^T in parts and dO^T (exact)
+        uint32_t* pQG = reinterpret_cast<uint32_t*>(smem + S::yQG);
+        uint32_t* pdO = reinterpret_cast<uint32_t*>(smem + S::ydO);
+        const uint32_t* pAq = reinterpret_cast<const uint32_t*>(smem + S::oAqkP);
+        {
+            float x[RPT];
 #pragma unroll
-    for (int m = 0; m < RPV; ++m) sdO[(r0v + m) * LO + cv] = keep(dv_[m], r0v + m, L);
+            for (int m = 0; m < RPT; ++m) x[m] = a.scale * qr[m] * ex(Gr[m]);
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) sQg[(r0 + m) * LG + c] = a.scale * qr[m] * ex(Gr[m]);
-    lds_barrier();
-    constexpr int NJU = NB * (DV / 16), NJP = (DK / 16) * (DV / 16);
-    for (int job = w; job < NJU + NJP; job += NW) {
-        f32x4 acc = zero4();
-        if (job < NJU) {
-            const int J = job / (DV / 16), Vt = job % (DV / 16);
-            for (int kk = 16 * J; kk < C; kk += 4)
-                acc = mma4(sAqk[(kk + q4) * LQ + 16 * J + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
-            *reinterpret_cast<f32x4*>(a.r.Ut + R * a.r.rs + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
-        } else {
-            const int jp = job - NJU, Rc = jp / (DV / 16), Vt = jp % (DV / 16);
-#pragma unroll 8
-            for (int kk = 0; kk < C; kk += 4)
-                acc = mma4(sQg[(kk + q4) * LG + 16 * Rc + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
-            *reinterpret_cast<f32x4*>(a.r.P + R * a.r.rs + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
+            for (int g = 0; g < RPT; g += 8) put3x8(pQG, DK * PW, c * PW + (r0 + g) / 2, x + g);
+            float y[RPV];
+#pragma unroll
+            for (int m = 0; m < RPV; ++m) y[m] = keep(dv_[m], r0v + m, L);
+#pragma unroll
+            for (int g = 0; g < RPV; g += 8) put1x8(pdO, cv * PW + (r0v + g) / 2, y + g);
+        }
+        lds_barrier();
+        constexpr int NJU = NB * (DV / 16), NJP = (DK / 16) * (DV / 16);
+        for (int job = w; job < NJU + NJP; job += NW) {
+            f32x4 acc = zero4();
+            if (job < NJU) {
+                // rows i >= 16 J; a step from 16 (J - 1) reads the zeroed block
+                const int J = job / (DV / 16), Vt = job % (DV / 16);
+                for (int k0 = 32 * (J / 2); k0 < C; k0 += 32)
+                    acc = mm3b(pfrag3(pAq + k0 / 2, C * PW, PW, 16 * J + r16, q4),
+                               pfrag(pdO + k0 / 2, PW, 16 * Vt + r16, q4), acc);
+                *reinterpret_cast<f32x4*>(a.r.Ut + R * a.r.rs + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
+            } else {
+                const int jp = job - NJU, Rc = jp / (DV / 16), Vt = jp % (DV / 16);
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += 32)
+                    acc = mm3b(pfrag3(pQG + k0 / 2, DK * PW, PW, 16 * Rc + r16, q4),
+                               pfrag(pdO + k0 / 2, PW, 16 * Vt + r16, q4), acc);
+                *reinterpret_cast<f32x4*>(a.r.P + R * a.r.rs + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
+            }
+        }
+    } else {
+        // phase 2: Ut = Aqk^T dO [C][DV] and P = (scale Q e^G)^T dO [DK][DV]
+    #pragma unroll
+        for (int m = 0; m < RPV; ++m) sdO[(r0v + m) * LO + cv] = keep(dv_[m], r0v + m, L);
+    #pragma unroll
+        for (int m = 0; m < RPT; ++m) sQg[(r0 + m) * LG + c] = a.scale * qr[m] * ex(Gr[m]);
+        lds_barrier();
+        constexpr int NJU = NB * (DV / 16), NJP = (DK / 16) * (DV / 16);
+        for (int job = w; job < NJU + NJP; job += NW) {
+            f32x4 acc = zero4();
+            if (job < NJU) {
+                const int J = job / (DV / 16), Vt = job % (DV / 16);
+                for (int kk = 16 * J; kk < C; kk += 4)
+                    acc = mma4(sAqk[(kk + q4) * LQ + 16 * J + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
+                *reinterpret_cast<f32x4*>(a.r.Ut + R * a.r.rs + (size_t)(16 * Vt + r16) * C + 16 * J + 4 * q4) = acc;
+            } else {
+                const int jp = job - NJU, Rc = jp / (DV / 16), Vt = jp % (DV / 16);
+    #pragma unroll 8
+                for (int kk = 0; kk < C; kk += 4)
+                    acc = mma4(sQg[(kk + q4) * LG + 16 * Rc + r16], sdO[(kk + q4) * LO + 16 * Vt + r16], acc);
+                *reinterpret_cast<f32x4*>(a.r.P + R * a.r.rs + (size_t)(16 * Vt + r16) * DK + 16 * Rc + 4 * q4) = acc;
+            }
         }
     }
 }
@@ -726,16 +930,6 @@ struct GradLds {
     static constexpr int SIZE = SL_END > E_END ? SL_END : E_END;
 };
 
-// x = hi + mid + lo in bf16 parts (each the nearest bf16 to what the
-// previous parts leave; the differences are exact in float32), good to
-// about 2^-24 of x
-__device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
-    hi = f32_to_bf16(x);
-    const float r = x - bf16_to_f32(hi);
-    mid = f32_to_bf16(r);
-    lo = f32_to_bf16(r - bf16_to_f32(mid));
-}
-
 template <int C, int DK, int DV, typename IO>
 __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
 {
@@ -832,30 +1026,8 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             plane[PS + o] = pack(m0, m1);
             plane[2 * PS + o] = pack(l0, l1);
         };
-        auto frag = [&](const uint32_t* plane, int row) -> u16x8 {
-            return *reinterpret_cast<const u16x8*>(plane + row * SW + 4 * q4);
-        };
-        struct F3 { u16x8 h, m, l; };
-        auto frag3 = [&](const uint32_t* plane, int PS, int row) -> F3 {
-            return F3{frag(plane, row), frag(plane + PS, row), frag(plane + 2 * PS, row)};
-        };
-        auto mmb = [](const u16x8& x, const u16x8& y, f32x4 acc) -> f32x4 {
-            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
-                                                           __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
-        };
-        auto mm6 = [&](const F3& x, const F3& y, f32x4 acc) -> f32x4 {
-            acc = mmb(x.m, y.m, acc);
-            acc = mmb(x.l, y.h, acc);
-            acc = mmb(x.h, y.l, acc);
-            acc = mmb(x.m, y.h, acc);
-            acc = mmb(x.h, y.m, acc);
-            return mmb(x.h, y.h, acc);
-        };
-        auto mm3x = [&](const u16x8& x, const F3& y, f32x4 acc) -> f32x4 {   // x exact
-            acc = mmb(x, y.l, acc);
-            acc = mmb(x, y.m, acc);
-            return mmb(x, y.h, acc);
-        };
+        auto frag = [&](const uint32_t* plane, int row) -> u16x8 { return pfrag(plane, SW, row, q4); };
+        auto frag3 = [&](const uint32_t* plane, int PS, int row) -> F3 { return pfrag3(plane, PS, SW, row, q4); };
         // element maps (tid-based, 64-lane groups): a state or E element is
         // (column quad cq, value-column pair p), with four consecutive quads
         // per 64 bytes of a record row; a dO / v element is (row i, pair p)
@@ -1001,7 +1173,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 for (int I = 0; I < NB; ++I) {
                     const int row = 16 * I + r16;
                     if constexpr (OEX)
-                        X1[I] = mm3x(frag(pO, row), fH, X1[I]);
+                        X1[I] = mm3a(frag(pO, row), fH, X1[I]);
                     else
                         X1[I] = mm6(frag3(pO, PC, row), fH, X1[I]);
                     const u16x8 fUh = frag(pU, row), fUm = frag(pU + PC, row);
@@ -1026,7 +1198,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                     if (job >= NY)
                         Y[sl] = mm6(frag3(pU, PC, 16 * I + r16), fB, Y[sl]);
                     else if constexpr (OEX)
-                        Y[sl] = mm3x(frag(pO, 16 * I + r16), fB, Y[sl]);
+                        Y[sl] = mm3a(frag(pO, 16 * I + r16), fB, Y[sl]);
                     else
                         Y[sl] = mm6(frag3(pO, PC, 16 * I + r16), fB, Y[sl]);
                 }
