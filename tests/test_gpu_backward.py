@@ -131,6 +131,23 @@ def test_bwd_bf16_mid(mode):
     _compare(f"bf16 {mode} T512", _run(w, cot, 64), _oracle(w, cot), TOL["bf16"])
 
 
+@pytest.mark.parametrize("chunk,Dk,Dv", [(32, 128, 128), (32, 64, 64), (64, 128, 64),
+                                          (64, 64, 128), (16, 128, 128), (32, 32, 32)])
+def test_bwd_bf16_chunks_and_dims(chunk, Dk, Dv):
+    """bf16 inputs over chunk lengths and head dims, ragged tail.  With bf16
+    inputs the preparation's products with T, Aqk and scale Q e^G run on bf16
+    matrix cores over three-part splits where the chunk is a multiple of 32
+    and each thread holds whole 8-row groups (the first four cases), the
+    float32 path elsewhere.  Both keep float32-level accuracy, so the bound
+    here is 2e-3, a tenth of the bf16 bar: a split that lost a part (about
+    2^-16 of each operand) would fail it."""
+    w = make_inputs(1, 200, 2, Dk, Dv, mode="channel", dtype="bf16", seed=40 + chunk + Dk + Dv,
+                    h0_std=0.05)
+    cot = make_cotangents(w, seed=3, dhT_std=0.1)
+    say("bwd bf16 chunk", chunk, "dims", Dk, Dv)
+    _compare(f"bf16 C{chunk} Dk{Dk} Dv{Dv}", _run(w, cot, chunk), _oracle(w, cot), 2e-3)
+
+
 @pytest.mark.parametrize("Hqk,G", [(4, 1), (2, 2)])
 def test_bf16_gradients_are_the_rounded_float32_ones(Hqk, G):
     from kda_workloads import bf16_round
