@@ -916,13 +916,13 @@ struct GradLds {
     // float T, V and dE (transposed), then bf16 planes [row][SB] of the
     // hi, mid and lo parts of the state, its gradient, E, dO and dUt
     // (offsets in floats)
-    static constexpr bool HL = VS == 32;
+    static constexpr bool SPLIT = VS == 32;
     static constexpr int SB = VS + 8;
     static constexpr int hT = 0, hV = hT + C * LT, hdE = hV + C * LV, hP = hdE + VS * LDE;
     static constexpr int pH = DK * SB / 2, pC = C * SB / 2;   // floats per plane
     static constexpr int hH = hP, hdH = hH + 3 * pH, hE = hdH + 3 * pH, hO = hE + 3 * pC,
                          hU = hO + 3 * pC, H_END = hU + 3 * pC;
-    static constexpr int SL_END = HL ? H_END : S_END;
+    static constexpr int SL_END = SPLIT ? H_END : S_END;
     // output phase
     static constexpr int oAq = 0, oAb = oAq + C * LA, oSrc = oAb + C * LA,
                          oRow = oSrc + NW * 2 * C * 16, oRowG = oRow + NW * C,
@@ -991,7 +991,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
     for (int s = 0; s < NYS; ++s) Y[s] = zero4();
     float zacc = 0.f, gacc = 0.f;
 
-    if constexpr (S::HL) {
+    if constexpr (S::SPLIT) {
         // Slices of 32 value columns: every product of the slice is a sum of
         // 32-deep steps of v_mfma_f32_16x16x32_bf16 over bf16 parts of the
         // float32 operands, x = x_h + x_m + x_l.  A product keeps the parts
@@ -1037,11 +1037,11 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         static_assert(4 * DK == NT, "one state element pair per thread");
         const int hcq = 4 * (tid >> 6) + (tid & 3), hp = (tid >> 2) & 15;
         float gpart[4] = {0.f, 0.f, 0.f, 0.f};     // sum_n H dH of channels 4 hcq + z
-        struct SliceHL {
+        struct SliceS {
             f32x4 h0, h1, d0, d1, e0[NEJ], e1[NEJ], de[NE];
             float o0[NOJ], o1[NOJ], v0[NOJ], v1[NOJ];
         };
-        auto load_slice = [&](SliceHL& x, int s) {
+        auto load_slice = [&](SliceS& x, int s) {
             const int v0 = s * VS;
             {
                 const size_t o = R * a.r.rs + (size_t)(v0 + 2 * hp) * DK + 4 * hcq;
@@ -1081,7 +1081,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 }
             }
         };
-        auto store_slice = [&](const SliceHL& x) {
+        auto store_slice = [&](const SliceS& x) {
 #pragma unroll
             for (int z = 0; z < 4; ++z) {
                 const int o = (4 * hcq + z) * SW + hp;
@@ -1127,7 +1127,7 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             }
         };
 
-        SliceHL nx;
+        SliceS nx;
         load_slice(nx, 0);
         uint16_t* pU16 = reinterpret_cast<uint16_t*>(pU);
         for (int s = 0; s < NS; ++s) {
