@@ -210,6 +210,21 @@ __device__ __forceinline__ void split3(float x, uint16_t& hi, uint16_t& mid, uin
     lo = f32_to_bf16(r - bf16_to_f32(mid));
 }
 
+// The same for a pair of values, each part packed two to a word (value 0 in
+// the low half): one conversion instruction per part for both values, with
+// the rounding of f32_to_bf16.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk(float x0, float x1) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+}
+__device__ __forceinline__ void split3x2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    hi = cvt_pk(x0, x1);
+    const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+    mid = cvt_pk(r0, r1);
+    lo = cvt_pk(r0 - __uint_as_float(mid << 16), r1 - __uint_as_float(mid & 0xffff0000u));
+}
+
 // Planes of bf16 rows (pw 32-bit words per row); a fragment is the 8
 // consecutive values at columns 8 q4 .. 8 q4 + 7 of one row, which is the
 // operand of lane (r, q4) of v_mfma_f32_16x16x32_bf16 (A[r][8g..8g+7] and
@@ -249,23 +264,19 @@ __device__ __forceinline__ f32x4 mm3b(const F3& x, const u16x8& y, f32x4 acc) {
 }
 // eight consecutive values of a row into the three part planes
 __device__ __forceinline__ void put3x8(uint32_t* plane, int ps, int off, const float* x) {
-    u16x8 h, m, l;
+    uint32_t h[4], m[4], l[4];
 #pragma unroll
-    for (int z = 0; z < 8; ++z) {
-        uint16_t a, b, c;
-        split3(x[z], a, b, c);
-        h[z] = a; m[z] = b; l[z] = c;
-    }
-    *reinterpret_cast<u16x8*>(plane + off) = h;
-    *reinterpret_cast<u16x8*>(plane + ps + off) = m;
-    *reinterpret_cast<u16x8*>(plane + 2 * ps + off) = l;
+    for (int z = 0; z < 4; ++z) split3x2(x[2 * z], x[2 * z + 1], h[z], m[z], l[z]);
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4_t*>(plane + off) = (u32x4_t){h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4_t*>(plane + ps + off) = (u32x4_t){m[0], m[1], m[2], m[3]};
+    *reinterpret_cast<u32x4_t*>(plane + 2 * ps + off) = (u32x4_t){l[0], l[1], l[2], l[3]};
 }
 // eight values exact in bf16 into one plane
 __device__ __forceinline__ void put1x8(uint32_t* plane, int off, const float* x) {
-    u16x8 h;
-#pragma unroll
-    for (int z = 0; z < 8; ++z) h[z] = f32_to_bf16(x[z]);
-    *reinterpret_cast<u16x8*>(plane + off) = h;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4_t*>(plane + off) =
+        (u32x4_t){cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3]), cvt_pk(x[4], x[5]), cvt_pk(x[6], x[7])};
 }
 
 // ---------------------------------------------------------------------------
@@ -444,18 +455,18 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             if constexpr (SPLIT) {
                 if (which == 1) {
                     // Aqk^T in bf16 parts: row j, the four columns i = 16 I + 4 q4 + ii
-                    u16x4 h4, m4, l4;
+                    float x[4];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        uint16_t x0, x1, x2;
-                        split3(16 * J + r16 <= 16 * I + 4 * q4 + ii ? acc[ii] : 0.f, x0, x1, x2);
-                        h4[ii] = x0; m4[ii] = x1; l4[ii] = x2;
-                    }
-                    uint16_t* pq = reinterpret_cast<uint16_t*>(smem + S::oAqkP);
-                    const int o = (16 * J + r16) * (2 * PW) + 16 * I + 4 * q4;
-                    *reinterpret_cast<u16x4*>(pq + o) = h4;
-                    *reinterpret_cast<u16x4*>(pq + 2 * C * PW + o) = m4;
-                    *reinterpret_cast<u16x4*>(pq + 4 * C * PW + o) = l4;
+                    for (int ii = 0; ii < 4; ++ii) x[ii] = 16 * J + r16 <= 16 * I + 4 * q4 + ii ? acc[ii] : 0.f;
+                    uint32_t h0, m0, l0, h1, m1, l1;
+                    split3x2(x[0], x[1], h0, m0, l0);
+                    split3x2(x[2], x[3], h1, m1, l1);
+                    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                    uint32_t* pq = reinterpret_cast<uint32_t*>(smem + S::oAqkP);
+                    const int o = (16 * J + r16) * PW + 8 * I + 2 * q4;
+                    *reinterpret_cast<u32x2_t*>(pq + o) = (u32x2_t){h0, h1};
+                    *reinterpret_cast<u32x2_t*>(pq + C * PW + o) = (u32x2_t){m0, m1};
+                    *reinterpret_cast<u32x2_t*>(pq + 2 * C * PW + o) = (u32x2_t){l0, l1};
                 }
             }
         }
@@ -1014,17 +1025,13 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         uint32_t* pU = reinterpret_cast<uint32_t*>(smem + S::hU);
         float* sVh = smem + S::hV;
         float* sdEh = smem + S::hdE;
-        auto pack = [](uint16_t x0, uint16_t x1) -> uint32_t {
-            return (uint32_t)x0 | ((uint32_t)x1 << 16);
-        };
         // the three parts of a pair of values into three planes of PS floats
         auto put3 = [&](uint32_t* plane, int PS, int o, float x0, float x1) {
-            uint16_t h0, m0, l0, h1, m1, l1;
-            split3(x0, h0, m0, l0);
-            split3(x1, h1, m1, l1);
-            plane[o] = pack(h0, h1);
-            plane[PS + o] = pack(m0, m1);
-            plane[2 * PS + o] = pack(l0, l1);
+            uint32_t h, m, l;
+            split3x2(x0, x1, h, m, l);
+            plane[o] = h;
+            plane[PS + o] = m;
+            plane[2 * PS + o] = l;
         };
         auto frag = [&](const uint32_t* plane, int row) -> u16x8 { return pfrag(plane, SW, row, q4); };
         auto frag3 = [&](const uint32_t* plane, int PS, int row) -> F3 { return pfrag3(plane, PS, SW, row, q4); };
