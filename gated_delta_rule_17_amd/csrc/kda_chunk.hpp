@@ -52,8 +52,15 @@ constexpr float kLog2e = 1.4426950408889634f;
 // 2^x on the transcendental unit (x in log2 units; underflows to 0)
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// log(sigmoid(a)) = min(a, 0) - log(1 + exp(-|a|)), without overflow
-__device__ __forceinline__ float log_sigmoid(float a) { return fminf(a, 0.f) - log1pf(expf(-fabsf(a))); }
+// log(sigmoid(a)) = min(a, 0) - log(1 + exp(-|a|)), without overflow, on the
+// transcendental unit: exp(-|a|) lies in (0, 1], so 1 + exp(-|a|) lies in
+// (1, 2] and its log2 carries an absolute error of about 1e-7.  That absolute
+// error is what the decays see (they are exponentials of differences of
+// prefix sums of these logs).
+__device__ __forceinline__ float log_sigmoid(float a) {
+    const float e = exp2_fast(-fabsf(a) * kLog2e);
+    return fminf(a, 0.f) - __builtin_amdgcn_logf(1.f + e) * (1.f / kLog2e);
+}
 
 template <int C, int DK, int DV, typename OT>
 struct CS {
