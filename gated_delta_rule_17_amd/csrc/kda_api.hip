@@ -8,7 +8,8 @@
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_dk(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_dv(int d) { return supported_dk(d) || d == 256; }
 bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 
 kda_status check_common(const void* q, const void* k, const void* v, const float* g,
@@ -21,7 +22,7 @@ kda_status check_common(const void* q, const void* k, const void* v, const float
         return KDA_ERROR_INVALID_VALUE;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
     if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
-    if (!supported_dim(Dk) || !supported_dim(Dv)) return KDA_ERROR_NOT_SUPPORTED;
+    if (!supported_dk(Dk) || !supported_dv(Dv)) return KDA_ERROR_NOT_SUPPORTED;
     // sizes must fit the 64-bit index arithmetic of the kernels comfortably
     const double tok = (double)B * (double)T * (double)H;
     if (tok * (double)(Dk > Dv ? Dk : Dv) > 9.0e15) return KDA_ERROR_INVALID_VALUE;
@@ -77,7 +78,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chu
 {
     (void)mode;
     if (B < 1 || H < 1 || T <= 0) return 0;
-    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     return kda::chunk_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
 }
@@ -91,7 +92,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
-    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    if (!supported_chunk(chunk) || !kda::chunk_fwd_supported(Dk, Dv, chunk, dtype))
+        return KDA_ERROR_NOT_SUPPORTED;
     // chunk records and state workgroups are counted in 32-bit integers
     const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
     if (nrec > 1073741824.0 || (double)B * H * (Dv / 16) + 64.0 > 2147483647.0)
@@ -134,7 +136,7 @@ size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, 
 {
     (void)mode;
     if (N < 1 || H < 1 || T < 0) return 0;
-    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     return kda::chunk_varlen_workspace_bytes(N, T, H, Dk, Dv, chunk, dtype);
 }
@@ -149,7 +151,8 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     if (N < 0 || (prologue & ~KDA_PROLOGUE_ALL)) return KDA_ERROR_INVALID_VALUE;
     kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
     if (st != KDA_SUCCESS) return st;
-    if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
+    if (!supported_chunk(chunk) || !kda::chunk_fwd_supported(Dk, Dv, chunk, dtype))
+        return KDA_ERROR_NOT_SUPPORTED;
     // chunk records and state workgroups are counted in 32-bit integers
     const double gmax = (double)((T + chunk - 1) / chunk) + (double)N;
     if (gmax * H > 1073741824.0 || (double)N * H * (Dv / 16) + 64.0 > 2147483647.0)
@@ -175,7 +178,7 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv
     (void)mode;
     if (B < 1 || H < 1 || T <= 0) return 0;
     if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
-    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     return kda::chunk_bwd_workspace_bytes(B, T, H, Hqk, Dk, Dv, chunk);
 }
@@ -223,7 +226,7 @@ size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int Hqk, int Dk,
     (void)mode;
     if (N < 1 || H < 1 || T < 0) return 0;
     if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
-    if (!supported_dim(Dk) || !supported_dim(Dv) || !supported_chunk(chunk)) return 0;
+    if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     return kda::chunk_bwd_varlen_workspace_bytes(N, T, H, Hqk, Dk, Dv, chunk);
 }

@@ -283,9 +283,25 @@ __device__ __forceinline__ void put1x8(uint32_t* plane, int off, const float* x)
 // 1. per-chunk preparation
 // ---------------------------------------------------------------------------
 template <int C, int DK, int DV>
+constexpr int prep_threads() { return (C * DK >= 512 && C * DV >= 512) ? 512 : 256; }
+
+// bf16 inputs: the products with T, Aqk and (scale Q e^G) run on bf16 matrix
+// cores over split operands (v and dO are exact in bf16), where the chunk is
+// a multiple of the 32-wide step and each thread's rows come in whole 8-row
+// groups
+template <int C, int DK, int DV, typename IO>
+constexpr bool prep_split()
+{
+    constexpr int NT = prep_threads<C, DK, DV>();
+    return std::is_same<IO, bf16_t>::value && C % 32 == 0 && (C * DK / NT) % 8 == 0 &&
+           (C * DV / NT) % 8 == 0;
+}
+
+// SPL: the split path, whose float32 staging rows hold key channels only
+template <int C, int DK, int DV, bool SPL>
 struct PrepLds {
     static constexpr int NB = C / 16;
-    static constexpr int DM = DK > DV ? DK : DV;
+    static constexpr int DM = SPL || DK > DV ? DK : DV;
     static constexpr int LS = DM + 2, LK = DK + 2, LC = C + 2, LQ = C + 16;
     static constexpr int LO = DV + 16, LG = DK + 16;
     // phase 1: couplings, inverse, W, U
@@ -308,21 +324,16 @@ struct PrepLds {
     static constexpr int SIZE_S = oAqkP + 3 * C * PW;
 };
 
-template <int C, int DK, int DV>
-constexpr int prep_threads() { return (C * DK >= 512 && C * DV >= 512) ? 512 : 256; }
-
 template <int C, int DK, int DV, typename IO>
 __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
 {
-    using S = PrepLds<C, DK, DV>;
+    constexpr bool SPLIT = prep_split<C, DK, DV, IO>();
+    using S = PrepLds<C, DK, DV, SPLIT>;
     constexpr int NB = S::NB, LS = S::LS, LK = S::LK, LC = S::LC, LQ = S::LQ, LO = S::LO,
                   LG = S::LG;
     constexpr int NT = prep_threads<C, DK, DV>(), NW = NT / 64;
     constexpr int TPC = NT / DK, RPT = C / TPC;    // threads per key channel, rows per thread
     constexpr int TPV = NT / DV, RPV = C / TPV;    // the same for value channels
-    // bf16 inputs: the products with T, Aqk and (scale Q e^G) run on bf16
-    // matrix cores over split operands (v and dO are exact in bf16)
-    constexpr bool SPLIT = std::is_same<IO, bf16_t>::value && C % 32 == 0 && RPT % 8 == 0 && RPV % 8 == 0;
     constexpr int PW = S::PW;
     __shared__ __align__(16) float smem[SPLIT ? S::SIZE_S : S::SIZE];
     __shared__ float sGref[NB + 1][DK];             // G at rows 16 I and at the last row
@@ -1616,7 +1627,8 @@ hipError_t launch3(const Args& a, hipStream_t s)
     KDA_BWD_CASE(CC, 16, 16) KDA_BWD_CASE(CC, 16, 32) KDA_BWD_CASE(CC, 16, 64) KDA_BWD_CASE(CC, 16, 128) \
     KDA_BWD_CASE(CC, 32, 16) KDA_BWD_CASE(CC, 32, 32) KDA_BWD_CASE(CC, 32, 64) KDA_BWD_CASE(CC, 32, 128) \
     KDA_BWD_CASE(CC, 64, 16) KDA_BWD_CASE(CC, 64, 32) KDA_BWD_CASE(CC, 64, 64) KDA_BWD_CASE(CC, 64, 128) \
-    KDA_BWD_CASE(CC, 128, 16) KDA_BWD_CASE(CC, 128, 32) KDA_BWD_CASE(CC, 128, 64) KDA_BWD_CASE(CC, 128, 128)
+    KDA_BWD_CASE(CC, 128, 16) KDA_BWD_CASE(CC, 128, 32) KDA_BWD_CASE(CC, 128, 64) KDA_BWD_CASE(CC, 128, 128) \
+    KDA_BWD_CASE(CC, 16, 256) KDA_BWD_CASE(CC, 32, 256) KDA_BWD_CASE(CC, 64, 256) KDA_BWD_CASE(CC, 128, 256)
 
 hipError_t launch_bwd_c16(const bwd::Args& a, int Dk, int Dv, kda_dtype dtype, hipStream_t s);
 hipError_t launch_bwd_c32(const bwd::Args& a, int Dk, int Dv, kda_dtype dtype, hipStream_t s);

@@ -104,6 +104,11 @@ size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int 
 
 size_t packed_chunk_slots(int N, int T, int chunk) { return varlen_gmax(N, T, chunk); }
 
+bool chunk_fwd_supported(int Dk, int Dv, int chunk, kda_dtype dtype)
+{
+    return records_bytes_any(chunk, 1, Dk, Dv, dtype) != 0;
+}
+
 hipError_t build_varlen_tables(const int* cu, int N, int T, int chunk, size_t gmax, void* ctab,
                                void* stab, hipStream_t s)
 {

@@ -1214,9 +1214,27 @@ int resident_blocks(K kernel, int threads)
 inline size_t varlen_gmax(int N, int Ttot, int C) { return (size_t)(Ttot + C - 1) / C + (size_t)N; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// LDS of chunk_prepare (its staging arrays, then the per-block gate terms,
+// norms, pair factors, flags and the diagonal blocks of A, as declared in the
+// kernel) against the 160 KiB of a compute unit: the shapes beyond it (float32
+// operands with chunk 64, d_k 128 and d_v 256) are not instantiated.
+template <int C, int DK, int DV, typename OT>
+constexpr bool chunk_shape_fits()
+{
+    using S = CS<C, DK, DV, OT>;
+    constexpr long other = C * 4 + 4L * S::NB * S::DKP * 4 + S::KSN * 2L * C * 4 + 2L * C * 4 +
+                           (S::NPAIR > 0 ? S::NPAIR : 1) * (long)S::DKP * 4 + (long)S::NB * S::DKP + 4 +
+                           S::NB * 16L * 20 * 4;
+    return S::BIG + other <= 160L * 1024;
+}
+
 template <int C, int DK, int DV, typename OT>
 hipError_t launch3(const ChunkArgs& a, hipStream_t s)
 {
+    if constexpr (!chunk_shape_fits<C, DK, DV, OT>()) {
+        (void)a; (void)s;
+        return hipErrorInvalidValue;
+    } else {
     const bool packed = a.cu != nullptr;
     int BH, NC, nitem;
     size_t nrec;
@@ -1264,15 +1282,25 @@ hipError_t launch3(const ChunkArgs& a, hipStream_t s)
         hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(512), 0, s,
                            a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
     return hipGetLastError();
+    }
 }
 
-// Bytes of the chunk records of nrec (chunk, head) items.
+// Bytes of the chunk records of nrec (chunk, head) items; 0 for a shape that
+// is not instantiated.
 template <int C, int DK, int DV, typename OT>
-size_t records_bytes(size_t nrec) { return WsLayout<C, DK, DV, OT>::bytes(nrec); }
+size_t records_bytes(size_t nrec)
+{
+    if constexpr (!chunk_shape_fits<C, DK, DV, OT>()) {
+        (void)nrec;
+        return 0;
+    } else {
+        return WsLayout<C, DK, DV, OT>::bytes(nrec);
+    }
+}
 
-// Every (Dk, Dv) the library supports, Dk and Dv in {16, 32, 64, 128}:
-// F(C, DK, DV) is expanded for each.
-#define KDA_FOR_DV(F, CC, DK) F(CC, DK, 16) F(CC, DK, 32) F(CC, DK, 64) F(CC, DK, 128)
+// Every (Dk, Dv) the library supports, Dk in {16, 32, 64, 128} and Dv in
+// {16, 32, 64, 128, 256}: F(C, DK, DV) is expanded for each.
+#define KDA_FOR_DV(F, CC, DK) F(CC, DK, 16) F(CC, DK, 32) F(CC, DK, 64) F(CC, DK, 128) F(CC, DK, 256)
 #define KDA_FOR_DKDV(F, CC) KDA_FOR_DV(F, CC, 16) KDA_FOR_DV(F, CC, 32) KDA_FOR_DV(F, CC, 64) KDA_FOR_DV(F, CC, 128)
 
 // One chunk length each (kda_chunk_c<C>.hip).

@@ -78,6 +78,10 @@ hipError_t launch_chunk(const ChunkArgs& a, hipStream_t s);
 // gmax chunk slots of (first token, length) and N sequences of (first token,
 // length, first slot, 0), from device offsets cu[N + 1].
 size_t packed_chunk_slots(int N, int T, int chunk);
+// Whether the chunk forward is built for this (Dk, Dv, chunk, dtype): every
+// supported pair except float32 operands with chunk 64, Dk 128 and Dv 256,
+// whose staging does not fit a compute unit's LDS.
+bool chunk_fwd_supported(int Dk, int Dv, int chunk, kda_dtype dtype);
 hipError_t build_varlen_tables(const int* cu, int N, int T, int chunk, size_t gmax, void* ctab,
                                void* stab, hipStream_t s);
 

@@ -29,7 +29,7 @@ namespace kda {
 
 template <int DK, int DV>
 struct RecShape {
-    static constexpr int DVT = DV;                  // columns per workgroup
+    static constexpr int DVT = DV > 128 ? 128 : DV; // columns per workgroup
     static constexpr int NCT = DV / DVT;            // workgroups per (b, h)
     static constexpr int NT = (DK * DVT / 4 < 512) ? DK * DVT / 4 : 512;  // threads
     static constexpr int CX = DVT / 4;       // threads across the slab (float4 each)
@@ -282,6 +282,7 @@ static hipError_t dispatch_dv(const RecArgs& a, hipStream_t s)
         case 32: return launch_rec<DK, 32, IO>(a, s);
         case 64: return launch_rec<DK, 64, IO>(a, s);
         case 128: return launch_rec<DK, 128, IO>(a, s);
+        case 256: return launch_rec<DK, 256, IO>(a, s);
     }
     return hipErrorInvalidValue;
 }

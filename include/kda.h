@@ -50,8 +50,12 @@
  *   aligned.  Inputs are not modified except where stated.
  * Shapes.  B, H >= 1, T >= 0 (T = 0 leaves every output untouched except
  *   that kda_chunk_fwd copies the initial state to the final state).
- *   1 <= Hqk <= H with H % Hqk == 0.  Dk, Dv in {16, 32, 64, 128}, in any
- *   combination; chunk in {16, 32, 64}; T need not be a multiple of chunk.
+ *   1 <= Hqk <= H with H % Hqk == 0.  Dk in {16, 32, 64, 128} and Dv in
+ *   {16, 32, 64, 128, 256}, in any combination; chunk in {16, 32, 64}; T
+ *   need not be a multiple of chunk.  One exception: the chunk forward
+ *   (kda_chunk_fwd, kda_chunk_fwd_varlen) with float32 operands, chunk 64,
+ *   Dk 128 and Dv 256 returns KDA_ERROR_NOT_SUPPORTED (its staging does not
+ *   fit a compute unit's LDS; chunk 32 serves that shape).
  * Values.  g must be finite (a hard forget is g = -30, say, not -inf).
  *   Keys are used as given unless KDA_NORMALIZE_QK is passed: the article
  *   assumes unit keys, but nothing else here normalises or checks them.

@@ -55,7 +55,7 @@ def _chunk(L, q=A, k=A, v=A, g=A, beta=A, h0=None, hT=None, o=A, B=1, T=64, H=1,
     (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(beta=None), 1),
     (dict(o=None), 1), (dict(state=None), 1), (dict(g=None, mode=0), 1),
     (dict(g=None, mode=1), 1), (dict(B=0), 1), (dict(H=0), 1), (dict(T=-1), 1),
-    (dict(mode=3), 1), (dict(dtype=2), 1), (dict(o_dtype=-1), 1), (dict(Dk=48), 2), (dict(Dv=256), 2),
+    (dict(mode=3), 1), (dict(dtype=2), 1), (dict(o_dtype=-1), 1), (dict(Dk=48), 2), (dict(Dv=512), 2), (dict(Dk=256), 2),
     (dict(H=4, Hqk=3), 1), (dict(H=2, Hqk=4), 1), (dict(Hqk=0), 1), (dict(pro=8), 1),
     (dict(pro=-1), 1),
     (dict(Dk=8), 2), (dict(q=MIS), 3), (dict(state=MIS), 3), (dict(g=MIS), 3),
@@ -68,13 +68,24 @@ def test_recurrent_validation(L, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(g=None, mode=0), 1), (dict(B=0), 1), (dict(mode=7), 1),
     (dict(o_dtype=5), 1),
-    (dict(chunk=48), 2), (dict(chunk=128), 2), (dict(Dk=256, Dv=256), 2), (dict(Dv=256), 2),
+    (dict(chunk=48), 2), (dict(chunk=128), 2), (dict(Dk=256, Dv=256), 2), (dict(Dv=512), 2),
+    (dict(Dv=256, dtype=0), 2),   # float32, chunk 64, d_k 128, d_v 256: staging exceeds the LDS
     (dict(H=6, Hqk=4), 1), (dict(pro=16), 1),
     (dict(q=MIS), 3), (dict(h0=MIS), 3), (dict(hT=MIS), 3), (dict(ws=None), 4),
     (dict(wsb=16), 4), (dict(ws=A + 16), 3),
 ])
 def test_chunk_validation(L, kw, code):
     assert _chunk(L, **kw) == code
+
+
+def test_value_dim_256_passes_validation(L):
+    # d_v = 256 with bf16 operands, and with float32 operands at chunk 32:
+    # only the workspace check remains to fail
+    assert _chunk(L, Dv=256, ws=None) == 4
+    assert _chunk(L, Dv=256, dtype=0, chunk=32, ws=None) == 4
+    assert _chunk(L, Dk=64, Dv=256, dtype=0, ws=None) == 4
+    assert _bwd(L, Dv=256, ws=None) == 4
+    assert _bwd(L, Dv=256, dtype=0, ws=None) == 4
 
 
 def test_none_mode_accepts_null_gate(L):
@@ -99,6 +110,11 @@ def test_workspace_size(L):
     # d_k != d_v is supported; the U record grows with d_v
     assert 0 < f(1, 64, 1, 64, 128, 64, 0, 1) and f(1, 64, 1, 128, 64, 64, 0, 1) > 0
     assert f(1, 64, 1, 64, 128, 64, 0, 1) > f(1, 64, 1, 64, 64, 64, 0, 1)
+    # d_v = 256; not built for float32 operands at chunk 64 with d_k 128
+    assert f(1, 64, 1, 128, 256, 64, 0, 1) > f(1, 64, 1, 128, 128, 64, 0, 1)
+    assert f(1, 64, 1, 128, 256, 64, 0, 0) == 0
+    assert f(1, 64, 1, 128, 256, 32, 0, 0) > 0
+    assert f(1, 64, 1, 128, 512, 64, 0, 1) == 0
 
 
 # ---- packed variable-length batches (host validation only)

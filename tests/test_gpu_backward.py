@@ -148,6 +148,19 @@ def test_bwd_bf16_chunks_and_dims(chunk, Dk, Dv):
     _compare(f"bf16 C{chunk} Dk{Dk} Dv{Dv}", _run(w, cot, chunk), _oracle(w, cot), 2e-3)
 
 
+@pytest.mark.parametrize("dtype,chunk,Dk", [("f32", 64, 128), ("f32", 32, 64), ("bf16", 64, 128),
+                                            ("bf16", 32, 16)])
+def test_bwd_value_dim_256(dtype, chunk, Dk):
+    """d_v = 256 (eight 32-column slices in the gradient kernel, sixteen
+    value tiles per head in the carries), ragged tail."""
+    w = make_inputs(1, 150, 2, Dk, 256, mode="channel", dtype=dtype, seed=256 + Dk + chunk,
+                    h0_std=0.05)
+    cot = make_cotangents(w, seed=4, dhT_std=0.1)
+    say("bwd d_v 256", dtype, chunk, Dk)
+    tol = TOL["f32"] if dtype == "f32" else 2e-3
+    _compare(f"{dtype} d_v 256 C{chunk} Dk{Dk}", _run(w, cot, chunk), _oracle(w, cot), tol)
+
+
 @pytest.mark.parametrize("Hqk,G", [(4, 1), (2, 2)])
 def test_bf16_gradients_are_the_rounded_float32_ones(Hqk, G):
     from kda_workloads import bf16_round

@@ -1,8 +1,8 @@
 """Parity of grouped value heads and d_k != d_v with the oracle (GPU).
 
 q and k have Hqk heads, v, g, beta, o and the state have H = G * Hqk value
-heads; value head h reads query/key head h // G.  d_k and d_v are any pair in
-{16, 32, 64, 128}.
+heads; value head h reads query/key head h // G.  d_k is any of {16, 32, 64,
+128} and d_v any of {16, 32, 64, 128, 256}.
 """
 import numpy as np
 import pytest
@@ -116,3 +116,66 @@ def test_full_size_prefill_grouped_or_mixed(Dk, Dv, Hqk):
     say("full size", Dk, Dv, Hqk)
     o, hT = _run(w, q, k, "chunk")
     _check(f"full size Dk{Dk} Dv{Dv} Hqk{Hqk}", w, q, k, o, hT, TOL["bf16"])
+
+
+@pytest.mark.parametrize("Dk,chunk", [(128, 32), (64, 64), (16, 16)])
+def test_value_dim_256_f32(Dk, chunk):
+    """d_v = 256 with float32 operands, both forms (the recurrent form as
+    two 128-column workgroups per head), ragged tail."""
+    w, q, k = _inputs(2, 2 * chunk + 7, 2, 1, Dk, 256, seed=Dk + chunk, h0_std=0.2)
+    say("d_v 256 f32", Dk, chunk)
+    for form in ("chunk", "recurrent"):
+        o, hT = _run(w, q, k, form, chunk=chunk)
+        _check(f"d_v 256 {form} Dk{Dk} C{chunk}", w, q, k, o, hT, TOL["f32"])
+
+
+def test_value_dim_256_f32_chunk64_dk128_not_supported():
+    """float32 operands with chunk 64, d_k 128 and d_v 256 are refused by the
+    chunk forward before anything is enqueued (chunk 32 serves the shape)."""
+    import torch
+    assert K.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 256, 64, K.GATE_CHANNEL, K.F32) == 0
+    w, q, k = _inputs(1, 64, 1, 1, 128, 256, seed=3)
+    dq, dk, dv, dg, db, dh0 = _dev(w, q, k)
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
+        K.kda_chunk_fwd(dq, dk, dv, dg, db, initial_state=dh0, chunk=64, scale=w.scale)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("form", ["chunk", "recurrent"])
+def test_value_dim_256_grouped_bf16(form):
+    w, q, k = _inputs(1, 300, 2, 2, 128, 256, dtype="bf16", seed=256, h0_std=0.05)
+    say("d_v 256 grouped bf16", form)
+    o, hT = _run(w, q, k, form)
+    _check(f"d_v 256 grouped bf16 {form}", w, q, k, o, hT, TOL["bf16"])
+
+
+def test_value_dim_256_decode_step():
+    """The decode step (one token per sequence) with d_v = 256, bf16."""
+    w, q, k = _inputs(8, 1, 4, 1, 128, 256, dtype="bf16", seed=11, h0_std=0.05)
+    say("d_v 256 decode")
+    o, hT = _run(w, q, k, "recurrent")
+    _check("d_v 256 decode bf16", w, q, k, o, hT, TOL["bf16"])
+
+
+def test_value_dim_256_packed():
+    """Packed batch with d_v = 256, both forms, bf16."""
+    import torch
+    lengths = make_lengths(7, max_len=150, seed=8, edge=(0, 1, 64, 65))
+    vw = make_varlen(lengths, 2, 128, 256, dtype="bf16", seed=8, h0_std=0.05)
+    w = vw.w
+    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(d)
+    dq, dk, dv = t(w.q[0], torch.bfloat16), t(w.k[0], torch.bfloat16), t(w.v[0], torch.bfloat16)
+    dg, db, dh0, cu = t(w.g[0]), t(w.beta[0]), t(vw.h0), torch.from_numpy(vw.cu).cuda()
+    say("d_v 256 packed", list(lengths))
+    o_c, h_c = K.kda_chunk_fwd_varlen(dq, dk, dv, dg, db, cu, initial_state=dh0, chunk=64,
+                                      scale=w.scale, out_dtype=torch.float32)
+    st = dh0.clone()
+    o_r = K.kda_recurrent_varlen(dq, dk, dv, dg, db, st, cu, scale=w.scale,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, h_ref = oracle.recurrent_varlen(w.q[0], w.k[0], w.v[0], w.g[0], w.beta[0], vw.cu,
+                                           vw.h0, scale=w.scale)
+    for tag, o, h in (("chunk", o_c, h_c), ("recurrent", o_r, st)):
+        eo, eh = rel_err(o.cpu().numpy(), o_ref), rel_err(h.cpu().numpy(), h_ref)
+        print(f"[parity] d_v 256 packed {tag} o {eo:.3e} state {eh:.3e}", flush=True)
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
