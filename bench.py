@@ -24,11 +24,12 @@ profiles/traffic.json and is null when the kernel source changed since.
 ``varlen`` (outside the timed steps) times the packed variable-length entry
 points (both forward forms and the gradient) on a serving mix: 64 sequences of log-uniform lengths 1..2048, H=16,
 d=128, bf16, in both forms.  ``grouped_heads`` (4 query/key heads for the 16
-value heads) and ``mixed_dims`` (d_k 64, d_v 128) time kda_chunk_fwd on the
-prefill shape B1 T4096 H16, likewise outside the timed steps.  ``backward``
-(also outside them) times kda_chunk_bwd, the gradients of the prefill
-call, on the prefill workload with seeded output gradients, against the
-float32 matrix-core peak (its products run on float32 operands).
+value heads), ``mixed_dims`` (d_k 64, d_v 128) and ``value_dim_256`` (d_k
+128, d_v 256) time kda_chunk_fwd on the prefill shape B1 T4096 H16, likewise
+outside the timed steps.  ``backward`` (also outside them) times
+kda_chunk_bwd, the gradients of the prefill call, on the prefill workload
+with seeded output gradients, against the float32 matrix-core peak (its
+products are computed to float32 accuracy).
 """
 from __future__ import annotations
 
@@ -132,7 +133,8 @@ def cpu_baseline():
     tv = time.perf_counter() - t0
     from kda_workloads import make_inputs
     rows = {}
-    for name, Hqk, Dk, Dv in (("grouped_heads", 4, 128, 128), ("mixed_dims", 16, 64, 128)):
+    for name, Hqk, Dk, Dv in (("grouped_heads", 4, 128, 128), ("mixed_dims", 16, 64, 128),
+                              ("value_dim_256", 16, 128, 256)):
         x = make_inputs(1, 4096, 16, Dk, Dv, dtype="bf16", seed=5, gate_shift=2.0, h0_std=0.01)
         G = 16 // Hqk
         t0 = time.perf_counter()
@@ -494,6 +496,8 @@ def main():
         out["varlen"] = bench_varlen(K, torch, dev, args.warmup, reps)
         out["grouped_heads"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=4, Dk=128, Dv=128)
         out["mixed_dims"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=16, Dk=64, Dv=128)
+        out["value_dim_256"] = bench_prefill_shape(K, torch, dev, args.warmup, reps, Hqk=16, Dk=128,
+                                                   Dv=256)
         out["prologue"] = bench_prologue(K, torch, dev, args.warmup, reps)
         out["backward"] = bench_backward(K, torch, dev, args.warmup, reps)
     if not args.no_cpu_baseline:
