@@ -806,7 +806,12 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     };
 
     // one chunk step with its early operands in `cur`
-    auto step = [&](const Pre& cur, int n) {
+    auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
+
+    // one chunk step with its early operands in `cur`; it requests the next
+    // step's into `nxt` right after its own update operands (loads complete
+    // in order, so the wait for the update operands does not cover them)
+    auto step = [&](const Pre& cur, Pre& nxt, int n) {
         const int ch = reverse ? NC - 1 - n : n;
         const size_t R = rbase + rstep * ch;
         // operands of the strip update, first used after the exchange
@@ -835,6 +840,8 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
                 }
             }
         }
+
+        load_pre(nxt, chunk_of(n + 1));
 
         // the state entering the chunk (forward) or the gradient leaving it (reverse)
         float* rec = recb + R * a.r.rs + (size_t)(v0 + r16) * DK + cbase;
@@ -899,19 +906,14 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
         }
         lds_barrier();
     };
-    auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
 
     // two sets of early operands in turn, so a prefetch is consumed a whole
     // step after it was issued and never copied
     Pre bufA, bufB;
     if (NC > 0) load_pre(bufA, chunk_of(0));
     for (int n = 0; n < NC; n += 2) {
-        load_pre(bufB, chunk_of(n + 1));
-        step(bufA, n);
-        if (n + 1 < NC) {
-            load_pre(bufA, chunk_of(n + 2));
-            step(bufB, n + 1);
-        }
+        step(bufA, bufB, n);
+        if (n + 1 < NC) step(bufB, bufA, n + 1);
     }
     if (reverse && a.dh0) {
 #pragma unroll
