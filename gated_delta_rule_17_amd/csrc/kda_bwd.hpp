@@ -782,7 +782,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
 
     // operands used at the start of a step: requested one step ahead, in two
     // sets that alternate (registers are scarce: the strip update's operands
-    // are requested at the start of their own step instead)
+    // are requested later, see load_A2 and step)
     struct Pre {
         float A1[NB][SQ];
         float add[NB][4];
@@ -808,14 +808,12 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     // one chunk step with its early operands in `cur`
     auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
 
-    // one chunk step with its early operands in `cur`; it requests the next
-    // step's into `nxt` right after its own update operands (loads complete
-    // in order, so the wait for the update operands does not cover them)
-    auto step = [&](const Pre& cur, Pre& nxt, int n) {
-        const int ch = reverse ? NC - 1 - n : n;
+    // the strip update's matrix operand (Kr^T or W^T rows of this wave's
+    // output tiles): requested at the end of the previous step, into the
+    // registers that step's update has just released
+    float A2[TPW][CQ];
+    auto load_A2 = [&](int ch) {
         const size_t R = rbase + rstep * ch;
-        // operands of the strip update, first used after the exchange
-        float A2[TPW][CQ], gam[SQ], Pv[SQ];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const float* p = A2b + R * a.r.rs + (size_t)(cw0 + 16 * t + r16) * C + 4 * q4;
@@ -825,6 +823,17 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
                 A2[t][s] = x[0]; A2[t][s + 1] = x[1]; A2[t][s + 2] = x[2]; A2[t][s + 3] = x[3];
             }
         }
+    };
+
+    // one chunk step with its early operands in `cur`; it requests the next
+    // step's into `nxt` right after its own small update operands, and the
+    // next update operand at its end (loads complete in order, so no wait for
+    // an operand covers a load issued after it)
+    auto step = [&](const Pre& cur, Pre& nxt, int n) {
+        const int ch = reverse ? NC - 1 - n : n;
+        const size_t R = rbase + rstep * ch;
+        // gates and P of the strip update, first used after the exchange
+        float gam[SQ], Pv[SQ];
         {
             const float* Gl = a.r.G + R * a.r.rs + (C - 1) * DK + cbase;
             const float* P = a.r.P + R * a.r.rs + (size_t)(v0 + r16) * DK + cbase;
@@ -904,13 +913,17 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
                 st[s] = reverse ? gm * st[s] + Pv[s] - acc[ii] : gm * st[s] + acc[ii];
             }
         }
+        load_A2(chunk_of(n + 1));
         lds_barrier();
     };
 
     // two sets of early operands in turn, so a prefetch is consumed a whole
     // step after it was issued and never copied
     Pre bufA, bufB;
-    if (NC > 0) load_pre(bufA, chunk_of(0));
+    if (NC > 0) {
+        load_pre(bufA, chunk_of(0));
+        load_A2(chunk_of(0));
+    }
     for (int n = 0; n < NC; n += 2) {
         step(bufA, bufB, n);
         if (n + 1 < NC) step(bufB, bufA, n + 1);
