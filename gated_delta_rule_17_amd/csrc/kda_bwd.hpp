@@ -366,14 +366,16 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     const int c = tid % DK, seg = tid / DK, r0 = seg * RPT;
     float kr[RPT], qr[RPT], Gr[RPT];
     {
+        // the gates first: loads complete in order, and the scan below needs
+        // only them
         const GatePtr gp = gate_ptr(a, b, t0, h, c, DK);
 #pragma unroll
+        for (int m = 0; m < RPT; ++m) Gr[m] = gp.base[clamp_row(r0 + m, L) * gp.stride] * gp.mul;
+#pragma unroll
         for (int m = 0; m < RPT; ++m) {
-            const int ic = clamp_row(r0 + m, L);
-            const size_t o = tok_qk(a, b, t0 + ic, hq) * DK + c;
+            const size_t o = tok_qk(a, b, t0 + clamp_row(r0 + m, L), hq) * DK + c;
             kr[m] = io<IO>::load(k + o);
             qr[m] = io<IO>::load(q + o);
-            Gr[m] = gp.base[ic * gp.stride] * gp.mul;
         }
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
