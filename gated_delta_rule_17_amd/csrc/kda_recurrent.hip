@@ -202,17 +202,31 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             token(tok0 * H + h);
         }
     } else {
-        for (int t = 0; t < Tn; ++t) {
+        // three tokens in flight: slot j holds the inputs of a token requested
+        // three token steps before it is committed (one step is shorter than a
+        // load's round trip).  The slots rotate statically, with no register
+        // copy of a load in flight; past the end the last token is requested
+        // again.  They are requested after the state's rows, so no wait for
+        // those rows counts them, and loads complete in order, so committing
+        // one slot does not wait for the two requested after it.
+        TokIn s0, s1, s2;
+        if (Tn > 0) {
+            fetch(tok0 + min(1, Tn - 1), s0);
+            fetch(tok0 + min(2, Tn - 1), s1);
+            fetch(tok0 + min(3, Tn - 1), s2);
+        }
+        auto step = [&](int t, TokIn& slot) {
             __syncthreads();   // token t's inputs are in LDS
-            // token t+1's inputs (the last token's once more at the end),
-            // requested unconditionally so that every wait for the state's
-            // rows in the first step counts them as younger loads
-            TokIn nxt;
-            fetch(tok0 + min(t + 1, Tn - 1), nxt);
             token((tok0 + t) * H + h);
             __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
-            commit(nxt);
-            bcur = nxt.b;
+            commit(slot);      // token t+1
+            bcur = slot.b;
+            fetch(tok0 + min(t + 4, Tn - 1), slot);
+        };
+        for (int t = 0; t < Tn; t += 3) {
+            step(t, s0);
+            if (t + 1 < Tn) step(t + 1, s1);
+            if (t + 2 < Tn) step(t + 2, s2);
         }
     }
 #pragma unroll
