@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 The C source is compiled with the host C compiler (``gcc -O2 -fopenmp``, no
 fast-math) into ``oracle/_build/libkda_oracle.so``.  ``build_oracle_library``
-is also what the package build step calls; building the checker is not using
+is also what the package build step calls: compiling the oracle is not running
 it.
 """
 from __future__ import annotations
