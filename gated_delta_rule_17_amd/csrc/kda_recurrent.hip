@@ -69,8 +69,12 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     const int cx = tid % S::CX, rg = tid / S::CX;
     const int lane = tid & 63, wave = tid >> 6;
 
-    __shared__ float sk[DK], sq[DK], sa[DK], sv[S::DVT];
-    __shared__ float red[S::NW > 1 ? S::NW : 1][S::CX][11];
+    // per key channel (alpha, k, scale * q, 0): one 16-byte read per row
+    __shared__ __align__(16) f32x4 akq[DK];
+    __shared__ float sv[S::DVT];
+    // per wavefront and column group the 11 partial sums, padded to 12 so
+    // that they move as three 16-byte accesses
+    __shared__ __align__(16) float red[S::NW > 1 ? S::NW : 1][S::CX][12];
 
     float* st = state + (size_t)bh * DK * DV + c0;
     // (value head h reads query/key head h / (H / HQ): grouped value heads)
@@ -99,13 +103,11 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     };
     auto commit = [&](const TokIn& x) {
         if (tid < DK) {
-            sk[tid] = io<IO>::load(&x.k);
-            sq[tid] = io<IO>::load(&x.q) * scale;
             // the retention alpha = exp(g), or sigmoid(a) from a pre-activation
             float a = 1.f;
             if (mode != KDA_GATE_NONE)
                 a = (pro & KDA_GATE_LOGSIGMOID) ? 1.f / (1.f + expf(-x.g)) : expf(x.g);
-            sa[tid] = a;
+            akq[tid] = (f32x4){a, io<IO>::load(&x.k), io<IO>::load(&x.q) * scale, 0.f};
         }
         if (tid < S::DVT) sv[tid] = io<IO>::load(&x.v);
     };
@@ -127,8 +129,8 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             float kq = 0.f, kk = 0.f, qq = 0.f;
     #pragma unroll
             for (int i = 0; i < S::RPT; ++i) {
-                const int r = rg + S::RG * i;
-                const float a = sa[r], kr = sk[r], qr = sq[r];
+                const f32x4 row = akq[rg + S::RG * i];
+                const float a = row[0], kr = row[1], qr = row[2];
                 hr[i] *= a;
                 ak += hr[i] * kr;
                 aq += hr[i] * qr;
@@ -150,28 +152,22 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             }
             if constexpr (S::NW > 1) {
                 if (lane < S::CX) {
-    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        red[wave][cx][u] = ak[u];
-                        red[wave][cx][4 + u] = aq[u];
-                    }
-                    red[wave][cx][8] = kq;
-                    red[wave][cx][9] = kk;
-                    red[wave][cx][10] = qq;
+                    f32x4* rp = reinterpret_cast<f32x4*>(&red[wave][cx][0]);
+                    rp[0] = ak;
+                    rp[1] = aq;
+                    rp[2] = (f32x4){kq, kk, qq, 0.f};
                 }
                 __syncthreads();
-                ak = zero4(); aq = zero4(); kq = 0.f; kk = 0.f; qq = 0.f;
+                ak = zero4(); aq = zero4();
+                f32x4 sc = zero4();
     #pragma unroll
                 for (int w = 0; w < S::NW; ++w) {
-    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        ak[u] += red[w][cx][u];
-                        aq[u] += red[w][cx][4 + u];
-                    }
-                    kq += red[w][cx][8];
-                    kk += red[w][cx][9];
-                    qq += red[w][cx][10];
+                    const f32x4* rp = reinterpret_cast<const f32x4*>(&red[w][cx][0]);
+                    ak += rp[0];
+                    aq += rp[1];
+                    sc += rp[2];
                 }
+                kq = sc[0]; kk = sc[1]; qq = sc[2];
             }
             // L2-normalised q and k: every product with them is linear, so the
             // norms are applied to the reduced sums (sq holds scale * q)
@@ -190,7 +186,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
             const f32x4 ek = e * fk;
     #pragma unroll
-            for (int i = 0; i < S::RPT; ++i) hr[i] += sk[rg + S::RG * i] * ek;
+            for (int i = 0; i < S::RPT; ++i) hr[i] += akq[rg + S::RG * i][1] * ek;
             if (rg == 0) {
                 Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
             }
@@ -218,7 +214,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         auto step = [&](int t, TokIn& slot) {
             __syncthreads();   // token t's inputs are in LDS
             token((tok0 + t) * H + h);
-            __syncthreads();   // sk/sq/sa/sv/red are rewritten by the next token
+            __syncthreads();   // akq/sv/red are rewritten by the next token
             commit(slot);      // token t+1
             bcur = slot.b;
             fetch(tok0 + min(t + 4, Tn - 1), slot);
@@ -265,8 +261,8 @@ static hipError_t launch_rec2(const RecArgs& a, hipStream_t s)
     using S = RecShape<DK, DV>;
     size_t dyn = 0;
     if constexpr (!MULTI) {
-        // the kernel's own LDS: sk, sq, sa, sv and the reduction array
-        const size_t static_bytes = (3 * DK + S::DVT) * 4 + (S::NW > 1 ? S::NW : 1) * S::CX * 11 * 4;
+        // the kernel's own LDS: akq, sv and the reduction array
+        const size_t static_bytes = (4 * DK + S::DVT) * 4 + (S::NW > 1 ? S::NW : 1) * S::CX * 12 * 4;
         dyn = decode_lds_reserve(static_bytes);
     }
     if (a.o_dtype == KDA_F32)
