@@ -27,6 +27,16 @@
 
 namespace kda {
 
+// x[l] + x[l ^ 32] in every lane l, on the vector unit: v_permlane32_swap
+// with x as both operands returns the lower half's values in the first
+// result and the upper half's in the second, in every lane (the same sums as
+// an xor-32 shuffle, without the LDS round trip)
+__device__ __forceinline__ float add_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int DK, int DV>
 struct RecShape {
     static constexpr int DVT = DV > 128 ? 128 : DV; // columns per workgroup
@@ -140,7 +150,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             }
             // reduce over the row groups held by this wavefront
     #pragma unroll
-            for (int off = S::CX; off < 64; off <<= 1) {
+            for (int off = S::CX; off < 32; off <<= 1) {
     #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     ak[u] += __shfl_xor(ak[u], off);
@@ -149,6 +159,16 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                 kq += __shfl_xor(kq, off);
                 kk += __shfl_xor(kk, off);
                 qq += __shfl_xor(qq, off);
+            }
+            if constexpr (S::CX < 64) {
+    #pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ak[u] = add_halves(ak[u]);
+                    aq[u] = add_halves(aq[u]);
+                }
+                kq = add_halves(kq);
+                kk = add_halves(kk);
+                qq = add_halves(qq);
             }
             if constexpr (S::NW > 1) {
                 if (lane < S::CX) {
