@@ -79,9 +79,11 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
     const int cx = tid % S::CX, rg = tid / S::CX;
     const int lane = tid & 63, wave = tid >> 6;
 
-    // per key channel (alpha, k, scale * q, 0): one 16-byte read per row
-    __shared__ __align__(16) f32x4 akq[DK];
-    __shared__ float sv[S::DVT];
+    // per key channel (alpha, k, scale * q, 0): one 16-byte read per row; two
+    // buffers, token t in buffer t & 1, so that token t+1's inputs are
+    // committed while token t's may still be read
+    __shared__ __align__(16) f32x4 akq[2][DK];
+    __shared__ float sv[2][S::DVT];
     // per wavefront and column group the 11 partial sums, padded to 12 so
     // that they move as three 16-byte accesses
     __shared__ __align__(16) float red[S::NW > 1 ? S::NW : 1][S::CX][12];
@@ -111,15 +113,15 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         x.v = v[tok * DV + c0 + cv];
         x.b = beta[tok];
     };
-    auto commit = [&](const TokIn& x) {
+    auto commit = [&](const TokIn& x, int buf) {
         if (tid < DK) {
             // the retention alpha = exp(g), or sigmoid(a) from a pre-activation
             float a = 1.f;
             if (mode != KDA_GATE_NONE)
                 a = (pro & KDA_GATE_LOGSIGMOID) ? 1.f / (1.f + expf(-x.g)) : expf(x.g);
-            akq[tid] = (f32x4){a, io<IO>::load(&x.k), io<IO>::load(&x.q) * scale, 0.f};
+            akq[buf][tid] = (f32x4){a, io<IO>::load(&x.k), io<IO>::load(&x.q) * scale, 0.f};
         }
-        if (tid < S::DVT) sv[tid] = io<IO>::load(&x.v);
+        if (tid < S::DVT) sv[buf][tid] = io<IO>::load(&x.v);
     };
     // the first token's inputs, requested before the state so that they arrive first
     TokIn cur;
@@ -130,16 +132,16 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         hr[i] = __builtin_nontemporal_load(
             reinterpret_cast<const f32x4*>(st + (size_t)(rg + S::RG * i) * DV + 4 * cx));
 
-    if (Tn > 0) commit(cur);
+    if (Tn > 0) commit(cur, 0);
     float bcur = cur.b;
     // one token: decay, the two reductions over the rows, correction, rank-1
     // write and read (inputs in LDS, beta in bcur)
-    auto token = [&](size_t tok) {
+    auto token = [&](size_t tok, int buf) {
             f32x4 ak = zero4(), aq = zero4();
             float kq = 0.f, kk = 0.f, qq = 0.f;
     #pragma unroll
             for (int i = 0; i < S::RPT; ++i) {
-                const f32x4 row = akq[rg + S::RG * i];
+                const f32x4 row = akq[buf][rg + S::RG * i];
                 const float a = row[0], kr = row[1], qr = row[2];
                 hr[i] *= a;
                 ak += hr[i] * kr;
@@ -203,10 +205,10 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             if (pro & KDA_BETA_SIGMOID) bt = 1.f / (1.f + expf(-bt));
             f32x4 e;
     #pragma unroll
-            for (int u = 0; u < 4; ++u) e[u] = bt * (sv[4 * cx + u] - ak[u]);
+            for (int u = 0; u < 4; ++u) e[u] = bt * (sv[buf][4 * cx + u] - ak[u]);
             const f32x4 ek = e * fk;
     #pragma unroll
-            for (int i = 0; i < S::RPT; ++i) hr[i] += akq[rg + S::RG * i][1] * ek;
+            for (int i = 0; i < S::RPT; ++i) hr[i] += akq[buf][rg + S::RG * i][1] * ek;
             if (rg == 0) {
                 Vec4<OUT>::store(o + tok * DV + c0 + 4 * cx, aq + e * kq);
             }
@@ -215,7 +217,7 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
         // a decode step: the state's rows are used as they arrive
         if (Tn == 1) {
             __syncthreads();
-            token(tok0 * H + h);
+            token(tok0 * H + h, 0);
         }
     } else {
         // three tokens in flight: slot j holds the inputs of a token requested
@@ -231,11 +233,14 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
             fetch(tok0 + min(2, Tn - 1), s1);
             fetch(tok0 + min(3, Tn - 1), s2);
         }
+        // One barrier per token besides the reduction's: token t+1's inputs
+        // go to the other buffer, whose last reader (token t-1) every thread
+        // has left at token t's reduction barrier, and the partial sums are
+        // rewritten only after the next token's first barrier.
         auto step = [&](int t, TokIn& slot) {
             __syncthreads();   // token t's inputs are in LDS
-            token((tok0 + t) * H + h);
-            __syncthreads();   // akq/sv/red are rewritten by the next token
-            commit(slot);      // token t+1
+            token((tok0 + t) * H + h, t & 1);
+            commit(slot, (t + 1) & 1);   // token t+1
             bcur = slot.b;
             fetch(tok0 + min(t + 4, Tn - 1), slot);
         };
@@ -281,8 +286,8 @@ static hipError_t launch_rec2(const RecArgs& a, hipStream_t s)
     using S = RecShape<DK, DV>;
     size_t dyn = 0;
     if constexpr (!MULTI) {
-        // the kernel's own LDS: akq, sv and the reduction array
-        const size_t static_bytes = (4 * DK + S::DVT) * 4 + (S::NW > 1 ? S::NW : 1) * S::CX * 12 * 4;
+        // the kernel's own LDS: akq and sv (two buffers each) and the reduction array
+        const size_t static_bytes = 2 * (4 * DK + S::DVT) * 4 + (S::NW > 1 ? S::NW : 1) * S::CX * 12 * 4;
         dyn = decode_lds_reserve(static_bytes);
     }
     if (a.o_dtype == KDA_F32)
