@@ -147,8 +147,14 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                 ak += hr[i] * kr;
                 aq += hr[i] * qr;
                 kq += kr * qr;
-                kk += kr * kr;
-                qq += qr * qr;
+            }
+            if (pro & KDA_NORMALIZE_QK) {   // the norms' partial sums
+    #pragma unroll
+                for (int i = 0; i < S::RPT; ++i) {
+                    const f32x4 row = akq[buf][rg + S::RG * i];
+                    kk += row[1] * row[1];
+                    qq += row[2] * row[2];
+                }
             }
             // reduce over the row groups held by this wavefront
     #pragma unroll
@@ -180,19 +186,26 @@ recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* _
                     rp[2] = (f32x4){kq, kk, qq, 0.f};
                 }
                 __syncthreads();
-                ak = zero4(); aq = zero4();
-                f32x4 sc = zero4();
+                // every thread needs the prediction sums (for e); only the
+                // threads that write o (row group 0) need the query sums and
+                // k.q, and k.k and q.q matter only for the normalisation
+                ak = zero4();
     #pragma unroll
-                for (int w = 0; w < S::NW; ++w) {
-                    const f32x4* rp = reinterpret_cast<const f32x4*>(&red[w][cx][0]);
-                    ak += rp[0];
-                    aq += rp[1];
-                    sc += rp[2];
+                for (int w = 0; w < S::NW; ++w) ak += reinterpret_cast<const f32x4*>(&red[w][cx][0])[0];
+                if (rg == 0 || (pro & KDA_NORMALIZE_QK)) {
+                    f32x4 sc = zero4();
+    #pragma unroll
+                    for (int w = 0; w < S::NW; ++w) sc += reinterpret_cast<const f32x4*>(&red[w][cx][0])[2];
+                    kq = sc[0]; kk = sc[1]; qq = sc[2];
                 }
-                kq = sc[0]; kk = sc[1]; qq = sc[2];
+                if (rg == 0) {
+                    aq = zero4();
+    #pragma unroll
+                    for (int w = 0; w < S::NW; ++w) aq += reinterpret_cast<const f32x4*>(&red[w][cx][0])[1];
+                }
             }
             // L2-normalised q and k: every product with them is linear, so the
-            // norms are applied to the reduced sums (sq holds scale * q)
+            // norms are applied to the reduced sums (akq holds scale * q)
             float fk = 1.f, fq = 1.f;
             if (pro & KDA_NORMALIZE_QK) {
                 fk = rsqrtf(kk + kNormEps);
