@@ -42,6 +42,20 @@ def test_shapes_f32(Dk, Dv):
     assert rel_err(o, o_r) <= 1e-4 and rel_err(hT, h_r) <= 1e-4
 
 
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 7, 300])
+def test_multi_token_lengths_f32(T):
+    """Multi-token sequences of every length modulo the three input slots
+    the kernel rotates (and one of 300 tokens): each token's inputs are
+    requested three token steps ahead, the last token's again past the end."""
+    w = make_inputs(2, T, 2, 64, 64, dtype="f32", seed=300 + T, h0_std=0.2)
+    say("recurrent f32 multi-token T", T)
+    o, hT = run_recurrent(w)
+    o_r, h_r = run_oracle(w)
+    eo, eh = rel_err(o, o_r), rel_err(hT, h_r)
+    print(f"[parity] recurrent multi-token T{T} o {eo:.3e} state {eh:.3e}", flush=True)
+    assert eo <= 1e-4 and eh <= 1e-4, (eo, eh)
+
+
 def test_multi_token_bf16():
     w = make_inputs(2, 37, 3, 128, 128, dtype="bf16", seed=11, gate_shift=-2.0, h0_std=0.05)
     say("recurrent bf16 T=37")
