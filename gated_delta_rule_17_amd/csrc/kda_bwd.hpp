@@ -787,7 +787,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     // are requested later, see load_A2 and step)
     struct Pre {
         float A1[NB][SQ];
-        float add[NB][4];
+        float add[(NB + NWS - 1) / NWS][4];   // U or Ut of blocks w, w + NWS, ...
     };
     auto load_pre = [&](Pre& o, int ch) {
         const size_t R = rbase + rstep * ch;
@@ -799,11 +799,15 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
                 const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * s);
                 o.A1[I][s] = x[0]; o.A1[I][s + 1] = x[1]; o.A1[I][s + 2] = x[2]; o.A1[I][s + 3] = x[3];
             }
-            if (w == 0) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(ADb + R * a.r.rs + (size_t)(v0 + r16) * C + 16 * I + 4 * q4);
+        }
+        // the term added to the partial sums of block I is added by wave
+        // I % NWS, so each wave holds a quarter of it (with four waves)
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) o.add[I][ii] = x[ii];
-            }
+        for (int j = 0; j < (NB + NWS - 1) / NWS; ++j) {
+            const int I = min(w + j * NWS, NB - 1);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(ADb + R * a.r.rs + (size_t)(v0 + r16) * C + 16 * I + 4 * q4);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) o.add[j][ii] = x[ii];
         }
     };
 
@@ -871,7 +875,7 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
             for (int ii = 0; ii < 4; ++ii) {
                 // forward: E = U - sum_w (W H)_w ; reverse: dE = Ut + sum_w (Kr dH)_w
                 const float x = reverse ? acc[ii] : -acc[ii];
-                part[ii] = w == 0 ? cur.add[I][ii] + x : x;
+                part[ii] = I % NWS == w ? cur.add[I / NWS][ii] + x : x;
             }
             *reinterpret_cast<f32x4*>(&sPart[w][r16][16 * I + 4 * q4]) = part;
         }
