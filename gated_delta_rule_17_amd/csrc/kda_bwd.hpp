@@ -16,14 +16,16 @@
 //
 // Four launches:
 //   1. bwd_prep   one workgroup per (sequence, head, chunk): G, A (before the
-//                 beta scaling), Aqk, T, W, U, Kr and Q e^G into per-chunk
-//                 float32 records.
+//                 beta scaling), T, W and W^T, U, Kr and Kr^T, and the two
+//                 products with dO that the reverse carry would otherwise
+//                 repeat each step, Ut = Aqk^T dO and P = (scale Q e^G)^T dO,
+//                 into per-chunk float32 records.
 //   2. bwd_states one launch, two roles: workgroups of the first half carry
 //                 the state forward through the chunks (storing the state
 //                 entering each chunk and E), those of the second half carry
 //                 the state gradient backward,
-//                   dE = Aqk^T dO + Kr dH' ;
-//                   dH = Diag(e^{G_last}) dH' + (scale Q e^G)^T dO - W^T dE,
+//                   dE = Ut + Kr dH' ;
+//                   dH = Diag(e^{G_last}) dH' + P - W^T dE,
 //                 storing dH' and dE per chunk.  Each workgroup owns one
 //                 16-column tile of the value dimension of one head.
 //   3. bwd_grad   one workgroup per chunk, one wave per 16 key channels:
