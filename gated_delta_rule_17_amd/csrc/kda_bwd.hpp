@@ -1078,6 +1078,12 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         static_assert(4 * DK == NT, "one state element pair per thread");
         const int hcq = 4 * (tid >> 6) + (tid & 3), hp = (tid >> 2) & 15;
         float gpart[4] = {0.f, 0.f, 0.f, 0.f};     // sum_n H dH of channels 4 hcq + z
+        // sum_n dUt v of chunk rows, spread over all threads: element e is
+        // (row e / 8, columns 4 (e % 8) .. + 3 of the slice)
+        constexpr int NZ = (8 * C + NT - 1) / NT;
+        float zpart[NZ];
+#pragma unroll
+        for (int j = 0; j < NZ; ++j) zpart[j] = 0.f;
         struct SliceS {
             f32x4 h0, h1, d0, d1, e0[NEJ], e1[NEJ], de[NE];
             float o0[NOJ], o1[NOJ], v0[NOJ], v1[NOJ];
@@ -1196,15 +1202,23 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
                 }
             }
             lds_barrier();
-            if (tid < C) {
-                for (int p = 0; p < VS / 2; ++p) {
-                    const uint32_t uh = pU[tid * SW + p], um = pU[PC + tid * SW + p],
-                                   ul = pU[2 * PC + tid * SW + p];
-                    const float u0 = __uint_as_float(uh << 16) + __uint_as_float(um << 16) +
-                                     __uint_as_float(ul << 16);
-                    const float u1 = __uint_as_float(uh & 0xffff0000u) + __uint_as_float(um & 0xffff0000u) +
-                                     __uint_as_float(ul & 0xffff0000u);
-                    zacc += u0 * sVh[tid * LV + 2 * p] + u1 * sVh[tid * LV + 2 * p + 1];
+#pragma unroll
+            for (int j = 0; j < NZ; ++j) {
+                const int e = tid + j * NT;
+                if (e < 8 * C) {
+                    const int i = e >> 3, p0 = 2 * (e & 7);
+                    float z = 0.f;
+#pragma unroll
+                    for (int p = p0; p < p0 + 2; ++p) {
+                        const uint32_t uh = pU[i * SW + p], um = pU[PC + i * SW + p],
+                                       ul = pU[2 * PC + i * SW + p];
+                        const float u0 = __uint_as_float(uh << 16) + __uint_as_float(um << 16) +
+                                         __uint_as_float(ul << 16);
+                        const float u1 = __uint_as_float(uh & 0xffff0000u) +
+                                         __uint_as_float(um & 0xffff0000u) + __uint_as_float(ul & 0xffff0000u);
+                        z += u0 * sVh[i * LV + 2 * p] + u1 * sVh[i * LV + 2 * p + 1];
+                    }
+                    zpart[j] += z;
                 }
             }
             // products with the state and its gradient for this wave's 16 channels
@@ -1255,14 +1269,32 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             t += __shfl_xor(t, 32);
             gpart[z] = t;
         }
-        // handed to the channel's own thread through LDS after the loop
+        // the row sums of dUt v: the eight threads of a row are consecutive lanes
+#pragma unroll
+        for (int j = 0; j < NZ; ++j) {
+            float t = zpart[j];
+            t += __shfl_xor(t, 1);
+            t += __shfl_xor(t, 2);
+            t += __shfl_xor(t, 4);
+            zpart[j] = t;
+        }
+        // both handed to the channel's (row's) own thread through LDS after
+        // the loop (sDb is rewritten with the whole dbeta term further on)
         lds_barrier();
         if (hp == 0) {
 #pragma unroll
             for (int z = 0; z < 4; ++z) sDgam[4 * hcq + z] = gpart[z];
         }
+        if ((tid & 7) == 0) {
+#pragma unroll
+            for (int j = 0; j < NZ; ++j) {
+                const int e = tid + j * NT;
+                if (e < 8 * C) sDb[e >> 3] = zpart[j];
+            }
+        }
         lds_barrier();
         if (tid < DK) gacc = sDgam[tid];
+        if (tid < C) zacc = sDb[tid];
     } else {
         // One value slice of the records and inputs, requested into registers
         // while the previous slice is being used and written to LDS at the start
