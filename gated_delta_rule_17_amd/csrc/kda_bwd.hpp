@@ -452,10 +452,13 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
         for (int job = w; job < 2 * (I + 1); job += NW) {
             const int which = job & 1, J = job >> 1;
             const float* A = which ? sAq : sAk;
-            f32x4 acc = zero4();
-#pragma unroll 8
-            for (int kk = 0; kk < DK; kk += 4)
+            f32x4 acc = zero4(), acc2 = zero4();   // two independent chains
+#pragma unroll 4
+            for (int kk = 0; kk < DK; kk += 8) {
                 acc = mma4(A[r16 * LK + kk + q4], sS[(16 * J + r16) * LS + kk + q4], acc);
+                acc2 = mma4(A[r16 * LK + kk + 4 + q4], sS[(16 * J + r16) * LS + kk + 4 + q4], acc2);
+            }
+            acc += acc2;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * I + 4 * q4 + ii, j = 16 * J + r16;
@@ -1186,9 +1189,13 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             // dUt = T^T dE (upper triangular: rows i take j >= 16 I), dv = beta dUt
             for (int job = w; job < NB * (VS / 16); job += NW) {
                 const int I = job / (VS / 16), Vt = job % (VS / 16);
-                f32x4 acc = zero4();
-                for (int kk = 16 * I; kk < C; kk += 4)
+                f32x4 acc = zero4(), acc2 = zero4();   // two independent chains
+                for (int kk = 16 * I; kk < C; kk += 8) {
                     acc = mma4(sT[(kk + q4) * LT + 16 * I + r16], sdEh[(16 * Vt + r16) * LDE + kk + q4], acc);
+                    acc2 = mma4(sT[(kk + 4 + q4) * LT + 16 * I + r16],
+                                sdEh[(16 * Vt + r16) * LDE + kk + 4 + q4], acc2);
+                }
+                acc += acc2;
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) {
                     const int i = 16 * I + 4 * q4 + ii, n = 16 * Vt + r16;
