@@ -189,6 +189,25 @@ def test_bwd_strong_gates_within_range():
     _compare("f32 strong gates", _run(w, cot, 64), _oracle(w, cot), TOL["f32"])
 
 
+def test_bwd_training_shape_sampled():
+    """The training shape at full size (B8 H32 T8192 d128, chunk 64, bf16, mixed
+    fast and slow channels): 32768 chunk records, a ~13 GB workspace whose
+    float offsets pass 2^31.  The gradient oracle runs on two (b, h)
+    sequences, stacked as a batch of two."""
+    w = make_config("train_b8_h32_t8192")
+    cot = make_cotangents(w, seed=0, dhT_std=0.01)
+    say("bwd train_b8_h32_t8192")
+    got = _run(w, cot, 64)
+    pairs = [(0, 0), (7, 31)]
+    tok = lambda x: None if x is None else np.stack([x[b, :, h] for b, h in pairs])[:, :, None]
+    st = lambda x: None if x is None else np.stack([x[b, h] for b, h in pairs])[:, None]
+    ref = oracle.recurrent_bwd(tok(w.q), tok(w.k), tok(w.v), tok(w.g), tok(w.beta), st(w.h0),
+                               tok(cot.do), st(cot.dhT), scale=w.scale, mode=w.mode)
+    sub = {n: None if got[n] is None else (st(got[n]) if n == "dh0" else tok(got[n]))
+           for n in NAMES}
+    _compare("training shape (b, h) = (0, 0), (7, 31)", sub, ref, TOL["bf16"])
+
+
 def test_bwd_full_size_prefill_sampled_heads():
     """The prefill workload at full size (B1 H16 T4096 d128, bf16), in the
     launch configuration the benchmark times; the oracle runs on three of
