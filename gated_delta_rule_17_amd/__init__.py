@@ -34,7 +34,9 @@ import re
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkda.so")
+# KDA_LIBRARY: load another build of the same library (e.g. one whose host
+# code carries sanitizers); by default the in-tree libkda.so
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(HERE, "libkda.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kda.h")
 
 GATE_CHANNEL, GATE_SCALAR, GATE_NONE = 0, 1, 2
@@ -124,17 +126,64 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _check_dev(name, t, dtype=None, shape=None):
+def _check_meta(name, t, dtype=None, shape=None):
+    """dtype and shape of an argument (no device access)."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_dev(name, t, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    _check_meta(name, t, dtype, shape)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gate_shape(m, lead, H, Dk):
+    """The shape the kernels index g with: lead + (H, Dk) per channel,
+    lead + (H,) per token and head, no tensor in the ungated mode."""
+    if m == GATE_CHANNEL:
+        return tuple(lead) + (H, Dk)
+    if m == GATE_SCALAR:
+        return tuple(lead) + (H,)
+    if m == GATE_NONE:
+        return None
+    raise ValueError(f"unknown gate mode {m}")
+
+
+def _check_gate(g, m, lead, H, Dk):
+    """g must match its mode: the kernels index it as [.., H, Dk] (channel)
+    or [.., H] (scalar), so any other shape would be read out of bounds."""
+    shape = _gate_shape(m, lead, H, Dk)
+    if shape is None:
+        if g is not None:
+            raise ValueError("g must be None in the ungated mode")
+        return
+    if g is None:
+        raise ValueError("g is required in the channel and scalar gate modes")
+    _check_meta("g", g, None, shape)
+
+
+def _check_workspace(ws, need, device):
+    """A caller-supplied workspace: a contiguous uint8 tensor on the device
+    of the other arguments, with at least `need` bytes (its numel() is the
+    byte count passed on)."""
+    torch = _torch()
+    _check_meta("workspace", ws, torch.uint8)
+    if ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} are needed")
+    _check_dev("workspace", ws, torch.uint8, None, device)
 
 
 def _mode_of(g, mode):
@@ -145,6 +194,39 @@ def _mode_of(g, mode):
     if isinstance(mode, str):
         return _MODE_NAMES[mode]
     return int(mode)
+
+
+def _common(q, k, v, g, beta, mode, packed, extra=()):
+    """Metadata checks shared by every compute entry (before any device
+    access): q, k [*lead, Hqk, Dk], v [*lead, H, Dv] of one dtype, g matching
+    the gate mode, beta [*lead, H] float32, where lead is (B, T) for a dense
+    batch and (T,) for a packed one.  `extra` are further (name, tensor)
+    pairs of the dtype of q with v's shape.  Returns (lead, Hqk, Dk, H, Dv,
+    mode code)."""
+    torch = _torch()
+    nd = 3 if packed else 4
+    if q.dim() != nd:
+        raise ValueError(f"q must have {nd} dimensions, got shape {tuple(q.shape)}")
+    lead, Hqk, Dk = tuple(q.shape[:-2]), q.shape[-2], q.shape[-1]
+    _dtype_code(q)
+    _check_meta("k", k, q.dtype, q.shape)
+    _check_meta("v", v, q.dtype)
+    if v.dim() != nd or tuple(v.shape[:-2]) != lead:
+        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
+    H, Dv = v.shape[-2], v.shape[-1]
+    for name, t in extra:
+        _check_meta(name, t, q.dtype, v.shape)
+    m = _mode_of_packed(g, mode) if packed else _mode_of(g, mode)
+    _check_meta("g", g, torch.float32)
+    _check_gate(g, m, lead, H, Dk)
+    _check_meta("beta", beta, torch.float32, lead + (H,))
+    return lead, Hqk, Dk, H, Dv, m
+
+
+def _on_device(dev, *named):
+    """Device, placement and contiguity of every (name, tensor) pair."""
+    for name, t in named:
+        _check_dev(name, t, None, None, dev)
 
 
 def _stream():
@@ -162,20 +244,15 @@ def kda_recurrent_step(q, k, v, g, beta, state, o=None, scale: Optional[float] =
     ``o`` is given).
     """
     torch = _torch()
-    B, T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
-    m = _mode_of(g, mode)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (B, T, H))
-    _check_dev("state", state, torch.float32, (B, H, Dk, Dv))
+    (B, T), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=False)
+    _check_meta("state", state, torch.float32, (B, H, Dk, Dv))
+    if state is None:
+        raise ValueError("state is required")
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
-    _check_dev("o", o, None, (B, T, H, Dv))
+    _check_meta("o", o, None, (B, T, H, Dv))
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("state", state), ("o", o))
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
@@ -203,27 +280,21 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
     Shapes as for :func:`kda_recurrent_step`.
     """
     torch = _torch()
-    B, T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
-    m = _mode_of(g, mode)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (B, T, H))
-    _check_dev("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
+    (B, T), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=False)
+    _check_meta("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
     if final_state is None and output_final_state:
         final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    _check_dev("final_state", final_state, torch.float32, (B, H, Dk, Dv))
+    _check_meta("final_state", final_state, torch.float32, (B, H, Dk, Dv))
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
-    _check_dev("o", o, None, (B, T, H, Dv))
+    _check_meta("o", o, None, (B, T, H, Dv))
     dt = _dtype_code(q)
     need = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, m, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("initial_state", initial_state), ("final_state", final_state), ("o", o))
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
@@ -249,7 +320,9 @@ def _mode_of_packed(g, mode):
 
 def _check_cu(cu_seqlens):
     torch = _torch()
-    _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+    if cu_seqlens is None:
+        raise ValueError("cu_seqlens is required")
+    _check_meta("cu_seqlens", cu_seqlens, torch.int32)
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
     return cu_seqlens.numel() - 1
@@ -265,21 +338,16 @@ def kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None,
     [N+1] on the device.  Returns o [T,H,Dv].
     """
     torch = _torch()
-    T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
+    (T,), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=True)
     N = _check_cu(cu_seqlens)
-    m = _mode_of_packed(g, mode)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (T, H))
-    _check_dev("state", state, torch.float32, (N, H, Dk, Dv))
+    _check_meta("state", state, torch.float32, (N, H, Dk, Dv))
+    if state is None:
+        raise ValueError("state is required")
     if o is None:
         o = torch.empty((T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
-    _check_dev("o", o, None, (T, H, Dv))
+    _check_meta("o", o, None, (T, H, Dv))
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("state", state), ("o", o), ("cu_seqlens", cu_seqlens))
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_recurrent_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
@@ -307,28 +375,23 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
     are [N,H,Dk,Dv] float32 (final_state may be initial_state itself).
     """
     torch = _torch()
-    T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
+    (T,), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=True)
     N = _check_cu(cu_seqlens)
-    m = _mode_of_packed(g, mode)
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (T, H))
-    _check_dev("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
+    _check_meta("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
-    _check_dev("final_state", final_state, torch.float32, (N, H, Dk, Dv))
+    _check_meta("final_state", final_state, torch.float32, (N, H, Dk, Dv))
     if o is None:
         o = torch.empty((T, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
-    _check_dev("o", o, None, (T, H, Dv))
+    _check_meta("o", o, None, (T, H, Dv))
     dt = _dtype_code(q)
     need = kda_chunk_fwd_varlen_workspace_size(N, T, H, Dk, Dv, chunk, m, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("initial_state", initial_state), ("final_state", final_state), ("o", o),
+               ("cu_seqlens", cu_seqlens))
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -343,6 +406,43 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None, final
 
 # ---------------------------------------------------------------------------
 # gradients of the chunkwise form
+_GRAD_KEYS = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
+
+
+def _grad_outputs(out, q, k, v, g, beta, m, grad_dtype, want_d_initial_state, state_shape):
+    """The gradient outputs: those given in `out` are checked (their dtype
+    sets the storage type of dq, dk, dv), the others allocated.  dg takes the
+    shape of g, which the gate check has already tied to the gate mode."""
+    torch = _torch()
+    out = dict(out or {})
+    dev = q.device
+    if out.get("dq") is not None:
+        grad_dtype = out["dq"].dtype
+    gdt = grad_dtype or q.dtype
+    if gdt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"gradients must be float32 or bfloat16, got {gdt}")
+    for name, ref in (("dq", q), ("dk", k), ("dv", v)):
+        if out.get(name) is None:
+            out[name] = torch.empty(ref.shape, dtype=gdt, device=dev)
+    if m == GATE_NONE:
+        out["dg"] = None
+    elif out.get("dg") is None:
+        out["dg"] = torch.empty(g.shape, dtype=torch.float32, device=dev)
+    if out.get("dbeta") is None:
+        out["dbeta"] = torch.empty(beta.shape, dtype=torch.float32, device=dev)
+    if not want_d_initial_state:
+        out["d_initial_state"] = None
+    elif out.get("d_initial_state") is None:
+        out["d_initial_state"] = torch.empty(state_shape, dtype=torch.float32, device=dev)
+    _check_meta("dq", out["dq"], gdt, q.shape)
+    _check_meta("dk", out["dk"], gdt, k.shape)
+    _check_meta("dv", out["dv"], gdt, v.shape)
+    _check_meta("dg", out["dg"], torch.float32, None if g is None else g.shape)
+    _check_meta("dbeta", out["dbeta"], torch.float32, beta.shape)
+    _check_meta("d_initial_state", out["d_initial_state"], torch.float32, state_shape)
+    return out
+
+
 def kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, mode, dtype) -> int:
     if isinstance(mode, str):
         mode = _MODE_NAMES[mode]
@@ -364,50 +464,20 @@ def kda_chunk_bwd(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
     dtype then sets the gradient storage type).
     """
     torch = _torch()
-    B, T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
-    m = _mode_of(g, mode)
-    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if tuple(v.shape[:-2]) != tuple(q.shape[:-2]):
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("d_o", d_o, q.dtype, v.shape)
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (B, T, H))
-    _check_dev("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
-    _check_dev("d_final_state", d_final_state, torch.float32, (B, H, Dk, Dv))
-    out = dict(out or {})
-    dev = q.device
-    if out.get("dq") is not None:
-        grad_dtype = out["dq"].dtype
-    gdt = grad_dtype or q.dtype
-    if out.get("dq") is None:
-        out["dq"] = torch.empty(q.shape, dtype=gdt, device=dev)
-    if out.get("dk") is None:
-        out["dk"] = torch.empty(k.shape, dtype=gdt, device=dev)
-    if out.get("dv") is None:
-        out["dv"] = torch.empty(v.shape, dtype=gdt, device=dev)
-    if m == GATE_NONE:
-        out["dg"] = None
-    elif out.get("dg") is None:
-        out["dg"] = torch.empty_like(g)
-    if out.get("dbeta") is None:
-        out["dbeta"] = torch.empty_like(beta)
-    if want_d_initial_state and out.get("d_initial_state") is None:
-        out["d_initial_state"] = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
-    if not want_d_initial_state:
-        out["d_initial_state"] = None
-    _check_dev("dq", out["dq"], gdt, q.shape)
-    _check_dev("dk", out["dk"], gdt, q.shape)
-    _check_dev("dv", out["dv"], gdt, v.shape)
-    _check_dev("dg", out["dg"], torch.float32, None if g is None else g.shape)
-    _check_dev("dbeta", out["dbeta"], torch.float32, (B, T, H))
-    _check_dev("d_initial_state", out["d_initial_state"], torch.float32, (B, H, Dk, Dv))
+    (B, T), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=False,
+                                         extra=(("d_o", d_o),))
+    _check_meta("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
+    _check_meta("d_final_state", d_final_state, torch.float32, (B, H, Dk, Dv))
+    out = _grad_outputs(out, q, k, v, g, beta, m, grad_dtype, want_d_initial_state,
+                        (B, H, Dk, Dv))
     dt = _dtype_code(q)
     need = kda_chunk_bwd_workspace_size(B, T, H, Hqk, Dk, Dv, chunk, m, dt)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o),
+               ("initial_state", initial_state), ("d_final_state", d_final_state),
+               *[(n, out[n]) for n in _GRAD_KEYS])
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
@@ -440,49 +510,21 @@ def kda_chunk_bwd_varlen(q, k, v, g, beta, d_o, cu_seqlens, initial_state=None,
     :func:`kda_chunk_bwd` (d_initial_state [N, H, Dk, Dv]).
     """
     torch = _torch()
-    T, Hqk, Dk = q.shape
-    H, Dv = v.shape[-2], v.shape[-1]
-    m = _mode_of_packed(g, mode)
-    _check_cu(cu_seqlens)
-    N = cu_seqlens.numel() - 1
-    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
-        _check_dev(name, t, q.dtype)
-    _check_dev("k", k, q.dtype, q.shape)
-    if v.shape[0] != T:
-        raise ValueError(f"v has shape {tuple(v.shape)}, inconsistent with q {tuple(q.shape)}")
-    _check_dev("d_o", d_o, q.dtype, v.shape)
-    _check_dev("g", g, torch.float32)
-    _check_dev("beta", beta, torch.float32, (T, H))
-    _check_dev("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
-    _check_dev("d_final_state", d_final_state, torch.float32, (N, H, Dk, Dv))
-    out = dict(out or {})
-    dev = q.device
-    if out.get("dq") is not None:
-        grad_dtype = out["dq"].dtype
-    gdt = grad_dtype or q.dtype
-    for name, ref in (("dq", q), ("dk", k), ("dv", v)):
-        if out.get(name) is None:
-            out[name] = torch.empty(ref.shape, dtype=gdt, device=dev)
-    if m == GATE_NONE:
-        out["dg"] = None
-    elif out.get("dg") is None:
-        out["dg"] = torch.empty_like(g)
-    if out.get("dbeta") is None:
-        out["dbeta"] = torch.empty_like(beta)
-    if want_d_initial_state and out.get("d_initial_state") is None:
-        out["d_initial_state"] = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
-    if not want_d_initial_state:
-        out["d_initial_state"] = None
-    _check_dev("dq", out["dq"], gdt, q.shape)
-    _check_dev("dk", out["dk"], gdt, q.shape)
-    _check_dev("dv", out["dv"], gdt, v.shape)
-    _check_dev("dg", out["dg"], torch.float32, None if g is None else g.shape)
-    _check_dev("dbeta", out["dbeta"], torch.float32, (T, H))
-    _check_dev("d_initial_state", out["d_initial_state"], torch.float32, (N, H, Dk, Dv))
+    (T,), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=True,
+                                      extra=(("d_o", d_o),))
+    N = _check_cu(cu_seqlens)
+    _check_meta("initial_state", initial_state, torch.float32, (N, H, Dk, Dv))
+    _check_meta("d_final_state", d_final_state, torch.float32, (N, H, Dk, Dv))
+    out = _grad_outputs(out, q, k, v, g, beta, m, grad_dtype, want_d_initial_state,
+                        (N, H, Dk, Dv))
     dt = _dtype_code(q)
     need = kda_chunk_bwd_varlen_workspace_size(N, T, H, Hqk, Dk, Dv, chunk, m, dt)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("d_o", d_o),
+               ("initial_state", initial_state), ("d_final_state", d_final_state),
+               ("cu_seqlens", cu_seqlens), *[(n, out[n]) for n in _GRAD_KEYS])
     if scale is None:
         scale = Dk ** -0.5
     st = lib().kda_chunk_bwd_varlen(
