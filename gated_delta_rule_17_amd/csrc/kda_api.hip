@@ -2,10 +2,26 @@
 // Every check runs on the host before any HIP call, so a bad argument returns
 // a status and enqueues nothing.
 #include <stdint.h>
+#include <string.h>
 
 #include "kda_internal.hpp"
 
 namespace {
+
+// A C caller may pass any int where an enum is declared.  In C++, reading an
+// enum object whose value lies outside the range its enumerators span is
+// undefined, so every enum argument is first read as its raw integer and
+// validated; only valid values are used as enums afterwards.
+template <typename E>
+int raw(const E& e)
+{
+    static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof v);
+    return v;
+}
+bool valid_mode(int m) { return m == KDA_GATE_CHANNEL || m == KDA_GATE_SCALAR || m == KDA_GATE_NONE; }
+bool valid_dtype(int d) { return d == KDA_F32 || d == KDA_BF16; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool supported_dk(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -14,14 +30,12 @@ bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 
 kda_status check_common(const void* q, const void* k, const void* v, const float* g,
                         const float* beta, const void* o, int B, int T, int H, int Hqk, int Dk,
-                        int Dv, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype)
+                        int Dv, int mode, int dtype, int o_dtype)
 {
     if (B < 1 || H < 1 || T < 0) return KDA_ERROR_INVALID_VALUE;
     if (Hqk < 1 || Hqk > H || H % Hqk != 0) return KDA_ERROR_INVALID_VALUE;
-    if (mode != KDA_GATE_CHANNEL && mode != KDA_GATE_SCALAR && mode != KDA_GATE_NONE)
+    if (!valid_mode(mode) || !valid_dtype(dtype) || !valid_dtype(o_dtype))
         return KDA_ERROR_INVALID_VALUE;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
-    if (o_dtype != KDA_F32 && o_dtype != KDA_BF16) return KDA_ERROR_INVALID_VALUE;
     if (!supported_dk(Dk) || !supported_dv(Dv)) return KDA_ERROR_NOT_SUPPORTED;
     // sizes must fit the 64-bit index arithmetic of the kernels comfortably
     const double tok = (double)B * (double)T * (double)H;
@@ -43,7 +57,7 @@ extern "C" {
 
 const char* kda_status_string(kda_status s)
 {
-    switch (s) {
+    switch (raw(s)) {
         case KDA_SUCCESS: return "KDA_SUCCESS";
         case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
         case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
@@ -62,7 +76,8 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
                               kda_dtype dtype, kda_dtype o_dtype, int prologue, void* stream)
 {
     if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(o_dtype));
     if (st != KDA_SUCCESS) return st;
     if (T == 0) return KDA_SUCCESS;
     if (!state) return KDA_ERROR_INVALID_VALUE;
@@ -79,7 +94,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, int chu
     (void)mode;
     if (B < 1 || H < 1 || T <= 0) return 0;
     if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (!valid_dtype(raw(dtype))) return 0;
     return kda::chunk_workspace_bytes(B, T, H, Dk, Dv, chunk, dtype);
 }
 
@@ -90,7 +105,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int prologue, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(o_dtype));
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk) || !kda::chunk_fwd_supported(Dk, Dv, chunk, dtype))
         return KDA_ERROR_NOT_SUPPORTED;
@@ -119,7 +135,8 @@ kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, con
                                 int prologue, void* stream)
 {
     if (N < 0 || (prologue & ~KDA_PROLOGUE_ALL)) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(o_dtype));
     if (st != KDA_SUCCESS) return st;
     if ((double)N * H > 2.0e9) return KDA_ERROR_INVALID_VALUE;
     if (N == 0 || T == 0) return KDA_SUCCESS;   // every sequence is empty: states unchanged
@@ -137,7 +154,7 @@ size_t kda_chunk_fwd_varlen_workspace_size(int N, int T, int H, int Dk, int Dv, 
     (void)mode;
     if (N < 1 || H < 1 || T < 0) return 0;
     if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (!valid_dtype(raw(dtype))) return 0;
     return kda::chunk_varlen_workspace_bytes(N, T, H, Dk, Dv, chunk, dtype);
 }
 
@@ -149,7 +166,8 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream)
 {
     if (N < 0 || (prologue & ~KDA_PROLOGUE_ALL)) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, mode, dtype, o_dtype);
+    kda_status st = check_common(q, k, v, g, beta, o, 1, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(o_dtype));
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk) || !kda::chunk_fwd_supported(Dk, Dv, chunk, dtype))
         return KDA_ERROR_NOT_SUPPORTED;
@@ -179,7 +197,7 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv
     if (B < 1 || H < 1 || T <= 0) return 0;
     if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
     if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (!valid_dtype(raw(dtype))) return 0;
     return kda::chunk_bwd_workspace_bytes(B, T, H, Hqk, Dk, Dv, chunk);
 }
 
@@ -191,7 +209,8 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
                          kda_dtype dtype, kda_dtype grad_dtype, void* workspace,
                          size_t workspace_bytes, void* stream)
 {
-    kda_status st = check_common(q, k, v, g, beta, d_o, B, T, H, Hqk, Dk, Dv, mode, dtype, grad_dtype);
+    kda_status st = check_common(q, k, v, g, beta, d_o, B, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(grad_dtype));
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
     const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
@@ -227,7 +246,7 @@ size_t kda_chunk_bwd_varlen_workspace_size(int N, int T, int H, int Hqk, int Dk,
     if (N < 1 || H < 1 || T < 0) return 0;
     if (Hqk < 1 || Hqk > H || H % Hqk != 0) return 0;
     if (!supported_dk(Dk) || !supported_dv(Dv) || !supported_chunk(chunk)) return 0;
-    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+    if (!valid_dtype(raw(dtype))) return 0;
     return kda::chunk_bwd_varlen_workspace_bytes(N, T, H, Hqk, Dk, Dv, chunk);
 }
 
@@ -241,7 +260,8 @@ kda_status kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
                                 size_t workspace_bytes, void* stream)
 {
     if (N < 0) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, d_o, 1, T, H, Hqk, Dk, Dv, mode, dtype, grad_dtype);
+    kda_status st = check_common(q, k, v, g, beta, d_o, 1, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(grad_dtype));
     if (st != KDA_SUCCESS) return st;
     if (!supported_chunk(chunk)) return KDA_ERROR_NOT_SUPPORTED;
     const double gmax = (double)((T + chunk - 1) / chunk) + (double)N;

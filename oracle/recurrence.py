@@ -52,7 +52,13 @@ def _load(mutant: int = 0):
     lib = _libs.get(mutant)
     if lib is not None:
         return lib
-    path = build_oracle_library(mutant=mutant, force=False)
+    # KDA_ORACLE_LIBRARY: an already built oracle library to load instead
+    # (the sanitizer test builds one with host ASan/UBSan)
+    override = os.environ.get("KDA_ORACLE_LIBRARY")
+    if override and mutant == 0:
+        path = override
+    else:
+        path = build_oracle_library(mutant=mutant, force=False)
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     lib.kda_oracle_recurrent.argtypes = [dp] * 8 + [ctypes.c_long] * 5 + \
