@@ -716,43 +716,69 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
         __syncthreads();
 
         if (fallback) {
-            // exact diagonal-block terms for key channels whose decay across the block
-            // exceeds kRangeMax (their factorised key side was zeroed above)
-            for (int p = tid; p < NB * DK; p += S::NT) {
-                const int I = p / DK, cc = p % DK;
-                if (!flag[I][cc]) continue;
-                float gi[16], ki[16], qi[16];
-                float run = 0.f;
-                for (int u = 0; u < 16; ++u) {
-                    const int i = 16 * I + u;
-                    float gv = 0.f, kv = 0.f, qv = 0.f;
-                    if (i < L) {
-                        const size_t tok = (loc.tok0 + i) * H + h;
-                        const size_t tkq = (loc.tok0 + i) * HQ + h / GH;
-                        if (mode == KDA_GATE_CHANNEL) gv = g[tok * DK + cc];
-                        else if (mode == KDA_GATE_SCALAR) gv = g[tok];
-                        if (PRO && mode != KDA_GATE_NONE && (pro & KDA_GATE_LOGSIGMOID)) gv = log_sigmoid(gv);
-                        kv = io<OT>::load(k + tkq * DK + cc);
-                        qv = io<OT>::load(q + tkq * DK + cc) * scale;
-                        if (PRO && (pro & KDA_NORMALIZE_QK)) {
-                            kv *= inrm[0][i];
-                            qv *= inrm[1][i];
+            // Exact diagonal-block terms for the key channels whose decay across a
+            // block exceeds kRangeMax (their factorised key side was zeroed above).
+            // Wave (Ib, ksl) owns block Ib and the 32 channels of slice ksl and
+            // walks its flagged channels in ascending order.  For each, every lane
+            // (r, gq) reloads token 16 Ib + r of that channel (the four lane groups
+            // hold the same values), the block-local log2 prefix of the gate is a
+            // row scan, and lane (r, gq) sums the terms of the entries
+            // (i = 16 Ib + r, j = 16 Ib + 4 gq + u):
+            //   Aqk_ij += q_i k_j 2^(G_i - G_j),   A_ij += beta_i k_i k_j 2^(G_i - G_j),
+            // every factor <= 1.  The next channel's values are requested before
+            // the current one is summed.  The slices then add their sums to the
+            // block one after another, so the result does not depend on wave timing.
+            uint32_t fmask = 0;
+#pragma unroll
+            for (int c = 0; c < 32; ++c)
+                if (32 * ksl + c < DK && flag[Ib][32 * ksl + c]) fmask |= 1u << c;
+            float pq[4] = {0.f, 0.f, 0.f, 0.f}, pa[4] = {0.f, 0.f, 0.f, 0.f};
+            if (fmask) {   // uniform over the wave
+                const size_t row = loc.tok0 + (tv ? it : 0);
+                const float* grow = mode == KDA_GATE_CHANNEL ? g + (row * H + h) * DK + 32 * ksl
+                                                             : g + row * H + h;
+                const OT* krow = k + (row * HQ + h / GH) * DK + 32 * ksl;
+                const OT* qrow = q + (row * HQ + h / GH) * DK + 32 * ksl;
+                const int gstep = mode == KDA_GATE_CHANNEL ? 1 : 0;
+                const float fk = (PRO && (pro & KDA_NORMALIZE_QK)) ? inrm[0][it] : 1.f;
+                const float fq = (PRO && (pro & KDA_NORMALIZE_QK)) ? inrm[1][it] : 1.f;
+                const float bi = sb[it];
+                uint32_t m = fmask;
+                int cn = __builtin_ctz(m);
+                float gn = grow[gstep * cn], kn = io<OT>::load(krow + cn), qn = io<OT>::load(qrow + cn);
+                while (m) {
+                    m &= m - 1;
+                    float gv = gn;
+                    const float kv = tv ? kn * fk : 0.f, qv = tv ? qn * scale * fq : 0.f;
+                    cn = m ? __builtin_ctz(m) : cn;            // uniform
+                    gn = grow[gstep * cn];
+                    kn = io<OT>::load(krow + cn);
+                    qn = io<OT>::load(qrow + cn);
+                    if (PRO && (pro & KDA_GATE_LOGSIGMOID)) gv = log_sigmoid(gv);
+                    const float G = row_scan16(tv ? gv * kLog2e : 0.f);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int jj = 4 * gq + u;
+                        const float Gj = __shfl(G, 16 * gq + jj), kj = __shfl(kv, 16 * gq + jj);
+                        if (jj <= r) {
+                            const float w = exp2_fast(G - Gj) * kj;
+                            pq[u] += qv * w;
+                            if (jj < r) pa[u] += bi * kv * w;
                         }
-                    }
-                    run += gv;
-                    gi[u] = run; ki[u] = kv; qi[u] = qv;
-                }
-                for (int ii = 0; ii < 16; ++ii) {
-                    const int i = 16 * I + ii;
-                    for (int jj = 0; jj <= ii; ++jj) {
-                        const int j = 16 * I + jj;
-                        const float w = __expf(gi[ii] - gi[jj]) * ki[jj];
-                        atomicAdd(&Aq32[i * SA + j], qi[ii] * w);
-                        if (jj < ii) atomicAdd(&ad(I, ii, jj), sb[i] * ki[ii] * w);
                     }
                 }
             }
-            __syncthreads();
+            for (int sl = 0; sl < KSN; ++sl) {
+                if (ksl == sl && fmask) {
+                    const int i = 16 * Ib + r, j0 = 16 * Ib + 4 * gq;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        Aq32[i * SA + j0 + u] += pq[u];
+                        ad(Ib, r, 4 * gq + u) += pa[u];
+                    }
+                }
+                __syncthreads();
+            }
             for (int p = tid; p < C * C; p += S::NT) {
                 const int i = p / C, j = p % C;
                 store_p(Waq, fragidx(i, j, CP / 32), Aq32[i * SA + j]);

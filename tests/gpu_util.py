@@ -68,3 +68,43 @@ def run_oracle(w, pairs=None):
 def pick(o_full, hT_full, pairs):
     return (np.stack([o_full[b, :, h] for b, h in pairs]),
             np.stack([hT_full[b, h] for b, h in pairs]))
+
+
+def per_head_errors(w, o, hT, batches=None):
+    """Oracle R one batch entry at a time (host memory stays bounded at the
+    largest workloads), compared with the kernels' o [B,T,H,Dv] and
+    hT [B,H,Dk,Dv] on every head of those entries.
+
+    Returns (whole, worst, table): ``whole`` = (o, state) errors over all
+    compared heads together (the max|d|/rms measure over the whole run);
+    ``worst`` = the largest per-head (o, state) errors, each with its (b, h);
+    ``table`` = {(b, h): (o error, state error)}, each against that head's
+    own rms."""
+    from tests.conftest import rel_err
+    batches = range(w.B) if batches is None else batches
+    table = {}
+    num_o = num_h = 0.0
+    ss_o = ss_h = 0.0
+    n_o = n_h = 0
+    for b in batches:
+        sl = lambda x: None if x is None else np.ascontiguousarray(x[b:b + 1])
+        o_r, h_r = oracle.recurrent(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), sl(w.h0),
+                                    scale=w.scale, mode=w.mode)
+        for h in range(w.H):
+            og, orf = o[b, :, h], o_r[0, :, h]
+            hg, hrf = hT[b, h], h_r[0, h]
+            table[(b, h)] = (rel_err(og, orf), rel_err(hg, hrf))
+            num_o = max(num_o, float(np.abs(og.astype(np.float64) - orf).max()) if og.size else 0.0)
+            num_h = max(num_h, float(np.abs(hg.astype(np.float64) - hrf).max()))
+            ss_o += float(np.sum(orf * orf))
+            ss_h += float(np.sum(hrf * hrf))
+            n_o += orf.size
+            n_h += hrf.size
+        del o_r, h_r
+    rms_o = np.sqrt(ss_o / max(n_o, 1))
+    rms_h = np.sqrt(ss_h / max(n_h, 1))
+    whole = (num_o / rms_o if rms_o > 0 else num_o, num_h / rms_h if rms_h > 0 else num_h)
+    wo = max(table.items(), key=lambda kv: kv[1][0])
+    wh = max(table.items(), key=lambda kv: kv[1][1])
+    worst = ((wo[1][0], wo[0]), (wh[1][1], wh[0]))
+    return whole, worst, table

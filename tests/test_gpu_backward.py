@@ -189,23 +189,37 @@ def test_bwd_strong_gates_within_range():
     _compare("f32 strong gates", _run(w, cot, 64), _oracle(w, cot), TOL["f32"])
 
 
-def test_bwd_training_shape_sampled():
+def test_bwd_training_shape_two_batch_entries():
     """The training shape at full size (B8 H32 T8192 d128, chunk 64, bf16, mixed
-    fast and slow channels): 32768 chunk records, a ~13 GB workspace whose
-    float offsets pass 2^31.  The gradient oracle runs on two (b, h)
-    sequences, stacked as a batch of two."""
+    fast and slow channels): 32768 chunk records, a workspace whose float
+    offsets pass 2^31.  The gradient oracle runs on every head of batch
+    entries 0 and 7 (64 sequences, at both ends of the workspace); the
+    measure is taken over those 64 sequences, and the worst single sequence
+    is reported and held to the same bound."""
     w = make_config("train_b8_h32_t8192")
     cot = make_cotangents(w, seed=0, dhT_std=0.01)
     say("bwd train_b8_h32_t8192")
     got = _run(w, cot, 64)
-    pairs = [(0, 0), (7, 31)]
-    tok = lambda x: None if x is None else np.stack([x[b, :, h] for b, h in pairs])[:, :, None]
-    st = lambda x: None if x is None else np.stack([x[b, h] for b, h in pairs])[:, None]
-    ref = oracle.recurrent_bwd(tok(w.q), tok(w.k), tok(w.v), tok(w.g), tok(w.beta), st(w.h0),
-                               tok(cot.do), st(cot.dhT), scale=w.scale, mode=w.mode)
-    sub = {n: None if got[n] is None else (st(got[n]) if n == "dh0" else tok(got[n]))
-           for n in NAMES}
-    _compare("training shape (b, h) = (0, 0), (7, 31)", sub, ref, TOL["bf16"])
+    bs = [0, 7]
+    sl = lambda x: None if x is None else np.ascontiguousarray(x[bs])
+    ref = oracle.recurrent_bwd(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), sl(w.h0),
+                               sl(cot.do), sl(cot.dhT), scale=w.scale, mode=w.mode)
+    sub = {n: None if got[n] is None else sl(got[n]) for n in NAMES}
+    _compare("training shape, b in {0, 7}, all 32 heads", sub, ref, TOL["bf16"])
+    worst = {}
+    for n in NAMES:
+        if ref[n] is None:
+            continue
+        for i, b in enumerate(bs):
+            for h in range(w.H):
+                x, y = (sub[n][i, h], ref[n][i, h]) if n == "dh0" else \
+                    (sub[n][i, :, h], ref[n][i, :, h])
+                e = rel_err(x, y)
+                if e > worst.get(n, (0.0, None))[0]:
+                    worst[n] = (e, (b, h))
+    print("[parity] bwd training shape worst sequence: " +
+          " ".join(f"{n} {e:.2e}@{bh}" for n, (e, bh) in worst.items()), flush=True)
+    assert all(e <= TOL["bf16"] for e, _ in worst.values()), worst
 
 
 def test_bwd_full_size_prefill_sampled_heads():

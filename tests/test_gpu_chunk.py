@@ -4,7 +4,8 @@ import pytest
 
 from kda_workloads import make_config, make_inputs
 from tests.conftest import rel_err
-from tests.gpu_util import TOL, pick, run_chunk, run_oracle, run_recurrent, say, to_device
+from tests.gpu_util import (TOL, per_head_errors, pick, run_chunk, run_oracle, run_recurrent,
+                             say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -54,25 +55,40 @@ def test_prefill_full_size(name):
     w = make_config(name)
     say(name)
     o, hT = run_chunk(w)
-    _check(w, o, hT, TOL["bf16"])
+    _check_every_head(w, o, hT, TOL["bf16"])
 
 
-def test_training_shape_sampled():
+def _check_every_head(w, o, hT, tol):
+    """Every (b, h) of a large workload against oracle R: the whole-run
+    measure and the worst single head (each against its own rms) must both
+    stay within the bound."""
+    assert np.isfinite(o).all() and np.isfinite(hT).all()
+    whole, worst, table = per_head_errors(w, o, hT)
+    (wo, bo), (wh, bh) = worst
+    print(f"[parity] {w.name} all {len(table)} heads: whole o {whole[0]:.3e} state "
+          f"{whole[1]:.3e}; worst head o {wo:.3e} at (b,h)={bo}, state {wh:.3e} at {bh}",
+          flush=True)
+    assert whole[0] <= tol and whole[1] <= tol, (w.name, whole)
+    assert wo <= tol and wh <= tol, (w.name, worst)
+
+
+def test_training_shape_every_head():
     """B8 H32 T8192 d128 chunk 64 with mixed fast/slow channels, run at full
-    size; oracle on a fixed sample of (b, h) sequences."""
+    size in one call; every one of the 256 (b, h) sequences is compared with
+    oracle R (run one batch entry at a time)."""
     w = make_config("train_b8_h32_t8192")
     say("train_b8_h32_t8192")
     o, hT = run_chunk(w)
-    _check(w, o, hT, TOL["bf16"], pairs=[(0, 0), (3, 17), (7, 31)])
+    _check_every_head(w, o, hT, TOL["bf16"])
 
 
 @pytest.mark.parametrize("name", ["long_t65536_channel", "long_t65536_scalar", "long_t65536_none"])
-def test_long_prefill_sampled(name):
-    """T = 65536 (1024 chunk steps), three gate modes; oracle on two heads."""
+def test_long_prefill_every_head(name):
+    """T = 65536 (1024 chunk steps), three gate modes; all 8 heads compared."""
     w = make_config(name)
     say(name)
     o, hT = run_chunk(w)
-    _check(w, o, hT, TOL["bf16"], pairs=[(0, 0), (0, 5)])
+    _check_every_head(w, o, hT, TOL["bf16"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -87,8 +103,29 @@ def test_hard_forget_and_adversarial_gates(dtype):
     w.g[0, 70, 1, :] = -95.0
     w.g[0, 100:128] = 0.0
     say("chunk hard forget", dtype)
-    o, hT = run_chunk(w, chunk=64)
+    d = to_device(w)
+    o, hT = run_chunk(w, chunk=64, d=d)
     _check(w, o, hT, TOL[dtype])
+    # the exact diagonal-block terms are summed in a fixed order: a second
+    # call gives the same bits
+    o2, hT2 = run_chunk(w, chunk=64, d=d)
+    assert np.array_equal(o, o2) and np.array_equal(hT, hT2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hard_forget_scalar_gates_every_block(dtype):
+    """Scalar gates (one decay for every channel): three hard-forget tokens
+    inside every 16-token block put all channels of every block on the exact
+    path at once; results match the oracle and repeat bit for bit."""
+    w = make_inputs(1, 160, 2, 128, 128, mode="scalar", dtype=dtype, seed=31, h0_std=0.2)
+    for b0 in range(0, 160, 16):
+        w.g[0, b0 + 4:b0 + 7] = -30.0
+    say("chunk hard forget scalar", dtype)
+    d = to_device(w)
+    o, hT = run_chunk(w, chunk=64, d=d)
+    _check(w, o, hT, TOL[dtype])
+    o2, hT2 = run_chunk(w, chunk=64, d=d)
+    assert np.array_equal(o, o2) and np.array_equal(hT, hT2)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
