@@ -29,7 +29,10 @@ value heads), ``mixed_dims`` (d_k 64, d_v 128) and ``value_dim_256`` (d_k
 outside the timed steps.  ``backward`` (also outside them) times
 kda_chunk_bwd, the gradients of the prefill call, on the prefill workload
 with seeded output gradients, against the float32 matrix-core peak (its
-products are computed to float32 accuracy).
+products are computed to float32 accuracy).  The large workloads -- the
+training shape B8 H32 T8192 and T = 65536 at H8 in the three gate modes --
+are timed last, each as a whole kda_chunk_fwd call (outside the timed steps),
+with the oracle's rate on a bounded sample of each beside them.
 """
 from __future__ import annotations
 
@@ -253,6 +256,89 @@ def bench_prefill_shape(K, torch, dev, warmup, reps, *, Hqk, Dk, Dv, H=16, T=409
             "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS}
 
 
+def config_bytes(w):
+    """Algorithmic HBM bytes of one kda_chunk_fwd call on workload w with a
+    bf16 output: q, k, v, o (bf16), the gates (float32: Dk per token-head in
+    channel mode, one in scalar mode, none in the ungated mode), beta, the
+    initial state when there is one and the final state."""
+    gate = {"channel": 4 * w.Dk, "scalar": 4, "none": 0}[w.mode]
+    per = (2 * w.Dk + w.Dv) * 2 + w.Dv * 2 + gate + 4
+    states = (2 if w.h0 is not None else 1) * w.Dk * w.Dv * 4
+    return w.B * w.H * (w.T * per + states)
+
+
+def bench_config(K, torch, dev, name, warmup, reps):
+    """kda_chunk_fwd on one named workload at full size (bf16 in and out,
+    float32 gates, beta and states), HIP events on the launch stream; the
+    whole call is timed (both kernels)."""
+    from kda_workloads import make_config
+    w = make_config(name)
+    t = lambda x, d=torch.float32: None if x is None else \
+        torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    bf = torch.bfloat16
+    q, k, v, g, beta, h0 = t(w.q, bf), t(w.k, bf), t(w.v, bf), t(w.g), t(w.beta), t(w.h0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, 64, w.mode, K.BF16),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((w.B, w.T, w.H, w.Dv), dtype=bf, device=dev)
+    hT = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device=dev)
+
+    def run():
+        K.kda_chunk_fwd(q, k, v, g, beta, initial_state=h0, final_state=hT, o=o, chunk=64,
+                        mode=w.mode, workspace=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    sec = a.elapsed_time(b) / reps / 1e3
+    nbytes = config_bytes(w)
+    flops = prefill_flops(w.B, w.H, w.T, w.Dk, 64)
+    res = {"workload": f"{name}: B{w.B} H{w.H} T{w.T} d_k {w.Dk} d_v {w.Dv}, chunk 64, "
+                       f"{w.mode} gates, bf16 q/k/v/o, fp32 gates/beta/states",
+           "ms": sec * 1e3, "tokens_per_s": w.B * w.T / sec,
+           "token_heads_per_s": w.B * w.T * w.H / sec,
+           "algorithmic_bytes": nbytes, "hbm_GBps": nbytes / sec / 1e9,
+           "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
+           "mfma_frac_algorithmic": flops / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+           "serial_chunk_steps": (w.T + 63) // 64}
+    del q, k, v, g, beta, h0, ws, o, hT
+    torch.cuda.empty_cache()
+    return res
+
+
+LARGE_LEGS = ("train_b8_h32_t8192", "long_t65536_channel", "long_t65536_scalar",
+              "long_t65536_none")
+
+
+def cpu_large_sample():
+    """The oracle's rate on bounded samples of the large workloads: batch
+    entry 0 of the training shape (32 heads x 8192 tokens), and head 0 of
+    each T = 65536 mode."""
+    import oracle
+    from kda_workloads import make_config
+    rows = {}
+    for name in LARGE_LEGS:
+        w = make_config(name)
+        if name.startswith("train"):
+            sl = lambda x: None if x is None else np.ascontiguousarray(x[:1])
+            what = "batch entry 0 (32 heads x 8192 tokens)"
+        else:
+            sl = lambda x: None if x is None else np.ascontiguousarray(x[:, :, :1])
+            what = "head 0 (65536 tokens)"
+        q, k, v, g, beta = sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta)
+        t0 = time.perf_counter()
+        oracle.recurrent(q, k, v, g, beta, None, scale=w.scale, mode=w.mode)
+        dt = time.perf_counter() - t0
+        th = q.shape[0] * q.shape[1] * q.shape[2]
+        rows[name] = {"token_heads_per_s": th / dt, "sample": what, "seconds": dt}
+        del w, q, k, v, g, beta
+    return rows
+
+
 def bench_backward(K, torch, dev, warmup, reps):
     """kda_chunk_bwd on the prefill workload (B1 H16 T4096 d128, chunk 64,
     bf16 q/k/v and output gradient, bf16 input gradients), HIP events on the
@@ -351,6 +437,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a float32 copy of exactly 256 MiB (reads 256 MiB, writes "
                          "256 MiB) three times, as the reference for HBM byte counters")
+    ap.add_argument("--only", choices=LARGE_LEGS,
+                    help="run only kda_chunk_fwd on this named workload (5 timed calls after 2 "
+                         "warm-ups) and print its JSON object: profiling runs of one workload")
     ap.add_argument("--backward-only", action="store_true",
                     help="run only the gradient leg (kda_chunk_bwd on the prefill workload) "
                          "and print its JSON object: profiling runs of the gradient kernels")
@@ -364,6 +453,9 @@ def main():
     import gated_delta_rule_17_amd as K
     from kda_workloads import make_config
     dev = torch.device("cuda:0")
+    if args.only:
+        print(json.dumps({args.only: bench_config(K, torch, dev, args.only, 2, 5)}), flush=True)
+        return
     if args.backward_only:
         if args.calibrate_copy:
             src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
@@ -500,8 +592,12 @@ def main():
                                                    Dv=256)
         out["prologue"] = bench_prologue(K, torch, dev, args.warmup, reps)
         out["backward"] = bench_backward(K, torch, dev, args.warmup, reps)
+        for name in LARGE_LEGS:
+            out[name] = bench_config(K, torch, dev, name, 2, 5)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+        if not args.no_extra_legs:
+            out["cpu_baseline"]["large_workloads"] = cpu_large_sample()
     print(json.dumps(out), flush=True)
 
 
