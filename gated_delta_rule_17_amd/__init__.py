@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None,
                 o=None, chunk=64, scale=None, mode=None, workspace=None)
   kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype)
+  kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, final_state, o,
+                        chunk=64, scale=None, mode=None)
   kda_recurrent_varlen(q, k, v, g, beta, state, cu_seqlens, o=None, scale=None, mode=None)
   kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, initial_state=None,
                        final_state=None, o=None, chunk=64, scale=None, mode=None,
@@ -45,7 +47,11 @@ NORMALIZE_QK, BETA_SIGMOID, GATE_LOGSIGMOID = 1, 2, 4
 F32, BF16 = 0, 1
 _MODE_NAMES = {"channel": GATE_CHANNEL, "scalar": GATE_SCALAR, "none": GATE_NONE}
 STATUS = {0: "KDA_SUCCESS", 1: "KDA_ERROR_INVALID_VALUE", 2: "KDA_ERROR_NOT_SUPPORTED",
-          3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_WORKSPACE", 5: "KDA_ERROR_HIP"}
+          3: "KDA_ERROR_MISALIGNED", 4: "KDA_ERROR_WORKSPACE", 5: "KDA_ERROR_HIP",
+          6: "KDA_ERROR_SCRATCH"}
+# bytes of the fixed device scratch array behind kda_chunk_fwd_noalloc
+# (KDA_NOALLOC_SCRATCH_BYTES in kda.h)
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 
 
 class KDAError(RuntimeError):
@@ -74,6 +80,9 @@ def lib():
     L.kda_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, i, f, i, i, i, i,
                                 vp, sz, vp]
     L.kda_chunk_fwd.restype = i
+    L.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, vp, i, i, i, i, i, i, i, f, i,
+                                        i, i, i, vp]
+    L.kda_chunk_fwd_noalloc.restype = i
     L.kda_recurrent_varlen.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, i, i, i, i, i, i, f, i, i, i,
                                        i, vp]
     L.kda_recurrent_varlen.restype = i
@@ -303,6 +312,34 @@ def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, final_state=None, o=None
                              _stream())
     if st != 0:
         raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, initial_state, final_state, o, chunk: int = 64,
+                          scale: Optional[float] = None, mode=None, prologue: int = 0):
+    """:func:`kda_chunk_fwd` without a workspace: the library's fixed device
+    scratch array (NOALLOC_SCRATCH_BYTES) holds the chunk records, and the
+    C entry point allocates nothing.  The caller passes every output
+    (``o``; ``final_state`` or None), so this wrapper allocates nothing
+    either.  Calls that overlap in time on one device race on the scratch.
+    Returns (o, final_state)."""
+    torch = _torch()
+    (B, T), Hqk, Dk, H, Dv, m = _common(q, k, v, g, beta, mode, packed=False)
+    _check_meta("initial_state", initial_state, torch.float32, (B, H, Dk, Dv))
+    _check_meta("final_state", final_state, torch.float32, (B, H, Dk, Dv))
+    if o is None:
+        raise ValueError("o is required (the allocation-free entry allocates no output)")
+    _check_meta("o", o, None, (B, T, H, Dv))
+    _on_device(q.device, ("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+               ("initial_state", initial_state), ("final_state", final_state), ("o", o))
+    if scale is None:
+        scale = Dk ** -0.5
+    st = lib().kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(initial_state), _ptr(final_state), _ptr(o), B, T, H, Hqk,
+                                     Dk, Dv, int(chunk), float(scale), m, _dtype_code(q),
+                                     _dtype_code(o), int(prologue), _stream())
+    if st != 0:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return o, final_state
 
 

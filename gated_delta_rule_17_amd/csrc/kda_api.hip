@@ -53,6 +53,33 @@ kda_status check_common(const void* q, const void* k, const void* v, const float
 
 }  // namespace
 
+namespace kda {
+
+// Every argument check of kda_chunk_fwd except those of the workspace, on
+// the host, before any HIP call.
+kda_status chunk_fwd_checks(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* initial_state,
+                            const float* final_state, const void* o, int B, int T, int H, int Hqk,
+                            int Dk, int Dv, int chunk, const kda_gate_mode& mode,
+                            const kda_dtype& dtype, const kda_dtype& o_dtype, int prologue)
+{
+    if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
+    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
+                                 raw(o_dtype));
+    if (st != KDA_SUCCESS) return st;
+    if (!supported_chunk(chunk) || !chunk_fwd_supported(Dk, Dv, chunk, dtype))
+        return KDA_ERROR_NOT_SUPPORTED;
+    // chunk records and state workgroups are counted in 32-bit integers
+    const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
+    if (nrec > 1073741824.0 || (double)B * H * (Dv / 16) + 64.0 > 2147483647.0)
+        return KDA_ERROR_INVALID_VALUE;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERROR_MISALIGNED;
+    return KDA_SUCCESS;
+}
+
+}  // namespace kda
+
 extern "C" {
 
 const char* kda_status_string(kda_status s)
@@ -64,11 +91,12 @@ const char* kda_status_string(kda_status s)
         case KDA_ERROR_MISALIGNED: return "KDA_ERROR_MISALIGNED";
         case KDA_ERROR_WORKSPACE: return "KDA_ERROR_WORKSPACE";
         case KDA_ERROR_HIP: return "KDA_ERROR_HIP";
+        case KDA_ERROR_SCRATCH: return "KDA_ERROR_SCRATCH";
     }
     return "KDA_ERROR_UNKNOWN";
 }
 
-int kda_version(void) { return 10200; }
+int kda_version(void) { return 10300; }
 
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* g,
                               const float* beta, float* state, void* o, int B, int T, int H,
@@ -104,18 +132,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          float scale, kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                          int prologue, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (prologue & ~KDA_PROLOGUE_ALL) return KDA_ERROR_INVALID_VALUE;
-    kda_status st = check_common(q, k, v, g, beta, o, B, T, H, Hqk, Dk, Dv, raw(mode), raw(dtype),
-                                 raw(o_dtype));
+    kda_status st = kda::chunk_fwd_checks(q, k, v, g, beta, initial_state, final_state, o, B, T,
+                                          H, Hqk, Dk, Dv, chunk, mode, dtype, o_dtype, prologue);
     if (st != KDA_SUCCESS) return st;
-    if (!supported_chunk(chunk) || !kda::chunk_fwd_supported(Dk, Dv, chunk, dtype))
-        return KDA_ERROR_NOT_SUPPORTED;
-    // chunk records and state workgroups are counted in 32-bit integers
-    const double nrec = (double)B * H * ((T + chunk - 1) / chunk);
-    if (nrec > 1073741824.0 || (double)B * H * (Dv / 16) + 64.0 > 2147483647.0)
-        return KDA_ERROR_INVALID_VALUE;
-    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
-        return KDA_ERROR_MISALIGNED;
     const size_t need = kda_chunk_fwd_workspace_size(B, T, H, Dk, Dv, chunk, mode, dtype);
     if (T > 0) {
         if (!workspace || workspace_bytes < need) return KDA_ERROR_WORKSPACE;

@@ -69,6 +69,16 @@ struct ChunkBwdArgs {
 
 hipError_t launch_recurrent(const RecArgs& a, hipStream_t s);
 
+// Every argument check of kda_chunk_fwd except those of the workspace (host
+// only, no HIP call).  The enum arguments are taken by reference and read by
+// their bytes: a C caller may pass any int, and only validated values are
+// used as enums.
+kda_status chunk_fwd_checks(const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* initial_state,
+                            const float* final_state, const void* o, int B, int T, int H, int Hqk,
+                            int Dk, int Dv, int chunk, const kda_gate_mode& mode,
+                            const kda_dtype& dtype, const kda_dtype& o_dtype, int prologue);
+
 // Workspace layout of the chunk path (bytes); 0 if unsupported.
 size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype);
 size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype);

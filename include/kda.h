@@ -44,7 +44,10 @@
  *   matrix cores (see the kernel sources); a bf16 o is the float32 result
  *   rounded to nearest-even at the final store.
  * Pointers.  All tensor pointers are DEVICE pointers owned by the caller.
- *   The library never allocates, frees or synchronises; all work is enqueued
+ *   The library never allocates, frees or synchronises (its one piece of
+ *   device memory, the fixed scratch array behind kda_chunk_fwd_noalloc, is
+ *   part of its code object and is placed on a device when the library is
+ *   loaded there); all work is enqueued
  *   on `stream` (a hipStream_t passed as void*, NULL = the null stream) and
  *   is asynchronous with respect to the host.  Pointers must be 16-byte
  *   aligned.  Inputs are not modified except where stated.
@@ -114,7 +117,9 @@ typedef enum {
     KDA_ERROR_NOT_SUPPORTED = 2,  /* Dk, Dv or chunk outside the supported set     */
     KDA_ERROR_MISALIGNED = 3,     /* a pointer is not 16-byte aligned (cu_seqlens: 4) */
     KDA_ERROR_WORKSPACE = 4,      /* workspace NULL or smaller than required        */
-    KDA_ERROR_HIP = 5             /* the HIP runtime reported an error at launch    */
+    KDA_ERROR_HIP = 5,            /* the HIP runtime reported an error at launch    */
+    KDA_ERROR_SCRATCH = 6         /* kda_chunk_fwd_noalloc: the call needs more
+                                     than KDA_NOALLOC_SCRATCH_BYTES of scratch      */
 } kda_status;
 
 /*
@@ -176,6 +181,35 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          int B, int T, int H, int Hqk, int Dk, int Dv, int chunk, float scale,
                          kda_gate_mode mode, kda_dtype dtype, kda_dtype o_dtype,
                          int prologue, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, hosts that
+ * forbid allocation.  It takes the same arguments as kda_chunk_fwd except
+ * the workspace, runs the same kernels and gives the same bits.  Its chunk
+ * records live in a fixed device array of KDA_NOALLOC_SCRATCH_BYTES owned
+ * by the library: every device the library runs on holds one copy of it
+ * until the process ends, and the call itself allocates nothing (the
+ * array's device address is looked up once per device, on the first call
+ * made with that device current).
+ *
+ * Limit: a call whose kda_chunk_fwd_workspace_size(...) exceeds
+ * KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERROR_SCRATCH and enqueues nothing.
+ * 128 MiB holds, e.g., B1 H16 T4096 d128 chunk 64 with bf16 operands
+ * (112.5 MiB).
+ * Concurrency: all calls on one device share that device's array; calls
+ * that overlap in time on one device (different streams or host threads)
+ * race on it and give undefined results.  Calls ordered on one stream are
+ * safe (each call writes every record it reads).
+ * Other errors are those of kda_chunk_fwd.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta,
+                                 const float* initial_state, float* final_state, void* o,
+                                 int B, int T, int H, int Hqk, int Dk, int Dv, int chunk,
+                                 float scale, kda_gate_mode mode, kda_dtype dtype,
+                                 kda_dtype o_dtype, int prologue, void* stream);
 
 /*
  * Packed variable-length batches

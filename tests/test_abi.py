@@ -262,3 +262,21 @@ def test_chunk_bwd_varlen_workspace_size(L):
     assert f(1, 64, 1, 1, 128, 128, 64, 0, 1) >= 2 * dense
     assert f(3, 64, 1, 1, 128, 128, 64, 0, 1) >= 4 * dense
     assert f(2, 0, 1, 1, 128, 128, 64, 0, 1) > 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    import re
+    text = open(K.HEADER).read()
+    m = re.search(r"#define\s+KDA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*\*\s*(\d+)u\s*\*\s*(\d+)u\)", text)
+    assert m, "KDA_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == K.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_validation_before_any_hip_call(L):
+    def call(B=1, T=64, H=1, Dk=128, Dv=128, chunk=64, mode=0, dtype=1, o_dtype=0, q=A):
+        return L.kda_chunk_fwd_noalloc(q, A, A, A, A, None, None, A, B, T, H, H, Dk, Dv, chunk,
+                                       1.0, mode, dtype, o_dtype, 0, None)
+    # beyond the fixed scratch: B1 H16 T8192 d128 needs 225 MiB of records
+    assert call(T=8192, H=16) == 6
+    assert call(mode=3) == 1 and call(dtype=2) == 1 and call(o_dtype=-1) == 1
+    assert call(q=None) == 1 and call(q=MIS) == 3 and call(Dk=48) == 2
