@@ -48,9 +48,11 @@
 // over the tokens of a chunk with a decay between the two tokens are split
 // at a reference row per 16-row output block: the first row of the block for
 // sums over earlier tokens, the last row for sums over later ones.  Every
-// factor is then either at most 1 or spans at most 15 tokens, so the path
-// stays finite while no key channel decays by more than about e^-80 across
-// 16 consecutive tokens.
+// factor is then either at most 1 or spans at most 15 tokens.  A key channel
+// whose decay across one block exceeds e^-kBlockRange (a hard forget) would
+// overflow the factor that spans the block; that (block, channel) is left
+// out of the block's own product and its in-block terms are summed exactly,
+// exp(G_i - G_j) <= 1 pair by pair, in a fixed order.
 #pragma once
 
 #include <type_traits>
@@ -116,6 +118,13 @@ __device__ __forceinline__ size_t tok_v(const Args& a, int b, int t, int h) {
 }
 
 __device__ __forceinline__ float ex(float x) { return __expf(x); }
+
+// A key channel whose log gates fall by more than this across one 16-row block
+// (block, channel "flagged") is left out of that block's factored products,
+// whose key side grows to exp(G at the block's first row - G at its last row);
+// the block's terms of that channel are taken exactly, exp(G_i - G_j) <= 1 for
+// each pair, on the vector units instead.
+constexpr float kBlockRange = 80.f;
 
 // Workgroup barrier that orders LDS only: LDS writes before it are visible to
 // LDS reads after it, while global loads and stores stay in flight.
@@ -341,6 +350,10 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     __shared__ float sGref[NB + 1][DK];             // G at rows 16 I and at the last row
     __shared__ float sSeg[TPC][DK];
     __shared__ float sBeta[C];
+    constexpr int FW = (DK + 31) / 32;
+    __shared__ uint32_t sFlag[NB][FW];              // flagged (block, channel) pairs
+    __shared__ float sX[3][16][17];                 // G, k, scale q of 16 flagged channels x 16 rows
+    __shared__ float sEx[2][16][17];                // exact diagonal-block terms: Ap, Aqk
     float* const sS = smem + S::oS;
     float* const sAk = smem + S::oAk;
     float* const sAq = smem + S::oAq;
@@ -391,6 +404,7 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     for (int m = 1; m < RPT; ++m) Gr[m] += Gr[m - 1];
     sSeg[seg][c] = Gr[RPT - 1];
     for (int i = tid; i < C; i += NT) sBeta[i] = i < L ? a.beta[tok_v(a, b, t0 + i, h)] : 0.f;
+    for (int i = tid; i < NB * FW; i += NT) sFlag[i / FW][i % FW] = 0u;
     lds_barrier();
     {
         float off = 0.f;
@@ -403,6 +417,15 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             if (i % 16 == 0) sGref[i / 16][c] = Gr[m];
             if (i == C - 1) sGref[NB][c] = Gr[m];
         }
+    }
+    lds_barrier();
+    // flagged (block, channel) pairs: the thread holding a block's last row
+    // compares it with the block's first row (bitwise OR is order-free)
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = r0 + m;
+        if (i % 16 == 15 && sGref[i / 16][c] - Gr[m] > kBlockRange)
+            atomicOr(&sFlag[i / 16][c >> 5], 1u << (c & 31));
     }
     lds_barrier();
 
@@ -435,9 +458,50 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     const int Ib = r0 / 16;
     for (int I = 0; I < NB; ++I) {
         const float gref = sGref[I][c];
+        uint32_t anyw = 0;
+#pragma unroll
+        for (int f = 0; f < FW; ++f) anyw |= sFlag[I][f];
+        const bool anyI = anyw != 0;                  // uniform over the workgroup
+        if (anyI) {
+            // exact terms of the flagged channels inside block I: thread t < 256
+            // owns entry (i, j) = (16 I + t / 16, 16 I + t % 16) and adds the
+            // channels in ascending order, 16 at a time through sX
+            float ea = 0.f, eq = 0.f;
+            const int ii = (tid >> 4) & 15, jj = tid & 15;
+            for (int cb = 0; cb < DK; cb += 16) {
+                const uint32_t bm = (sFlag[I][cb >> 5] >> (cb & 31)) & 0xffffu;
+                if (!bm) continue;                    // uniform
+                if (Ib == I && c >= cb && c < cb + 16 && ((bm >> (c - cb)) & 1u)) {
+#pragma unroll
+                    for (int m = 0; m < RPT; ++m) {
+                        const int row = r0 + m - 16 * I;
+                        sX[0][c - cb][row] = Gr[m];
+                        sX[1][c - cb][row] = kr[m];
+                        sX[2][c - cb][row] = a.scale * qr[m];
+                    }
+                }
+                lds_barrier();
+                if (tid < 256 && jj <= ii) {
+                    for (uint32_t mm = bm; mm; mm &= mm - 1) {
+                        const int cc = __builtin_ctz(mm);
+                        const float kj = sX[1][cc][jj] * ex(sX[0][cc][ii] - sX[0][cc][jj]);
+                        if (jj < ii) ea += sX[1][cc][ii] * kj;
+                        eq += sX[2][cc][ii] * kj;
+                    }
+                }
+                lds_barrier();
+            }
+            if (tid < 256) {
+                sEx[0][ii][jj] = ea;
+                sEx[1][ii][jj] = eq;
+            }
+        }
+        // a flagged channel's key side is left out of the diagonal block
+        const bool flc = (sFlag[I][c >> 5] >> (c & 31)) & 1u;
         if (Ib <= I) {
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) sS[(r0 + m) * LS + c] = kr[m] * ex(gref - Gr[m]);
+            for (int m = 0; m < RPT; ++m)
+                sS[(r0 + m) * LS + c] = (Ib == I && flc) ? 0.f : kr[m] * ex(gref - Gr[m]);
         }
         if (Ib == I) {
 #pragma unroll
@@ -459,6 +523,10 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
                 acc2 = mma4(A[r16 * LK + kk + 4 + q4], sS[(16 * J + r16) * LS + kk + 4 + q4], acc2);
             }
             acc += acc2;
+            if (J == I && anyI) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) acc[ii] += sEx[which][4 * q4 + ii][r16];
+            }
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * I + 4 * q4 + ii, j = 16 * J + r16;
@@ -1503,17 +1571,22 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             qd[I][ii] = keep(qd[I][ii], i, L);
         }
     }
-    // sums over later tokens i >= j, reference row 16 J + 15
+    // sums over later tokens i >= j, reference row 16 J + 15.  A channel
+    // flagged in block J (decay across the block beyond kBlockRange) leaves
+    // block J out of the product and takes its terms exactly: lane (r16, q4)
+    // gathers the block's 16 rows of its channel from the four lanes of its
+    // column and sums exp(G_i - G_j) <= 1 pair by pair.
     f32x4 Pinv[NB];
 #pragma unroll
     for (int J = NB - 1; J >= 0; --J) {
         const float Ge = __shfl(Gd[J][3], 48 + r16);
+        const bool flJ = __shfl(Gd[J][0], r16) - Ge > kBlockRange;
 #pragma unroll
         for (int I = J; I < NB; ++I) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int row = 16 * I + 4 * q4 + ii;
-                const float f = ex(Gd[I][ii] - Ge);
+                const float f = (I == J && flJ) ? 0.f : ex(Gd[I][ii] - Ge);
                 src0[row * 16 + r16] = kd[I][ii] * f;
                 src1[row * 16 + r16] = a.scale * qd[I][ii] * f;
             }
@@ -1526,6 +1599,29 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) Pinv[J][ii] = ex(Ge - Gd[J][ii]) * acc[ii];
+        if (__any(flJ)) {
+            float Gx[16], kx[16], qx[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                Gx[t] = __shfl(Gd[J][t & 3], 16 * (t >> 2) + r16);
+                kx[t] = __shfl(kd[J][t & 3], 16 * (t >> 2) + r16);
+                qx[t] = __shfl(qd[J][t & 3], 16 * (t >> 2) + r16);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int jl = 4 * q4 + ii, j = 16 * J + jl;
+                float sum = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    if (t >= jl) {
+                        const int i = 16 * J + t;
+                        sum += (sdAb[i * LA + j] * kx[t] + sdAq[i * LA + j] * a.scale * qx[t]) *
+                               ex(Gx[t] - Gd[J][ii]);
+                    }
+                }
+                if (flJ) Pinv[J][ii] += sum;
+            }
+        }
         wave_lds_sync();
     }
 
@@ -1538,11 +1634,13 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
 #pragma unroll
     for (int I = 0; I < NB; ++I) {
         const float Gs = __shfl(Gd[I][0], r16);
+        const bool flI = Gs - __shfl(Gd[I][3], 48 + r16) > kBlockRange;
 #pragma unroll
         for (int J = 0; J <= I; ++J) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                src0[(16 * J + 4 * q4 + ii) * 16 + r16] = kd[J][ii] * ex(Gs - Gd[J][ii]);
+                src0[(16 * J + 4 * q4 + ii) * 16 + r16] =
+                    (J == I && flI) ? 0.f : kd[J][ii] * ex(Gs - Gd[J][ii]);
         }
         wave_lds_sync();
         f32x4 ra = zero4(), rb = zero4();
@@ -1551,12 +1649,39 @@ __global__ void __launch_bounds__(4 * DK) bwd_grad(Args a)
             ra = mma4(sdAq[(16 * I + r16) * LA + kk + q4], bs, ra);
             rb = mma4(sdAb[(16 * I + r16) * LA + kk + q4], bs, rb);
         }
+        // a channel flagged in block I: the block's own terms, exactly
+        float xq[4] = {0.f, 0.f, 0.f, 0.f}, xb[4] = {0.f, 0.f, 0.f, 0.f};
+        if (__any(flI)) {
+            float Gx[16], kx[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                Gx[t] = __shfl(Gd[I][t & 3], 16 * (t >> 2) + r16);
+                kx[t] = __shfl(kd[I][t & 3], 16 * (t >> 2) + r16);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int il = 4 * q4 + ii, i = 16 * I + il;
+                float sq = 0.f, sb = 0.f;
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    if (t <= il) {
+                        const float kj = kx[t] * ex(Gd[I][ii] - Gx[t]);
+                        sq += sdAq[i * LA + 16 * I + t] * kj;
+                        sb += sdAb[i * LA + 16 * I + t] * kj;
+                    }
+                }
+                if (flI) {
+                    xq[ii] = sq;
+                    xb[ii] = sb;
+                }
+            }
+        }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int i = 16 * I + 4 * q4 + ii;
             const float f = ex(Gd[I][ii] - Gs), eg = ex(Gd[I][ii]);
-            const float dqv = a.scale * (eg * X1[I][ii] + f * ra[ii]);
-            const float pg = -sBeta[i] * eg * X3[I][ii] + f * rb[ii];
+            const float dqv = a.scale * (eg * X1[I][ii] + f * ra[ii] + xq[ii]);
+            const float pg = -sBeta[i] * eg * X3[I][ii] + f * rb[ii] + xb[ii];
             const float pr = ex(Gl - Gd[I][ii]) * X2[I][ii];
             const float dkv = pg + Pinv[I][ii] + pr;
             src1[i * 16 + r16] = kd[I][ii] * (pg - Pinv[I][ii] - pr) + qd[I][ii] * dqv;

@@ -329,10 +329,9 @@ size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int Hqk, int Dk, int Dv
  *
  * Outputs must not alias inputs or each other.  The fused prologue is
  * forward-only: pass the transformed inputs (and take the prologue's own
- * gradients outside).  Within a
- * chunk the kernels split decays at 16-token boundaries, so results stay
- * finite while no key channel's log gates sum below about -80 over 16
- * consecutive tokens (a per-token g above about -5).
+ * gradients outside).  Gates are handled over the same range as the
+ * forward: any finite g, hard forgets (g = -30, say) included (GeekNews
+ * #31925, section "Gated DeltaNet: forget the whole state first").
  */
 kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const float* g,
                          const float* beta, const float* initial_state, const void* d_o,

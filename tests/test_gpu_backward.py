@@ -189,6 +189,56 @@ def test_bwd_strong_gates_within_range():
     _compare("f32 strong gates", _run(w, cot, 64), _oracle(w, cot), TOL["f32"])
 
 
+def _extreme_gates(mode, dtype, seed=21, T=150, D=64):
+    """The forward's gate-boundary cases: three hard-forget tokens (g = -30)
+    inside one 16-token block, a single channel at g = -40 for four tokens
+    followed by exact keeps (g = 0), one token at g = -95 (beyond the float32
+    exponent range on its own), and a run of g = 0."""
+    w = make_inputs(1, T, 2, D, D, mode=mode, dtype=dtype, seed=seed, h0_std=0.2)
+    w.g[:, 3:6] = -30.0
+    if mode == "channel":
+        w.g[0, 40:44, 0, 5] = -40.0
+        w.g[0, 44:60, 0, 5] = 0.0
+        w.g[0, 70, 1, :] = -95.0
+    else:
+        w.g[0, 70, 1] = -95.0
+    w.g[0, 100:128] = 0.0
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["channel", "scalar"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bwd_hard_forget_and_extreme_gates(dtype, mode, chunk):
+    """Gradients at the gate boundaries the forward supports ([GN] "Gated
+    DeltaNet: forget the whole state first"): key channels whose decay
+    across a 16-token block leaves the factored range take their in-block
+    terms exactly in both gradient kernels.  Everything stays finite and
+    matches R-bwd at the forward tolerances."""
+    w = _extreme_gates(mode, dtype)
+    cot = make_cotangents(w, seed=9, dhT_std=0.2)
+    say("bwd extreme gates", mode, dtype, chunk)
+    got = _run(w, cot, chunk)
+    _compare(f"extreme gates {mode} {dtype} C{chunk}", got, _oracle(w, cot), TOL[dtype])
+
+
+def test_bwd_extreme_gates_every_block_deterministic():
+    """Every 16-token block holds three hard-forget tokens (all channels of
+    all blocks on the exact path at once, d 128); the gradients match R-bwd
+    and a second call gives the same bits."""
+    w = make_inputs(1, 192, 2, 128, 128, mode="channel", dtype="bf16", seed=33, h0_std=0.1)
+    for b0 in range(0, 192, 16):
+        w.g[0, b0 + 5:b0 + 8] = -30.0
+    cot = make_cotangents(w, seed=10, dhT_std=0.1)
+    say("bwd extreme gates every block")
+    got = _run(w, cot, 64)
+    _compare("extreme gates every block", got, _oracle(w, cot), TOL["bf16"])
+    again = _run(w, cot, 64)
+    for n in NAMES:
+        if got[n] is not None:
+            np.testing.assert_array_equal(got[n], again[n], err_msg=n)
+
+
 def test_bwd_training_shape_two_batch_entries():
     """The training shape at full size (B8 H32 T8192 d128, chunk 64, bf16, mixed
     fast and slow channels): 32768 chunk records, a workspace whose float
