@@ -928,7 +928,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 // H published), so the output work and its operand loads run beside the
 // chain on the same SIMDs instead of in series with it.
 // ---------------------------------------------------------------------------
-template <int C, int DK, int DV, typename OT, typename OUT>
+template <int C, int DK, int DV, typename OT, typename OUT, int NT2>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             int T, int H, int BH, int NC, const void* ws, size_t nrec, const int4* __restrict__ stab)
@@ -938,17 +938,23 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     // barriers to the point of use, which undoes the prefetch)
     using S = CS<C, DK, DV, OT>;
     constexpr int NB = S::NB, CP = S::CP, DKP = S::DKP, SK = S::SK, SC = S::SC, NP = S::NP;
-    constexpr int NCT = DV / 16;          // column tiles per head
+    constexpr int NCOL = 16 * NT2;        // value columns of one workgroup (NT2 16-column tiles)
+    constexpr int NCT = DV / NCOL;        // workgroups per head
     constexpr int MH = DK / 16;           // 16-row tiles of the state
     constexpr int MHW = (MH + 3) / 4;     // state tiles per chain wave
     constexpr int KS = DKP / 32, KC = CP / 32;
     constexpr bool ALLE = NB >= 4;        // every wave of a role owns a token tile
     constexpr bool ALLH = (MH % 4) == 0;  // every chain wave owns MHW state tiles
+    // bf16 operands with one tile: three operand sets in rotation (a chunk's
+    // operands are requested two steps ahead); otherwise two (a third does not
+    // fit the registers)
+    constexpr bool THREE = S::SPLIT && NT2 == 1;
+    static_assert(DV % NCOL == 0, "whole tiles per workgroup");
 
-    __shared__ __align__(16) OT HTs[NP * 16 * SK];   // H^T tile [n][c] (precise operand)
-    __shared__ __align__(16) OT ETs[NP * 16 * SC];   // E^T tile [n][j] (precise operand)
-    const PArr<OT> HT{HTs, HTs + 16 * SK};
-    const PArr<OT> ET{ETs, ETs + 16 * SC};
+    __shared__ __align__(16) OT HTs[NP * NCOL * SK];   // H^T [n][c] (precise operand)
+    __shared__ __align__(16) OT ETs[NP * NCOL * SC];   // E^T [n][j] (precise operand)
+    const PArr<OT> HT{HTs, HTs + NCOL * SK};
+    const PArr<OT> ET{ETs, ETs + NCOL * SC};
 
     // XCD-aware mapping: all column tiles of one head on the same XCD (id % 8),
     // so the chunk records they all read are shared through that XCD's L2.
@@ -958,7 +964,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const int ct = slot % NCT;
     if (bh >= BH) return;
     const int h = bh - (bh / H) * H;
-    const int n0 = 16 * ct;
+    const int n0 = NCOL * ct;
     // The sequence of this workgroup: its first token, its length, its number
     // of chunks and where its chunk records start.  Dense batches: sequence b
     // of [B, T], records (b*H + h) * NC + chunk.  Packed variable-length
@@ -991,36 +997,39 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const bool has_t = ALLE || wr < NB;
 
     // zero the operand tiles (padding stays zero)
-    for (int p = tid; p < NP * 16 * SK; p += 512) store_op(HTs + p, 0.f);
-    for (int p = tid; p < NP * 16 * SC; p += 512) store_op(ETs + p, 0.f);
+    for (int p = tid; p < NP * NCOL * SK; p += 512) store_op(HTs + p, 0.f);
+    for (int p = tid; p < NP * NCOL * SC; p += 512) store_op(ETs + p, 0.f);
     __syncthreads();
 
     auto rec_of = [&](int cidx) { return recbase + (size_t)cidx * recstride; };
 
     if (chain) {
-        f32x4 hacc[MHW];
+        f32x4 hacc[MHW][NT2];
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
-            hacc[s] = zero4();
             const int mt = wr + 4 * s;
-            if (mt < MH && h0) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    hacc[s][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r];
+            for (int n = 0; n < NT2; ++n) {
+                hacc[s][n] = zero4();
+                if (mt < MH && h0) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        hacc[s][n][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r];
+                }
+                if (mt < MH) store4_p(HT, (16 * n + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
             }
-            if (mt < MH) store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
         }
         __syncthreads();
 
-        // Operands of one chunk step.  Two sets alternate: the next chunk's set
-        // is loaded while the current one is used.  The loads are
-        // unconditional straight-line code (indices clamped; zero padding in
-        // the records makes the extra fragments harmless) so that the wait for
-        // one set never includes the loads of the other.
+        // Operands of one chunk step, shared by the workgroup's NT2 column
+        // tiles (only U is per tile).  The loads are unconditional
+        // straight-line code (indices clamped; zero padding in the records
+        // makes the extra fragments harmless) so that the wait for one set
+        // never includes the loads of another.
         struct Ops {
             Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
             PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
-            f32x4 u;                 // U^T init of E
+            f32x4 u[NT2];            // U^T init of E
             f32x4 gl[MHW];           // exp(G_last) for the state rows
         };
         auto mt_of = [&](int s) { return ALLH ? wr + 4 * s : min(wr + 4 * s, MH - 1); };
@@ -1028,7 +1037,9 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const size_t rec = rec_of(cidx);
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
-            P.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
+#pragma unroll
+            for (int n = 0; n < NT2; ++n)
+                P.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + n, we, NB, lane));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) P.wn[ks].load(wn + fragbase(we, ks, KS, lane));
 #pragma unroll
@@ -1040,57 +1051,77 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 for (int ks = 0; ks < KC; ++ks) P.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
             }
         };
-        // One chunk step with operands P; the operands of chunk `nxt` are
-        // loaded into Q one fragment per matrix-core step, spreading the load
-        // traffic over the step.
         // One chunk step with operands P.  The operands of chunk `nxt` are
-        // all loaded into Q in the first half of the step, in the order the
-        // next step consumes them (U, -W, gl, Kr^T): the memory counter
-        // retires in order, so every wait of the next step covers only loads
-        // issued a whole step before.  Accumulations are split into independent chains so
-        // that the matrix-core latency is not paid once per k step.
+        // loaded into Q in the order the next step consumes them (U, -W, gl,
+        // Kr^T): the memory counter retires in order, so every wait of the
+        // next step covers only loads issued a whole step before.  U and -W
+        // are requested in the E phase, gl and Kr^T in the update phase, so
+        // the record traffic of a step is spread over both of its phases (the
+        // load unit of the compute unit, not the matrix cores, bounds the
+        // step).  Accumulations are split into independent chains so that the
+        // matrix-core latency is not paid once per k step.
         auto step = [&](const Ops& P, Ops& Q, int nxt) {
             const size_t rec = rec_of(nxt);
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
-            Q.u = Vec4<float>::load(W.ut + rec * S::U_N + accbase(ct, we, NB, lane));
-            f32x4 ea = P.u, eb = zero4();
+#pragma unroll
+            for (int n = 0; n < NT2; ++n)
+                Q.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + n, we, NB, lane));
+            f32x4 ea[NT2], eb[NT2];
+#pragma unroll
+            for (int n = 0; n < NT2; ++n) {
+                ea[n] = P.u[n];
+                eb[n] = zero4();
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 Q.wn[ks].load(wn + fragbase(we, ks, KS, lane));
                 if (has_t) {
-                    if (ks & 1) eb = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), eb);
-                    else ea = mma2(P.wn[ks], HT.frag(r * SK + 32 * ks + 8 * gq), ea);
+#pragma unroll
+                    for (int n = 0; n < NT2; ++n) {
+                        const PFrag<OT> hf = HT.frag((16 * n + r) * SK + 32 * ks + 8 * gq);
+                        if (ks & 1) eb[n] = mma2(P.wn[ks], hf, eb[n]);
+                        else ea[n] = mma2(P.wn[ks], hf, ea[n]);
+                    }
                 }
             }
-            if (has_t) store4_p(ET, r * SC + 16 * wr + 4 * gq, ea + eb);
+            if (has_t) {
+#pragma unroll
+                for (int n = 0; n < NT2; ++n)
+                    store4_p(ET, (16 * n + r) * SC + 16 * wr + 4 * gq, ea[n] + eb[n]);
+            }
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, NT2, 0);
             __syncthreads();
-            // H = Diag(gl) H + Kr^T E; the next Kr^T and gl are requested here,
-            // so that the record traffic of a step is spread over both of its
-            // phases (the load unit of the compute unit, not the matrix
-            // cores, bounds the step)
-            f32x4 part[MHW];
+            // H = Diag(gl) H + Kr^T E
+            f32x4 part[MHW][NT2];
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
-                if (ALLH || wr + 4 * s < MH) hacc[s] *= P.gl[s];
-                part[s] = zero4();
+#pragma unroll
+                for (int n = 0; n < NT2; ++n) {
+                    if (ALLH || wr + 4 * s < MH) hacc[s][n] *= P.gl[s];
+                    part[s][n] = zero4();
+                }
                 Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
             }
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
-                const PFrag<OT> et = ET.frag(r * SC + 32 * ks + 8 * gq);
+                PFrag<OT> et[NT2];
+#pragma unroll
+                for (int n = 0; n < NT2; ++n) et[n] = ET.frag((16 * n + r) * SC + 32 * ks + 8 * gq);
 #pragma unroll
                 for (int s = 0; s < MHW; ++s) {
                     Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
                     if (ALLH || wr + 4 * s < MH) {
-                        if (ks & 1) part[s] = mma3(P.kr[s][ks], et, part[s]);
-                        else hacc[s] = mma3(P.kr[s][ks], et, hacc[s]);
+#pragma unroll
+                        for (int n = 0; n < NT2; ++n) {
+                            if (ks & 1) part[s][n] = mma3(P.kr[s][ks], et[n], part[s][n]);
+                            else hacc[s][n] = mma3(P.kr[s][ks], et[n], hacc[s][n]);
+                        }
                     }
                 }
             }
@@ -1098,13 +1129,16 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             for (int s = 0; s < MHW; ++s) {
                 const int mt = wr + 4 * s;
                 if (ALLH || mt < MH) {
-                    hacc[s] += part[s];
-                    store4_p(HT, r * SK + 16 * mt + 4 * gq, hacc[s]);
+#pragma unroll
+                    for (int n = 0; n < NT2; ++n) {
+                        hacc[s][n] += part[s][n];
+                        store4_p(HT, (16 * n + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
+                    }
                 }
             }
             __syncthreads();
         };
-        if (NCs > 0 && S::SPLIT) {
+        if (NCs > 0 && THREE) {
             // three operand sets in rotation: a chunk's operands are requested
             // two steps before they are used (the records come from beyond the
             // L2, whose latency one step does not cover)
@@ -1117,7 +1151,6 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 if (cidx + 2 < NCs) step(D, B, min(cidx + 4, NCs - 1));
             }
         } else if (NCs > 0) {
-            // float32 operands: two sets (a third does not fit the registers)
             Ops A, B;
             load_ops(A, 0);
             for (int cidx = 0; cidx < NCs; cidx += 2) {
@@ -1131,8 +1164,11 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 const int mt = wr + 4 * s;
                 if (mt < MH) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + r] = hacc[s][u];
+                    for (int n = 0; n < NT2; ++n) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r] = hacc[s][n][u];
+                    }
                 }
             }
         }
@@ -1155,42 +1191,55 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const size_t rec = rec_of(nxt);
             const OT* qg = W.qg_rec(rec);
             const PArr<OT> aq = W.aqk(rec);
-            f32x4 oa = zero4(), ob = zero4();   // two independent accumulation chains
+            f32x4 oa[NT2], ob[NT2];   // two independent accumulation chains per tile
+#pragma unroll
+            for (int n = 0; n < NT2; ++n) {
+                oa[n] = zero4();
+                ob[n] = zero4();
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 Q.qg[ks].load(qg + fragbase(we, ks, KS, lane));
                 if (has_t) {
-                    if (ks & 1) ob = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], ob);
-                    else oa = mma2(HT.frag(r * SK + 32 * ks + 8 * gq), P.qg[ks], oa);
+#pragma unroll
+                    for (int n = 0; n < NT2; ++n) {
+                        const PFrag<OT> hf = HT.frag((16 * n + r) * SK + 32 * ks + 8 * gq);
+                        if (ks & 1) ob[n] = mma2(hf, P.qg[ks], ob[n]);
+                        else oa[n] = mma2(hf, P.qg[ks], oa[n]);
+                    }
                 }
             }
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT2, 0);
             }
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
                 Q.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
                 if (has_t) {
-                    if (ks & 1) ob = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], ob);
-                    else oa = mma3(ET.frag(r * SC + 32 * ks + 8 * gq), P.aq[ks], oa);
+#pragma unroll
+                    for (int n = 0; n < NT2; ++n) {
+                        const PFrag<OT> ef = ET.frag((16 * n + r) * SC + 32 * ks + 8 * gq);
+                        if (ks & 1) ob[n] = mma3(ef, P.aq[ks], ob[n]);
+                        else oa[n] = mma3(ef, P.aq[ks], oa[n]);
+                    }
                 }
             }
             if (has_t) {
-                const f32x4 oacc = oa + ob;
-                // lane holds o^T[n = 4gq + u][i = 16*wr + r]
+                // lane holds o^T[n = 4gq + u][i = 16*wr + r] of each tile
                 const int t0 = cidx * C;
                 const int i = 16 * wr + r;
                 if (i < min(C, seqlen - t0)) {
                     OUT* op = o + ((tokbase + t0 + i) * H + h) * DV + n0 + 4 * gq;
-                    Vec4<OUT>::store(op, oacc);
+#pragma unroll
+                    for (int n = 0; n < NT2; ++n) Vec4<OUT>::store(op + 16 * n, oa[n] + ob[n]);
                 }
             }
             __syncthreads();
         };
-        if (NCs > 0 && S::SPLIT) {
+        if (NCs > 0 && THREE) {
             Ops A, B, D;
             load_ops(A, 0);
             load_ops(B, min(1, NCs - 1));
@@ -1254,6 +1303,42 @@ constexpr bool chunk_shape_fits()
     return S::BIG + other <= 160L * 1024;
 }
 
+// The state pass: one workgroup per (sequence, head, NT2 16-column value
+// tiles).  Two tiles per workgroup share every record load and halve the
+// pass's compute-unit time; one tile per workgroup gives the most
+// workgroups.  Two tiles are taken once one tile per workgroup would need
+// more workgroups than the device holds at once (the pass then runs in
+// several waves of workgroups anyway).
+template <int C, int DK, int DV, typename OT, int NT2>
+hipError_t launch_state_nt(const ChunkArgs& a, int BH, int NC, size_t nrec, const int4* stab,
+                           hipStream_t s)
+{
+    const int groups = (BH + 7) / 8;
+    const dim3 grid(groups * 8 * (DV / (16 * NT2)));
+    if (a.o_dtype == KDA_F32)
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float, NT2>), grid, dim3(512), 0, s,
+                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
+    else
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t, NT2>), grid, dim3(512), 0, s,
+                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
+    return hipGetLastError();
+}
+
+template <int C, int DK, int DV, typename OT>
+hipError_t launch_state(const ChunkArgs& a, int BH, int NC, size_t nrec, const int4* stab,
+                        hipStream_t s)
+{
+    if constexpr (DV >= 32) {
+        int ncu = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            ncu = 256;
+        if ((double)BH * (DV / 16) > (double)ncu)
+            return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, s);
+    }
+    return launch_state_nt<C, DK, DV, OT, 1>(a, BH, NC, nrec, stab, s);
+}
+
 template <int C, int DK, int DV, typename OT>
 hipError_t launch3(const ChunkArgs& a, hipStream_t s)
 {
@@ -1299,15 +1384,7 @@ hipError_t launch3(const ChunkArgs& a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     if (BH == 0) return hipSuccess;
-    const int groups = (BH + 7) / 8;
-    const dim3 grid(groups * 8 * (DV / 16));
-    if (a.o_dtype == KDA_F32)
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
-    else
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
-    return hipGetLastError();
+    return launch_state<C, DK, DV, OT>(a, BH, NC, nrec, stab, s);
     }
 }
 
