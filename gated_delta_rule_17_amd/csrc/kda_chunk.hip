@@ -93,8 +93,11 @@ static PackedLayout packed_layout(int N, int T, int H, int Dk, int Dv, int C, kd
 
 size_t chunk_workspace_bytes(int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype dtype)
 {
+    // the records, then (segmented state pass only) the segment states
     const size_t NC = (size_t)(T + chunk - 1) / chunk;
-    return records_bytes_any(chunk, (size_t)B * H * NC, Dk, Dv, dtype);
+    const size_t rec = records_bytes_any(chunk, (size_t)B * H * NC, Dk, Dv, dtype);
+    const size_t sb = seg_bytes(B, T, H, Dk, Dv, chunk);
+    return rec == 0 || sb == 0 ? rec : align_up(rec, 256) + sb;
 }
 
 size_t chunk_varlen_workspace_bytes(int N, int Ttot, int H, int Dk, int Dv, int chunk, kda_dtype dtype)

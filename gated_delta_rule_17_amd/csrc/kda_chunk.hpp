@@ -931,7 +931,8 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 template <int C, int DK, int DV, typename OT, typename OUT, int NT2>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
-            int T, int H, int BH, int NC, const void* ws, size_t nrec, const int4* __restrict__ stab)
+            int T, int H, int BH, int NC, const void* ws, size_t nrec, const int4* __restrict__ stab,
+            float* seg, int nseg, int seglen, int phase)
 {
     // (ws is deliberately not __restrict__: with it, the record loads count as
     // invariant and the compiler sinks the next chunk's operand loads past the
@@ -956,15 +957,59 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const PArr<OT> HT{HTs, HTs + NCOL * SK};
     const PArr<OT> ET{ETs, ETs + NCOL * SC};
 
-    // XCD-aware mapping: all column tiles of one head on the same XCD (id % 8),
+    // Workgroups come in groups of G, one group per (sequence-head, segment).
+    // XCD-aware mapping: all workgroups of a group on the same XCD (id % 8),
     // so the chunk records they all read are shared through that XCD's L2.
+    //
+    // phase 0: one segment per sequence, every workgroup a state chain with
+    //   outputs (role 0), from h0 to hT.
+    // Segmented sequences (nseg segments of seglen chunks; seg holds three
+    // sets of nseg states [BH, DK, DV]: the true states entering the
+    // segments, the segments' final states from a zero state, and the
+    // segments' transition matrices):
+    // phase 1: segment 0 runs role 0 from h0 and leaves its final state as
+    //   the state entering segment 1; every later segment runs role 1 (state
+    //   from zero, no outputs) in its first NCT workgroups and role 2 (the
+    //   transition matrix: the same chain from the identity, with U = 0, no
+    //   outputs) in the next NCT;
+    // phase 3: segments 1 .. nseg-1 run role 0 from their true entering
+    //   states (chunk_seg_combine forms them in between); the last one
+    //   writes hT.
     const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
-    const int bh = (slot / NCT) * 8 + xcd;
-    const int ct = slot % NCT;
+    const int G = phase == 1 ? 2 * NCT : NCT;
+    const int nsl = phase == 1 ? nseg : (phase == 3 ? nseg - 1 : 1);
+    const int grp = (slot / G) * 8 + xcd;
+    const int wg = slot % G;
+    const int bh = grp / nsl;
     if (bh >= BH) return;
+    const int segi = grp - bh * nsl + (phase == 3 ? 1 : 0);
+    int role = 0;
+    if (phase == 1) {
+        if (wg >= NCT) {
+            if (segi == 0) return;
+            role = 2;
+        } else {
+            role = segi == 0 ? 0 : 1;
+        }
+    }
+    const int ct = wg % NCT;
     const int h = bh - (bh / H) * H;
     const int n0 = NCOL * ct;
+    const size_t SS = (size_t)BH * DK * DV;   // one set of states
+    const float* h0p = h0;
+    float* hTp = hT;
+    if (phase == 1) {
+        if (role == 0) {
+            hTp = seg + SS;                    // the state entering segment 1
+        } else {
+            h0p = nullptr;
+            hTp = seg + ((size_t)role * nseg + segi) * SS;
+        }
+    } else if (phase == 3) {
+        h0p = seg + (size_t)segi * SS;
+        hTp = segi == nseg - 1 ? hT : nullptr;
+    }
     // The sequence of this workgroup: its first token, its length, its number
     // of chunks and where its chunk records start.  Dense batches: sequence b
     // of [B, T], records (b*H + h) * NC + chunk.  Packed variable-length
@@ -986,6 +1031,9 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
         recbase = (size_t)bh * NC;
         recstride = 1;
     }
+    // this workgroup's chunks: c0 .. c0 + NCs - 1 of its sequence
+    const int c0 = phase == 0 ? 0 : segi * seglen;
+    if (phase != 0) NCs = max(0, min(seglen, NCs - c0));
     const WsLayout<C, DK, DV, OT> W(const_cast<void*>(ws), nrec);
 
     const int tid = threadIdx.x;
@@ -1001,7 +1049,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     for (int p = tid; p < NP * NCOL * SC; p += 512) store_op(ETs + p, 0.f);
     __syncthreads();
 
-    auto rec_of = [&](int cidx) { return recbase + (size_t)cidx * recstride; };
+    auto rec_of = [&](int cidx) { return recbase + (size_t)(c0 + cidx) * recstride; };
 
     if (chain) {
         f32x4 hacc[MHW][NT2];
@@ -1011,10 +1059,14 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
             for (int n = 0; n < NT2; ++n) {
                 hacc[s][n] = zero4();
-                if (mt < MH && h0) {
+                if (mt < MH && role == 2) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        hacc[s][n][u] = h0[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r];
+                        hacc[s][n][u] = (16 * mt + 4 * gq + u == n0 + 16 * n + r) ? 1.f : 0.f;
+                } else if (mt < MH && h0p) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        hacc[s][n][u] = h0p[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r];
                 }
                 if (mt < MH) store4_p(HT, (16 * n + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
             }
@@ -1070,7 +1122,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             f32x4 ea[NT2], eb[NT2];
 #pragma unroll
             for (int n = 0; n < NT2; ++n) {
-                ea[n] = P.u[n];
+                ea[n] = role == 2 ? zero4() : P.u[n];   // the transition matrix has no U term
                 eb[n] = zero4();
             }
 #pragma unroll
@@ -1158,7 +1210,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 if (cidx + 1 < NCs) step(B, A, min(cidx + 2, NCs - 1));
             }
         }
-        if (hT) {
+        if (hTp) {
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
                 const int mt = wr + 4 * s;
@@ -1167,10 +1219,17 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                     for (int n = 0; n < NT2; ++n) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            hT[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r] = hacc[s][n][u];
+                            hTp[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r] = hacc[s][n][u];
                     }
                 }
             }
+        }
+    } else if (role != 0) {
+        // no outputs: the output waves only keep the chain's barriers
+        __syncthreads();
+        for (int cidx = 0; cidx < NCs; ++cidx) {
+            __syncthreads();
+            __syncthreads();
         }
     } else {
         __syncthreads();   // initial state published
@@ -1229,7 +1288,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
             if (has_t) {
                 // lane holds o^T[n = 4gq + u][i = 16*wr + r] of each tile
-                const int t0 = cidx * C;
+                const int t0 = (c0 + cidx) * C;
                 const int i = 16 * wr + r;
                 if (i < min(C, seqlen - t0)) {
                     OUT* op = o + ((tokbase + t0 + i) * H + h) * DV + n0 + 4 * gq;
@@ -1256,6 +1315,65 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 if (cidx + 1 < NCs) step(B, cidx + 1, A, min(cidx + 2, NCs - 1));
             }
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Segmented sequences: the true state entering each segment, in order,
+//   H_{s+1} = M_s H_s + Z_s,   s = 1 .. nseg - 2,
+// from H_1 (left by segment 0) with the segments' transition matrices M_s and
+// their final states from zero Z_s (the chunk carry is affine in the state
+// it starts from).  One workgroup per (sequence-head, 16 value columns);
+// float32 on the vector units.
+template <int DK, int DV>
+__global__ void __launch_bounds__(2 * DK) chunk_seg_combine(float* seg, int BH, int nseg)
+{
+    // thread t: row i = t / 2 of the 16-column tile, columns 8 (t % 2) .. + 7;
+    // the state tile sits in LDS, row i of M_s streams in as 16-byte loads
+    // (the next segment's row is requested before this segment's sums)
+    constexpr int NCT = DV / 16;
+    __shared__ __align__(16) float Hs[DK][16];
+    const int bh = blockIdx.x / NCT, ct = blockIdx.x % NCT;
+    if (bh >= BH) return;
+    const size_t SS = (size_t)BH * DK * DV;
+    const int tid = threadIdx.x, i = tid >> 1, c8 = 8 * (tid & 1);
+    const size_t base = (size_t)bh * DK * DV;
+    const size_t hoff = base + (size_t)i * DV + 16 * ct + c8;
+    {
+        const f32x4* h1 = reinterpret_cast<const f32x4*>(seg + SS + hoff);
+        *reinterpret_cast<f32x4*>(&Hs[i][c8]) = h1[0];
+        *reinterpret_cast<f32x4*>(&Hs[i][c8 + 4]) = h1[1];
+    }
+    __syncthreads();
+    f32x4 m[DK / 4];
+    auto load_row = [&](int s2) {
+        const f32x4* M = reinterpret_cast<const f32x4*>(seg + ((size_t)2 * nseg + s2) * SS + base +
+                                                        (size_t)i * DV);
+#pragma unroll
+        for (int k4 = 0; k4 < DK / 4; ++k4) m[k4] = M[k4];
+    };
+    if (nseg > 2) load_row(1);
+    for (int s2 = 1; s2 + 1 < nseg; ++s2) {
+        const f32x4* Z = reinterpret_cast<const f32x4*>(seg + ((size_t)nseg + s2) * SS + hoff);
+        f32x4 a0 = Z[0], a1 = Z[1];
+#pragma unroll
+        for (int k4 = 0; k4 < DK / 4; ++k4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x4 h0v = *reinterpret_cast<const f32x4*>(&Hs[4 * k4 + e][c8]);
+                const f32x4 h1v = *reinterpret_cast<const f32x4*>(&Hs[4 * k4 + e][c8 + 4]);
+                a0 += m[k4][e] * h0v;
+                a1 += m[k4][e] * h1v;
+            }
+        }
+        if (s2 + 2 < nseg) load_row(s2 + 1);
+        __syncthreads();
+        *reinterpret_cast<f32x4*>(&Hs[i][c8]) = a0;
+        *reinterpret_cast<f32x4*>(&Hs[i][c8 + 4]) = a1;
+        f32x4* out = reinterpret_cast<f32x4*>(seg + (size_t)(s2 + 1) * SS + hoff);
+        out[0] = a0;
+        out[1] = a1;
+        __syncthreads();
     }
 }
 
@@ -1289,6 +1407,31 @@ int resident_blocks(K kernel, int threads)
 inline size_t varlen_gmax(int N, int Ttot, int C) { return (size_t)(Ttot + C - 1) / C + (size_t)N; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Segments per sequence of the dense state pass.  A long sequence over few
+// heads walks a long serial chain on a small part of the device (one
+// workgroup per head and 32 value columns; 256 of them fill an MI355X); it is
+// cut into up to 8 segments of at least 32 chunks that run side by side.
+// 1 (no segments) unless d_k = d_v >= 32 and the sequence has at least 256
+// chunks.  A function of the shape alone, so that the workspace size does not
+// depend on the device.
+inline int seg_count(int B, int T, int H, int Dk, int Dv, int C)
+{
+    if (Dk != Dv || Dv < 32) return 1;
+    const long nc = (T + C - 1) / C;
+    if (nc < 256) return 1;
+    const long tiles = (long)B * H * (Dv / 32);
+    long s = 256 / (tiles > 0 ? tiles : 1);
+    if (s > 8) s = 8;
+    while (s > 1 && nc < 32 * s) --s;
+    return s < 2 ? 1 : (int)s;
+}
+// Bytes of the segment states (three sets of nseg states [B, H, Dk, Dv]).
+inline size_t seg_bytes(int B, int T, int H, int Dk, int Dv, int C)
+{
+    const int ns = seg_count(B, T, H, Dk, Dv, C);
+    return ns > 1 ? (size_t)3 * ns * B * H * Dk * Dv * 4 : 0;
+}
+
 // LDS of chunk_prepare (its staging arrays, then the per-block gate terms,
 // norms, pair factors, flags and the diagonal blocks of A, as declared in the
 // kernel) against the 160 KiB of a compute unit: the shapes beyond it (float32
@@ -1311,32 +1454,60 @@ constexpr bool chunk_shape_fits()
 // several waves of workgroups anyway).
 template <int C, int DK, int DV, typename OT, int NT2>
 hipError_t launch_state_nt(const ChunkArgs& a, int BH, int NC, size_t nrec, const int4* stab,
-                           hipStream_t s)
+                           float* seg, int nseg, int seglen, int phase, hipStream_t s)
 {
-    const int groups = (BH + 7) / 8;
-    const dim3 grid(groups * 8 * (DV / (16 * NT2)));
+    constexpr int NCT = DV / (16 * NT2);
+    const int nsl = phase == 1 ? nseg : (phase == 3 ? nseg - 1 : 1);
+    const int G = phase == 1 ? 2 * NCT : NCT;
+    const long groups = ((long)BH * nsl + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8 * G));
     if (a.o_dtype == KDA_F32)
         hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float, NT2>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
+                           a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab,
+                           seg, nseg, seglen, phase);
     else
         hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t, NT2>), grid, dim3(512), 0, s,
-                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab);
+                           a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab,
+                           seg, nseg, seglen, phase);
     return hipGetLastError();
 }
 
+// The state pass, in one of two shapes.
+// Plain: one workgroup per (sequence, head, NT2 16-column value tiles).  Two
+// tiles per workgroup share every record load and halve the pass's
+// compute-unit time; one tile per workgroup gives the most workgroups.  Two
+// tiles are taken once one tile per workgroup would need more workgroups
+// than the device holds at once (the pass then runs in several waves of
+// workgroups anyway).
+// Segmented (nseg > 1, see seg_count): phase 1, chunk_seg_combine, phase 3,
+// two tiles per workgroup.
 template <int C, int DK, int DV, typename OT>
 hipError_t launch_state(const ChunkArgs& a, int BH, int NC, size_t nrec, const int4* stab,
-                        hipStream_t s)
+                        float* seg, int nseg, hipStream_t s)
 {
     if constexpr (DV >= 32) {
+        if (nseg > 1) {
+            if constexpr (DK == DV) {
+                const int seglen = (NC + nseg - 1) / nseg;
+                hipError_t e = launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg,
+                                                                 seglen, 1, s);
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL((chunk_seg_combine<DK, DV>), dim3(BH * (DV / 16)), dim3(2 * DK), 0, s,
+                                   seg, BH, nseg);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg, seglen,
+                                                         3, s);
+            }
+            return hipErrorInvalidValue;
+        }
         int ncu = 0, dev = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             ncu = 256;
         if ((double)BH * (DV / 16) > (double)ncu)
-            return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, s);
+            return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, nullptr, 1, NC, 0, s);
     }
-    return launch_state_nt<C, DK, DV, OT, 1>(a, BH, NC, nrec, stab, s);
+    return launch_state_nt<C, DK, DV, OT, 1>(a, BH, NC, nrec, stab, nullptr, 1, NC, 0, s);
 }
 
 template <int C, int DK, int DV, typename OT>
@@ -1384,7 +1555,10 @@ hipError_t launch3(const ChunkArgs& a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     if (BH == 0) return hipSuccess;
-    return launch_state<C, DK, DV, OT>(a, BH, NC, nrec, stab, s);
+    const int nseg = packed ? 1 : seg_count(a.B, a.T, a.H, a.Dk, a.Dv, C);
+    float* seg = nseg > 1 ? (float*)((char*)a.ws + align_up(WsLayout<C, DK, DV, OT>::bytes(nrec), 256))
+                          : nullptr;
+    return launch_state<C, DK, DV, OT>(a, BH, NC, nrec, stab, seg, nseg, s);
     }
 }
 

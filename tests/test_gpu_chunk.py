@@ -91,6 +91,37 @@ def test_long_prefill_every_head(name):
     _check_every_head(w, o, hT, TOL["bf16"])
 
 
+@pytest.mark.parametrize("mode", ["channel", "scalar", "none"])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_segmented_long_sequence_f32(mode, chunk):
+    """A long sequence over few heads (at least 256 chunks, d_k = d_v) runs
+    its state pass in segments side by side: each later segment from a zero
+    state plus its transition matrix, the true entering states chained
+    between two passes.  f32 with an initial state and a ragged last chunk
+    must still match the recurrence at 1e-4."""
+    T = 256 * chunk + 37
+    w = make_inputs(1, T, 2, 32, 32, mode=mode, dtype="f32", seed=chunk + len(mode), h0_std=0.3,
+                    gate_law="softplus" if mode != "none" else "zero")
+    say("segmented f32", mode, chunk, T)
+    o, hT = run_chunk(w, chunk=chunk)
+    _check(w, o, hT, TOL["f32"])
+
+
+def test_segmented_in_place_state_bf16():
+    """Segmented state pass (B1 H3 T20000 d128 bf16), the final state written
+    over the initial one; every head compared."""
+    import torch
+    import gated_delta_rule_17_amd as K
+    w = make_inputs(1, 20000, 3, 128, 128, dtype="bf16", seed=44, h0_std=0.05, gate_shift=-1.0)
+    d = to_device(w)
+    say("segmented in place")
+    st = d["h0"].clone()
+    o, _ = K.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=st,
+                           final_state=st, chunk=64, scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check_every_head(w, o.cpu().numpy(), st.cpu().numpy(), TOL["bf16"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_hard_forget_and_adversarial_gates(dtype):
     """Gate boundaries: hard forget (g = -30) on whole tokens and on single
