@@ -453,17 +453,17 @@ def main():
     import gated_delta_rule_17_amd as K
     from kda_workloads import make_config
     dev = torch.device("cuda:0")
+    if args.calibrate_copy and (args.only or args.backward_only):
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.only:
         print(json.dumps({args.only: bench_config(K, torch, dev, args.only, 2, 5)}), flush=True)
         return
     if args.backward_only:
-        if args.calibrate_copy:
-            src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
-            dst = torch.empty_like(src)
-            for _ in range(3):
-                dst.copy_(src)
-            torch.cuda.synchronize()
-            del src, dst
         print(json.dumps({"backward": bench_backward(K, torch, dev, args.warmup, args.steps)}),
               flush=True)
         return
