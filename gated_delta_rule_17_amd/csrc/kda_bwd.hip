@@ -1,4 +1,6 @@
 // Gradient of the chunkwise form: workspace layout and dispatch.
+#include <algorithm>
+
 #include "kda_bwd.hpp"
 
 namespace kda {
@@ -60,12 +62,47 @@ BwdLayout bwd_layout(int B, int T, int H, int Hq, int Dk, int Dv, int C, int N =
     return l;
 }
 
+// Dense batches run in groups of whole batch entries, so that the records of
+// one group stay within kRecordCap bytes (at least one entry per group): the
+// workspace is sized for one group and reused by the next.  A group of one
+// entry still holds H * ceil(T / C) chunks, which fills the device.
+constexpr size_t kRecordCap = (size_t)4 << 30;
+
+int bwd_group(int B, int T, int H, int Hq, int Dk, int Dv, int C)
+{
+    const BwdLayout one = bwd_layout(1, T, H, Hq, Dk, Dv, C);
+    const size_t per = (size_t)H * (size_t)((T + C - 1) / C) * one.rs * sizeof(float);
+    const size_t fit = per > 0 ? kRecordCap / per : (size_t)B;
+    return (int)std::max<size_t>(1, std::min<size_t>((size_t)B, fit));
+}
+
+// The three kernels (and the grouped-head sum) over the batch entries and
+// records that `a` describes.
+hipError_t run_bwd(const bwd::Args& a, const ChunkBwdArgs& h, hipStream_t s)
+{
+    hipError_t e = hipErrorInvalidValue;
+    if (h.chunk == 16) e = launch_bwd_c16(a, h.Dk, h.Dv, h.dtype, s);
+    else if (h.chunk == 32) e = launch_bwd_c32(a, h.Dk, h.Dv, h.dtype, s);
+    else if (h.chunk == 64) e = launch_bwd_c64(a, h.Dk, h.Dv, h.dtype, s);
+    if (e != hipSuccess || !a.dqp) return e;
+    const size_t n = (size_t)a.B * a.T * a.Hq * h.Dk;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    const int G = a.H / a.Hq;
+    if (a.gdt == KDA_BF16)
+        hipLaunchKernelGGL(bwd::bwd_group_sum<bf16_t>, dim3(blocks), dim3(256), 0, s, a.dqp, a.dkp,
+                           (bf16_t*)a.dq, (bf16_t*)a.dk, n, a.Hq, G, h.Dk);
+    else
+        hipLaunchKernelGGL(bwd::bwd_group_sum<float>, dim3(blocks), dim3(256), 0, s, a.dqp, a.dkp,
+                           (float*)a.dq, (float*)a.dk, n, a.Hq, G, h.Dk);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int Hq, int Dk, int Dv, int chunk)
 {
     if (T <= 0) return 0;
-    return bwd_layout(B, T, H, Hq, Dk, Dv, chunk).total;
+    return bwd_layout(bwd_group(B, T, H, Hq, Dk, Dv, chunk), T, H, Hq, Dk, Dv, chunk).total;
 }
 
 size_t chunk_bwd_varlen_workspace_bytes(int N, int T, int H, int Hq, int Dk, int Dv, int chunk)
@@ -78,7 +115,8 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
 {
     const int C = h.chunk;
     const bool packed = h.cu != nullptr;
-    const BwdLayout l = bwd_layout(h.B, h.T, h.H, h.Hq, h.Dk, h.Dv, C, packed ? h.N : 0);
+    const int Bg = packed ? 1 : bwd_group(h.B, h.T, h.H, h.Hq, h.Dk, h.Dv, C);
+    const BwdLayout l = bwd_layout(Bg, h.T, h.H, h.Hq, h.Dk, h.Dv, C, packed ? h.N : 0);
     char* ws = (char*)h.ws;
     bwd::Args a{};
     a.q = h.q; a.k = h.k; a.v = h.v; a.dO = h.dO;
@@ -112,6 +150,9 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
     a.stab = nullptr;
     a.N = 0;
     a.Gmax = 0;
+    a.mode = (int)h.mode;
+    a.gdt = (int)h.grad_dtype;
+    a.scale = h.scale;
     if (packed) {
         if (h.N == 0) return hipSuccess;
         a.B = 1;
@@ -121,26 +162,39 @@ hipError_t launch_chunk_bwd(const ChunkBwdArgs& h, hipStream_t s)
         a.stab = (const int4*)(ws + l.stab);
         hipError_t e = build_varlen_tables(h.cu, h.N, h.T, C, l.gmax, ws + l.ctab, ws + l.stab, s);
         if (e != hipSuccess) return e;
+        return run_bwd(a, h, s);
     }
-    a.mode = (int)h.mode;
-    a.gdt = (int)h.grad_dtype;
-    a.scale = h.scale;
     if (h.T == 0 && !h.dh0) return hipSuccess;
-    hipError_t e = hipErrorInvalidValue;
-    if (C == 16) e = launch_bwd_c16(a, h.Dk, h.Dv, h.dtype, s);
-    else if (C == 32) e = launch_bwd_c32(a, h.Dk, h.Dv, h.dtype, s);
-    else if (C == 64) e = launch_bwd_c64(a, h.Dk, h.Dv, h.dtype, s);
-    if (e != hipSuccess || !grouped) return e;
-    const size_t n = (size_t)h.B * h.T * h.Hq * h.Dk;
-    const unsigned blocks = (unsigned)((n + 255) / 256);
-    const int G = h.H / h.Hq;
-    if (h.grad_dtype == KDA_BF16)
-        hipLaunchKernelGGL(bwd::bwd_group_sum<bf16_t>, dim3(blocks), dim3(256), 0, s, a.dqp, a.dkp,
-                           (bf16_t*)h.dq, (bf16_t*)h.dk, n, h.Hq, G, h.Dk);
-    else
-        hipLaunchKernelGGL(bwd::bwd_group_sum<float>, dim3(blocks), dim3(256), 0, s, a.dqp, a.dkp,
-                           (float*)h.dq, (float*)h.dk, n, h.Hq, G, h.Dk);
-    return hipGetLastError();
+    // per batch entry: elements of each tensor (storage sizes apply below)
+    const size_t tq = (size_t)h.T * h.Hq * h.Dk, tv = (size_t)h.T * h.H * h.Dv;
+    const size_t tr = (size_t)h.T * h.H, tg = h.mode == KDA_GATE_CHANNEL ? tr * h.Dk : tr;
+    const size_t st = (size_t)h.H * h.Dk * h.Dv;
+    const size_t io = h.dtype == KDA_BF16 ? 2 : 4, gs = h.grad_dtype == KDA_BF16 ? 2 : 4;
+    auto at = [](const void* p, size_t bytes) -> void* {
+        return p ? (void*)((const char*)p + bytes) : nullptr;
+    };
+    for (int b0 = 0; b0 < h.B; b0 += Bg) {
+        bwd::Args x = a;
+        const size_t e = (size_t)b0;
+        x.B = std::min(Bg, h.B - b0);
+        x.q = at(h.q, e * tq * io);
+        x.k = at(h.k, e * tq * io);
+        x.v = at(h.v, e * tv * io);
+        x.dO = at(h.dO, e * tv * io);
+        x.g = (const float*)at(h.g, e * tg * 4);
+        x.beta = (const float*)at(h.beta, e * tr * 4);
+        x.h0 = (const float*)at(h.h0, e * st * 4);
+        x.dhT = (const float*)at(h.dhT, e * st * 4);
+        x.dq = at(h.dq, e * tq * gs);
+        x.dk = at(h.dk, e * tq * gs);
+        x.dv = at(h.dv, e * tv * gs);
+        x.dg = (float*)at(h.dg, e * tg * 4);
+        x.dbeta = (float*)at(h.dbeta, e * tr * 4);
+        x.dh0 = (float*)at(h.dh0, e * st * 4);
+        const hipError_t err = run_bwd(x, h, s);
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -27,7 +27,10 @@
 //                   dE = Ut + Kr dH' ;
 //                   dH = Diag(e^{G_last}) dH' + P - W^T dE,
 //                 storing dH' and dE per chunk.  Each workgroup owns one
-//                 16-column tile of the value dimension of one head.
+//                 16-column tile of the value dimension of one head.  For
+//                 bf16 inputs (bwd_states_mc) W, W^T, Kr and Kr^T come as bf16
+//                 pairs in matrix-core fragment order and the products run on
+//                 the bf16 matrix cores.
 //   3. bwd_grad   one workgroup per chunk, one wave per 16 key channels:
 //                 dUt = T^T dE, dv = beta dUt, the products with the chunk
 //                 state and its gradient, dA = -(strict lower dUt E^T),
@@ -42,7 +45,8 @@
 // dimension in bwd_grad and, for bf16 inputs, the products with T, Aqk and
 // scale Q e^G in bwd_prep: those take v_mfma_f32_16x16x32_bf16 over bf16
 // parts (hi + mid + lo) of their float32 operands, which keeps them good to
-// about 2^-24 of each operand.
+// about 2^-24 of each operand; and, for bf16 inputs, the state passes, over
+// hi + lo pairs (about 2^-16).
 //
 // Decays inside a chunk come from differences of G.  Products that sum
 // over the tokens of a chunk with a decay between the two tokens are split
@@ -67,6 +71,9 @@ namespace bwd {
 // unit = b * H + h (dense batch), or r = h * Gmax + g for chunk slot g of a
 // packed batch (the chunks of one sequence are consecutive slots).  Rows of a ragged last chunk beyond its length are zero
 // (G repeats its last valid row).
+// W, WT, Kr and KrT of bf16 inputs (prep_split) hold instead the bf16 pairs
+// of store_mc in the same bytes: fragments of [C][DK] (W, Kr) and of [DK][C]
+// (WT, KrT), hi plane then lo plane.
 struct Records {
     float* G;    // [C][DK]  inclusive prefix of the log gates
     float* W;    // [C][DK]
@@ -288,6 +295,59 @@ __device__ __forceinline__ void put1x8(uint32_t* plane, int off, const float* x)
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     *reinterpret_cast<u32x4_t*>(plane + off) =
         (u32x4_t){cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3]), cvt_pk(x[4], x[5]), cvt_pk(x[6], x[7])};
+}
+
+// ---- 16-byte loads through a buffer resource ----------------------------------
+// The base address sits in scalar registers (one resource per record) and each
+// lane supplies a 32-bit byte offset, so a loop that walks the records keeps no
+// 64-bit vector addresses; soff is a constant added on top.
+// A resource of zero length returns zeros without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t record_rsrc(const void* base, int bytes = 0x7fffffff) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+template <typename V>
+__device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float bload1(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+// Value of lane J of this lane's 16-lane row (DPP row broadcast).
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + J, 0xf, 0xf, false));
+}
+
+// ---- operands of the matrix-core state passes (bf16 inputs) -----------------
+// An operand of logical shape [rows][K] (K = 32 KSn) is stored as its 16 x 32
+// fragments (row tile, k step), each as 64 lanes x 8 values, so that one
+// wave's fragment load is 1 KiB of contiguous memory.  Lane (r, g) of
+// fragment (rt, ks) holds row 16 rt + r; its value e is the one at
+// k = 32 ks + 16 (e / 4) + 4 g + e % 4.  A lane thus holds two runs of four
+// consecutive k, which is how the 16 x 16 accumulators of two adjacent tiles
+// hold a column: the producer's accumulators are a fragment as they stand.
+// The contraction is the same for any order of k as long as both operands
+// use it; the state and E staged in LDS for the other side follow it too.
+// The values are float32 stored as bf16 pairs, hi = bf16(x) and
+// lo = bf16(x - hi), in two planes `plane` elements apart.
+__device__ __forceinline__ int mc_pos(int k) {   // position of k within its 32-wide step
+    return 8 * ((k >> 2) & 3) + 4 * ((k >> 4) & 1) + (k & 3);
+}
+__device__ __forceinline__ void store_mc(uint16_t* base, int plane, int idx, f32x4 x0, f32x4 x1) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int z = 0; z < 2; ++z) {
+        const f32x4 x = z ? x1 : x0;
+        h[2 * z] = cvt_pk(x[0], x[1]);
+        h[2 * z + 1] = cvt_pk(x[2], x[3]);
+        l[2 * z] = cvt_pk(x[0] - __uint_as_float(h[2 * z] << 16), x[1] - __uint_as_float(h[2 * z] & 0xffff0000u));
+        l[2 * z + 1] = cvt_pk(x[2] - __uint_as_float(h[2 * z + 1] << 16),
+                              x[3] - __uint_as_float(h[2 * z + 1] & 0xffff0000u));
+    }
+    *reinterpret_cast<u32x4_t*>(base + idx) = (u32x4_t){h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4_t*>(base + plane + idx) = (u32x4_t){l[0], l[1], l[2], l[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -632,21 +692,40 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
             for (int g = 0; g < RPV; g += 8) put1x8(pVT, cv * PW + (r0v + g) / 2, y + g);
         }
         lds_barrier();
-        // W = TB (K e^G), stored as [C][DK] and transposed [DK][C]; U = TB V
-        constexpr int NJW = NB * (DK / 16);
-        for (int job = w; job < NJW + NB * (DV / 16); job += NW) {
-            f32x4 acc = zero4();
-            if (job < NJW) {
-                const int I = job / (DK / 16), Rc = job % (DK / 16);
-                for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
-                    acc = mm6(pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4),
-                              pfrag3(pKG + k0 / 2, DK * PW, PW, 16 * Rc + r16, q4), acc);
+        // W = TB (K e^G) for the matrix-core state passes, in both
+        // orientations: W [C][DK] (job (I, ks): tokens 16 I.., channels
+        // 32 ks..) and W^T [DK][C] (job (Rc, kc): channels 16 Rc.., tokens
+        // 32 kc..).  Each job forms the two 16 x 16 tiles of one fragment with
+        // the operand whose rows are the fragment's k first, so that lane
+        // (r16, q4) ends with its fragment values.  U = TB V, [DV][C].
+        constexpr int KS = DK / 32, KC = C / 32;
+        constexpr int NJ1 = NB * KS, NJ2 = (DK / 16) * KC, NJU = NB * (DV / 16);
+        for (int job = w; job < NJ1 + NJ2 + NJU; job += NW) {
+            if (job < NJ1) {
+                const int I = job / KS, ks = job % KS;
+                f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii)
-                    a.r.W[R * a.r.rs + (16 * I + 4 * q4 + ii) * DK + 16 * Rc + r16] = acc[ii];
-                *reinterpret_cast<f32x4*>(a.r.WT + R * a.r.rs + (16 * Rc + r16) * C + 16 * I + 4 * q4) = acc;
+                for (int hh = 0; hh < 2; ++hh)
+                    for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
+                        acc[hh] = mm6(pfrag3(pKG + k0 / 2, DK * PW, PW, 32 * ks + 16 * hh + r16, q4),
+                                      pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4), acc[hh]);
+                store_mc(reinterpret_cast<uint16_t*>(a.r.W + R * a.r.rs), C * DK,
+                         ((I * KS + ks) * 64 + lane) * 8, acc[0], acc[1]);
+            } else if (job < NJ1 + NJ2) {
+                const int Rc = (job - NJ1) / KC, kc = (job - NJ1) % KC;
+                f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int I = 2 * kc + hh;
+                    for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
+                        acc[hh] = mm6(pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4),
+                                      pfrag3(pKG + k0 / 2, DK * PW, PW, 16 * Rc + r16, q4), acc[hh]);
+                }
+                store_mc(reinterpret_cast<uint16_t*>(a.r.WT + R * a.r.rs), C * DK,
+                         ((Rc * KC + kc) * 64 + lane) * 8, acc[0], acc[1]);
             } else {
-                const int ju = job - NJW, I = ju / (DV / 16), Vt = ju % (DV / 16);
+                const int ju = job - NJ1 - NJ2, I = ju / (DV / 16), Vt = ju % (DV / 16);
+                f32x4 acc = zero4();
                 for (int k0 = 0; k0 < 16 * (I + 1); k0 += 32)
                     acc = mm3b(pfrag3(pTB + k0 / 2, C * PW, PW, 16 * I + r16, q4),
                                pfrag(pVT + k0 / 2, PW, 16 * Vt + r16, q4), acc);
@@ -691,7 +770,43 @@ __global__ void __launch_bounds__((prep_threads<C, DK, DV>())) bwd_prep(Args a)
     }
 
     // Kr = K e^{G_last - G}, stored as [C][DK] and transposed [DK][C]
-    {
+    if constexpr (SPLIT) {
+        // in the matrix-core fragment order of the state passes: staged as
+        // float32 [C][DK] over the operand planes of W and U (dead once every
+        // wave is past the loop above), then read back a fragment lane at a time
+        constexpr int LR = DK + 4, KS = DK / 32, KC = C / 32;
+        static_assert(C * LR <= S::oAqkP, "staging clear of Aqk^T");
+        float* const sKr = smem;
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) sKr[(r0 + m) * LR + c] = kr[m] * ex(sGref[NB][c] - Gr[m]);
+        lds_barrier();
+        uint16_t* const kb = reinterpret_cast<uint16_t*>(a.r.Kr + R * a.r.rs);
+        uint16_t* const kt = reinterpret_cast<uint16_t*>(a.r.KrT + R * a.r.rs);
+        constexpr int N1 = NB * KS * 64, N2 = (DK / 16) * KC * 64;
+        for (int e = tid; e < N1 + N2; e += NT) {
+            const int ln = e & 63, rr = ln & 15, gg = ln >> 4;
+            f32x4 x0, x1;
+            if (e < N1) {
+                // Kr: fragment (token tile, channel step)
+                const int f = e >> 6, rt = f / KS, ks = f % KS;
+                const float* p = sKr + (16 * rt + rr) * LR + 32 * ks + 4 * gg;
+                x0 = *reinterpret_cast<const f32x4*>(p);
+                x1 = *reinterpret_cast<const f32x4*>(p + 16);
+                store_mc(kb, C * DK, 8 * e, x0, x1);
+            } else {
+                // Kr^T: fragment (channel tile, token step)
+                const int e2 = e - N1, f = e2 >> 6, rt = f / KC, kc = f % KC;
+                const float* p = sKr + (32 * kc + 4 * gg) * LR + 16 * rt + rr;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    x0[u] = p[u * LR];
+                    x1[u] = p[(16 + u) * LR];
+                }
+                store_mc(kt, C * DK, 8 * e2, x0, x1);
+            }
+        }
+    } else {
         float kx[RPT];
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
@@ -1010,6 +1125,203 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
     if (reverse && a.dh0) {
 #pragma unroll
         for (int s = 0; s < SQ; ++s) a.dh0[(size_t)u * DD + (size_t)chan(s) * DV + v0 + r16] = st[s];
+    }
+}
+
+// The same two carries on the bf16 matrix cores, for bf16 inputs (where
+// bwd_prep stores W, W^T, Kr and Kr^T as bf16 pairs in the fragment order of
+// store_mc).  Every product is hi*hi + hi*lo + lo*hi of the pairs (mma3),
+// good to about 2^-16 of its operands, against float32 products in
+// bwd_states; the carried state stays in float32 accumulators.
+//
+// Workgroup = (role, sequence-head, 16 value columns), four waves.  Wave w
+// computes token tile w of E = U - W H (forward) or dE = Ut + Kr dH'
+// (reverse) over all key channels, with the state's 16 columns read from LDS
+// as the right operand; after the barrier it updates state tiles w, w + 4, ..
+// with Kr^T E (or P - W^T dE) over the chunk's tokens, E read from LDS.  Two
+// barriers per chunk; the next chunk's operands are requested at the start of
+// each step.
+template <int C, int DK, int DV>
+__global__ void __launch_bounds__(256) bwd_states_mc(Args a)
+{
+    constexpr int NB = C / 16, KS = DK / 32, KC = C / 32, MH = DK / 16, MHW = MH / 4;
+    constexpr int SK = DK + 8, SC = C + 8;      // LDS row strides (bf16 elements)
+    constexpr int PL = C * DK;                  // elements per bf16 plane of a record operand
+    static_assert(DK % 64 == 0 && DK <= 128 && C % 32 == 0, "whole fragments for every wave, at most two state tiles");
+    __shared__ __align__(16) bf16_t HTs[2 * 16 * SK];   // state^T [column][channel], hi and lo
+    __shared__ __align__(16) bf16_t ETs[2 * 16 * SC];   // E^T [column][token], hi and lo
+    const PArr<bf16_t> HT{HTs, HTs + 16 * SK};
+    const PArr<bf16_t> ET{ETs, ETs + 16 * SC};
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int units = (a.stab ? a.N : a.B) * a.H;
+    // XCD-aware: the DV / 16 value tiles of one (role, head) take ids 8
+    // apart, so they share an XCD and its L2, which serves their common records
+    constexpr int NVT = DV / 16;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int ur = (slot / NVT) * 8 + xcd, vt = slot % NVT;
+    if (ur >= 2 * units) return;
+    const bool reverse = ur >= units;
+    const int u = reverse ? ur - units : ur;
+    const int v0 = vt * 16;
+    const size_t DD = (size_t)DK * DV;
+    int NC;
+    size_t rbase;
+    if (a.stab) {
+        const int4 sq = a.stab[u / a.H];
+        NC = (sq.y + C - 1) / C;
+        rbase = (size_t)(u % a.H) * a.Gmax + sq.z;
+    } else {
+        NC = a.NC;
+        rbase = (size_t)u * a.NC;
+    }
+    const bool has_t = w < NB;                  // this wave owns a token tile
+    const int we = has_t ? w : NB - 1;
+
+    // the state strip: accumulator s holds rows 16 (w + 4 s) + 4 g + 0..3 of column v0 + r
+    f32x4 hacc[MHW];
+    {
+        const float* init = reverse ? a.dhT : a.h0;
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = w + 4 * s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                hacc[s][e] = init ? init[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + r] : 0.f;
+            store4_p(HT, r * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s]);
+        }
+    }
+    __syncthreads();
+
+    const float* const A1b = reverse ? a.r.Kr : a.r.W;     // [C][DK] fragments, token tile we
+    const float* const A2b = reverse ? a.r.WT : a.r.KrT;   // [DK][C] fragments, state tiles
+    const float* const ADb = reverse ? a.r.Ut : a.r.U;
+    float* const recb = reverse ? a.r.dH : a.r.Hs;
+    float* const erb = reverse ? a.r.dE : a.r.E;
+
+    struct Ops {
+        PFrag<bf16_t> a1[KS];
+        PFrag<bf16_t> a2[MHW][KC];
+        f32x4 add;
+        f32x4 p[MHW];
+        float gl;        // G_last of one channel of this lane's row (see oGl1)
+    };
+    // Record fields are addressed as a uniform record base plus per-lane
+    // 32-bit byte offsets fixed for the whole pass, so that every load takes
+    // its address from scalar registers and one loop-invariant vector offset.
+    const char* const wsb = reinterpret_cast<const char*>(a.r.G);
+    const uint32_t fA1 = (uint32_t)(reinterpret_cast<const char*>(A1b) - wsb);
+    const uint32_t fA2 = (uint32_t)(reinterpret_cast<const char*>(A2b) - wsb);
+    const uint32_t fAD = (uint32_t)(reinterpret_cast<const char*>(ADb) - wsb);
+    const uint32_t fP = (uint32_t)(reinterpret_cast<const char*>(a.r.P) - wsb);
+    const uint32_t oAdd = fAD + 4u * (uint32_t)((v0 + r) * C + 16 * we + 4 * g);
+    const uint32_t oA1 = fA1 + 16u * (uint32_t)(we * KS * 64 + lane);
+    const uint32_t oA2 = fA2 + 16u * (uint32_t)(w * KC * 64 + lane);
+    // the last gate row: lane (r, g) loads channel 16 (w + 4 s) + 4 g + e for
+    // r = 4 s + e (r mod 8), and lane 4 s + e of each 16-lane row then hands
+    // it to the whole row (every lane of a row needs the same eight values)
+    const uint32_t oGl1 =
+        4u * (uint32_t)((C - 1) * DK + 16 * (w + 4 * ((r >> 2) & (MHW - 1))) + 4 * g + (r & 3));
+    // P, added on the reverse role only: the forward role reads it through a
+    // resource of zero length, which returns zeros without a memory access
+    const uint32_t oP = fP + 4u * (uint32_t)((v0 + r) * DK + 16 * w + 4 * g);
+    const int pbytes = reverse ? 0x7fffffff : 0;
+    const uint32_t oRec = (uint32_t)(reinterpret_cast<const char*>(recb) - wsb) + 4u * (uint32_t)((v0 + r) * DK + 16 * w + 4 * g);
+    const uint32_t oE = (uint32_t)(reinterpret_cast<const char*>(erb) - wsb) + 4u * (uint32_t)((v0 + r) * C + 16 * we + 4 * g);
+    auto load_ops = [&](Ops& o, int ch) {
+        const char* const base = wsb + (rbase + (size_t)ch) * a.r.rs * sizeof(float);
+        const __amdgpu_buffer_rsrc_t rb = record_rsrc(base);
+        const __amdgpu_buffer_rsrc_t rp = record_rsrc(base, pbytes);
+        o.add = bload<f32x4>(rb, oAdd, 0);
+        o.gl = bload1(rb, oGl1, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            o.a1[ks].h.v = bload<u16x8>(rb, oA1, 1024 * ks);
+            o.a1[ks].l.v = bload<u16x8>(rb, oA1, 2 * PL + 1024 * ks);
+        }
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            // state tile w + 4 s: 64 channels further on
+            o.p[s] = bload<f32x4>(rp, oP, 256 * s);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                o.a2[s][kc].h.v = bload<u16x8>(rb, oA2, 1024 * (4 * s * KC + kc));
+                o.a2[s][kc].l.v = bload<u16x8>(rb, oA2, 2 * PL + 1024 * (4 * s * KC + kc));
+            }
+        }
+    };
+    auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
+
+    auto step = [&](const Ops& P, Ops& Q, int n) {
+        char* const rb = const_cast<char*>(wsb) + (rbase + (size_t)chunk_of(n)) * a.r.rs * sizeof(float);
+        load_ops(Q, chunk_of(n + 2));
+        // the state entering the chunk (forward) or the gradient leaving it (reverse)
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) *reinterpret_cast<f32x4*>(rb + oRec + 256u * s) = hacc[s];
+        if (has_t) {
+            f32x4 ea = zero4(), eb = zero4();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const PFrag<bf16_t> hf = HT.frag(r * SK + 32 * ks + 8 * g);
+                if (ks & 1) eb = mma3(P.a1[ks], hf, eb);
+                else ea = mma3(P.a1[ks], hf, ea);
+            }
+            const f32x4 e = reverse ? P.add + (ea + eb) : P.add - (ea + eb);
+            store4_p(ET, r * SC + 32 * (we >> 1) + mc_pos(16 * (we & 1) + 4 * g), e);
+            *reinterpret_cast<f32x4*>(rb + oE) = e;
+        }
+        lds_barrier();
+        float gm[MHW][4];
+        {
+            const float egl = ex(P.gl);
+            gm[0][0] = row_bcast<0>(egl); gm[0][1] = row_bcast<1>(egl);
+            gm[0][2] = row_bcast<2>(egl); gm[0][3] = row_bcast<3>(egl);
+            if constexpr (MHW > 1) {
+                gm[MHW - 1][0] = row_bcast<4>(egl); gm[MHW - 1][1] = row_bcast<5>(egl);
+                gm[MHW - 1][2] = row_bcast<6>(egl); gm[MHW - 1][3] = row_bcast<7>(egl);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = w + 4 * s;
+            f32x4 xa = zero4(), xb = zero4();
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const PFrag<bf16_t> ef = ET.frag(r * SC + 32 * kc + 8 * g);
+                if (kc & 1) xb = mma3(P.a2[s][kc], ef, xb);
+                else xa = mma3(P.a2[s][kc], ef, xa);
+            }
+            const f32x4 x = xa + xb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hacc[s][e] = gm[s][e] * hacc[s][e] + P.p[s][e] + (reverse ? -x[e] : x[e]);
+            }
+            store4_p(HT, r * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s]);
+        }
+        lds_barrier();
+    };
+
+    // three operand sets in rotation: a chunk's operands are requested two
+    // steps before their use
+    Ops bufA, bufB, bufC;
+    if (NC > 0) {
+        load_ops(bufA, chunk_of(0));
+        load_ops(bufB, chunk_of(1));
+    }
+    for (int n = 0; n < NC; n += 3) {
+        step(bufA, bufC, n);
+        if (n + 1 < NC) step(bufB, bufA, n + 1);
+        if (n + 2 < NC) step(bufC, bufB, n + 2);
+    }
+    if (reverse && a.dh0) {
+#pragma unroll
+        for (int s = 0; s < MHW; ++s) {
+            const int mt = w + 4 * s;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                a.dh0[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + r] = hacc[s][e];
+        }
     }
 }
 // ---------------------------------------------------------------------------
@@ -1797,8 +2109,11 @@ hipError_t launch3(const Args& a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     const unsigned ur8 = (unsigned)((2 * units + 7) / 8) * 8;
-    hipLaunchKernelGGL((bwd_states<C, DK, DV, IO>), dim3(ur8 * (DV / 16)),
-                       dim3(64 * StateShape<C, DK>::NWS), 0, s, a);
+    if constexpr (prep_split<C, DK, DV, IO>())
+        hipLaunchKernelGGL((bwd_states_mc<C, DK, DV>), dim3(ur8 * (DV / 16)), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_states<C, DK, DV, IO>), dim3(ur8 * (DV / 16)),
+                           dim3(64 * StateShape<C, DK>::NWS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (nrec > 0) {

@@ -224,6 +224,11 @@ def test_chunk_bwd_workspace_size(L):
     assert f(1, 65, 1, 1, 128, 128, 64, 0, 1) >= 2 * one - 16 * 256
     # grouped heads add float partials of dq and dk per value head
     assert f(1, 64, 4, 2, 128, 128, 64, 0, 1) >= 4 * one + 2 * 4 * 64 * 4 * 128 - 16 * 256
+    # large batches run in groups of whole batch entries whose records fit in
+    # 4 GiB: the workspace is one group's
+    assert f(2, 4096, 16, 16, 128, 128, 64, 0, 1) == 2 * f(1, 4096, 16, 16, 128, 128, 64, 0, 1)
+    train = f(8, 8192, 32, 32, 128, 128, 64, 0, 1)
+    assert train == 2 * f(1, 8192, 32, 32, 128, 128, 64, 0, 1) <= 4 * 2 ** 30 + 2 ** 20
 
 
 def _bwd_v(L, q=A, k=A, v=A, g=A, beta=A, h0=None, do=A, dhT=None, dq=A, dk=A, dv=A, dg=A,
