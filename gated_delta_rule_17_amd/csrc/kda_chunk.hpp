@@ -1489,8 +1489,14 @@ hipError_t launch_state(const ChunkArgs& a, int BH, int NC, size_t nrec, const i
         if (nseg > 1) {
             if constexpr (DK == DV) {
                 const int seglen = (NC + nseg - 1) / nseg;
-                hipError_t e = launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg,
-                                                                 seglen, 1, s);
+                // phase 1 runs two chains per later segment (its zero-state
+                // part and its transition matrix): four tiles per workgroup
+                // (bf16 operands) keep it to one workgroup per compute unit
+                hipError_t e;
+                if constexpr (std::is_same<OT, bf16_t>::value && DV % 64 == 0)
+                    e = launch_state_nt<C, DK, DV, OT, 4>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
+                else
+                    e = launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
                 if (e != hipSuccess) return e;
                 hipLaunchKernelGGL((chunk_seg_combine<DK, DV>), dim3(BH * (DV / 16)), dim3(2 * DK), 0, s,
                                    seg, BH, nseg);
