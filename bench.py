@@ -32,7 +32,9 @@ with seeded output gradients, against the float32 matrix-core peak (its
 products are computed to float32 accuracy).  The large workloads -- the
 training shape B8 H32 T8192 and T = 65536 at H8 in the three gate modes --
 are timed last, each as a whole kda_chunk_fwd call (outside the timed steps),
-with the oracle's rate on a bounded sample of each beside them.
+with the oracle's rate on a bounded sample of each beside them; then
+``backward_train_b8_h32_t8192`` times kda_chunk_bwd at the training shape
+(its workspace holds one group of batch entries).
 """
 from __future__ import annotations
 
@@ -312,6 +314,8 @@ def bench_config(K, torch, dev, name, warmup, reps):
 
 LARGE_LEGS = ("train_b8_h32_t8192", "long_t65536_channel", "long_t65536_scalar",
               "long_t65536_none")
+# gradient legs at full size (the workspace holds one group of batch entries)
+LARGE_BWD_LEGS = ("train_b8_h32_t8192",)
 
 
 def cpu_large_sample():
@@ -339,26 +343,27 @@ def cpu_large_sample():
     return rows
 
 
-def bench_backward(K, torch, dev, warmup, reps):
-    """kda_chunk_bwd on the prefill workload (B1 H16 T4096 d128, chunk 64,
-    bf16 q/k/v and output gradient, bf16 input gradients), HIP events on the
-    launch stream."""
+def bench_backward(K, torch, dev, warmup, reps, name="prefill_h16_t4096"):
+    """kda_chunk_bwd on a named workload (by default the prefill workload, B1
+    H16 T4096 d128; chunk 64, bf16 q/k/v and output gradient, bf16 input
+    gradients), HIP events on the launch stream."""
     from kda_workloads import make_config, make_cotangents
-    w = make_config("prefill_h16_t4096")
+    w = make_config(name)
     cot = make_cotangents(w, seed=0, dhT_std=0.01)
-    t = lambda x, d=torch.float32: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
+    t = lambda x, d=torch.float32: None if x is None else \
+        torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(d)
     bf = torch.bfloat16
     q, k, v, do = t(w.q, bf), t(w.k, bf), t(w.v, bf), t(cot.do, bf)
     g, beta, h0, dhT = t(w.g), t(w.beta), t(w.h0), t(cot.dhT)
     B, T, H, Dk, Dv, C = w.B, w.T, w.H, w.Dk, w.Dv, 64
-    ws = torch.empty(K.kda_chunk_bwd_workspace_size(B, T, H, H, Dk, Dv, C, 0, K.BF16),
+    ws = torch.empty(K.kda_chunk_bwd_workspace_size(B, T, H, H, Dk, Dv, C, w.mode, K.BF16),
                      dtype=torch.uint8, device=dev)
     out = K.kda_chunk_bwd(q, k, v, g, beta, do, initial_state=h0, d_final_state=dhT, chunk=C,
-                          workspace=ws)
+                          mode=w.mode, workspace=ws)
 
     def run():
         K.kda_chunk_bwd(q, k, v, g, beta, do, initial_state=h0, d_final_state=dhT, chunk=C,
-                        workspace=ws, out=out)
+                        mode=w.mode, workspace=ws, out=out)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -371,7 +376,9 @@ def bench_backward(K, torch, dev, warmup, reps):
     sec = a.elapsed_time(b) / reps / 1e3
     flops = backward_flops(B, H, T, Dk, Dv, C)
     nbytes = backward_bytes(B, H, T, Dk, Dv)
-    return {"workload": "gradients of the prefill call: B1 H16 T4096 d128, chunk 64, bf16 "
+    what = ("the prefill call: B1 H16 T4096 d128" if name == "prefill_h16_t4096" else
+            f"{name}: B{B} H{H} T{T} d_k {Dk} d_v {Dv}, {w.mode} gates")
+    res = {"workload": f"gradients of {what}, chunk 64, bf16 "
                         "q/k/v/dO and input gradients, fp32 gates/beta/states",
             "ms": sec * 1e3, "tokens_per_s": B * T / sec,
             "roofline": {"kernel": "kda_chunk_bwd (bwd_prep + bwd_states + bwd_grad)",
@@ -381,6 +388,9 @@ def bench_backward(K, torch, dev, warmup, reps):
                          "algorithmic_flops_per_launch": flops},
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
             "workspace_bytes": int(ws.numel())}
+    del q, k, v, do, g, beta, h0, dhT, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_prologue(K, torch, dev, warmup, reps):
@@ -441,8 +451,11 @@ def main():
                     help="run only kda_chunk_fwd on this named workload (5 timed calls after 2 "
                          "warm-ups) and print its JSON object: profiling runs of one workload")
     ap.add_argument("--backward-only", action="store_true",
-                    help="run only the gradient leg (kda_chunk_bwd on the prefill workload) "
-                         "and print its JSON object: profiling runs of the gradient kernels")
+                    help="run only the gradient leg (kda_chunk_bwd on the prefill workload, or "
+                         "on --backward-workload) and print its JSON object: profiling runs of "
+                         "the gradient kernels")
+    ap.add_argument("--backward-workload", choices=("prefill_h16_t4096",) + LARGE_BWD_LEGS,
+                    default="prefill_h16_t4096")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -464,8 +477,8 @@ def main():
         print(json.dumps({args.only: bench_config(K, torch, dev, args.only, 2, 5)}), flush=True)
         return
     if args.backward_only:
-        print(json.dumps({"backward": bench_backward(K, torch, dev, args.warmup, args.steps)}),
-              flush=True)
+        print(json.dumps({"backward": bench_backward(K, torch, dev, args.warmup, args.steps,
+                                                     args.backward_workload)}), flush=True)
         return
 
     def dev_inputs(w):
@@ -594,6 +607,8 @@ def main():
         out["backward"] = bench_backward(K, torch, dev, args.warmup, reps)
         for name in LARGE_LEGS:
             out[name] = bench_config(K, torch, dev, name, 2, 5)
+        for name in LARGE_BWD_LEGS:
+            out["backward_" + name] = bench_backward(K, torch, dev, 2, 5, name)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
         if not args.no_extra_legs:
