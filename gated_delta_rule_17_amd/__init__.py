@@ -71,6 +71,16 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m gated_delta_rule_17_amd.build`")
+    # The HIP runtime (torch's, which the library binds to) is brought up
+    # before the library registers its code objects: code objects registered
+    # while the runtime is still down fail every launch (hipErrorNoDevice)
+    # once it comes up.  Without a GPU nothing is initialised.
+    try:
+        import torch
+        if torch.cuda.is_available():
+            torch.cuda.init()
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.kda_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i, f, i, i, i, i, vp]

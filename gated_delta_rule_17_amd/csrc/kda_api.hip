@@ -80,6 +80,12 @@ kda_status chunk_fwd_checks(const void* q, const void* k, const void* v, const f
 
 }  // namespace kda
 
+// Launch errors are read with hipGetLastError after each launch.  An error
+// left on this thread by an earlier, unrelated runtime call (one the caller
+// already recovered from) would be read there as well, so it is discarded
+// before the entry point launches anything.
+static inline void discard_stale_error() { (void)hipGetLastError(); }
+
 extern "C" {
 
 const char* kda_status_string(kda_status s)
@@ -112,6 +118,7 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     if (!aligned16(state)) return KDA_ERROR_MISALIGNED;
     kda::RecArgs a{q, k, v, g, beta, state, o, B, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype, nullptr,
                    prologue};
+    discard_stale_error();
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -143,6 +150,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     if (T == 0 && !final_state) return KDA_SUCCESS;
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, B, T, H, Dk, Dv, chunk, Hqk,
                      scale, mode, dtype, o_dtype, workspace, workspace_bytes, nullptr, 0, prologue};
+    discard_stale_error();
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -163,6 +171,7 @@ kda_status kda_recurrent_varlen(const void* q, const void* k, const void* v, con
     if (!aligned16(state) || ((uintptr_t)cu_seqlens & 3u) != 0) return KDA_ERROR_MISALIGNED;
     kda::RecArgs a{q, k, v, g, beta, state, o, N, T, H, Dk, Dv, Hqk, scale, mode, dtype, o_dtype,
                    cu_seqlens, prologue};
+    discard_stale_error();
     hipError_t e = kda::launch_recurrent(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -205,6 +214,7 @@ kda_status kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, con
     if (T == 0 && !final_state) return KDA_SUCCESS;
     kda::ChunkArgs a{q, k, v, g, beta, initial_state, final_state, o, 1, T, H, Dk, Dv, chunk, Hqk,
                      scale, mode, dtype, o_dtype, workspace, workspace_bytes, cu_seqlens, N, prologue};
+    discard_stale_error();
     hipError_t e = kda::launch_chunk(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -254,6 +264,7 @@ kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const floa
     kda::ChunkBwdArgs a{q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
                         d_initial_state, B, T, H, Hqk, Dk, Dv, chunk, scale, mode, dtype,
                         grad_dtype, workspace, workspace_bytes};
+    discard_stale_error();
     hipError_t e = kda::launch_chunk_bwd(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }
@@ -306,6 +317,7 @@ kda_status kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, con
     kda::ChunkBwdArgs a{q, k, v, g, beta, initial_state, d_o, d_final_state, dq, dk, dv, dg, dbeta,
                         d_initial_state, 1, T, H, Hqk, Dk, Dv, chunk, scale, mode, dtype,
                         grad_dtype, workspace, workspace_bytes, cu_seqlens, N};
+    discard_stale_error();
     hipError_t e = kda::launch_chunk_bwd(a, (hipStream_t)stream);
     return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_HIP;
 }

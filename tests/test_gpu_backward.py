@@ -272,6 +272,27 @@ def test_bwd_training_shape_two_batch_entries():
     assert all(e <= TOL["bf16"] for e, _ in worst.values()), worst
 
 
+def test_bwd_batch_groups_with_grouped_heads():
+    """Records over 4 GiB run in groups of whole batch entries: B3 H32 T8192
+    d128 (2 GiB of records per entry) runs as entries {0, 1} and then {2},
+    here with two value heads per query/key head, so the second group's
+    float partials of dq and dk and their sum land at that entry's offsets.
+    The grouped-head gradient oracle runs on entry 2."""
+    w = make_inputs(3, 8192, 32, 128, 128, mode="channel", dtype="bf16", seed=21, h0_std=0.02)
+    q = np.ascontiguousarray(w.q[:, :, ::2])
+    k = np.ascontiguousarray(w.k[:, :, ::2])
+    cot = make_cotangents(w, seed=21, dhT_std=0.05)
+    assert K.kda_chunk_bwd_workspace_size(3, 8192, 32, 16, 128, 128, 64, w.mode, K.BF16) == \
+        K.kda_chunk_bwd_workspace_size(2, 8192, 32, 16, 128, 128, 64, w.mode, K.BF16)
+    say("bwd batch groups, grouped heads, B3 H32 T8192")
+    got = _run(w, cot, 64, q, k)
+    sl = lambda x: None if x is None else np.ascontiguousarray(x[2:3])
+    ref = oracle.recurrent_grouped_bwd(sl(q), sl(k), sl(w.v), sl(w.g), sl(w.beta), sl(w.h0),
+                                       sl(cot.do), sl(cot.dhT), scale=w.scale, mode=w.mode)
+    sub = {n: None if got[n] is None else sl(got[n]) for n in NAMES}
+    _compare("batch groups, grouped heads, entry 2", sub, ref, TOL["bf16"])
+
+
 def test_bwd_full_size_prefill_sampled_heads():
     """The prefill workload at full size (B1 H16 T4096 d128, bf16), in the
     launch configuration the benchmark times; the oracle runs on three of
@@ -387,6 +408,19 @@ def test_bwd_varlen_empty_sequences_pass_the_state_gradient():
     np.testing.assert_array_equal(got["dh0"][0], dhT[0])
     np.testing.assert_array_equal(got["dh0"][2], dhT[2])
     _compare("varlen empty", got, _oracle_varlen(vw, do, dhT), TOL["f32"])
+
+
+def test_bwd_varlen_empty_sequences_matrix_core_carries():
+    """bf16 inputs at d = 64, chunk 64 take the matrix-core carries
+    (bwd_states_mc): an empty sequence there passes its final-state gradient
+    through unchanged, and the others match the oracle."""
+    vw = make_varlen([0, 70, 0, 130], 2, 64, 64, dtype="bf16", seed=10, h0_std=0.05)
+    do, dhT = _varlen_cot(vw, 11, 0.1)
+    say("bwd varlen empty, matrix-core carries")
+    got = _run_varlen(vw, do, dhT, 64)
+    np.testing.assert_array_equal(got["dh0"][0], dhT[0])
+    np.testing.assert_array_equal(got["dh0"][2], dhT[2])
+    _compare("varlen empty bf16 d64", got, _oracle_varlen(vw, do, dhT), TOL["bf16"])
 
 
 def test_bwd_varlen_serving_mix_sampled():
