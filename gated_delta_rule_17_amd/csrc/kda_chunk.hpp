@@ -1478,7 +1478,7 @@ hipError_t launch_state_nt(const ChunkArgs& a, int BH, int NC, size_t nrec, cons
 // compute-unit time; one tile per workgroup gives the most workgroups.  Two
 // tiles are taken once one tile per workgroup would need more workgroups
 // than the device holds at once (the pass then runs in several waves of
-// workgroups anyway).
+// workgroups anyway), and four (bf16 operands) once two would.
 // Segmented (nseg > 1, see seg_count): phase 1, chunk_seg_combine, phase 3,
 // two tiles per workgroup.
 template <int C, int DK, int DV, typename OT>
@@ -1510,6 +1510,12 @@ hipError_t launch_state(const ChunkArgs& a, int BH, int NC, size_t nrec, const i
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             ncu = 256;
+        // four tiles (bf16 operands) once two would still need more than one
+        // workgroup per compute unit
+        if constexpr (std::is_same<OT, bf16_t>::value && DV % 64 == 0) {
+            if ((double)BH * (DV / 32) > (double)ncu)
+                return launch_state_nt<C, DK, DV, OT, 4>(a, BH, NC, nrec, stab, nullptr, 1, NC, 0, s);
+        }
         if ((double)BH * (DV / 16) > (double)ncu)
             return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, nullptr, 1, NC, 0, s);
     }
