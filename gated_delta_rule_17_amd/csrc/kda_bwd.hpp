@@ -59,6 +59,7 @@
 // exp(G_i - G_j) <= 1 pair by pair, in a fixed order.
 #pragma once
 
+#include <atomic>
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -208,6 +209,28 @@ __device__ __forceinline__ ChunkLoc locate_chunk(const Args& a, int rec) {
         l.L = min(C, a.T - l.t0);
     }
     return l;
+}
+
+// Compute units of the current device, queried once per device (256 if the
+// query fails; its error is then cleared so that no later launch check sees it).
+inline int device_cus()
+{
+    constexpr int MAXDEV = 64;
+    static std::atomic<int> cache[MAXDEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        dev = 0;
+    }
+    const int slot = dev < MAXDEV ? dev : MAXDEV - 1;
+    int n = cache[slot].load(std::memory_order_relaxed);
+    if (n > 0 && dev < MAXDEV) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    if (dev < MAXDEV) cache[slot].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // Index of the n-th lower block tile (I, J), J <= I, of an NB x NB grid.
@@ -1141,30 +1164,32 @@ __global__ void __launch_bounds__(256) bwd_states(Args a)
 // with Kr^T E (or P - W^T dE) over the chunk's tokens, E read from LDS.  Two
 // barriers per chunk; the next chunk's operands are requested at the start of
 // each step.
-template <int C, int DK, int DV>
+template <int C, int DK, int DV, int NT2>
 __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
 {
     constexpr int NB = C / 16, KS = DK / 32, KC = C / 32, MH = DK / 16, MHW = MH / 4;
+    constexpr int NCOL = 16 * NT2;              // value columns of one workgroup (NT2 16-column tiles)
     constexpr int SK = DK + 8, SC = C + 8;      // LDS row strides (bf16 elements)
     constexpr int PL = C * DK;                  // elements per bf16 plane of a record operand
     static_assert(DK % 64 == 0 && DK <= 128 && C % 32 == 0, "whole fragments for every wave, at most two state tiles");
-    __shared__ __align__(16) bf16_t HTs[2 * 16 * SK];   // state^T [column][channel], hi and lo
-    __shared__ __align__(16) bf16_t ETs[2 * 16 * SC];   // E^T [column][token], hi and lo
-    const PArr<bf16_t> HT{HTs, HTs + 16 * SK};
-    const PArr<bf16_t> ET{ETs, ETs + 16 * SC};
+    static_assert(DV % NCOL == 0, "whole tiles per workgroup");
+    __shared__ __align__(16) bf16_t HTs[2 * NCOL * SK];   // state^T [column][channel], hi and lo
+    __shared__ __align__(16) bf16_t ETs[2 * NCOL * SC];   // E^T [column][token], hi and lo
+    const PArr<bf16_t> HT{HTs, HTs + NCOL * SK};
+    const PArr<bf16_t> ET{ETs, ETs + NCOL * SC};
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
     const int units = (a.stab ? a.N : a.B) * a.H;
-    // XCD-aware: the DV / 16 value tiles of one (role, head) take ids 8
+    // XCD-aware: the DV / NCOL workgroups of one (role, head) take ids 8
     // apart, so they share an XCD and its L2, which serves their common records
-    constexpr int NVT = DV / 16;
+    constexpr int NVT = DV / NCOL;
     const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
     const int ur = (slot / NVT) * 8 + xcd, vt = slot % NVT;
     if (ur >= 2 * units) return;
     const bool reverse = ur >= units;
     const int u = reverse ? ur - units : ur;
-    const int v0 = vt * 16;
+    const int v0 = vt * NCOL;
     const size_t DD = (size_t)DK * DV;
     int NC;
     size_t rbase;
@@ -1179,17 +1204,22 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
     const bool has_t = w < NB;                  // this wave owns a token tile
     const int we = has_t ? w : NB - 1;
 
-    // the state strip: accumulator s holds rows 16 (w + 4 s) + 4 g + 0..3 of column v0 + r
-    f32x4 hacc[MHW];
+    // the state strip: accumulator [s][n] holds rows 16 (w + 4 s) + 4 g + 0..3
+    // of column v0 + 16 n + r
+    f32x4 hacc[MHW][NT2];
     {
         const float* init = reverse ? a.dhT : a.h0;
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = w + 4 * s;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                hacc[s][e] = init ? init[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + r] : 0.f;
-            store4_p(HT, r * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s]);
+            for (int n = 0; n < NT2; ++n) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hacc[s][n][e] = init ? init[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + 16 * n + r]
+                                         : 0.f;
+                store4_p(HT, (16 * n + r) * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s][n]);
+            }
         }
     }
     __syncthreads();
@@ -1200,16 +1230,19 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
     float* const recb = reverse ? a.r.dH : a.r.Hs;
     float* const erb = reverse ? a.r.dE : a.r.E;
 
+    // operands of one chunk step: the fragments and the gate row are shared
+    // by the workgroup's tiles, U (or Ut) and P are per tile
     struct Ops {
         PFrag<bf16_t> a1[KS];
         PFrag<bf16_t> a2[MHW][KC];
-        f32x4 add;
-        f32x4 p[MHW];
+        f32x4 add[NT2];
+        f32x4 p[MHW][NT2];
         float gl;        // G_last of one channel of this lane's row (see oGl1)
     };
     // Record fields are addressed as a uniform record base plus per-lane
     // 32-bit byte offsets fixed for the whole pass, so that every load takes
-    // its address from scalar registers and one loop-invariant vector offset.
+    // its address from scalar registers and one loop-invariant vector offset
+    // (tile n of a workgroup adds a constant).
     const char* const wsb = reinterpret_cast<const char*>(a.r.G);
     const uint32_t fA1 = (uint32_t)(reinterpret_cast<const char*>(A1b) - wsb);
     const uint32_t fA2 = (uint32_t)(reinterpret_cast<const char*>(A2b) - wsb);
@@ -1233,7 +1266,8 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
         const char* const base = wsb + (rbase + (size_t)ch) * a.r.rs * sizeof(float);
         const __amdgpu_buffer_rsrc_t rb = record_rsrc(base);
         const __amdgpu_buffer_rsrc_t rp = record_rsrc(base, pbytes);
-        o.add = bload<f32x4>(rb, oAdd, 0);
+#pragma unroll
+        for (int n = 0; n < NT2; ++n) o.add[n] = bload<f32x4>(rb, oAdd, 64 * C * n);
         o.gl = bload1(rb, oGl1, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -1243,7 +1277,8 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             // state tile w + 4 s: 64 channels further on
-            o.p[s] = bload<f32x4>(rp, oP, 256 * s);
+#pragma unroll
+            for (int n = 0; n < NT2; ++n) o.p[s][n] = bload<f32x4>(rp, oP, 256 * s + 64 * DK * n);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 o.a2[s][kc].h.v = bload<u16x8>(rb, oA2, 1024 * (4 * s * KC + kc));
@@ -1252,24 +1287,43 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
         }
     };
     auto chunk_of = [&](int n) { return reverse ? max(NC - 1 - n, 0) : min(n, NC - 1); };
+    // one tile: three operand sets in rotation, a chunk's operands requested
+    // two steps before their use; two tiles: two sets, one step ahead (a
+    // third does not fit the registers)
+    constexpr int AHEAD = NT2 == 1 ? 2 : 1;
 
     auto step = [&](const Ops& P, Ops& Q, int n) {
         char* const rb = const_cast<char*>(wsb) + (rbase + (size_t)chunk_of(n)) * a.r.rs * sizeof(float);
-        load_ops(Q, chunk_of(n + 2));
+        load_ops(Q, chunk_of(n + AHEAD));
         // the state entering the chunk (forward) or the gradient leaving it (reverse)
 #pragma unroll
-        for (int s = 0; s < MHW; ++s) *reinterpret_cast<f32x4*>(rb + oRec + 256u * s) = hacc[s];
+        for (int s = 0; s < MHW; ++s) {
+#pragma unroll
+            for (int t = 0; t < NT2; ++t)
+                *reinterpret_cast<f32x4*>(rb + oRec + 256u * s + 64u * DK * t) = hacc[s][t];
+        }
         if (has_t) {
-            f32x4 ea = zero4(), eb = zero4();
+            f32x4 ea[NT2], eb[NT2];
+#pragma unroll
+            for (int t = 0; t < NT2; ++t) {
+                ea[t] = zero4();
+                eb[t] = zero4();
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const PFrag<bf16_t> hf = HT.frag(r * SK + 32 * ks + 8 * g);
-                if (ks & 1) eb = mma3(P.a1[ks], hf, eb);
-                else ea = mma3(P.a1[ks], hf, ea);
+#pragma unroll
+                for (int t = 0; t < NT2; ++t) {
+                    const PFrag<bf16_t> hf = HT.frag((16 * t + r) * SK + 32 * ks + 8 * g);
+                    if (ks & 1) eb[t] = mma3(P.a1[ks], hf, eb[t]);
+                    else ea[t] = mma3(P.a1[ks], hf, ea[t]);
+                }
             }
-            const f32x4 e = reverse ? P.add + (ea + eb) : P.add - (ea + eb);
-            store4_p(ET, r * SC + 32 * (we >> 1) + mc_pos(16 * (we & 1) + 4 * g), e);
-            *reinterpret_cast<f32x4*>(rb + oE) = e;
+#pragma unroll
+            for (int t = 0; t < NT2; ++t) {
+                const f32x4 e = reverse ? P.add[t] + (ea[t] + eb[t]) : P.add[t] - (ea[t] + eb[t]);
+                store4_p(ET, (16 * t + r) * SC + 32 * (we >> 1) + mc_pos(16 * (we & 1) + 4 * g), e);
+                *reinterpret_cast<f32x4*>(rb + oE + 64u * C * t) = e;
+            }
         }
         lds_barrier();
         float gm[MHW][4];
@@ -1285,42 +1339,54 @@ __global__ void __launch_bounds__(256) bwd_states_mc(Args a)
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = w + 4 * s;
-            f32x4 xa = zero4(), xb = zero4();
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const PFrag<bf16_t> ef = ET.frag(r * SC + 32 * kc + 8 * g);
-                if (kc & 1) xb = mma3(P.a2[s][kc], ef, xb);
-                else xa = mma3(P.a2[s][kc], ef, xa);
-            }
-            const f32x4 x = xa + xb;
+            for (int t = 0; t < NT2; ++t) {
+                f32x4 xa = zero4(), xb = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hacc[s][e] = gm[s][e] * hacc[s][e] + P.p[s][e] + (reverse ? -x[e] : x[e]);
+                for (int kc = 0; kc < KC; ++kc) {
+                    const PFrag<bf16_t> ef = ET.frag((16 * t + r) * SC + 32 * kc + 8 * g);
+                    if (kc & 1) xb = mma3(P.a2[s][kc], ef, xb);
+                    else xa = mma3(P.a2[s][kc], ef, xa);
+                }
+                const f32x4 x = xa + xb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hacc[s][t][e] = gm[s][e] * hacc[s][t][e] + P.p[s][t][e] + (reverse ? -x[e] : x[e]);
+                store4_p(HT, (16 * t + r) * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s][t]);
             }
-            store4_p(HT, r * SK + 32 * (mt >> 1) + mc_pos(16 * (mt & 1) + 4 * g), hacc[s]);
         }
         lds_barrier();
     };
 
-    // three operand sets in rotation: a chunk's operands are requested two
-    // steps before their use
-    Ops bufA, bufB, bufC;
-    if (NC > 0) {
-        load_ops(bufA, chunk_of(0));
-        load_ops(bufB, chunk_of(1));
-    }
-    for (int n = 0; n < NC; n += 3) {
-        step(bufA, bufC, n);
-        if (n + 1 < NC) step(bufB, bufA, n + 1);
-        if (n + 2 < NC) step(bufC, bufB, n + 2);
+    if constexpr (NT2 == 1) {
+        Ops bufA, bufB, bufC;
+        if (NC > 0) {
+            load_ops(bufA, chunk_of(0));
+            load_ops(bufB, chunk_of(1));
+        }
+        for (int n = 0; n < NC; n += 3) {
+            step(bufA, bufC, n);
+            if (n + 1 < NC) step(bufB, bufA, n + 1);
+            if (n + 2 < NC) step(bufC, bufB, n + 2);
+        }
+    } else {
+        Ops bufA, bufB;
+        if (NC > 0) load_ops(bufA, chunk_of(0));
+        for (int n = 0; n < NC; n += 2) {
+            step(bufA, bufB, n);
+            if (n + 1 < NC) step(bufB, bufA, n + 1);
+        }
     }
     if (reverse && a.dh0) {
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = w + 4 * s;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                a.dh0[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + r] = hacc[s][e];
+            for (int t = 0; t < NT2; ++t) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    a.dh0[(size_t)u * DD + (size_t)(16 * mt + 4 * g + e) * DV + v0 + 16 * t + r] = hacc[s][t][e];
+            }
         }
     }
 }
@@ -2109,9 +2175,16 @@ hipError_t launch3(const Args& a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     const unsigned ur8 = (unsigned)((2 * units + 7) / 8) * 8;
-    if constexpr (prep_split<C, DK, DV, IO>())
-        hipLaunchKernelGGL((bwd_states_mc<C, DK, DV>), dim3(ur8 * (DV / 16)), dim3(256), 0, s, a);
-    else
+    if constexpr (prep_split<C, DK, DV, IO>()) {
+        // two value tiles per workgroup once one-tile workgroups would
+        // outnumber the compute units (the records of a step are then loaded
+        // once for both tiles)
+        if (DV % 32 == 0 && (double)ur8 * (DV / 16) > (double)device_cus())
+            hipLaunchKernelGGL((bwd_states_mc<C, DK, DV, DV % 32 == 0 ? 2 : 1>), dim3(ur8 * (DV / (DV % 32 == 0 ? 32 : 16))),
+                               dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_states_mc<C, DK, DV, 1>), dim3(ur8 * (DV / 16)), dim3(256), 0, s, a);
+    } else
         hipLaunchKernelGGL((bwd_states<C, DK, DV, IO>), dim3(ur8 * (DV / 16)),
                            dim3(64 * StateShape<C, DK>::NWS), 0, s, a);
     hipError_t e = hipGetLastError();
