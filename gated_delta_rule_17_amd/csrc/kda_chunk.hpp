@@ -928,7 +928,7 @@ chunk_prepare(const OT* __restrict__ q, const OT* __restrict__ k, const OT* __re
 // H published), so the output work and its operand loads run beside the
 // chain on the same SIMDs instead of in series with it.
 // ---------------------------------------------------------------------------
-template <int C, int DK, int DV, typename OT, typename OUT, int NT2>
+template <int C, int DK, int DV, typename OT, typename OUT, int NT2, bool C8>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             int T, int H, int BH, int NC, const void* ws, size_t nrec, const int4* __restrict__ stab,
@@ -949,8 +949,13 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     // bf16 operands with one tile: three operand sets in rotation (a chunk's
     // operands are requested two steps ahead); otherwise two (a third does not
     // fit the registers)
-    constexpr bool THREE = S::SPLIT && NT2 == 1;
+    // C8 (chains alone, no outputs: phase 1 of the segmented pass): all eight
+    // waves are chain waves, in two groups of four that each carry half of
+    // the workgroup's tiles, so two chains share every SIMD instead of one
+    constexpr int NTW = C8 ? NT2 / 2 : NT2;   // 16-column tiles per chain wave
+    constexpr bool THREE = S::SPLIT && NTW == 1;
     static_assert(DV % NCOL == 0, "whole tiles per workgroup");
+    static_assert(!C8 || NT2 % 2 == 0, "two groups of whole tiles");
 
     __shared__ __align__(16) OT HTs[NP * NCOL * SK];   // H^T [n][c] (precise operand)
     __shared__ __align__(16) OT ETs[NP * NCOL * SC];   // E^T [n][j] (precise operand)
@@ -967,30 +972,33 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     // sets of nseg states [BH, DK, DV]: the true states entering the
     // segments, the segments' final states from a zero state, and the
     // segments' transition matrices):
-    // phase 1: segment 0 runs role 0 from h0 and leaves its final state as
-    //   the state entering segment 1; every later segment runs role 1 (state
-    //   from zero, no outputs) in its first NCT workgroups and role 2 (the
-    //   transition matrix: the same chain from the identity, with U = 0, no
-    //   outputs) in the next NCT;
-    // phase 3: segments 1 .. nseg-1 run role 0 from their true entering
-    //   states (chunk_seg_combine forms them in between); the last one
-    //   writes hT.
+    // phase 1 (no outputs: every workgroup of this pass is a chain alone):
+    //   segment 0 runs role 1 from h0, keeps h0 as the state entering segment
+    //   0 and leaves its final state as the state entering segment 1; every
+    //   later segment runs role 1 from a zero state in its first NCT
+    //   workgroups and role 2 (the transition matrix: the same chain from
+    //   the identity, with U = 0) in the next NCT;
+    // phase 3: every segment runs role 0 (outputs) from its true entering
+    //   state (chunk_seg_combine forms those of segments 2 .. nseg-1 in
+    //   between); the last one writes hT.  h0 itself is not read here, so a
+    //   final state written over the initial one is safe.
     const int id = blockIdx.x;
     const int xcd = id & 7, slot = id >> 3;
     const int G = phase == 1 ? 2 * NCT : NCT;
-    const int nsl = phase == 1 ? nseg : (phase == 3 ? nseg - 1 : 1);
+    const int nsl = phase == 0 ? 1 : nseg;
     const int grp = (slot / G) * 8 + xcd;
     const int wg = slot % G;
     const int bh = grp / nsl;
     if (bh >= BH) return;
-    const int segi = grp - bh * nsl + (phase == 3 ? 1 : 0);
+    const int segi = grp - bh * nsl;
     int role = 0;
+    if (C8 && phase != 1) return;      // (not launched that way)
     if (phase == 1) {
         if (wg >= NCT) {
             if (segi == 0) return;
             role = 2;
         } else {
-            role = segi == 0 ? 0 : 1;
+            role = 1;
         }
     }
     const int ct = wg % NCT;
@@ -1000,7 +1008,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const float* h0p = h0;
     float* hTp = hT;
     if (phase == 1) {
-        if (role == 0) {
+        if (segi == 0) {
             hTp = seg + SS;                    // the state entering segment 1
         } else {
             h0p = nullptr;
@@ -1039,7 +1047,8 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, gq = lane >> 4;
-    const bool chain = wave < 4;
+    const bool chain = C8 || wave < 4;
+    const int tb = C8 ? (wave >> 2) * NTW : 0;             // first tile of this wave's group
     const int wr = wave & 3;                               // index within the role
     const int we = ALLE ? wr : (wr < NB ? wr : NB - 1);    // token tile of E / o
     const bool has_t = ALLE || wr < NB;
@@ -1052,23 +1061,28 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     auto rec_of = [&](int cidx) { return recbase + (size_t)(c0 + cidx) * recstride; };
 
     if (chain) {
-        f32x4 hacc[MHW][NT2];
+        f32x4 hacc[MHW][NTW];
 #pragma unroll
         for (int s = 0; s < MHW; ++s) {
             const int mt = wr + 4 * s;
 #pragma unroll
-            for (int n = 0; n < NT2; ++n) {
+            for (int n = 0; n < NTW; ++n) {
                 hacc[s][n] = zero4();
                 if (mt < MH && role == 2) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        hacc[s][n][u] = (16 * mt + 4 * gq + u == n0 + 16 * n + r) ? 1.f : 0.f;
+                        hacc[s][n][u] = (16 * mt + 4 * gq + u == n0 + 16 * (tb + n) + r) ? 1.f : 0.f;
                 } else if (mt < MH && h0p) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        hacc[s][n][u] = h0p[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r];
+                        hacc[s][n][u] = h0p[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * (tb + n) + r];
                 }
-                if (mt < MH) store4_p(HT, (16 * n + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
+                if (mt < MH && phase == 1 && segi == 0) {   // the state entering segment 0, for phase 3
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        seg[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * (tb + n) + r] = hacc[s][n][u];
+                }
+                if (mt < MH) store4_p(HT, (16 * (tb + n) + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
             }
         }
         __syncthreads();
@@ -1081,7 +1095,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
         struct Ops {
             Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
             PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
-            f32x4 u[NT2];            // U^T init of E
+            f32x4 u[NTW];            // U^T init of E
             f32x4 gl[MHW];           // exp(G_last) for the state rows
         };
         auto mt_of = [&](int s) { return ALLH ? wr + 4 * s : min(wr + 4 * s, MH - 1); };
@@ -1090,8 +1104,8 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
 #pragma unroll
-            for (int n = 0; n < NT2; ++n)
-                P.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + n, we, NB, lane));
+            for (int n = 0; n < NTW; ++n)
+                P.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + tb + n, we, NB, lane));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) P.wn[ks].load(wn + fragbase(we, ks, KS, lane));
 #pragma unroll
@@ -1117,11 +1131,11 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             const OT* wn = W.wneg_rec(rec);
             const PArr<OT> kr = W.krt(rec);
 #pragma unroll
-            for (int n = 0; n < NT2; ++n)
-                Q.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + n, we, NB, lane));
-            f32x4 ea[NT2], eb[NT2];
+            for (int n = 0; n < NTW; ++n)
+                Q.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + tb + n, we, NB, lane));
+            f32x4 ea[NTW], eb[NTW];
 #pragma unroll
-            for (int n = 0; n < NT2; ++n) {
+            for (int n = 0; n < NTW; ++n) {
                 ea[n] = role == 2 ? zero4() : P.u[n];   // the transition matrix has no U term
                 eb[n] = zero4();
             }
@@ -1130,8 +1144,8 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 Q.wn[ks].load(wn + fragbase(we, ks, KS, lane));
                 if (has_t) {
 #pragma unroll
-                    for (int n = 0; n < NT2; ++n) {
-                        const PFrag<OT> hf = HT.frag((16 * n + r) * SK + 32 * ks + 8 * gq);
+                    for (int n = 0; n < NTW; ++n) {
+                        const PFrag<OT> hf = HT.frag((16 * (tb + n) + r) * SK + 32 * ks + 8 * gq);
                         if (ks & 1) eb[n] = mma2(P.wn[ks], hf, eb[n]);
                         else ea[n] = mma2(P.wn[ks], hf, ea[n]);
                     }
@@ -1139,22 +1153,22 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
             if (has_t) {
 #pragma unroll
-                for (int n = 0; n < NT2; ++n)
-                    store4_p(ET, (16 * n + r) * SC + 16 * wr + 4 * gq, ea[n] + eb[n]);
+                for (int n = 0; n < NTW; ++n)
+                    store4_p(ET, (16 * (tb + n) + r) * SC + 16 * wr + 4 * gq, ea[n] + eb[n]);
             }
 #pragma unroll
             for (int g2 = 0; g2 < KS; ++g2) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NT2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, NT2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, NTW, 0);
             __syncthreads();
             // H = Diag(gl) H + Kr^T E
-            f32x4 part[MHW][NT2];
+            f32x4 part[MHW][NTW];
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
 #pragma unroll
-                for (int n = 0; n < NT2; ++n) {
+                for (int n = 0; n < NTW; ++n) {
                     if (ALLH || wr + 4 * s < MH) hacc[s][n] *= P.gl[s];
                     part[s][n] = zero4();
                 }
@@ -1162,15 +1176,15 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             }
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
-                PFrag<OT> et[NT2];
+                PFrag<OT> et[NTW];
 #pragma unroll
-                for (int n = 0; n < NT2; ++n) et[n] = ET.frag((16 * n + r) * SC + 32 * ks + 8 * gq);
+                for (int n = 0; n < NTW; ++n) et[n] = ET.frag((16 * (tb + n) + r) * SC + 32 * ks + 8 * gq);
 #pragma unroll
                 for (int s = 0; s < MHW; ++s) {
                     Q.kr[s][ks] = kr.frag(fragbase(mt_of(s), ks, KC, lane));
                     if (ALLH || wr + 4 * s < MH) {
 #pragma unroll
-                        for (int n = 0; n < NT2; ++n) {
+                        for (int n = 0; n < NTW; ++n) {
                             if (ks & 1) part[s][n] = mma3(P.kr[s][ks], et[n], part[s][n]);
                             else hacc[s][n] = mma3(P.kr[s][ks], et[n], hacc[s][n]);
                         }
@@ -1182,9 +1196,9 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 const int mt = wr + 4 * s;
                 if (ALLH || mt < MH) {
 #pragma unroll
-                    for (int n = 0; n < NT2; ++n) {
+                    for (int n = 0; n < NTW; ++n) {
                         hacc[s][n] += part[s][n];
-                        store4_p(HT, (16 * n + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
+                        store4_p(HT, (16 * (tb + n) + r) * SK + 16 * mt + 4 * gq, hacc[s][n]);
                     }
                 }
             }
@@ -1216,10 +1230,10 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 const int mt = wr + 4 * s;
                 if (mt < MH) {
 #pragma unroll
-                    for (int n = 0; n < NT2; ++n) {
+                    for (int n = 0; n < NTW; ++n) {
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            hTp[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * n + r] = hacc[s][n][u];
+                            hTp[((size_t)bh * DK + 16 * mt + 4 * gq + u) * DV + n0 + 16 * (tb + n) + r] = hacc[s][n][u];
                     }
                 }
             }
@@ -1323,57 +1337,76 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 //   H_{s+1} = M_s H_s + Z_s,   s = 1 .. nseg - 2,
 // from H_1 (left by segment 0) with the segments' transition matrices M_s and
 // their final states from zero Z_s (the chunk carry is affine in the state
-// it starts from).  One workgroup per (sequence-head, 16 value columns);
-// float32 on the vector units.
+// it starts from).  One workgroup per (sequence-head, 16 value columns), one
+// wave per 16 rows of the state, float32 products on the matrix cores
+// (v_mfma_f32_16x16x4_f32: exact float32 products, float32 sums).
 template <int DK, int DV>
-__global__ void __launch_bounds__(2 * DK) chunk_seg_combine(float* seg, int BH, int nseg)
+__global__ void __launch_bounds__(4 * DK) chunk_seg_combine(float* seg, int BH, int nseg)
 {
-    // thread t: row i = t / 2 of the 16-column tile, columns 8 (t % 2) .. + 7;
-    // the state tile sits in LDS, row i of M_s streams in as 16-byte loads
-    // (the next segment's row is requested before this segment's sums)
-    constexpr int NCT = DV / 16;
-    __shared__ __align__(16) float Hs[DK][16];
+    static_assert(DK == DV, "square transition matrices");
+    // Wave t forms rows 16t .. 16t+15 of the new state tile.  Lane (r, g)
+    // holds them as an accumulator (rows 16t + 4g + u, column r) and, for
+    // the product, supplies M_s[16t + r][k] and H_s[k][r] for the keys
+    // k = KQ*g .. KQ*g + KQ-1, one per 16x16x4 step (any fixed assignment of
+    // the keys to the steps gives the same sum).  The state tile sits in LDS
+    // transposed ([column][row]), in two buffers used in turn, so that one
+    // barrier per segment suffices.  The next segment's operands (this
+    // lane's keys of its row of M, and its Z entries) are requested before
+    // this segment's products, into the other of two register sets, from a
+    // clamped (always valid) segment index.
+    constexpr int D = DK, NCT = DV / 16, KQ = D / 4, SH = D + 4;
+    __shared__ __align__(16) float HsT[2][16 * SH];
     const int bh = blockIdx.x / NCT, ct = blockIdx.x % NCT;
     if (bh >= BH) return;
-    const size_t SS = (size_t)BH * DK * DV;
-    const int tid = threadIdx.x, i = tid >> 1, c8 = 8 * (tid & 1);
-    const size_t base = (size_t)bh * DK * DV;
-    const size_t hoff = base + (size_t)i * DV + 16 * ct + c8;
+    const size_t SS = (size_t)BH * D * DV;
+    const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6, r = lane & 15, g = lane >> 4;
+    const size_t base = (size_t)bh * D * DV;
+    const int row0 = 16 * t + 4 * g;                              // this lane's accumulator rows
+    const size_t ooff = base + (size_t)row0 * DV + 16 * ct + r;   // (row0, column r) of a state
     {
-        const f32x4* h1 = reinterpret_cast<const f32x4*>(seg + SS + hoff);
-        *reinterpret_cast<f32x4*>(&Hs[i][c8]) = h1[0];
-        *reinterpret_cast<f32x4*>(&Hs[i][c8 + 4]) = h1[1];
+        f32x4 h;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = seg[SS + ooff + (size_t)u * DV];
+        *reinterpret_cast<f32x4*>(&HsT[0][r * SH + row0]) = h;
     }
-    __syncthreads();
-    f32x4 m[DK / 4];
-    auto load_row = [&](int s2) {
-        const f32x4* M = reinterpret_cast<const f32x4*>(seg + ((size_t)2 * nseg + s2) * SS + base +
-                                                        (size_t)i * DV);
-#pragma unroll
-        for (int k4 = 0; k4 < DK / 4; ++k4) m[k4] = M[k4];
+    struct Ops {
+        f32x4 m[KQ / 4];   // M_s[16t + r][KQ*g ..]
+        f32x4 z;           // Z_s[row0 + u][column r]
     };
-    if (nseg > 2) load_row(1);
-    for (int s2 = 1; s2 + 1 < nseg; ++s2) {
-        const f32x4* Z = reinterpret_cast<const f32x4*>(seg + ((size_t)nseg + s2) * SS + hoff);
-        f32x4 a0 = Z[0], a1 = Z[1];
+    const int last = nseg - 2;     // the last segment whose map is applied
+    auto load = [&](Ops& P, int s2) {
+        const f32x4* M = reinterpret_cast<const f32x4*>(seg + ((size_t)2 * nseg + s2) * SS + base +
+                                                        (size_t)(16 * t + r) * DV + KQ * g);
 #pragma unroll
-        for (int k4 = 0; k4 < DK / 4; ++k4) {
+        for (int j = 0; j < KQ / 4; ++j) P.m[j] = M[j];
+        const float* Z = seg + ((size_t)nseg + s2) * SS + ooff;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const f32x4 h0v = *reinterpret_cast<const f32x4*>(&Hs[4 * k4 + e][c8]);
-                const f32x4 h1v = *reinterpret_cast<const f32x4*>(&Hs[4 * k4 + e][c8 + 4]);
-                a0 += m[k4][e] * h0v;
-                a1 += m[k4][e] * h1v;
-            }
+        for (int u = 0; u < 4; ++u) P.z[u] = Z[(size_t)u * DV];
+    };
+    auto step = [&](const Ops& P, Ops& Q, int s2, int buf) {
+        load(Q, min(s2 + 1, last));
+        const float* hb = &HsT[buf][r * SH + KQ * g];
+        f32x4 acc[4] = {P.z, zero4(), zero4(), zero4()};   // four independent chains
+#pragma unroll
+        for (int j = 0; j < KQ / 4; ++j) {
+            const f32x4 hv = *reinterpret_cast<const f32x4*>(hb + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = mma4(P.m[j][e], hv[e], acc[e]);
         }
-        if (s2 + 2 < nseg) load_row(s2 + 1);
+        const f32x4 hn = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        *reinterpret_cast<f32x4*>(&HsT[buf ^ 1][r * SH + row0]) = hn;
+        float* out = seg + (size_t)(s2 + 1) * SS + ooff;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) out[(size_t)u * DV] = hn[u];
         __syncthreads();
-        *reinterpret_cast<f32x4*>(&Hs[i][c8]) = a0;
-        *reinterpret_cast<f32x4*>(&Hs[i][c8 + 4]) = a1;
-        f32x4* out = reinterpret_cast<f32x4*>(seg + (size_t)(s2 + 1) * SS + hoff);
-        out[0] = a0;
-        out[1] = a1;
-        __syncthreads();
+    };
+    if (last < 1) return;
+    Ops A, B;
+    load(A, 1);
+    __syncthreads();               // H_1 in LDS
+    for (int s2 = 1; s2 <= last; s2 += 2) {
+        step(A, B, s2, 0);
+        if (s2 + 1 <= last) step(B, A, s2 + 1, 1);
     }
 }
 
@@ -1452,21 +1485,21 @@ constexpr bool chunk_shape_fits()
 // workgroups.  Two tiles are taken once one tile per workgroup would need
 // more workgroups than the device holds at once (the pass then runs in
 // several waves of workgroups anyway).
-template <int C, int DK, int DV, typename OT, int NT2>
+template <int C, int DK, int DV, typename OT, int NT2, bool C8 = false>
 hipError_t launch_state_nt(const ChunkArgs& a, int BH, int NC, size_t nrec, const int4* stab,
                            float* seg, int nseg, int seglen, int phase, hipStream_t s)
 {
     constexpr int NCT = DV / (16 * NT2);
-    const int nsl = phase == 1 ? nseg : (phase == 3 ? nseg - 1 : 1);
+    const int nsl = phase == 0 ? 1 : nseg;
     const int G = phase == 1 ? 2 * NCT : NCT;
     const long groups = ((long)BH * nsl + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * G));
     if (a.o_dtype == KDA_F32)
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float, NT2>), grid, dim3(512), 0, s,
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, float, NT2, C8>), grid, dim3(512), 0, s,
                            a.h0, a.hT, (float*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab,
                            seg, nseg, seglen, phase);
     else
-        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t, NT2>), grid, dim3(512), 0, s,
+        hipLaunchKernelGGL((chunk_state<C, DK, DV, OT, bf16_t, NT2, C8>), grid, dim3(512), 0, s,
                            a.h0, a.hT, (bf16_t*)a.o, a.T, a.H, BH, NC, (const void*)a.ws, nrec, stab,
                            seg, nseg, seglen, phase);
     return hipGetLastError();
@@ -1491,14 +1524,15 @@ hipError_t launch_state(const ChunkArgs& a, int BH, int NC, size_t nrec, const i
                 const int seglen = (NC + nseg - 1) / nseg;
                 // phase 1 runs two chains per later segment (its zero-state
                 // part and its transition matrix): four tiles per workgroup
-                // (bf16 operands) keep it to one workgroup per compute unit
+                // (bf16 operands) keep it to one workgroup per compute unit;
+                // it has no outputs, so all eight waves carry chains
                 hipError_t e;
                 if constexpr (std::is_same<OT, bf16_t>::value && DV % 64 == 0)
-                    e = launch_state_nt<C, DK, DV, OT, 4>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
+                    e = launch_state_nt<C, DK, DV, OT, 4, true>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
                 else
-                    e = launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
+                    e = launch_state_nt<C, DK, DV, OT, 2, true>(a, BH, NC, nrec, stab, seg, nseg, seglen, 1, s);
                 if (e != hipSuccess) return e;
-                hipLaunchKernelGGL((chunk_seg_combine<DK, DV>), dim3(BH * (DV / 16)), dim3(2 * DK), 0, s,
+                hipLaunchKernelGGL((chunk_seg_combine<DK, DV>), dim3(BH * (DV / 16)), dim3(4 * DK), 0, s,
                                    seg, BH, nseg);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 return launch_state_nt<C, DK, DV, OT, 2>(a, BH, NC, nrec, stab, seg, nseg, seglen,
