@@ -107,6 +107,39 @@ def test_segmented_long_sequence_f32(mode, chunk):
     _check(w, o, hT, TOL["f32"])
 
 
+@pytest.mark.parametrize("D", [32, 64])
+def test_segmented_bf16_narrow_dims(D):
+    """Segmented state pass with bf16 operands at d_k = d_v = 32 (phase 1 with
+    two tiles per workgroup, one per wave group, three operand sets in
+    rotation) and 64 (four tiles, two per wave group, two state tiles per
+    workgroup): B1 H2 T16413 (8 segments, a ragged last chunk), every head."""
+    T = 256 * 64 + 29
+    w = make_inputs(1, T, 2, D, D, dtype="bf16", seed=900 + D, h0_std=0.1, gate_shift=-1.0)
+    say("segmented bf16", D, T)
+    o, hT = run_chunk(w, chunk=64)
+    _check_every_head(w, o, hT, TOL["bf16"])
+
+
+@pytest.mark.parametrize("H,nseg", [(100, 2), (70, 3), (60, 4)])
+def test_segment_counts_f32(H, nseg):
+    """Two, three and four segments per sequence (the segment count follows
+    the number of heads: B1, d 32, chunk 16, 257 chunks): with two segments
+    the combine has no map to apply, with three exactly one.  f32 at 1e-4,
+    every head."""
+    T = 256 * 16 + 5
+    # the library's rule: up to 8 segments, 256 // (B*H*Dv/32) of them, each of
+    # at least 32 chunks, once a sequence has 256 chunks (d_k = d_v >= 32)
+    nc = (T + 15) // 16
+    s = min(8, 256 // H)
+    while s > 1 and nc < 32 * s:
+        s -= 1
+    assert nc >= 256 and s == nseg
+    w = make_inputs(1, T, H, 32, 32, dtype="f32", seed=H, h0_std=0.3)
+    say("segment counts f32", H, nseg)
+    o, hT = run_chunk(w, chunk=16)
+    _check_every_head(w, o, hT, TOL["f32"])
+
+
 def test_segmented_in_place_state_bf16():
     """Segmented state pass (B1 H3 T20000 d128 bf16), the final state written
     over the initial one; every head compared."""
