@@ -91,6 +91,17 @@ def test_long_prefill_every_head(name):
     _check_every_head(w, o, hT, TOL["bf16"])
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_long_prefill_ungated_more_seeds(seed):
+    """The tightest large case, T = 65536 without a gate (nothing decays the
+    rounding of the plain-bf16 operands over 1024 chunks), on three more
+    seeds; all 8 heads compared."""
+    w = make_config("long_t65536_none", seed=seed)
+    say("long_t65536_none seed", seed)
+    o, hT = run_chunk(w)
+    _check_every_head(w, o, hT, TOL["bf16"])
+
+
 @pytest.mark.parametrize("mode", ["channel", "scalar", "none"])
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_segmented_long_sequence_f32(mode, chunk):
