@@ -946,13 +946,13 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
     constexpr int KS = DKP / 32, KC = CP / 32;
     constexpr bool ALLE = NB >= 4;        // every wave of a role owns a token tile
     constexpr bool ALLH = (MH % 4) == 0;  // every chain wave owns MHW state tiles
-    // bf16 operands with one tile: three operand sets in rotation (a chunk's
-    // operands are requested two steps ahead); otherwise two (a third does not
-    // fit the registers)
     // C8 (chains alone, no outputs: phase 1 of the segmented pass): all eight
     // waves are chain waves, in two groups of four that each carry half of
     // the workgroup's tiles, so two chains share every SIMD instead of one
     constexpr int NTW = C8 ? NT2 / 2 : NT2;   // 16-column tiles per chain wave
+    // bf16 operands with one tile per wave: three operand sets in rotation (a
+    // chunk's operands are requested two steps ahead); otherwise two (with two
+    // tiles a third fits the registers but measured no faster)
     constexpr bool THREE = S::SPLIT && NTW == 1;
     static_assert(DV % NCOL == 0, "whole tiles per workgroup");
     static_assert(!C8 || NT2 % 2 == 0, "two groups of whole tiles");

@@ -76,6 +76,35 @@ def test_chunk_and_decode_replay():
     _replays("chunk + decode", run, reset, lambda: [o, hT, st, od], eager)
 
 
+def test_segmented_replay():
+    """A long sequence over few heads takes the segmented state pass (phase 1,
+    the combine of the segment states, phase 3), all inside the captured
+    call; the segment states in the workspace are written before they are
+    read in every call, so replays repeat the eager bits."""
+    import torch
+    T = 256 * 32 + 5
+    w = make_inputs(1, T, 2, 32, 32, dtype="bf16", seed=12, h0_std=0.05)
+    q, k, v = (_t(x, torch.bfloat16) for x in (w.q, w.k, w.v))
+    g_, beta, h0 = _t(w.g), _t(w.beta), _t(w.h0)
+    ws = torch.empty(K.kda_chunk_fwd_workspace_size(1, T, 2, 32, 32, 32, 0, K.BF16),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((1, T, 2, 32), dtype=torch.float32, device="cuda")
+    hT = torch.empty_like(h0)
+
+    def run():
+        K.kda_chunk_fwd(q, k, v, g_, beta, initial_state=h0, final_state=hT, o=o, chunk=32,
+                        workspace=ws)
+
+    def reset():
+        for x in (o, hT):
+            x.fill_(float("nan"))
+    reset()
+    run()
+    torch.cuda.synchronize()
+    eager = [o.clone(), hT.clone()]
+    _replays("segmented", run, reset, lambda: [o, hT], eager)
+
+
 def test_packed_replay():
     import torch
     lengths = make_lengths(9, max_len=200, seed=8, edge=(0, 1, 64, 65))
