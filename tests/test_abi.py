@@ -117,6 +117,21 @@ def test_workspace_size(L):
     assert f(1, 64, 1, 128, 512, 64, 0, 1) == 0
 
 
+def test_workspace_size_of_the_segmented_state_pass(L):
+    """A sequence of 256 or more chunks over few heads runs its state pass in
+    segments; the workspace then holds three sets of per-segment states
+    (entering states, final states from zero, transition matrices) after the
+    chunk records: 8 segments at B1 H2 d128, none below 256 chunks."""
+    f = L.kda_chunk_fwd_workspace_size
+    a = f(1, 64, 1, 128, 128, 64, 0, 1)          # one chunk record
+    assert f(1, 255 * 64, 2, 128, 128, 64, 0, 1) == 2 * 255 * a
+    rec = 2 * 256 * a
+    seg = 3 * 8 * 2 * 128 * 128 * 4
+    assert f(1, 256 * 64, 2, 128, 128, 64, 0, 1) == (rec + 255) // 256 * 256 + seg
+    # d_k != d_v: never segmented
+    assert f(1, 256 * 64, 2, 64, 128, 64, 0, 1) == 2 * 256 * f(1, 64, 1, 64, 128, 64, 0, 1)
+
+
 # ---- packed variable-length batches (host validation only)
 CU = 0x20000          # a 4-byte aligned fake device address of the offsets
 
