@@ -1096,9 +1096,16 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             Frag<OT> wn[KS];         // -W rows 16*we.. (A operand of E)
             PFrag<OT> kr[MHW][KC];   // Kr^T rows 16*mt.. (A operand of the state update)
             f32x4 u[NTW];            // U^T init of E
-            f32x4 gl[MHW];           // exp(G_last) for the state rows
+            float gl;                // exp(G_last) of one state row (see gl_of)
         };
         auto mt_of = [&](int s) { return ALLH ? wr + 4 * s : min(wr + 4 * s, MH - 1); };
+        // The decays exp(G_last) of a wave's state rows are one 4-byte load per
+        // lane (lane l: row l % 16 of state tile (l / 16) % MHW) rather than a
+        // 16-byte load per lane and tile of which every 16 lanes share each
+        // value; each lane takes its four rows of a tile by lane exchange.
+        auto gl_of = [&](size_t rec) {
+            return W.gl[rec * DK + 16 * mt_of((lane >> 4) % MHW) + (lane & 15)];
+        };
         auto load_ops = [&](Ops& P, int cidx) {
             const size_t rec = rec_of(cidx);
             const OT* wn = W.wneg_rec(rec);
@@ -1108,9 +1115,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
                 P.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + tb + n, we, NB, lane));
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) P.wn[ks].load(wn + fragbase(we, ks, KS, lane));
-#pragma unroll
-            for (int s = 0; s < MHW; ++s)
-                P.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
+            P.gl = gl_of(rec);
 #pragma unroll
             for (int s = 0; s < MHW; ++s) {
 #pragma unroll
@@ -1133,6 +1138,13 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
             for (int n = 0; n < NTW; ++n)
                 Q.u[n] = Vec4<float>::load(W.ut + rec * S::U_N + accbase(NT2 * ct + tb + n, we, NB, lane));
+            // this lane's rows 4 gq .. 4 gq + 3 of each state tile
+            f32x4 g4[MHW];
+#pragma unroll
+            for (int s = 0; s < MHW; ++s) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) g4[s][u] = __shfl(P.gl, 16 * s + 4 * gq + u);
+            }
             f32x4 ea[NTW], eb[NTW];
 #pragma unroll
             for (int n = 0; n < NTW; ++n) {
@@ -1169,11 +1181,11 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             for (int s = 0; s < MHW; ++s) {
 #pragma unroll
                 for (int n = 0; n < NTW; ++n) {
-                    if (ALLH || wr + 4 * s < MH) hacc[s][n] *= P.gl[s];
+                    if (ALLH || wr + 4 * s < MH) hacc[s][n] *= g4[s];
                     part[s][n] = zero4();
                 }
-                Q.gl[s] = *reinterpret_cast<const f32x4*>(W.gl + rec * DK + 16 * mt_of(s) + 4 * gq);
             }
+            Q.gl = gl_of(rec);
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
                 PFrag<OT> et[NTW];
