@@ -10,9 +10,14 @@ One step = one pass of the whole hot path over one batch of synthetic input:
 Prints ONE JSON line.  ``value`` is prefill tokens/s; the decode step's state
 GB/s is reported next to it (the metric names both).  Timing uses HIP events
 on the stream the kernels are launched on (torch's current stream), W untimed
-warm-up steps, then exactly K timed steps between device synchronisations.
-Prefill inputs rotate over three resident copies so that they do not sit in
-the 256 MB last-level cache between steps.
+warm-up steps, then exactly K timed steps between device synchronisations:
+the K prefill calls back to back, then the K decode steps.  The prefill time
+is the event interval from the end of the first timed prefill call to the end
+of the last, over K - 1 calls (the first call covers the host's launch lead);
+the decode time is the interval over the K decode steps that follow.  An event
+pair around every call would add the events' own GPU time (~5 us a pair) to
+each measured call.  Prefill inputs rotate over three resident copies so that
+they do not sit in the 256 MB last-level cache between calls.
 
 ``roofline`` is the decode kernel (the step's dominant kernel by time, HBM
 bound); ``roofline_prefill`` is the prefill call (two kernels).  Achieved
@@ -521,23 +526,25 @@ def main():
         decode()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if args.steps < 2:
+        raise SystemExit("bench.py needs --steps >= 2 (the prefill time spans calls 2 .. K)")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record()
+    prefill(0)
+    ev[0].record()
+    for i in range(1, args.steps):
         prefill(i)
-        ev[i][1].record()
+    ev[1].record()
+    for i in range(args.steps):
         decode()
-        ev[i][2].record()
+    ev[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     step_ms = wall * 1e3 / args.steps
 
-    pre_s = pre_ms.mean() / 1e3
-    dec_s = dec_ms.mean() / 1e3
+    pre_s = ev[0].elapsed_time(ev[1]) / (args.steps - 1) / 1e3
+    dec_s = ev[1].elapsed_time(ev[2]) / args.steps / 1e3
     tokens = P["B"] * P["T"]
     pbytes = prefill_bytes(P["B"], P["H"], P["T"], P["D"])
     pflops = prefill_flops(P["B"], P["H"], P["T"], P["D"], P["chunk"])
