@@ -1263,6 +1263,11 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             Frag<OT> qg[KS];         // Qg rows 16*we.. (B operand of o^T)
             PFrag<OT> aq[KC];        // Aqk rows 16*we.. (B operand of o^T)
         };
+        // Aqk is lower triangular: the 32-column fragments right of this
+        // wave's token tile are zero and are neither loaded nor multiplied
+        // (a condition uniform over the wave)
+        const int weu = __builtin_amdgcn_readfirstlane(we);
+        auto aq_live = [&](int ks) { return 32 * ks <= 16 * weu + 15; };
         auto load_ops = [&](Ops& P, int cidx) {
             const size_t rec = rec_of(cidx);
             const OT* qg = W.qg_rec(rec);
@@ -1270,7 +1275,8 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) P.qg[ks].load(qg + fragbase(we, ks, KS, lane));
 #pragma unroll
-            for (int ks = 0; ks < KC; ++ks) P.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
+            for (int ks = 0; ks < KC; ++ks)
+                if (aq_live(ks)) P.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
         };
         auto step = [&](const Ops& P, int cidx, Ops& Q, int nxt) {
             const size_t rec = rec_of(nxt);
@@ -1302,6 +1308,7 @@ chunk_state(const float* h0, float* hT, OUT* __restrict__ o,
             __syncthreads();
 #pragma unroll
             for (int ks = 0; ks < KC; ++ks) {
+                if (!aq_live(ks)) continue;
                 Q.aq[ks] = aq.frag(fragbase(we, ks, KC, lane));
                 if (has_t) {
 #pragma unroll
