@@ -5,7 +5,8 @@
 // order, each token doing decay -> prediction (a reduction over the key
 // dimension) -> residual -> rank-1 write -> read (a second reduction).
 //
-// MI355X mapping: one workgroup of up to 512 threads owns the whole state of
+// MI355X mapping: one workgroup (up to 512 threads for a decode step, 256 for
+// several tokens per sequence; see RecShape) owns the whole state of
 // one (batch, head), so every wave instruction reads and writes whole
 // contiguous rows (a slab split of the columns over two workgroups, with
 // half-rows per instruction, measured 5% slower).  The transposed state
@@ -37,29 +38,36 @@ __device__ __forceinline__ float add_halves(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DK, int DV>
+// Threads per workgroup: up to 512 for a decode step (the state streamed at
+// the HBM rate); up to 256 for several tokens per sequence, whose token steps
+// are a serial chain: with one wave per SIMD and twice the rows per thread, a
+// step issues fewer vector instructions per SIMD (the cross-wave sums of the
+// reductions shrink with the number of waves).
+template <int DK, int DV, bool MULTI>
 struct RecShape {
     static constexpr int DVT = DV > 128 ? 128 : DV; // columns per workgroup
     static constexpr int NCT = DV / DVT;            // workgroups per (b, h)
-    static constexpr int NT = (DK * DVT / 4 < 512) ? DK * DVT / 4 : 512;  // threads
+    static constexpr int NTMAX = MULTI ? 256 : 512;
+    static constexpr int NT = (DK * DVT / 4 < NTMAX) ? DK * DVT / 4 : NTMAX;  // threads
     static constexpr int CX = DVT / 4;       // threads across the slab (float4 each)
     static constexpr int RG = NT / CX;       // row groups
     static constexpr int RPT = DK / RG;      // rows per thread
     static constexpr int NW = NT / 64;       // wavefronts
     static_assert(NT % 64 == 0 && RPT >= 1 && RG * RPT == DK && CX <= 64, "shape");
+    static_assert(NT >= DK && NT >= DVT, "every key channel and value column has a thread");
 };
 
 // MULTI: sequences of more than one token (the next token's inputs are
 // prefetched during the current one); without it every sequence has at most
 // one token (a decode step), and the state's rows are used as they arrive.
 template <int DK, int DV, typename IO, typename OUT, bool MULTI>
-__global__ void __launch_bounds__((RecShape<DK, DV>::NT))
+__global__ void __launch_bounds__((RecShape<DK, DV, MULTI>::NT))
 recurrent_kernel(const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
                  const float* __restrict__ g, const float* __restrict__ beta,
                  float* __restrict__ state, OUT* __restrict__ o,
                  int T, int H, int HQ, float scale, int mode, const int* __restrict__ cu, int pro)
 {
-    using S = RecShape<DK, DV>;
+    using S = RecShape<DK, DV, MULTI>;
     const int bh = blockIdx.x / S::NCT;
     const int c0 = (blockIdx.x - bh * S::NCT) * S::DVT;   // first column of the slab
     const int b = bh / H, h = bh - (bh / H) * H;
@@ -296,7 +304,7 @@ static size_t decode_lds_reserve(size_t static_bytes)
 template <int DK, int DV, typename IO, bool MULTI>
 static hipError_t launch_rec2(const RecArgs& a, hipStream_t s)
 {
-    using S = RecShape<DK, DV>;
+    using S = RecShape<DK, DV, MULTI>;
     size_t dyn = 0;
     if constexpr (!MULTI) {
         // the kernel's own LDS: akq and sv (two buffers each) and the reduction array
