@@ -147,24 +147,28 @@ def test_chunk_varlen_in_place_state_and_empty_batch():
     assert torch.equal(hT, de["h0"])
 
 
-def test_serving_mix_full_size_sampled():
+def test_serving_mix_full_size_every_sequence():
     """64 sequences of log-uniform lengths up to 2048 (H16, d128, bf16), the
-    chunk form and the recurrent form; 8 sampled sequences against the oracle."""
+    chunk form and the recurrent form; every sequence (all heads) against the
+    oracle, the worst printed."""
     lengths = make_lengths(64, max_len=2048, seed=17, edge=(1, 64, 2048))
     vw = make_varlen(lengths, 16, 128, 128, dtype="bf16", seed=17, h0_std=0.02)
     d = _dev(vw)
     say("serving mix", int(vw.cu[-1]), "tokens")
     o_c, h_c = _run_chunk(vw, 64, d)
     o_r, h_r = _run_rec(vw, d)
-    picks = [0, 1, 2, 7, 19, 33, 48, 63]
     w = vw.w
-    for n in picks:
+    worst = {"chunk": (0.0, -1), "recurrent": (0.0, -1)}
+    for n in range(vw.N):
         a, b = int(vw.cu[n]), int(vw.cu[n + 1])
         sl = lambda x: None if x is None else x[0, a:b][None]
         on, hn = oracle.recurrent(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta),
                                   vw.h0[n:n + 1], scale=w.scale, mode=w.mode)
         for tag, o, h in (("chunk", o_c, h_c), ("recurrent", o_r, h_r)):
             eo, eh = rel_err(o[a:b], on[0]), rel_err(h[n], hn[0])
-            print(f"[parity] varlen serving {tag} seq {n} len {b - a} o {eo:.3e} state {eh:.3e}",
-                  flush=True)
+            if b > a:
+                worst[tag] = max(worst[tag], (max(eo, eh), n))
             assert eo <= TOL["bf16"] and eh <= TOL["bf16"], (tag, n, eo, eh)
+    print(f"[parity] varlen serving, all {vw.N} sequences: worst chunk {worst['chunk'][0]:.3e} "
+          f"(seq {worst['chunk'][1]}), recurrent {worst['recurrent'][0]:.3e} "
+          f"(seq {worst['recurrent'][1]})", flush=True)
