@@ -276,7 +276,7 @@ def test_bwd_batch_groups_with_grouped_heads():
     d128 (2 GiB of records per entry) runs as entries {0, 1} and then {2},
     here with two value heads per query/key head, so the second group's
     float partials of dq and dk and their sum land at that entry's offsets.
-    The grouped-head gradient oracle runs on entry 2."""
+    The grouped-head gradient oracle runs on every entry, one at a time."""
     w = make_inputs(3, 8192, 32, 128, 128, mode="channel", dtype="bf16", seed=21, h0_std=0.02)
     q = np.ascontiguousarray(w.q[:, :, ::2])
     k = np.ascontiguousarray(w.k[:, :, ::2])
@@ -285,11 +285,12 @@ def test_bwd_batch_groups_with_grouped_heads():
         K.kda_chunk_bwd_workspace_size(2, 8192, 32, 16, 128, 128, 64, w.mode, K.BF16)
     say("bwd batch groups, grouped heads, B3 H32 T8192")
     got = _run(w, cot, 64, q, k)
-    sl = lambda x: None if x is None else np.ascontiguousarray(x[2:3])
-    ref = oracle.recurrent_grouped_bwd(sl(q), sl(k), sl(w.v), sl(w.g), sl(w.beta), sl(w.h0),
-                                       sl(cot.do), sl(cot.dhT), scale=w.scale, mode=w.mode)
-    sub = {n: None if got[n] is None else sl(got[n]) for n in NAMES}
-    _compare("batch groups, grouped heads, entry 2", sub, ref, TOL["bf16"])
+    for b in range(w.B):
+        sl = lambda x: None if x is None else np.ascontiguousarray(x[b:b + 1])
+        ref = oracle.recurrent_grouped_bwd(sl(q), sl(k), sl(w.v), sl(w.g), sl(w.beta), sl(w.h0),
+                                           sl(cot.do), sl(cot.dhT), scale=w.scale, mode=w.mode)
+        sub = {n: None if got[n] is None else sl(got[n]) for n in NAMES}
+        _compare(f"batch groups, grouped heads, entry {b}", sub, ref, TOL["bf16"])
 
 
 def test_bwd_full_size_prefill_every_head():
